@@ -1,0 +1,72 @@
+"""Number formats the layer's inputs use, decoded from their published bit
+layouts (oracle; test infrastructure only).
+
+The pages name the expert format only as NVFP4, a 4-bit floating point
+format "trained natively at 4 bits" (yodev.dev article, section on what
+Edge0-145B is; Hugging Face card header). They do not define it. The
+definitions below are the OCP ones:
+
+* e2m1 (OCP Microscaling Formats v1.0, FP4 element type): 1 sign bit, 2
+  exponent bits with bias 1, 1 mantissa bit, no infinities or NaN. Exponent
+  field 0 is subnormal: magnitude = mantissa * 2^(1-1) * 0.5.
+* E4M3 (OCP 8-bit Floating Point v1.0, "fn" variant): 1 sign, 4 exponent bits
+  with bias 7, 3 mantissa bits, no infinities; S.1111.111 is NaN. Exponent
+  field 0 is subnormal: magnitude = mantissa/8 * 2^-6.
+* bf16: the upper 16 bits of an IEEE binary32.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def e2m1_value(code) -> np.ndarray:
+    """Value of 4-bit e2m1 codes (low 4 bits of each entry), float64."""
+    c = np.asarray(code).astype(np.int64) & 0xF
+    sign = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = c & 1
+    normal = np.ldexp(1.0 + m / 2.0, (e - 1).astype(np.int32))
+    subnormal = m * 0.5
+    return sign * np.where(e == 0, subnormal, normal)
+
+
+def e4m3fn_value(byte) -> np.ndarray:
+    """Value of E4M3fn bytes, float64 (NaN for S.1111.111)."""
+    b = np.asarray(byte).astype(np.int64) & 0xFF
+    sign = np.where((b >> 7) & 1, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 7
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32))
+    subnormal = np.ldexp(m / 8.0, -6)
+    mag = np.where(e == 0, subnormal, normal)
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def bf16_value(bits) -> np.ndarray:
+    """Value of bf16 bit patterns (uint16), float64."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def unpack_codes(codes: np.ndarray) -> np.ndarray:
+    """[..., n, k/2] packed bytes -> [..., n, k] 4-bit codes; element 2j is the
+    low nibble of byte j, element 2j+1 the high nibble."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = codes & 0xF
+    out[..., 1::2] = codes >> 4
+    return out
+
+
+def dequant_fp4(codes: np.ndarray, scales: np.ndarray, gscale) -> np.ndarray:
+    """One quantised matrix [n][k] -> float64 weights.
+
+    W[n, k] = e2m1(code[n, k]) * e4m3(scale[n, k // 16]) * gscale
+    (two-level NVFP4-style scaling: a block scale per 16 consecutive k of one
+    row, and one fp32 scale for the whole matrix).
+    """
+    q = e2m1_value(unpack_codes(codes))
+    s = e4m3fn_value(scales)
+    s_full = np.repeat(s, 16, axis=-1)
+    return q * s_full * np.float64(np.float32(gscale))

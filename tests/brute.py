@@ -1,0 +1,107 @@
+"""Independent brute-force evaluation of the latent-MoE layer, used to pin the
+oracle. It shares no code with ``oracle/``: the number formats are decoded a
+different way (e2m1 by lookup in the OCP table of magnitudes, E4M3 through
+torch's float8_e4m3fn dtype, bf16 through torch's bfloat16 dtype) and the
+layer runs token by token, expert by expert, with Python loops over rows and
+torch float64 dot products. Only for small shapes."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+# OCP Microscaling Formats v1.0, FP4 E2M1: magnitudes of codes 0..7 (bit 3 is
+# the sign).
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+_E2M1_SIGNED = torch.tensor(E2M1_MAGNITUDES + [-v for v in E2M1_MAGNITUDES],
+                            dtype=torch.float64)
+
+
+def bf16_to_f64(bits: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float64)
+
+
+def e4m3_to_f64(b: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(b, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def fp4_matrix(codes: np.ndarray, scales: np.ndarray, gscale: float) -> torch.Tensor:
+    """[n][k/2] packed codes (low nibble = even column) -> float64 [n][k]."""
+    c = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).to(torch.int64)
+    n, half = c.shape
+    nib = torch.stack([c & 0xF, c >> 4], dim=-1).reshape(n, 2 * half)
+    vals = _E2M1_SIGNED[nib]
+    sc = e4m3_to_f64(scales).repeat_interleave(16, dim=1)
+    return vals * sc * float(gscale)
+
+
+class BruteLayer:
+    def __init__(self, layer):
+        self.layer = layer
+        self._cache = {}
+
+    def expert(self, bank_name: str, e: int):
+        key = (bank_name, e)
+        if key not in self._cache:
+            bank = getattr(self.layer, bank_name)
+            mats = []
+            for proj in ("gate", "up", "down"):
+                m = getattr(bank, proj)
+                mats.append(fp4_matrix(m.codes[e], m.scales[e], float(m.gscale[e])))
+            self._cache[key] = mats
+        return self._cache[key]
+
+
+def silu(v: float) -> float:
+    return v / (1.0 + math.exp(-v))
+
+
+def run_expert(bl: BruteLayer, bank_name: str, e: int, h: torch.Tensor) -> torch.Tensor:
+    wg, wu, wd = bl.expert(bank_name, e)
+    inter = wg.shape[0]
+    a = torch.empty(inter, dtype=torch.float64)
+    for i in range(inter):
+        g = float(torch.dot(wg[i], h))
+        u = float(torch.dot(wu[i], h))
+        a[i] = silu(g) * u
+    return torch.mv(wd, a)
+
+
+def brute_forward(layer, x_bits: np.ndarray = None, x_values=None):
+    """Returns (out [T][hidden] float64, idx [T][k], w [T][k], logits32 [T][E])."""
+    d = layer.dims
+    x = bf16_to_f64(x_bits) if x_values is None else torch.as_tensor(x_values, dtype=torch.float64)
+    D = bf16_to_f64(layer.D)
+    U = bf16_to_f64(layer.U)
+    R = bf16_to_f64(layer.R)
+    b = (torch.zeros(d.n_experts, dtype=torch.float64) if layer.bias is None
+         else torch.from_numpy(np.asarray(layer.bias, dtype=np.float32)).to(torch.float64))
+    bl = BruteLayer(layer)
+    T = x.shape[0]
+    outs, idxs, ws, logits_all = [], [], [], []
+    for t in range(T):
+        h = torch.mv(D, x[t])
+        logits = torch.mv(R, h) + b
+        l32 = logits.to(torch.float32).to(torch.float64).tolist()
+        logits_all.append(l32)
+        order = sorted(range(d.n_experts), key=lambda e: (-l32[e], e))
+        sel = order[: d.top_k]
+        mx = max(l32)
+        ex = [math.exp(v - mx) for v in l32]
+        tot = sum(ex)
+        p = [v / tot for v in ex]
+        ps = sum(p[e] for e in sel)
+        w = [p[e] / ps for e in sel]
+        z = torch.zeros(d.latent, dtype=torch.float64)
+        for j, e in enumerate(sel):
+            z += w[j] * run_expert(bl, "experts", e, h)
+        if d.n_shared:
+            z += run_expert(bl, "shared", 0, h)
+        outs.append(torch.mv(U, z))
+        idxs.append(sel)
+        ws.append(w)
+    return (torch.stack(outs).numpy(), np.array(idxs, dtype=np.int32), np.array(ws),
+            np.array(logits_all))

@@ -1,0 +1,158 @@
+"""Each test plants one plausible mistake in the oracle (CPU only, through
+monkeypatch) and asserts that at least one pin then fails. This shows the pins
+are sharp enough to catch a dropped term, a wrong sign, a wrong index or a
+transposed operand."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.formats as F
+import oracle.latent_moe as M
+import pins
+import synth
+
+
+def _fails(*checks):
+    for chk in checks:
+        try:
+            chk()
+        except Exception:
+            return True
+    return False
+
+
+def _tiny_vs_brute():
+    layers, x = synth.make_config("tiny")
+    pins.check_vs_brute(layers[0], x)
+
+
+def test_swapped_nibbles_caught(monkeypatch):
+    def bad_unpack(codes):
+        codes = np.asarray(codes, dtype=np.uint8)
+        out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.uint8)
+        out[..., 0::2] = codes >> 4
+        out[..., 1::2] = codes & 0xF
+        return out
+    monkeypatch.setattr(F, "unpack_codes", bad_unpack)
+    assert _fails(pins.check_nibble_order)
+    assert _fails(_tiny_vs_brute)
+
+
+def test_e2m1_exponent_bias_caught(monkeypatch):
+    orig = F.e2m1_value
+    monkeypatch.setattr(F, "e2m1_value", lambda c: orig(c) * np.where((np.asarray(c) >> 1) & 3, 2.0, 1.0))
+    monkeypatch.setattr(oracle, "e2m1_value", F.e2m1_value)
+    assert _fails(pins.check_e2m1_table)
+    assert _fails(_tiny_vs_brute)
+
+
+def test_e4m3_subnormal_caught(monkeypatch):
+    orig = F.e4m3fn_value
+    def bad(b):
+        v = orig(b)
+        e = (np.asarray(b).astype(np.int64) >> 3) & 0xF
+        return np.where(e == 0, v * 2.0, v)
+    monkeypatch.setattr(F, "e4m3fn_value", bad)
+    monkeypatch.setattr(oracle, "e4m3fn_value", bad)
+    assert _fails(pins.check_e4m3_vs_torch)
+    assert _fails(pins.check_closed_form_signs_and_subnormal)
+
+
+def test_scale_block_index_caught(monkeypatch):
+    def bad_dequant(codes, scales, gscale):
+        q = F.e2m1_value(F.unpack_codes(codes))
+        s = F.e4m3fn_value(scales)
+        s_full = np.roll(np.repeat(s, 16, axis=-1), 8, axis=-1)  # blocks off by 8
+        return q * s_full * np.float64(np.float32(gscale))
+    monkeypatch.setattr(F, "dequant_fp4", bad_dequant)
+    monkeypatch.setattr(M, "dequant_fp4", bad_dequant)
+    monkeypatch.setattr(oracle, "dequant_fp4", bad_dequant)
+    assert _fails(pins.check_dequant_vs_brute)
+    assert _fails(_tiny_vs_brute)
+
+
+def test_matrix_scale_dropped_caught(monkeypatch):
+    orig = F.dequant_fp4
+    bad = lambda c, s, g: orig(c, s, 1.0)
+    monkeypatch.setattr(M, "dequant_fp4", bad)
+    assert _fails(_tiny_vs_brute)
+
+
+def test_silu_sign_caught(monkeypatch):
+    monkeypatch.setattr(M, "silu", lambda v: v / (1.0 + np.exp(v)))
+    assert _fails(pins.check_closed_form_all_ones)
+    assert _fails(_tiny_vs_brute)
+
+
+def test_silu_on_up_instead_of_gate_caught(monkeypatch):
+    def bad(v, bank, e):
+        wg = M._bank_matrix(bank, "gate", e)
+        wu = M._bank_matrix(bank, "up", e)
+        wd = M._bank_matrix(bank, "down", e)
+        return ((v @ wg.T) * M.silu(v @ wu.T)) @ wd.T
+    monkeypatch.setattr(M, "swiglu_expert", bad)
+    assert _fails(pins.check_closed_form_signs_and_subnormal, _tiny_vs_brute)
+
+
+def test_shared_expert_dropped_caught(monkeypatch):
+    orig = M.forward
+    def bad(layer, *a, **k):
+        d = layer.dims
+        layer2 = synth.replace(layer, dims=synth.replace(d, n_shared=0))
+        return orig(layer2, *a, **k)
+    monkeypatch.setattr(oracle, "forward", bad)
+    assert _fails(pins.check_closed_form_all_ones)
+
+
+def test_no_renormalisation_caught(monkeypatch):
+    orig = M.gate_topk
+    def bad(l32, k):
+        idx, w, gap = orig(l32, k)
+        l64 = np.asarray(l32, np.float64)
+        p = np.exp(l64 - l64.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        return idx, np.take_along_axis(p, idx.astype(np.int64), 1), gap
+    monkeypatch.setattr(M, "gate_topk", bad)
+    monkeypatch.setattr(oracle, "gate_topk", bad)
+    assert _fails(pins.check_gate_vs_torch_topk)
+    assert _fails(pins.check_closed_form_routing)
+
+
+def test_ties_to_higher_index_caught(monkeypatch):
+    def bad(l32, k):
+        l32 = np.asarray(l32, np.float32)
+        T, E = l32.shape
+        order = np.lexsort((-np.broadcast_to(np.arange(E), (T, E)), -l32.astype(np.float64)), axis=-1)
+        idx = order[:, :k].astype(np.int32)
+        l64 = l32.astype(np.float64)
+        p = np.exp(l64 - l64.max(1, keepdims=True))
+        ps = np.take_along_axis(p, idx.astype(np.int64), 1)
+        srt = np.take_along_axis(l64, order, 1)
+        return idx, ps / ps.sum(1, keepdims=True), srt[:, k - 1] - srt[:, k]
+    monkeypatch.setattr(oracle, "gate_topk", bad)
+    assert _fails(pins.check_gate_ties_lower_index)
+
+
+def test_unstable_permutation_caught(monkeypatch):
+    orig = M.route_bookkeeping
+    def bad(idx, E):
+        counts, offsets, perm = orig(idx, E)
+        perm = perm.copy()
+        for e in range(E):
+            perm[offsets[e]:offsets[e + 1]] = perm[offsets[e]:offsets[e + 1]][::-1]
+        return counts, offsets, perm
+    monkeypatch.setattr(oracle, "route_bookkeeping", bad)
+    assert _fails(pins.check_bookkeeping)
+
+
+def test_transposed_projection_caught(monkeypatch):
+    """U applied transposed (only expressible when hidden == latent)."""
+    orig = M.forward
+    monkeypatch.setattr(oracle, "forward",
+                        lambda layer, *a, **k: orig(synth.replace(layer, U=np.ascontiguousarray(layer.U.T)), *a, **k))
+
+    def check():
+        dims = synth.Dims(hidden=64, latent=64, n_experts=8, inter=32, top_k=3, n_shared=1)
+        layer = synth.make_layer(dims, 9)
+        pins.check_vs_brute(layer, synth.make_x(4, 64, 9))
+    assert _fails(check)
