@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of the latent-MoE layer forward on one MI355X.
+
+Headline (the JSON line's ``value``): the 145B-shaped layer at decode /
+speculative-verify size, T = 4 tokens per call (hidden 2560, latent 1792,
+512 experts of SwiGLU width 640 in 4-bit e2m1 + E4M3/16 scales, top-10 + one
+shared expert), in tokens/s. One step is one full layer forward. The weights
+rotate over ``--copies`` copies at distinct HBM addresses (and each copy has
+its own input tokens) so successive steps cannot be served by the 256 MB
+Infinity Cache: one layer call touches ~97 MB.
+
+Secondary (``prefill`` object): the same layer on a 16K-token prefill with a
+Zipf(1.1) router bias, in tokens/s and matrix-core utilisation.
+
+``roofline`` is for the dominant kernel, timed live with HIP events recorded
+on the launch stream around that kernel in every timed step. ``cpu_baseline``
+is the float64 oracle on the host cores, on a bounded sample of the same
+decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix cores
+
+REC_BYTES_CODES = lambda L, I: 3 * L * I // 2 + 3 * L * I // 16   # one expert, codes + block scales
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=8, help="rotating weight copies (decode)")
+    p.add_argument("--path", choices=["auto", "grouped", "decode"], default="auto")
+    p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--prefill-warmup", type=int, default=3)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+def clone_layer(lsm, dl):
+    import dataclasses
+
+    def c(v):
+        if v is None:
+            return None
+        if dataclasses.is_dataclass(v) and not isinstance(v, type):
+            return type(v)(**{f.name: (c(getattr(v, f.name)) if f.name != "dims" else getattr(v, f.name))
+                              for f in dataclasses.fields(v)})
+        return v.clone()
+    return c(dl)
+
+
+def event_pair(torch):
+    """Two timing events whose HIP handles exist (torch creates them lazily
+    on first record), so the library can record them on its stream."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    return a, b
+
+
+def stage_times(lsm, torch, run, stages, n=5):
+    """Average duration (ms) of each stage over n untimed calls."""
+    acc = {s: 0.0 for s in stages}
+    for _ in range(n):
+        ev = {s: event_pair(torch) for s in stages}
+        torch.cuda.synchronize()
+        run(ev)
+        torch.cuda.synchronize()
+        for s, (a, b) in ev.items():
+            acc[s] += a.elapsed_time(b) / n  # ~0 for stages this path does not run
+    return acc
+
+
+def bench_decode(args, torch, lsm, synth, dev):
+    cfg = synth.CONFIGS["decode145"]
+    d, T = cfg.dims, cfg.T
+    t0 = time.time()
+    host = synth.make_layer(d, cfg.seed, cfg.bias, cfg.zipf_s)
+    log(f"[decode] generated layer in {time.time() - t0:.1f}s")
+    base = lsm.DeviceLayer.from_host(host, dev)
+    layers = [base] + [clone_layer(lsm, base) for _ in range(args.copies - 1)]
+    xs_host = [synth.make_x(T, d.hidden, cfg.seed + i) for i in range(args.copies)]
+    xs = [torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev) for x in xs_host]
+    outs = [torch.empty_like(x) for x in xs]
+    ws = lsm.alloc_workspace(d, T, dev)
+    path = {"auto": lsm.PATH_AUTO, "grouped": lsm.PATH_GROUPED, "decode": lsm.PATH_DECODE}[args.path]
+
+    # routing of each copy's tokens (untimed) -> experts touched -> algorithmic bytes
+    n_touched = []
+    for i in range(args.copies):
+        dbg = lsm.RouteDebug.alloc(d, T, dev)
+        lsm.forward(xs[i], layers[i], out=outs[i], workspace=ws, debug=dbg, path=path)
+        torch.cuda.synchronize()
+        n_touched.append(int((dbg.counts > 0).sum().item()))
+    rec = REC_BYTES_CODES(d.latent, d.inter)
+    dense = 2 * d.latent * d.hidden * 2 + d.n_experts * d.latent * 2 + 2 * T * d.hidden * 2
+    layer_bytes = [(n + d.n_shared) * (rec + 12) + dense for n in n_touched]
+    gateup_bytes = [(n + d.n_shared) * (2 * d.inter * d.latent // 2 + 2 * d.inter * d.latent // 16 + 8)
+                    for n in n_touched]
+
+    def step(i, ev=None):
+        c = i % args.copies
+        lsm.forward(xs[c], layers[c], out=outs[c], workspace=ws, path=path, stage_events=ev)
+
+    # which kernel dominates (untimed pass over every stage)
+    names = [s for s in lsm.STAGES if s != "norm"]
+    st = stage_times(lsm, torch, lambda ev: step(0, ev), names)
+    ran = {s: v for s, v in st.items() if v > 1e-4}
+    dom = max(ran, key=ran.get)
+    log(f"[decode] stage ms: " + ", ".join(f"{s}={v * 1e3:.1f}us" for s, v in ran.items()))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [event_pair(torch) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i, {dom: evs[i]})
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    mean_bytes = sum(layer_bytes[i % args.copies] for i in range(args.steps)) / args.steps
+    if dom == "decode":
+        dom_bytes = mean_bytes
+    elif dom == "gateup":
+        dom_bytes = sum(gateup_bytes[i % args.copies] for i in range(args.steps)) / args.steps
+    else:
+        dom_bytes = None
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_bytes else None
+    res = {
+        "tok_s": T * args.steps / (total_ms * 1e-3),
+        "ms_per_step": ms_step,
+        "dominant": dom,
+        "dominant_ms": dom_ms,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS if achieved else None, "traffic": None,
+            "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes,
+        },
+        "detail": {
+            "layer_bytes_per_step": mean_bytes,
+            "layer_GBps": mean_bytes / (ms_step * 1e-3) / 1e9,
+            "layer_frac_of_hbm_peak": mean_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "experts_touched_per_copy": n_touched,
+            "stage_us_untimed_pass": {s: round(v * 1e3, 2) for s, v in ran.items()},
+            "copies": args.copies,
+        },
+        "host": host, "x0": xs_host[0],
+    }
+    return res
+
+
+def bench_prefill(args, torch, lsm, synth, dev):
+    cfg = synth.CONFIGS["prefill145"]
+    d, T = cfg.dims, cfg.T
+    t0 = time.time()
+    host = synth.make_layer(d, cfg.seed, cfg.bias, cfg.zipf_s)
+    log(f"[prefill] generated layer in {time.time() - t0:.1f}s")
+    dl = lsm.DeviceLayer.from_host(host, dev)
+    del host
+    x = torch.from_numpy(synth.make_x(T, d.hidden, cfg.seed).view("int16")).view(torch.bfloat16).to(dev)
+    out = torch.empty_like(x)
+    ws = lsm.alloc_workspace(d, T, dev)
+    P = T * d.top_k
+    rows = P + T * d.n_shared
+    fl = {
+        "dproj": 2.0 * T * d.hidden * d.latent,
+        "router": 2.0 * T * d.latent * d.n_experts,
+        "gateup": 2.0 * rows * d.latent * 2 * d.inter,
+        "down": 2.0 * rows * d.inter * d.latent,
+        "uproj": 2.0 * T * d.latent * d.hidden,
+    }
+    total_flop = sum(fl.values())
+
+    def step(ev=None):
+        lsm.forward(x, dl, out=out, workspace=ws, path=lsm.PATH_GROUPED, stage_events=ev)
+
+    names = [s for s in lsm.STAGES if s not in ("norm", "decode")]
+    st = stage_times(lsm, torch, step, names, n=3)
+    st = {s: v for s, v in st.items() if v > 1e-4}
+    dom = max(st, key=st.get)
+    log(f"[prefill] stage ms: " + ", ".join(f"{s}={v:.3f}" for s, v in st.items()))
+    for _ in range(args.prefill_warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [event_pair(torch) for _ in range(args.prefill_steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.prefill_steps):
+        step({dom: evs[i]})
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.prefill_steps
+    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / args.prefill_steps
+    dom_tf = fl[dom] / (dom_ms * 1e-3) / 1e12 if dom in fl else None
+    layer_tf = total_flop / (ms * 1e-3) / 1e12
+    return {
+        "metric": "16K prefill tokens/s (145B-shaped layer, Zipf router bias)",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+        "steps": args.prefill_steps, "warmup": args.prefill_warmup,
+        "layer_tflops": layer_tf, "layer_frac_of_bf16_peak": layer_tf / BF16_PEAK_TFLOPS,
+        "algorithmic_tflop_per_step": total_flop / 1e12,
+        "roofline": {"bound": "mfma", "achieved": dom_tf, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": dom_tf / BF16_PEAK_TFLOPS if dom_tf else None,
+                     "traffic": None, "kernel": dom},
+        "stage_ms_untimed_pass": {s: round(v, 4) for s, v in st.items()},
+        "config": {"workload": "prefill145", "T": T, "hidden": d.hidden, "latent": d.latent,
+                   "experts": d.n_experts, "inter": d.inter, "top_k": d.top_k,
+                   "shared": d.n_shared, "router_bias": "zipf(1.1)"},
+    }
+
+
+def cpu_baseline(args, host, x0):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(host, x0)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or n >= 200:
+            break
+    T = x0.shape[0]
+    return {"value": T * n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} full decode-layer calls (T={T}) of the float64 oracle, {el:.1f}s; "
+                      f"host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import latent_sparse_moe_amd as lsm
+    import synth
+
+    lsm.load_library()
+    dev = torch.device("cuda:0")
+    dec = bench_decode(args, torch, lsm, synth, dev)
+    host, x0 = dec.pop("host"), dec.pop("x0")
+    torch.cuda.empty_cache()
+    line = {
+        "metric": "latent-MoE layer tokens/sec: decode T=4 (HBM GB/s) and 16K prefill (MFMA %)",
+        "value": dec["tok_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": dec["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode145", "T": 4, "hidden": 2560, "latent": 1792,
+                   "experts": 512, "inter": 640, "top_k": 10, "shared": 1,
+                   "weights": "e2m1 + E4M3/16 + fp32 per matrix",
+                   "rotating_copies": args.copies, "path": args.path},
+        "roofline": dec["roofline"],
+        "decode_detail": dec["detail"],
+    }
+    if not args.no_prefill:
+        del host
+        line["prefill"] = bench_prefill(args, torch, lsm, synth, dev)
+        host = None
+    if not args.no_cpu:
+        if host is None:
+            import synth as _s
+            cfg = _s.CONFIGS["decode145"]
+            host = _s.make_layer(cfg.dims, cfg.seed, cfg.bias, cfg.zipf_s)
+        line["cpu_baseline"] = cpu_baseline(args, host, x0)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * moe_latent.h -- C ABI of the latent mixture-of-experts layer forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes (Hugging Face card "Edge0-145B . Q3_K", section
+ * "Architecture", the paragraph under the architecture table, and its table
+ * rows "Experts" and "Expert pool"; agentspulse tutorial "Edge0-145B hardware
+ * requirements", section "latent MoE architecture"; alphasignal news, table
+ * "Released model variants"):
+ *
+ *   h    = x D^T                   the token is projected down from the
+ *                                  residual width (hidden) to the latent width
+ *   l    = h R^T + b               router logits over all experts
+ *   S, w = top_k(softmax(l))       the router picks k experts per token;
+ *                                  weights renormalised over the chosen k
+ *   z    = sum_j w_j E_{S_j}(h) + E_shared(h)
+ *                                  routed SwiGLU experts latent -> inter ->
+ *                                  latent, plus one shared expert alongside
+ *   out  = z U^T                   the combined result projected back up
+ *
+ *   E_e(v) = W_down,e (silu(W_gate,e v) * (W_up,e v)),  silu(v) = v/(1+e^-v)
+ *
+ * The 145B layer has hidden 2560, latent 1792, 512 experts, inter 640,
+ * top_k 10, one shared expert; the 120B layer has latent 1280.
+ *
+ * Readings where the pages are silent (they name the weight format "NVFP4"
+ * and say the router "picks 10 of 512", nothing more):
+ *   - gating: softmax over every expert's logit, the k largest logits (exact
+ *     ties to the lower index, descending order), weights renormalised over
+ *     the chosen k; no scaling factor, noise, capacity limit or dropping;
+ *   - expert weights: 4-bit e2m1 codes (OCP MX v1.0), one E4M3fn block scale
+ *     (OCP FP8 v1.0) per 16 consecutive input elements of one output row, one
+ *     fp32 scale per matrix:  W[n][k] = e2m1(c[n][k]) * e4m3(s[n][k/16]) * g;
+ *   - one D and one U per layer; the shared expert has weight 1 and the same
+ *     shape and format as a routed expert;
+ *   - the residual block used to stack layers is x + MoE(rmsnorm(x) * g_norm).
+ *
+ * Precision: bf16 matrix-core products with fp32 accumulation. The router
+ * reads the latent vector at (better than) 2^-16 relative precision, so its
+ * logits agree with an fp32 evaluation to about 1e-5; the experts read it
+ * rounded to bf16. Expert activations and combined outputs are bf16 between
+ * kernels; `out` is bf16, rounded to nearest even.
+ *
+ * Layouts (all row-major, innermost index contiguous; "bf16" is the upper
+ * half of an IEEE binary32, passed as uint16_t):
+ *   x, out         bf16 [T][hidden]
+ *   D              bf16 [latent][hidden]
+ *   U              bf16 [hidden][latent]
+ *   router.w       bf16 [n_experts][latent];  router.bias fp32 [n_experts] or NULL
+ *   fp4 matrix set of `count` matrices of shape [N][K]:
+ *     codes  uint8 [count][N][K/2]   element 2j in the low nibble of byte j,
+ *                                    element 2j+1 in the high nibble
+ *     scales uint8 [count][N][K/16]  E4M3fn bits, block b covers k in [16b, 16b+16)
+ *     gscale fp32  [count]
+ *   experts.gate, experts.up: N = inter, K = latent;  experts.down: N = latent,
+ *   K = inter. The shared expert uses the same layout with count 1.
+ *
+ * Ownership: the caller allocates every buffer (device memory) and owns it.
+ * Calls never allocate or free device memory and keep no pointer after they
+ * return; buffers must stay valid until the work enqueued on `stream`
+ * completes. Concurrent calls must not share a workspace.
+ *
+ * Errors: 0 on success, else a negative code. Every argument is validated
+ * before anything is enqueued, so an error return leaves the device
+ * untouched (except MOE_LATENT_EHIP, returned when a launch fails).
+ * moe_latent_last_error() describes the last error of the calling thread.
+ * Faults inside kernels surface at the caller's next synchronisation.
+ */
+#ifndef MOE_LATENT_H
+#define MOE_LATENT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_LATENT_ABI_VERSION 1
+
+#define MOE_LATENT_OK 0
+#define MOE_LATENT_EINVAL (-1)       /* null pointer, bad size, misaligned pointer, aliasing */
+#define MOE_LATENT_EUNSUPPORTED (-2) /* dims outside what the kernels handle */
+#define MOE_LATENT_EWORKSPACE (-3)   /* workspace smaller than moe_latent_workspace_bytes() */
+#define MOE_LATENT_EHIP (-4)         /* a HIP launch failed; message in last_error */
+
+/* Supported dims: hidden, latent, inter positive multiples of 32;
+ * 1 <= n_experts <= 1024; 1 <= top_k <= min(16, n_experts);
+ * n_shared in {0, 1}; T * top_k < 2^31. */
+typedef struct moe_latent_dims {
+  int32_t hidden;    /* residual width (2560) */
+  int32_t latent;    /* latent width (1792 for 145B, 1280 for 120B) */
+  int32_t n_experts; /* routed experts per layer (512) */
+  int32_t inter;     /* SwiGLU width of every expert (640) */
+  int32_t top_k;     /* routed experts per token (10) */
+  int32_t n_shared;  /* shared experts (0 or 1) */
+} moe_latent_dims;
+
+typedef struct moe_fp4_matrix {
+  const uint8_t *codes;  /* [count][N][K/2], 16-byte aligned */
+  const uint8_t *scales; /* [count][N][K/16], 16-byte aligned */
+  const float *gscale;   /* [count] */
+} moe_fp4_matrix;
+
+typedef struct moe_fp4_experts {
+  moe_fp4_matrix gate; /* N = inter,  K = latent */
+  moe_fp4_matrix up;   /* N = inter,  K = latent */
+  moe_fp4_matrix down; /* N = latent, K = inter  */
+  int32_t count;       /* n_experts for the routed set, n_shared for the shared one */
+} moe_fp4_experts;
+
+typedef struct moe_router {
+  const uint16_t *w; /* bf16 [n_experts][latent], 16-byte aligned */
+  const float *bias; /* fp32 [n_experts], or NULL for no bias */
+} moe_router;
+
+/* Optional copies of the routing, written when the pointer is non-NULL
+ * (device memory). Pair p = t * top_k + j is the j-th choice of token t. */
+typedef struct moe_route_debug {
+  int32_t *topk_idx; /* [T][top_k], descending logit order */
+  float *topk_w;     /* [T][top_k], renormalised weights */
+  int32_t *counts;   /* [n_experts] pairs routed to each expert */
+  int32_t *offsets;  /* [n_experts + 1] exclusive prefix sum of counts */
+  int32_t *perm;     /* [T * top_k] pairs grouped by expert, ascending p within one */
+  float *logits;     /* [T][n_experts] router logits (fp32) */
+} moe_route_debug;
+
+/* Execution path: the grouped-GEMM pipeline (any T) or the fused
+ * weight-streaming decode kernel (T <= MOE_LATENT_DECODE_MAX_T). AUTO picks
+ * the fused kernel whenever T allows it. */
+#define MOE_LATENT_PATH_AUTO 0
+#define MOE_LATENT_PATH_GROUPED 1
+#define MOE_LATENT_PATH_DECODE 2
+#define MOE_LATENT_DECODE_MAX_T 16
+
+/* Stages of one call, for optional timing (moe_latent_opts.stage_events). */
+#define MOE_LATENT_STAGE_NORM 0     /* RMSNorm of the residual block */
+#define MOE_LATENT_STAGE_DPROJ 1    /* h = x D^T */
+#define MOE_LATENT_STAGE_ROUTER 2   /* logits = h R^T + b */
+#define MOE_LATENT_STAGE_TOPK 3     /* top-k + renormalised weights */
+#define MOE_LATENT_STAGE_ROUTE 4    /* histogram, prefix sums, permutation */
+#define MOE_LATENT_STAGE_GATEUP 5   /* grouped gate/up GEMM + SiLU*mul */
+#define MOE_LATENT_STAGE_DOWN 6     /* grouped down GEMM */
+#define MOE_LATENT_STAGE_COMBINE 7  /* weighted combine */
+#define MOE_LATENT_STAGE_UPROJ 8    /* out = z U^T (+ residual) */
+#define MOE_LATENT_STAGE_DECODE 9   /* the fused decode kernel (whole layer) */
+#define MOE_LATENT_N_STAGES 10
+
+typedef struct moe_latent_opts {
+  int32_t path;             /* MOE_LATENT_PATH_* */
+  int32_t residual;         /* 1: out = x + MoE(rmsnorm(x) * norm_weight) */
+  const float *norm_weight; /* fp32 [hidden], required when residual = 1 */
+  float norm_eps;           /* RMSNorm epsilon (e.g. 1e-6) */
+  /* NULL, or 2 * MOE_LATENT_N_STAGES hipEvent_t created by the caller:
+   * entries 2s and 2s+1 (when non-NULL) are recorded on `stream` just
+   * before and just after stage s's kernels. Stages a path does not run
+   * leave their events untouched. */
+  void *const *stage_events;
+} moe_latent_opts;
+
+/* Device bytes of scratch one call needs for `T` tokens (the maximum over
+ * paths, so any path runs with it). Returns 0 for invalid dims or T <= 0. */
+size_t moe_latent_workspace_bytes(const moe_latent_dims *dims, int64_t T);
+
+/* The layer forward for T tokens: out = MoE(x). Enqueues every kernel on
+ * `stream` (a hipStream_t; NULL = the null stream) and returns without
+ * synchronising. T = 0 returns 0 and enqueues nothing once dims and opts
+ * are valid (the buffers may then be NULL). `shared` may be NULL
+ * only when dims->n_shared = 0. `out` must not overlap `x`. `workspace` is
+ * device memory of at least moe_latent_workspace_bytes(dims, T) bytes,
+ * 256-byte aligned; its contents need not be initialised. `debug` may be
+ * NULL. */
+int moe_latent_forward(const moe_latent_dims *dims, int64_t T, const void *x, const void *D,
+                       const void *U, const moe_router *router,
+                       const moe_fp4_experts *experts, const moe_fp4_experts *shared,
+                       void *out, void *workspace, size_t workspace_bytes,
+                       moe_route_debug *debug, void *stream);
+
+/* As moe_latent_forward, with options (NULL = defaults: AUTO path, no
+ * residual). With opts->residual = 1 this is the residual block
+ * out = x + MoE(rmsnorm(x) * norm_weight): the RMSNorm runs in fp32 and its
+ * result is rounded to bf16 before D; the residual add is fp32, then rounded. */
+int moe_latent_forward_ex(const moe_latent_dims *dims, int64_t T, const void *x, const void *D,
+                          const void *U, const moe_router *router,
+                          const moe_fp4_experts *experts, const moe_fp4_experts *shared,
+                          void *out, void *workspace, size_t workspace_bytes,
+                          moe_route_debug *debug, const moe_latent_opts *opts, void *stream);
+
+/* Human-readable description of the last non-zero return on this thread
+ * ("" if none). The pointer stays valid until the next call on the thread. */
+const char *moe_latent_last_error(void);
+
+/* MOE_LATENT_ABI_VERSION of the library. */
+int moe_latent_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LATENT_H */

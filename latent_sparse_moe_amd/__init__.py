@@ -1,0 +1,246 @@
+"""Python binding of the latent-MoE layer library (``include/moe_latent.h``).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``_lib/libmoe_latent.so``. PyTorch provides device memory and the stream.
+There is no fallback: if the library is missing, loading raises.
+
+    layer = DeviceLayer.from_host(host_layer, device)     # weights to HBM
+    out = forward(x, layer)                                # x: bf16 [T][hidden] on device
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libmoe_latent.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+PATH_AUTO, PATH_GROUPED, PATH_DECODE = 0, 1, 2
+DECODE_MAX_T = 16
+
+c_i32, c_i64, c_size, c_vp, c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+
+class CDims(ctypes.Structure):
+    _fields_ = [("hidden", c_i32), ("latent", c_i32), ("n_experts", c_i32), ("inter", c_i32),
+                ("top_k", c_i32), ("n_shared", c_i32)]
+
+
+class CFp4Matrix(ctypes.Structure):
+    _fields_ = [("codes", c_vp), ("scales", c_vp), ("gscale", c_vp)]
+
+
+class CFp4Experts(ctypes.Structure):
+    _fields_ = [("gate", CFp4Matrix), ("up", CFp4Matrix), ("down", CFp4Matrix), ("count", c_i32)]
+
+
+class CRouter(ctypes.Structure):
+    _fields_ = [("w", c_vp), ("bias", c_vp)]
+
+
+class CRouteDebug(ctypes.Structure):
+    _fields_ = [("topk_idx", c_vp), ("topk_w", c_vp), ("counts", c_vp), ("offsets", c_vp),
+                ("perm", c_vp), ("logits", c_vp)]
+
+
+class COpts(ctypes.Structure):
+    _fields_ = [("path", c_i32), ("residual", c_i32), ("norm_weight", c_vp), ("norm_eps", c_f32),
+                ("stage_events", ctypes.POINTER(c_vp))]
+
+
+STAGES = ("norm", "dproj", "router", "topk", "route", "gateup", "down", "combine", "uproj",
+          "decode")
+N_STAGES = len(STAGES)
+
+
+EXPORTS = ("moe_latent_forward", "moe_latent_forward_ex", "moe_latent_workspace_bytes",
+           "moe_latent_last_error", "moe_latent_version")
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with latent_sparse_moe_amd/build.py "
+                           "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    fwd_args = [P(CDims), c_i64, c_vp, c_vp, c_vp, P(CRouter), P(CFp4Experts), P(CFp4Experts),
+                c_vp, c_vp, c_size, P(CRouteDebug)]
+    lib.moe_latent_forward.argtypes = fwd_args + [c_vp]
+    lib.moe_latent_forward.restype = ctypes.c_int
+    lib.moe_latent_forward_ex.argtypes = fwd_args + [P(COpts), c_vp]
+    lib.moe_latent_forward_ex.restype = ctypes.c_int
+    lib.moe_latent_workspace_bytes.argtypes = [P(CDims), c_i64]
+    lib.moe_latent_workspace_bytes.restype = c_size
+    lib.moe_latent_last_error.argtypes = []
+    lib.moe_latent_last_error.restype = ctypes.c_char_p
+    lib.moe_latent_version.argtypes = []
+    lib.moe_latent_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+class MoeLatentError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"moe_latent error {code}: {msg}")
+        self.code = code
+
+
+def _dims(d) -> CDims:
+    return CDims(d.hidden, d.latent, d.n_experts, d.inter, d.top_k, d.n_shared)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+@dataclass
+class DeviceFp4:
+    codes: torch.Tensor   # uint8 [count][N][K/2]
+    scales: torch.Tensor  # uint8 [count][N][K/16]
+    gscale: torch.Tensor  # float32 [count]
+
+    def c(self) -> CFp4Matrix:
+        return CFp4Matrix(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr())
+
+
+@dataclass
+class DeviceExperts:
+    gate: DeviceFp4
+    up: DeviceFp4
+    down: DeviceFp4
+
+    @property
+    def count(self) -> int:
+        return self.gate.codes.shape[0]
+
+    def c(self) -> CFp4Experts:
+        return CFp4Experts(self.gate.c(), self.up.c(), self.down.c(), self.count)
+
+
+@dataclass
+class DeviceLayer:
+    """One layer's weights in device memory, laid out as moe_latent.h describes."""
+    dims: object
+    D: torch.Tensor                 # bf16 [latent][hidden]
+    U: torch.Tensor                 # bf16 [hidden][latent]
+    R: torch.Tensor                 # bf16 [n_experts][latent]
+    bias: Optional[torch.Tensor]    # float32 [n_experts]
+    experts: DeviceExperts
+    shared: Optional[DeviceExperts]
+    norm_w: Optional[torch.Tensor] = None  # float32 [hidden]
+
+    @staticmethod
+    def from_host(h, device) -> "DeviceLayer":
+        """Copy a host layer (numpy: bf16 as uint16 bits, fp4 codes/scales as
+        uint8, scales fp32) to ``device``."""
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+        def u8(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+        def f32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+        def bank(b):
+            if b is None:
+                return None
+            return DeviceExperts(*[DeviceFp4(u8(getattr(b, p).codes), u8(getattr(b, p).scales),
+                                             f32(getattr(b, p).gscale)) for p in ("gate", "up", "down")])
+
+        return DeviceLayer(dims=h.dims, D=bf16(h.D), U=bf16(h.U), R=bf16(h.R),
+                           bias=None if h.bias is None else f32(h.bias),
+                           experts=bank(h.experts), shared=bank(h.shared),
+                           norm_w=None if getattr(h, "norm_w", None) is None else f32(h.norm_w))
+
+
+def workspace_bytes(dims, T: int) -> int:
+    return int(load_library().moe_latent_workspace_bytes(ctypes.byref(_dims(dims)), int(T)))
+
+
+def alloc_workspace(dims, T: int, device) -> torch.Tensor:
+    n = workspace_bytes(dims, T)
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class RouteDebug:
+    topk_idx: torch.Tensor
+    topk_w: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    perm: torch.Tensor
+    logits: torch.Tensor
+
+    @staticmethod
+    def alloc(dims, T: int, device) -> "RouteDebug":
+        k, E = dims.top_k, dims.n_experts
+        i32 = dict(dtype=torch.int32, device=device)
+        return RouteDebug(torch.empty((T, k), **i32), torch.empty((T, k), dtype=torch.float32, device=device),
+                          torch.empty((E,), **i32), torch.empty((E + 1,), **i32),
+                          torch.empty((T * k,), **i32),
+                          torch.empty((T, E), dtype=torch.float32, device=device))
+
+    def c(self) -> CRouteDebug:
+        return CRouteDebug(*[getattr(self, f).data_ptr() for f, _ in CRouteDebug._fields_])
+
+
+def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, debug: Optional[RouteDebug] = None,
+            path: int = PATH_AUTO, residual: bool = False, norm_eps: float = 1e-6,
+            stream: Optional[torch.cuda.Stream] = None, stage_events=None) -> torch.Tensor:
+    """out = MoE(x) (or x + MoE(rmsnorm(x) * norm_w) with residual=True),
+    enqueued on ``stream`` (default: torch's current stream).
+
+    ``stage_events``: optional dict {stage name: (start, end)} of
+    torch.cuda.Event(enable_timing=True), recorded around that stage's
+    kernels on ``stream``."""
+    lib = load_library()
+    d = layer.dims
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None and T > 0:
+        workspace = alloc_workspace(d, T, x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    router = CRouter(layer.R.data_ptr(), _ptr(layer.bias))
+    ex = layer.experts.c()
+    sh = layer.shared.c() if layer.shared is not None else None
+    ev_arr = None
+    if stage_events:
+        ev_arr = (c_vp * (2 * N_STAGES))()
+        for name, (a, b) in stage_events.items():
+            i = STAGES.index(name)
+            ev_arr[2 * i] = a.cuda_event
+            ev_arr[2 * i + 1] = b.cuda_event
+    opts = COpts(path, 1 if residual else 0, _ptr(layer.norm_w) if residual else None, norm_eps,
+                 ev_arr)
+    dbg = debug.c() if debug is not None else None
+    rc = lib.moe_latent_forward_ex(
+        ctypes.byref(_dims(d)), T, x.data_ptr(), layer.D.data_ptr(), layer.U.data_ptr(),
+        ctypes.byref(router), ctypes.byref(ex), ctypes.byref(sh) if sh is not None else None,
+        out.data_ptr(), workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0,
+        ctypes.byref(dbg) if dbg is not None else None, ctypes.byref(opts), stream.cuda_stream)
+    if rc != 0:
+        raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
+    return out
+
+
+__all__ = ["load_library", "DeviceLayer", "DeviceExperts", "DeviceFp4", "RouteDebug", "forward",
+           "workspace_bytes", "alloc_workspace", "MoeLatentError", "EXPORTS",
+           "PATH_AUTO", "PATH_GROUPED", "PATH_DECODE", "DECODE_MAX_T", "STAGES"]

@@ -1,0 +1,115 @@
+// Device helpers shared by the latent-MoE kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even (the hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// 32x32x16 bf16 matrix-core product, fp32 accumulate. Operand lane layout:
+// lane l holds A[l%32][(l/32)*8 + i] and B[(l/32)*8 + i][l%32], i = 0..7;
+// result register r of lane l is C[(r/4)*8 + (l/32)*4 + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 bf16: lane l holds A[l%16][(l/16)*8 + i], B[(l/16)*8 + i][l%16];
+// result register r of lane l is C[(l/16)*4 + r][l%16].
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// OCP E4M3fn byte -> float (gfx950 converts the OCP encoding natively).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8(byte, 0);
+}
+
+// Eight e2m1 codes (one dword: byte j holds element 2j in its low nibble and
+// 2j+1 in its high nibble) times the block scale s -> eight bf16 in element
+// order. e2m1 * E4M3 needs at most 6 significant bits, so the products are
+// exact in fp32 and in bf16: nothing is rounded here.
+//
+// The scaled fp4 conversions of gfx950 apply only the exponent of their f32
+// scale operand (the MX convention of power-of-two block scales), so they are
+// used with scale 1.0 and the E4M3 block scale is applied by an fp32 multiply.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float s) {
+  const f32x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const f32x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const f32x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const f32x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  bf16x8 r;
+  r[0] = (__bf16)(q0[0] * s); r[1] = (__bf16)(q0[1] * s);
+  r[2] = (__bf16)(q1[0] * s); r[3] = (__bf16)(q1[1] * s);
+  r[4] = (__bf16)(q2[0] * s); r[5] = (__bf16)(q2[1] * s);
+  r[6] = (__bf16)(q3[0] * s); r[7] = (__bf16)(q3[1] * s);
+  return r;
+}
+
+// Eight e2m1 codes -> their plain values as bf16 (exact; no block scale).
+__device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t codes) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+template <class T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Inclusive prefix sum across the wave (lane order).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int u = __shfl_up(v, d, kWave);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace moe

@@ -1,0 +1,80 @@
+// Kernel-side views and launcher declarations of the latent-MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// One set of quantised matrices [count][N][K] (see include/moe_latent.h).
+struct Fp4Mat {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gscale;
+};
+
+struct Fp4Set {
+  Fp4Mat gate, up, down;
+};
+
+// Routed experts and the shared expert. Grouped kernels number the groups
+// 0..n_experts-1 (routed) and n_experts (shared, when present).
+struct ExpertsView {
+  Fp4Set routed;
+  Fp4Set shared;
+};
+
+// Routing as the grouped GEMMs consume it. Rows of the permuted activation
+// matrices: [0, pairs) are the routed (token, choice) pairs grouped by expert,
+// [pairs, pairs + T) the shared expert's rows (token t at pairs + t).
+struct RouteView {
+  const int* tile_off;  // [n_groups + 1] exclusive prefix of ceil(count_g / 128)
+  const int* off;       // [n_groups + 1] first permuted row of each group
+  const int* perm;      // [pairs] pair index at each permuted row
+  int n_experts;
+  int n_shared;
+  int pairs;  // T * top_k
+  int top_k;
+};
+
+enum { kEpiSplit = 0, kEpiLogits = 1, kEpiOut = 2 };
+
+struct DenseEpilogue {
+  void* out;
+  int ldo;
+  int lo_off;              // kEpiSplit: column offset of the lo half
+  const float* bias;       // kEpiLogits: [N] or null
+  const uint16_t* resid;   // kEpiOut: bf16 [M][ldr] added before rounding, or null
+  int ldr;
+};
+
+hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t* B, int ldb,
+                             int kwrap, int M, int N, int K, const DenseEpilogue& ep,
+                             hipStream_t stream);
+hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& rv,
+                                const ExpertsView& ex, uint16_t* act, int inter, int latent,
+                                int max_mtiles, hipStream_t stream);
+hipError_t launch_expert_down(const uint16_t* act, const RouteView& rv, const ExpertsView& ex,
+                              uint16_t* y, int inter, int latent, int max_mtiles,
+                              hipStream_t stream);
+
+// Routing bookkeeping (route.hip).
+constexpr int kRouteChunk = 4096;  // pairs per histogram / permute chunk
+constexpr int kMaxExperts = 1024;
+
+hipError_t launch_rmsnorm(const uint16_t* x, const float* w, float eps, uint16_t* u, int T,
+                          int hidden, hipStream_t stream);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                       hipStream_t stream);
+hipError_t launch_route_hist(const int32_t* idx, int pairs, int E, int32_t* chunk_hist,
+                             hipStream_t stream);
+hipError_t launch_route_scan(int32_t* chunk_hist, int n_chunks, int E, int pairs, int T,
+                             int n_shared, int32_t* counts, int32_t* off, int32_t* tile_off,
+                             hipStream_t stream);
+hipError_t launch_route_permute(const int32_t* idx, int pairs, int E,
+                                const int32_t* chunk_base, int32_t* perm, int32_t* slot,
+                                hipStream_t stream);
+hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w, int T, int k,
+                          int pairs, int latent, int n_shared, uint16_t* z, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,309 @@
+// Host side of the latent-MoE layer library: argument validation, workspace
+// layout and the launch sequence (see include/moe_latent.h for the contract).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "kernels.hpp"
+#include "moe_latent.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Byte offsets of the scratch buffers inside the workspace.
+struct Layout {
+  size_t u;         // bf16 [T][hidden]       RMSNorm output (residual block)
+  size_t hcat;      // bf16 [T][2*latent]     latent vector: hi | lo halves
+  size_t logits;    // fp32 [T][E]
+  size_t idx;       // int32 [T][k]
+  size_t w;         // fp32 [T][k]
+  size_t chunk;     // int32 [n_chunks][E]    per-chunk histogram, then chunk bases
+  size_t counts;    // int32 [E]
+  size_t off;       // int32 [E + 2]
+  size_t tile_off;  // int32 [E + 2]
+  size_t perm;      // int32 [P]
+  size_t slot;      // int32 [P]
+  size_t act;       // bf16 [P + T*n_shared][inter]
+  size_t y;         // bf16 [P + T*n_shared][latent]
+  size_t z;         // bf16 [T][latent]
+  size_t total;
+};
+
+Layout layout_of(const moe_latent_dims& d, int64_t T) {
+  const int64_t P = T * d.top_k;
+  const int64_t nch = (P + moe::kRouteChunk - 1) / moe::kRouteChunk;
+  const int64_t rows = P + T * d.n_shared;
+  Layout L;
+  size_t at = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t o = at;
+    at = align256(at + (size_t)bytes);
+    return o;
+  };
+  L.u = take(T * d.hidden * 2);
+  L.hcat = take(T * 2 * d.latent * 2);
+  L.logits = take(T * d.n_experts * 4);
+  L.idx = take(P * 4);
+  L.w = take(P * 4);
+  L.chunk = take(nch * d.n_experts * 4);
+  L.counts = take(d.n_experts * 4);
+  L.off = take((d.n_experts + 2) * 4);
+  L.tile_off = take((d.n_experts + 2) * 4);
+  L.perm = take(P * 4);
+  L.slot = take(P * 4);
+  L.act = take(rows * d.inter * 2);
+  L.y = take(rows * d.latent * 2);
+  L.z = take(T * d.latent * 2);
+  L.total = at;
+  return L;
+}
+
+int check_dims(const moe_latent_dims* d) {
+  if (!d) return fail(MOE_LATENT_EINVAL, "dims is NULL");
+  if (d->hidden <= 0 || d->latent <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0)
+    return fail(MOE_LATENT_EINVAL, "dims must be positive (hidden %d latent %d inter %d experts %d top_k %d)",
+                d->hidden, d->latent, d->inter, d->n_experts, d->top_k);
+  if (d->hidden % 32 || d->latent % 32 || d->inter % 32)
+    return fail(MOE_LATENT_EUNSUPPORTED, "hidden, latent and inter must be multiples of 32 (%d, %d, %d)",
+                d->hidden, d->latent, d->inter);
+  if (d->n_experts > moe::kMaxExperts)
+    return fail(MOE_LATENT_EUNSUPPORTED, "n_experts %d > %d", d->n_experts, moe::kMaxExperts);
+  if (d->top_k > 16 || d->top_k > d->n_experts)
+    return fail(MOE_LATENT_EUNSUPPORTED, "top_k %d must be <= 16 and <= n_experts %d", d->top_k,
+                d->n_experts);
+  if (d->n_shared != 0 && d->n_shared != 1)
+    return fail(MOE_LATENT_EUNSUPPORTED, "n_shared must be 0 or 1 (got %d)", d->n_shared);
+  return 0;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_set(const moe_fp4_experts* s, const char* name, int count) {
+  if (!s) return fail(MOE_LATENT_EINVAL, "%s is NULL", name);
+  if (s->count != count)
+    return fail(MOE_LATENT_EINVAL, "%s->count is %d, expected %d", name, s->count, count);
+  const moe_fp4_matrix* m[3] = {&s->gate, &s->up, &s->down};
+  const char* mn[3] = {"gate", "up", "down"};
+  for (int i = 0; i < 3; ++i) {
+    if (!m[i]->codes || !m[i]->scales || !m[i]->gscale)
+      return fail(MOE_LATENT_EINVAL, "%s->%s has a NULL pointer", name, mn[i]);
+    if (!aligned(m[i]->codes, 16) || !aligned(m[i]->scales, 16) || !aligned(m[i]->gscale, 4))
+      return fail(MOE_LATENT_EINVAL, "%s->%s: codes and scales must be 16-byte aligned", name, mn[i]);
+  }
+  return 0;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+moe::Fp4Set to_set(const moe_fp4_experts* s) {
+  moe::Fp4Set r;
+  r.gate = {s->gate.codes, s->gate.scales, s->gate.gscale};
+  r.up = {s->up.codes, s->up.scales, s->up.gscale};
+  r.down = {s->down.codes, s->down.scales, s->down.gscale};
+  return r;
+}
+
+// Records stage_events[2*stage + end] on the stream when the caller asked.
+struct StageMarks {
+  void* const* ev;
+  hipStream_t st;
+  hipError_t mark(int stage, int end) const {
+    if (!ev) return hipSuccess;
+    void* e = ev[2 * stage + end];
+    return e ? hipEventRecord((hipEvent_t)e, st) : hipSuccess;
+  }
+};
+
+#define HIP_TRY(expr)                                                                 \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(MOE_LATENT_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));    \
+  } while (0)
+
+int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_t* D,
+                const uint16_t* U, const moe_router* router, const moe_fp4_experts* experts,
+                const moe_fp4_experts* shared, uint16_t* out, char* ws, const Layout& L,
+                moe_route_debug* dbg, const moe_latent_opts& o, hipStream_t st) {
+  const int H = d.hidden, Lat = d.latent, E = d.n_experts, I = d.inter, k = d.top_k;
+  const int P = T * k;
+  const int nch = (P + moe::kRouteChunk - 1) / moe::kRouteChunk;
+  uint16_t* u = (uint16_t*)(ws + L.u);
+  uint16_t* hcat = (uint16_t*)(ws + L.hcat);
+  float* logits = (float*)(ws + L.logits);
+  int32_t* idx = (int32_t*)(ws + L.idx);
+  float* w = (float*)(ws + L.w);
+  int32_t* chunk = (int32_t*)(ws + L.chunk);
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* off = (int32_t*)(ws + L.off);
+  int32_t* tile_off = (int32_t*)(ws + L.tile_off);
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  int32_t* slot = (int32_t*)(ws + L.slot);
+  uint16_t* act = (uint16_t*)(ws + L.act);
+  uint16_t* y = (uint16_t*)(ws + L.y);
+  uint16_t* z = (uint16_t*)(ws + L.z);
+
+  const StageMarks sm{o.stage_events, st};
+  // S0 (residual block only): pre-norm.
+  const uint16_t* a_in = x;
+  if (o.residual) {
+    HIP_TRY(sm.mark(MOE_LATENT_STAGE_NORM, 0));
+    HIP_TRY(moe::launch_rmsnorm(x, o.norm_weight, o.norm_eps, u, T, H, st));
+    HIP_TRY(sm.mark(MOE_LATENT_STAGE_NORM, 1));
+    a_in = u;
+  }
+  // S1: h = x D^T, stored as bf16 hi | lo.
+  moe::DenseEpilogue ep{};
+  ep.out = hcat;
+  ep.ldo = 2 * Lat;
+  ep.lo_off = Lat;
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_DPROJ, 0));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiSplit, a_in, H, D, H, H, T, Lat, H, ep, st));
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_DPROJ, 1));
+  // S2: logits = (hi + lo) R^T + b, as a GEMM over K = 2*latent with R read twice.
+  ep = moe::DenseEpilogue{};
+  ep.out = logits;
+  ep.ldo = E;
+  ep.bias = router->bias;
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_ROUTER, 0));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiLogits, hcat, 2 * Lat, router->w, Lat, Lat, T, E,
+                                 2 * Lat, ep, st));
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_ROUTER, 1));
+  // S3: top-k + renormalised softmax weights.
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_TOPK, 0));
+  HIP_TRY(moe::launch_topk(logits, T, E, k, idx, w, st));
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_TOPK, 1));
+  // S4-S6: histogram, prefix sums, stable permutation.
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_ROUTE, 0));
+  HIP_TRY(moe::launch_route_hist(idx, P, E, chunk, st));
+  HIP_TRY(moe::launch_route_scan(chunk, nch, E, P, T, d.n_shared, counts, off, tile_off, st));
+  HIP_TRY(moe::launch_route_permute(idx, P, E, chunk, perm, slot, st));
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_ROUTE, 1));
+  // S7-S9: grouped expert GEMMs (routed groups, then the shared expert).
+  moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k};
+  moe::ExpertsView ex{};
+  ex.routed = to_set(experts);
+  if (d.n_shared) ex.shared = to_set(shared);
+  const int max_mtiles = (P + 127) / 128 + (E < P ? E : P) + d.n_shared * ((T + 127) / 128);
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_GATEUP, 0));
+  HIP_TRY(moe::launch_expert_gateup(hcat, 2 * Lat, rv, ex, act, I, Lat, max_mtiles, st));
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_GATEUP, 1));
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_DOWN, 0));
+  HIP_TRY(moe::launch_expert_down(act, rv, ex, y, I, Lat, max_mtiles, st));
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_DOWN, 1));
+  // S10: weighted combine in fixed order.
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_COMBINE, 0));
+  HIP_TRY(moe::launch_combine(y, slot, w, T, k, P, Lat, d.n_shared, z, st));
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_COMBINE, 1));
+  // S11: out = z U^T (+ x for the residual block).
+  ep = moe::DenseEpilogue{};
+  ep.out = out;
+  ep.ldo = H;
+  if (o.residual) {
+    ep.resid = x;
+    ep.ldr = H;
+  }
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_UPROJ, 0));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiOut, z, Lat, U, Lat, Lat, T, H, Lat, ep, st));
+  HIP_TRY(sm.mark(MOE_LATENT_STAGE_UPROJ, 1));
+
+  if (dbg) {
+    if (dbg->topk_idx) HIP_TRY(hipMemcpyAsync(dbg->topk_idx, idx, (size_t)P * 4, hipMemcpyDeviceToDevice, st));
+    if (dbg->topk_w) HIP_TRY(hipMemcpyAsync(dbg->topk_w, w, (size_t)P * 4, hipMemcpyDeviceToDevice, st));
+    if (dbg->counts) HIP_TRY(hipMemcpyAsync(dbg->counts, counts, (size_t)E * 4, hipMemcpyDeviceToDevice, st));
+    if (dbg->offsets) HIP_TRY(hipMemcpyAsync(dbg->offsets, off, (size_t)(E + 1) * 4, hipMemcpyDeviceToDevice, st));
+    if (dbg->perm) HIP_TRY(hipMemcpyAsync(dbg->perm, perm, (size_t)P * 4, hipMemcpyDeviceToDevice, st));
+    if (dbg->logits) HIP_TRY(hipMemcpyAsync(dbg->logits, logits, (size_t)T * E * 4, hipMemcpyDeviceToDevice, st));
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_latent_version(void) { return MOE_LATENT_ABI_VERSION; }
+
+const char* moe_latent_last_error(void) { return g_err.c_str(); }
+
+size_t moe_latent_workspace_bytes(const moe_latent_dims* dims, int64_t T) {
+  if (check_dims(dims) != 0 || T <= 0) return 0;
+  if (T * dims->top_k >= ((int64_t)1 << 31)) return 0;
+  return layout_of(*dims, T).total;
+}
+
+int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x, const void* D,
+                          const void* U, const moe_router* router,
+                          const moe_fp4_experts* experts, const moe_fp4_experts* shared,
+                          void* out, void* workspace, size_t workspace_bytes,
+                          moe_route_debug* debug, const moe_latent_opts* opts, void* stream) {
+  g_err.clear();
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  const moe_latent_dims& d = *dims;
+  if (T < 0) return fail(MOE_LATENT_EINVAL, "T must be >= 0 (got %lld)", (long long)T);
+  if (T * d.top_k >= ((int64_t)1 << 31))
+    return fail(MOE_LATENT_EUNSUPPORTED, "T * top_k must be < 2^31");
+  moe_latent_opts o{};
+  if (opts) o = *opts;
+  if (o.path < MOE_LATENT_PATH_AUTO || o.path > MOE_LATENT_PATH_DECODE)
+    return fail(MOE_LATENT_EINVAL, "unknown path %d", o.path);
+  if (o.path == MOE_LATENT_PATH_DECODE && T > MOE_LATENT_DECODE_MAX_T)
+    return fail(MOE_LATENT_EUNSUPPORTED, "the decode path takes T <= %d (got %lld)",
+                MOE_LATENT_DECODE_MAX_T, (long long)T);
+  if (T == 0) return 0;  // nothing to do; buffers may be empty (NULL)
+  if (!x || !D || !U || !out) return fail(MOE_LATENT_EINVAL, "x, D, U and out must be non-NULL");
+  if (!aligned(x, 16) || !aligned(D, 16) || !aligned(U, 16) || !aligned(out, 16))
+    return fail(MOE_LATENT_EINVAL, "x, D, U and out must be 16-byte aligned");
+  if (!router || !router->w) return fail(MOE_LATENT_EINVAL, "router and router->w must be non-NULL");
+  if (!aligned(router->w, 16) || (router->bias && !aligned(router->bias, 4)))
+    return fail(MOE_LATENT_EINVAL, "router->w must be 16-byte aligned");
+  if ((rc = check_set(experts, "experts", d.n_experts))) return rc;
+  if (d.n_shared && (rc = check_set(shared, "shared", d.n_shared))) return rc;
+  if (o.residual) {
+    if (!o.norm_weight) return fail(MOE_LATENT_EINVAL, "residual block needs norm_weight");
+    if (!(o.norm_eps >= 0.0f)) return fail(MOE_LATENT_EINVAL, "norm_eps must be >= 0");
+  }
+  const size_t xbytes = (size_t)T * d.hidden * 2;
+  if (overlaps(x, xbytes, out, xbytes)) return fail(MOE_LATENT_EINVAL, "out overlaps x");
+  const Layout L = layout_of(d, T);
+  if (!workspace) return fail(MOE_LATENT_EINVAL, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(MOE_LATENT_EINVAL, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(MOE_LATENT_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  if (overlaps(workspace, L.total, out, xbytes) || overlaps(workspace, L.total, x, xbytes))
+    return fail(MOE_LATENT_EINVAL, "workspace overlaps x or out");
+
+  return run_grouped(d, (int)T, (const uint16_t*)x, (const uint16_t*)D, (const uint16_t*)U,
+                     router, experts, shared, (uint16_t*)out, (char*)workspace, L, debug, o,
+                     (hipStream_t)stream);
+}
+
+int moe_latent_forward(const moe_latent_dims* dims, int64_t T, const void* x, const void* D,
+                       const void* U, const moe_router* router,
+                       const moe_fp4_experts* experts, const moe_fp4_experts* shared,
+                       void* out, void* workspace, size_t workspace_bytes,
+                       moe_route_debug* debug, void* stream) {
+  return moe_latent_forward_ex(dims, T, x, D, U, router, experts, shared, out, workspace,
+                               workspace_bytes, debug, nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,324 @@
+// Routing, combine and normalisation kernels of the latent-MoE layer (gfx950).
+//
+// Routing follows the layer description on the Hugging Face card
+// "Edge0-145B . Q3_K" (section "Architecture": the router picks 10 of 512
+// experts per token). Gating reading: softmax over all expert logits, the k
+// largest (ties to the lower index), weights renormalised over the k. The
+// renormalised weight of a chosen expert is exp(l_j - l_max) over the sum of
+// the same terms for the chosen k: the full softmax denominator cancels, so
+// only the k chosen logits are exponentiated.
+//
+// Everything here is deterministic: integer counting uses LDS atomics only
+// for order-free sums, positions come from wave ballots in lane order, and
+// floating-point reductions run in a fixed order.
+#include <limits.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// ------------------------------------------------------------------ RMSNorm
+
+// u[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps) * w), one workgroup per token.
+__global__ __launch_bounds__(256) void k_rmsnorm(const uint16_t* __restrict__ x,
+                                                 const float* __restrict__ w, float eps,
+                                                 uint16_t* __restrict__ u, int hidden) {
+  __shared__ float part[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* row = x + (size_t)t * hidden;
+  const int nch = hidden / 8;
+  float ss = 0.0f;
+  for (int c = tid; c < nch; c += 256) {
+    const uint4 v = *(const uint4*)(row + c * 8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = bf16_bits_to_f32(d[q] & 0xFFFFu), b = bf16_bits_to_f32(d[q] >> 16);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  const float r = 1.0f / sqrtf(tot / (float)hidden + eps);
+  uint16_t* urow = u + (size_t)t * hidden;
+  for (int c = tid; c < nch; c += 256) {
+    const uint4 v = *(const uint4*)(row + c * 8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = c * 8 + 2 * q;
+      const float a = bf16_bits_to_f32(d[q] & 0xFFFFu) * r * w[k];
+      const float b = bf16_bits_to_f32(d[q] >> 16) * r * w[k + 1];
+      o[q] = pack_bf16x2(a, b);
+    }
+    *(uint4*)(urow + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_rmsnorm(const uint16_t* x, const float* w, float eps, uint16_t* u, int T,
+                          int hidden, hipStream_t stream) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, stream, x, w, eps, u, hidden);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ top-k
+
+// One wave per token; lane l holds logits of experts l, l+64, ... (EPL of
+// them). k rounds of a wave-wide arg-max (larger value wins, ties to the
+// lower expert index); lane j keeps the j-th choice.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E,
+                                              int k, int32_t* __restrict__ idx,
+                                              float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  float v[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : -INFINITY;
+  }
+  uint32_t taken = 0;
+  float my_v = 0.0f;
+  int my_e = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int be = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
+        bv = v[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oe = __shfl_xor(be, m, 64);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == r) {
+      my_v = bv;
+      my_e = be;
+    }
+  }
+  const float mx = __shfl(my_v, 0, 64);
+  const float ex = lane < k ? expf(my_v - mx) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_e;
+    w[(size_t)t * k + lane] = ex / sum;
+  }
+}
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                       hipStream_t stream) {
+  const int epl = (E + 63) / 64;
+  dim3 grid((T + 3) / 4), block(256);
+  if (epl <= 1) hipLaunchKernelGGL(k_topk<1>, grid, block, 0, stream, logits, T, E, k, idx, w);
+  else if (epl <= 2) hipLaunchKernelGGL(k_topk<2>, grid, block, 0, stream, logits, T, E, k, idx, w);
+  else if (epl <= 4) hipLaunchKernelGGL(k_topk<4>, grid, block, 0, stream, logits, T, E, k, idx, w);
+  else if (epl <= 8) hipLaunchKernelGGL(k_topk<8>, grid, block, 0, stream, logits, T, E, k, idx, w);
+  else hipLaunchKernelGGL(k_topk<16>, grid, block, 0, stream, logits, T, E, k, idx, w);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ histogram
+
+// chunk_hist[c][e] = pairs of chunk c (pairs [c*CH, (c+1)*CH)) routed to e.
+__global__ __launch_bounds__(256) void k_route_hist(const int32_t* __restrict__ idx, int pairs,
+                                                    int E, int32_t* __restrict__ chunk_hist) {
+  __shared__ int h[kMaxExperts];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  for (int e = tid; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int p0 = c * kRouteChunk, p1 = min(p0 + kRouteChunk, pairs);
+  for (int p = p0 + tid; p < p1; p += 256) atomicAdd(&h[idx[p]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) chunk_hist[(size_t)c * E + e] = h[e];
+}
+
+hipError_t launch_route_hist(const int32_t* idx, int pairs, int E, int32_t* chunk_hist,
+                             hipStream_t stream) {
+  const int nch = (pairs + kRouteChunk - 1) / kRouteChunk;
+  hipLaunchKernelGGL(k_route_hist, dim3(nch), dim3(256), 0, stream, idx, pairs, E, chunk_hist);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ scan
+
+// Exclusive prefix sum over the 1024 threads of the block; *total gets the sum.
+__device__ int block_exclusive_scan_1024(int v, int* total) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int s = lane < 16 ? wsum[lane] : 0;
+    const int sinc = wave_inclusive_scan(s);
+    if (lane < 16) wsum[lane] = sinc - s;  // exclusive over waves
+    if (lane == 15) *total = sinc;
+  }
+  __syncthreads();
+  const int r = wsum[wave] + inc - v;
+  __syncthreads();
+  return r;
+}
+
+// One block of 1024 threads, thread e for expert e:
+//   counts[e]; off[e] = exclusive prefix of counts (off[E] = pairs,
+//   off[E+1] = pairs + n_shared*T for the shared expert's rows);
+//   tile_off likewise over ceil(count/128) (the grouped GEMM m-tiles);
+//   chunk_hist[c][e] becomes the first permuted row of chunk c's pairs of e.
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_hist,
+                                                     int n_chunks, int E, int pairs, int T,
+                                                     int n_shared, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ off,
+                                                     int32_t* __restrict__ tile_off) {
+  __shared__ int totals[2];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      const int v = chunk_hist[(size_t)c * E + e];
+      chunk_hist[(size_t)c * E + e] = cnt;
+      cnt += v;
+    }
+  }
+  const int tiles = (cnt + 127) / 128;
+  const int ex_cnt = block_exclusive_scan_1024(cnt, &totals[0]);
+  const int ex_tiles = block_exclusive_scan_1024(tiles, &totals[1]);
+  if (e < E) {
+    counts[e] = cnt;
+    off[e] = ex_cnt;
+    tile_off[e] = ex_tiles;
+    for (int c = 0; c < n_chunks; ++c) chunk_hist[(size_t)c * E + e] += ex_cnt;
+  }
+  if (e == 0) {
+    off[E] = pairs;
+    off[E + 1] = pairs + n_shared * T;
+    tile_off[E] = totals[1];
+    tile_off[E + 1] = totals[1] + n_shared * ((T + 127) / 128);
+  }
+}
+
+hipError_t launch_route_scan(int32_t* chunk_hist, int n_chunks, int E, int pairs, int T,
+                             int n_shared, int32_t* counts, int32_t* off, int32_t* tile_off,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, chunk_hist, n_chunks, E, pairs,
+                     T, n_shared, counts, off, tile_off);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ permute
+
+// One wave per chunk walks its pairs in order, 64 at a time. Lanes holding
+// the same expert find each other with one ballot per bit of the expert id;
+// a lane's rank among them (lanes below it) gives its position after the
+// chunk's running cursor for that expert, so the result is the stable
+// counting sort: ascending pair index within each expert.
+__global__ __launch_bounds__(64) void k_route_permute(const int32_t* __restrict__ idx, int pairs,
+                                                      int E, const int32_t* __restrict__ chunk_base,
+                                                      int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ slot) {
+  __shared__ int cursor[kMaxExperts + 1];
+  const int lane = threadIdx.x, c = blockIdx.x;
+  for (int e = lane; e < E; e += 64) cursor[e] = chunk_base[(size_t)c * E + e];
+  if (lane == 0) cursor[E] = 0;
+  __syncthreads();
+  const int nbits = 32 - __clz(E);  // enough bits for the sentinel value E
+  const uint64_t below = lanemask_lt();
+  const int p0 = c * kRouteChunk, p1 = min(p0 + kRouteChunk, pairs);
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    const bool valid = p < p1;
+    const int e = valid ? idx[p] : E;
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const int bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    const int start = cursor[e];
+    if (valid) {
+      const int pos = start + rank;
+      perm[pos] = p;
+      slot[p] = pos;
+      if (rank == 0) cursor[e] = start + __popcll(peers);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_route_permute(const int32_t* idx, int pairs, int E, const int32_t* chunk_base,
+                                int32_t* perm, int32_t* slot, hipStream_t stream) {
+  const int nch = (pairs + kRouteChunk - 1) / kRouteChunk;
+  hipLaunchKernelGGL(k_route_permute, dim3(nch), dim3(64), 0, stream, idx, pairs, E, chunk_base,
+                     perm, slot);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ combine
+
+// z[t] = sum_j w[t][j] * y[slot(t, j)] (+ y[pairs + t], the shared expert),
+// summed in the fixed order j = 0..k-1 then shared, fp32, one bf16 rounding.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
+                                                 const int32_t* __restrict__ slot,
+                                                 const float* __restrict__ w, int T, int k,
+                                                 int pairs, int latent, int n_shared,
+                                                 uint16_t* __restrict__ z) {
+  const int cpt = latent / 8;
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int t = gid / cpt, c8 = gid % cpt;
+  if (t >= T) return;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int r = slot[(size_t)t * k + j];
+    const float wt = w[(size_t)t * k + j];
+    const uint4 v = *(const uint4*)(y + (size_t)r * latent + c8 * 8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = fmaf(wt, bf16_bits_to_f32(d[q] & 0xFFFFu), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(wt, bf16_bits_to_f32(d[q] >> 16), acc[2 * q + 1]);
+    }
+  }
+  if (n_shared) {
+    const uint4 v = *(const uint4*)(y + (size_t)(pairs + t) * latent + c8 * 8);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += bf16_bits_to_f32(d[q] & 0xFFFFu);
+      acc[2 * q + 1] += bf16_bits_to_f32(d[q] >> 16);
+    }
+  }
+  *(uint4*)(z + (size_t)t * latent + c8 * 8) =
+      make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+}
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w, int T, int k,
+                          int pairs, int latent, int n_shared, uint16_t* z, hipStream_t stream) {
+  const long total = (long)T * (latent / 8);
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, y,
+                     slot, w, T, k, pairs, latent, n_shared, z);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -184,11 +184,13 @@ def rmsnorm(x: np.ndarray, weight: np.ndarray, eps: float = 1e-6) -> np.ndarray:
 
 def block_forward(layer, x_bits: np.ndarray, eps: float = 1e-6,
                   tokens: Optional[Sequence[int]] = None):
-    """Residual block: x + MoE(rmsnorm(x) * g). Returns (float64 output rows for
-    ``tokens``, OracleResult of the MoE)."""
+    """Residual block: x + MoE(u), u = rmsnorm(x) * g. The layer's input is a
+    bf16 tensor (its interface type), so u enters the layer rounded to bf16
+    (nearest even). Returns (float64 output rows for ``tokens``, the
+    OracleResult of the MoE)."""
     x = bf16_value(x_bits)
-    u = rmsnorm(x, layer.norm_w, eps)
-    res = forward(layer, x_values=u, tokens=tokens)
+    u_bits = _to_bf16_bits(rmsnorm(x, layer.norm_w, eps))
+    res = forward(layer, u_bits, tokens=tokens)
     return x[res.tokens] + res.out, res
 
 

@@ -354,13 +354,15 @@ def check_rmsnorm_vs_torch(seed=13):
 
 
 def check_block_residual(seed=14):
+    """x + brute(bf16(rms_norm(x) * g)), with torch's rms_norm and bfloat16 cast."""
     dims = synth.Dims(hidden=64, latent=32, n_experts=8, inter=32, top_k=2, n_shared=1)
     layer = synth.make_layer(dims, seed)
     x = synth.make_x(3, 64, seed)
     got, _ = oracle.block_forward(layer, x, 1e-6)
     xb = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(torch.float64)
     u = torch.nn.functional.rms_norm(xb, (64,), torch.from_numpy(layer.norm_w).to(torch.float64), 1e-6)
-    out_b, _, _, _ = brute_forward(layer, x_values=u.numpy())
+    u_bits = u.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    out_b, _, _, _ = brute_forward(layer, u_bits)
     assert np.allclose(got, xb.numpy() + out_b, rtol=1e-10, atol=1e-10)
 
 

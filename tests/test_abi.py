@@ -1,0 +1,132 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function the public header declares, and rejects bad arguments before any
+HIP call (so these error paths never touch a device)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+import latent_sparse_moe_amd as lsm
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(moe_latent_\w+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lsm.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert "moe_latent_forward" in names and len(names) >= 5
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(lsm.EXPORTS) == set(names)
+
+
+def test_version(lib):
+    assert lib.moe_latent_version() == 1
+
+
+def _dims(**kw):
+    d = dict(hidden=2560, latent=1792, n_experts=512, inter=640, top_k=10, n_shared=1)
+    d.update(kw)
+    return lsm.CDims(**d)
+
+
+def test_workspace_bytes(lib):
+    d = _dims()
+    b4 = lib.moe_latent_workspace_bytes(ctypes.byref(d), 4)
+    b16k = lib.moe_latent_workspace_bytes(ctypes.byref(d), 16384)
+    assert 0 < b4 < b16k
+    assert b16k > 16384 * 11 * (1792 + 640) * 2  # expert activations dominate
+    assert lib.moe_latent_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.moe_latent_workspace_bytes(ctypes.byref(_dims(latent=100)), 4) == 0
+    assert lib.moe_latent_workspace_bytes(None, 4) == 0
+
+
+# Fake, never dereferenced device addresses (every validation precedes use).
+A = 1 << 20
+
+
+def _call(lib, dims, T=4, x=A, D=2 * A, U=3 * A, router=True, experts=True, shared=True,
+          out=5 * A, ws=64 * A, ws_bytes=1 << 40, opts=None, bias=None, count=None):
+    r = lsm.CRouter(7 * A, bias) if router else None
+    m = lsm.CFp4Matrix(8 * A, 9 * A, 10 * A)
+    ex = lsm.CFp4Experts(m, m, m, dims.n_experts if count is None else count) if experts else None
+    sh = lsm.CFp4Experts(m, m, m, dims.n_shared) if shared else None
+    rc = lib.moe_latent_forward_ex(ctypes.byref(dims), T, x, D, U,
+                                   ctypes.byref(r) if r else None,
+                                   ctypes.byref(ex) if ex else None,
+                                   ctypes.byref(sh) if sh else None, out, ws, ws_bytes, None,
+                                   ctypes.byref(opts) if opts else None, None)
+    return rc, lib.moe_latent_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=0), lsm.EINVAL),
+    (dict(latent=100), lsm.EUNSUPPORTED),
+    (dict(inter=48), lsm.EUNSUPPORTED),
+    (dict(top_k=17, n_experts=32), lsm.EUNSUPPORTED),
+    (dict(top_k=11, n_experts=10), lsm.EUNSUPPORTED),
+    (dict(n_experts=2048), lsm.EUNSUPPORTED),
+    (dict(n_shared=2), lsm.EUNSUPPORTED),
+])
+def test_bad_dims(lib, kw, code):
+    rc, msg = _call(lib, _dims(**kw))
+    assert rc == code and msg
+
+
+def test_error_paths(lib):
+    d = _dims()
+    assert _call(lib, d, T=-1)[0] == lsm.EINVAL
+    assert _call(lib, d, x=0)[0] == lsm.EINVAL
+    assert _call(lib, d, x=A + 8)[0] == lsm.EINVAL            # misaligned
+    assert _call(lib, d, router=False)[0] == lsm.EINVAL
+    assert _call(lib, d, experts=False)[0] == lsm.EINVAL
+    assert _call(lib, d, shared=False)[0] == lsm.EINVAL       # n_shared = 1 needs it
+    assert _call(lib, d, count=511)[0] == lsm.EINVAL
+    assert _call(lib, d, out=A)[0] == lsm.EINVAL              # out aliases x
+    assert _call(lib, d, ws=0)[0] == lsm.EINVAL
+    assert _call(lib, d, ws=64 * A + 16)[0] == lsm.EINVAL     # workspace alignment
+    rc, msg = _call(lib, d, ws_bytes=1000)
+    assert rc == lsm.EWORKSPACE and "needed" in msg
+    assert _call(lib, d, opts=lsm.COpts(7, 0, None, 0.0, None))[0] == lsm.EINVAL
+    assert _call(lib, d, T=17, opts=lsm.COpts(lsm.PATH_DECODE, 0, None, 0.0, None))[0] == lsm.EUNSUPPORTED
+    assert _call(lib, d, opts=lsm.COpts(0, 1, None, 1e-6, None))[0] == lsm.EINVAL  # residual w/o weight
+    assert _call(lib, d, T=2 ** 31 // 10 + 1)[0] == lsm.EUNSUPPORTED
+    # T = 0 is a valid no-op; shared may be NULL when n_shared = 0
+    assert _call(lib, d, T=0)[0] == 0
+    assert _call(lib, _dims(n_shared=0), T=0, shared=False)[0] == 0
+    assert _call(lib, d, T=0, x=0, out=0, ws=0, ws_bytes=0)[0] == 0
+
+
+def test_last_error_cleared(lib):
+    _call(lib, _dims(hidden=0))
+    assert lib.moe_latent_last_error()
+    assert _call(lib, _dims(), T=0)[0] == 0
+    assert lib.moe_latent_last_error() == b""
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = lsm._lib
+    try:
+        lsm._lib = None
+        with pytest.raises(RuntimeError, match="no fallback"):
+            lsm.load_library(str(tmp_path / "missing.so"))
+    finally:
+        lsm._lib = saved
