@@ -31,6 +31,36 @@ BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix cores
 REC_BYTES_CODES = lambda L, I: 3 * L * I // 2 + 3 * L * I // 16   # one expert, codes + block scales
 
 
+def kernel_bytes(d, T, n_routed, decode=True):
+    """Algorithmic HBM bytes of each kernel of one layer call: every weight
+    byte it must read once (4-bit codes + E4M3 block scales + fp32 matrix
+    scales for experts, bf16 for D / R / U) plus its activation inputs and
+    outputs."""
+    L, H, E, I, k = d.latent, d.hidden, d.n_experts, d.inter, d.top_k
+    fp4 = lambda n_, k_: n_ * k_ // 2 + n_ * k_ // 16
+    gu = 2 * fp4(I, L) + 8           # gate + up of one expert
+    dn = fp4(L, I) + 4               # down of one expert
+    sh = d.n_shared
+    x = out = T * H * 2
+    h2 = T * L * 2 * 2               # latent as bf16 hi + lo
+    if decode:
+        return {
+            "dproj": L * H * 2 + x + h2,
+            "router": E * L * 2 + E * 4 + h2 + T * E * 4 + sh * (gu + T * I * 2),
+            "gateup": n_routed * (gu + T * I * 2) + T * L * 2 + T * E * 4,
+            "down": (n_routed + sh) * (dn + T * I * 2) + 2 * T * L * 4,
+            "uproj": H * L * 2 + 2 * T * L * 4 + out,
+        }
+    rows = T * k + T * sh
+    return {
+        "dproj": L * H * 2 + x + h2,
+        "router": E * L * 2 + h2 + T * E * 4,
+        "gateup": (n_routed + sh) * gu + rows * (L * 2 + I * 2),
+        "down": (n_routed + sh) * dn + rows * (I * 2 + L * 2),
+        "uproj": H * L * 2 + T * L * 2 + out,
+    }
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -109,17 +139,18 @@ def bench_decode(args, torch, lsm, synth, dev):
     rec = REC_BYTES_CODES(d.latent, d.inter)
     dense = 2 * d.latent * d.hidden * 2 + d.n_experts * d.latent * 2 + 2 * T * d.hidden * 2
     layer_bytes = [(n + d.n_shared) * (rec + 12) + dense for n in n_touched]
-    gateup_bytes = [(n + d.n_shared) * (2 * d.inter * d.latent // 2 + 2 * d.inter * d.latent // 16 + 8)
-                    for n in n_touched]
+    use_decode = path == lsm.PATH_DECODE or (path == lsm.PATH_AUTO and T <= lsm.DECODE_MAX_T)
+    stage_bytes = [kernel_bytes(d, T, n, decode=use_decode) for n in n_touched]
 
     def step(i, ev=None):
         c = i % args.copies
         lsm.forward(xs[c], layers[c], out=outs[c], workspace=ws, path=path, stage_events=ev)
 
-    # which kernel dominates (untimed pass over every stage)
-    names = [s for s in lsm.STAGES if s != "norm"]
+    # which kernel dominates (untimed pass over the stages this path runs)
+    names = (["dproj", "router", "gateup", "down", "uproj"] if use_decode
+             else ["dproj", "router", "topk", "route", "gateup", "down", "combine", "uproj"])
     st = stage_times(lsm, torch, lambda ev: step(0, ev), names)
-    ran = {s: v for s, v in st.items() if v > 1e-4}
+    ran = dict(st)
     dom = max(ran, key=ran.get)
     log(f"[decode] stage ms: " + ", ".join(f"{s}={v * 1e3:.1f}us" for s, v in ran.items()))
 
@@ -138,12 +169,8 @@ def bench_decode(args, torch, lsm, synth, dev):
     ms_step = total_ms / args.steps
     dom_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     mean_bytes = sum(layer_bytes[i % args.copies] for i in range(args.steps)) / args.steps
-    if dom == "decode":
-        dom_bytes = mean_bytes
-    elif dom == "gateup":
-        dom_bytes = sum(gateup_bytes[i % args.copies] for i in range(args.steps)) / args.steps
-    else:
-        dom_bytes = None
+    dom_bytes = sum(stage_bytes[i % args.copies].get(dom, 0) for i in range(args.steps)) / args.steps
+    dom_bytes = dom_bytes or None
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if dom_bytes else None
     res = {
         "tok_s": T * args.steps / (total_ms * 1e-3),
@@ -161,6 +188,9 @@ def bench_decode(args, torch, lsm, synth, dev):
             "layer_frac_of_hbm_peak": mean_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "experts_touched_per_copy": n_touched,
             "stage_us_untimed_pass": {s: round(v * 1e3, 2) for s, v in ran.items()},
+            "stage_GBps_untimed_pass": {s: round(stage_bytes[0].get(s, 0) / (v * 1e-3) / 1e9, 1)
+                                        for s, v in ran.items() if stage_bytes[0].get(s)},
+            "path": "decode" if use_decode else "grouped",
             "copies": args.copies,
         },
         "host": host, "x0": xs_host[0],
@@ -193,9 +223,8 @@ def bench_prefill(args, torch, lsm, synth, dev):
     def step(ev=None):
         lsm.forward(x, dl, out=out, workspace=ws, path=lsm.PATH_GROUPED, stage_events=ev)
 
-    names = [s for s in lsm.STAGES if s not in ("norm", "decode")]
+    names = ["dproj", "router", "topk", "route", "gateup", "down", "combine", "uproj"]
     st = stage_times(lsm, torch, step, names, n=3)
-    st = {s: v for s, v in st.items() if v > 1e-4}
     dom = max(st, key=st.get)
     log(f"[prefill] stage ms: " + ", ".join(f"{s}={v:.3f}" for s, v in st.items()))
     for _ in range(args.prefill_warmup):

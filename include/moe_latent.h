@@ -125,26 +125,30 @@ typedef struct moe_route_debug {
   float *logits;     /* [T][n_experts] router logits (fp32) */
 } moe_route_debug;
 
-/* Execution path: the grouped-GEMM pipeline (any T) or the fused
- * weight-streaming decode kernel (T <= MOE_LATENT_DECODE_MAX_T). AUTO picks
- * the fused kernel whenever T allows it. */
+/* Execution path: the grouped-GEMM pipeline (any T) or the weight-streaming
+ * decode kernels (T <= MOE_LATENT_DECODE_MAX_T; hidden and latent multiples
+ * of 256 with latent <= 1792, inter a multiple of 128). AUTO picks the decode
+ * kernels whenever T and the dims allow it; DECODE with other sizes returns
+ * MOE_LATENT_EUNSUPPORTED. */
 #define MOE_LATENT_PATH_AUTO 0
 #define MOE_LATENT_PATH_GROUPED 1
 #define MOE_LATENT_PATH_DECODE 2
-#define MOE_LATENT_DECODE_MAX_T 16
+#define MOE_LATENT_DECODE_MAX_T 8
 
-/* Stages of one call, for optional timing (moe_latent_opts.stage_events). */
+/* Stages of one call, for optional timing (moe_latent_opts.stage_events).
+ * The decode path runs five kernels and reports them as DPROJ, ROUTER
+ * (which also runs the shared expert's gate/up), GATEUP (which includes the
+ * top-k), DOWN (which includes the combine) and UPROJ. */
 #define MOE_LATENT_STAGE_NORM 0     /* RMSNorm of the residual block */
 #define MOE_LATENT_STAGE_DPROJ 1    /* h = x D^T */
 #define MOE_LATENT_STAGE_ROUTER 2   /* logits = h R^T + b */
 #define MOE_LATENT_STAGE_TOPK 3     /* top-k + renormalised weights */
 #define MOE_LATENT_STAGE_ROUTE 4    /* histogram, prefix sums, permutation */
-#define MOE_LATENT_STAGE_GATEUP 5   /* grouped gate/up GEMM + SiLU*mul */
-#define MOE_LATENT_STAGE_DOWN 6     /* grouped down GEMM */
+#define MOE_LATENT_STAGE_GATEUP 5   /* gate/up GEMMs + SiLU*mul */
+#define MOE_LATENT_STAGE_DOWN 6     /* down GEMMs */
 #define MOE_LATENT_STAGE_COMBINE 7  /* weighted combine */
 #define MOE_LATENT_STAGE_UPROJ 8    /* out = z U^T (+ residual) */
-#define MOE_LATENT_STAGE_DECODE 9   /* the fused decode kernel (whole layer) */
-#define MOE_LATENT_N_STAGES 10
+#define MOE_LATENT_N_STAGES 9
 
 typedef struct moe_latent_opts {
   int32_t path;             /* MOE_LATENT_PATH_* */

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libmoe_latent.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 PATH_AUTO, PATH_GROUPED, PATH_DECODE = 0, 1, 2
-DECODE_MAX_T = 16
+DECODE_MAX_T = 8
 
 c_i32, c_i64, c_size, c_vp, c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 
@@ -54,8 +54,7 @@ class COpts(ctypes.Structure):
                 ("stage_events", ctypes.POINTER(c_vp))]
 
 
-STAGES = ("norm", "dproj", "router", "topk", "route", "gateup", "down", "combine", "uproj",
-          "decode")
+STAGES = ("norm", "dproj", "router", "topk", "route", "gateup", "down", "combine", "uproj")
 N_STAGES = len(STAGES)
 
 

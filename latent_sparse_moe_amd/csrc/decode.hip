@@ -1,0 +1,766 @@
+// Weight-streaming decode path of the latent-MoE layer (T <= 8 tokens).
+//
+// At a handful of tokens every weight byte feeds only T multiply-adds, so the
+// layer is bound by HBM bandwidth. Five kernels; in each, every wave issues
+// all of its weight loads before anything else (a kernel boundary is the
+// cheapest grid-wide synchronisation on this chip and needs no co-residency
+// assumption):
+//
+//   1. dec_dproj   h = x D^T (RMSNorm fused for the residual block); K split
+//                  over the 8 waves; h leaves as bf16 hi + lo
+//   2. dec_router  logits = (hi + lo) R^T + b, 16 experts per workgroup; the
+//                  last router workgroup to finish takes the top-k of every
+//                  token and publishes the routing table. The shared expert's
+//                  gate/up (routing-independent) runs in the same launch.
+//   3. dec_gateup  one wave per (routed expert, 16 intermediate rows):
+//                  silu(gate) * up
+//   4. dec_down    one workgroup per (16 latent rows, 8 expert slots), one
+//                  expert per wave: down rows, weighted by the gate weights
+//                  and summed over the waves in a fixed order
+//   5. dec_uproj   z = sum of the per-group partials (fixed order);
+//                  out = z U^T (+ x)
+//
+// Matrix-core tiles are v_mfma_f32_16x16x32_bf16 with weight rows as the M
+// operand (16 rows) and tokens as the N operand (16 columns, T used; the rest
+// are zero). Lane l serves weight row l%16; its lane group g = l/16 takes
+// every fourth chunk of the wave's K range (chunk c*4 + g at step c), so one
+// load instruction reads 64 contiguous bytes of each of 16 rows. K order
+// inside a dot product is free; the token operand is read with the same
+// chunk mapping.
+//
+// Cross-workgroup data inside one launch (router logits -> the last router
+// workgroup) moves through agent-scope relaxed atomic accesses, which are
+// coherent across the chip's XCDs without flushing the L2 caches; everything
+// else crosses kernel boundaries.
+#include <limits.h>
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kDecThreads = 512;  // 8 waves
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kSlotsPerGroup = kDecWaves;  // down kernel: one expert slot per wave
+
+#define AGENT __HIP_MEMORY_SCOPE_AGENT
+
+// ------------------------------------------------------------------ wave tiles
+
+// NCH chunks of 8 bf16 per lane group: the wave's K range is [kb, kb + 32*NCH).
+template <int NCH>
+struct Bf16Rows {
+  uint4 w[NCH];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ row, int kb, int g) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) w[c] = *(const uint4*)(row + kb + (c * 4 + g) * 8);
+  }
+  // acc += W . act over the range; act = token row (LDS) or null (zero column)
+  __device__ __forceinline__ void mma(const uint16_t* act, int kb, int g, f32x4& acc) const {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      bf16x8 b = {};
+      if (act) b = *(const bf16x8*)(act + kb + (c * 4 + g) * 8);
+      acc = mfma16x16x32(__builtin_bit_cast(bf16x8, w[c]), b, acc);
+    }
+  }
+  // two token operands: the hi and lo bf16 halves of one fp32 vector
+  __device__ __forceinline__ void mma2(const uint16_t* hi, const uint16_t* lo, int kb, int g,
+                                       f32x4& acc) const {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      bf16x8 bh = {}, bl = {};
+      if (hi) {
+        bh = *(const bf16x8*)(hi + kb + (c * 4 + g) * 8);
+        bl = *(const bf16x8*)(lo + kb + (c * 4 + g) * 8);
+      }
+      const bf16x8 a = __builtin_bit_cast(bf16x8, w[c]);
+      acc = mfma16x16x32(a, bh, acc);
+      acc = mfma16x16x32(a, bl, acc);
+    }
+  }
+};
+
+// NCH chunks of 32 fp4 weights (16 bytes of codes + 2 E4M3 scales) per lane
+// group: the wave's K range is [kb, kb + 128*NCH).
+template <int NCH>
+struct Fp4Rows {
+  uint4 c[NCH];
+  uint32_t s[NCH];
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ crow,
+                                       const uint8_t* __restrict__ srow, int kb, int g) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) c[i] = *(const uint4*)(crow + (kb + (i * 4 + g) * 32) / 2);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) s[i] = *(const uint16_t*)(srow + (kb + (i * 4 + g) * 32) / 16);
+  }
+  // token operand from a row in memory (LDS or global), or null (zero column)
+  __device__ __forceinline__ void mma(const uint16_t* act, int kb, int g, f32x4& acc) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float s0 = e4m3_to_f32(s[i] & 0xFFu), s1 = e4m3_to_f32((s[i] >> 8) & 0xFFu);
+      const uint32_t d[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x8 b = {};
+        if (act) b = *(const bf16x8*)(act + kb + (i * 4 + g) * 32 + q * 8);
+        acc = mfma16x16x32(dequant8(d[q], q < 2 ? s0 : s1), b, acc);
+      }
+    }
+  }
+  // token operand already in registers (4 x 8 bf16 per chunk)
+  __device__ __forceinline__ void mma_regs(const uint4 (&b)[NCH * 4], f32x4& acc) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float s0 = e4m3_to_f32(s[i] & 0xFFu), s1 = e4m3_to_f32((s[i] >> 8) & 0xFFu);
+      const uint32_t d[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc = mfma16x16x32(dequant8(d[q], q < 2 ? s0 : s1),
+                           __builtin_bit_cast(bf16x8, b[i * 4 + q]), acc);
+    }
+  }
+};
+
+// Sum the per-wave partial tiles through LDS in wave order; lane l of wave 0
+// returns the totals of rows (l/16)*4 + r, token l%16.
+__device__ __forceinline__ f32x4 reduce_waves(f32x4 acc, float* red /*[8][64][4]*/) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  *(f32x4*)(red + (wave * 64 + lane) * 4) = acc;
+  __syncthreads();
+  f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+  if (wave == 0)
+    for (int w = 0; w < kDecWaves; ++w) tot += *(const f32x4*)(red + (w * 64 + lane) * 4);
+  return tot;
+}
+
+// Up to kDecodeMaxT rows of activations moved to LDS in two steps, so their
+// global loads can be issued before a wave's weight loads (memory counters
+// drain in order: whatever is loaded first can be used first).
+constexpr int kStageVec = 5;  // 16-byte vectors per thread: 512 * 5 * 8 = 8 * 2560
+struct RowStage {
+  uint4 v[kStageVec];
+  // count is a multiple of 8 and >= 8; out-of-range slots re-read the last
+  // vector (never stored), which keeps the loads unconditional
+  __device__ __forceinline__ void load(const uint16_t* src, int count) {
+#pragma unroll
+    for (int j = 0; j < kStageVec; ++j) {
+      const int i = min((int)(threadIdx.x + j * kDecThreads) * 8, count - 8);
+      v[j] = *(const uint4*)(src + i);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int count) const {
+#pragma unroll
+    for (int j = 0; j < kStageVec; ++j) {
+      const int i = (threadIdx.x + j * kDecThreads) * 8;
+      if (i < count) *(uint4*)(dst + i) = v[j];
+    }
+  }
+};
+
+// ------------------------------------------------------------------ 1. D
+
+template <int NCH>
+__global__ __launch_bounds__(kDecThreads) void k_dec_dproj(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int H = a.hidden, L = a.latent, T = a.T;
+  uint16_t* xs = lds;                                // [T][H] bf16
+  float* red = (float*)(lds + kDecodeMaxT * H);      // [8][64][4]
+  float* rstd = red + kDecWaves * 64 * 4;            // [T]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, t = lane & 15;
+  const int row0 = blockIdx.x * 16;
+  const int row = min(row0 + (lane & 15), L - 1);
+  const int kb = wave * (H / kDecWaves);
+  if (blockIdx.x == 0 && tid == 0) *a.route_counter = 0u;  // for the router's last workgroup
+  RowStage xr;
+  xr.load(a.x, T * H);
+  Bf16Rows<NCH> wr;
+  wr.load(a.D + (size_t)row * H, kb, g);
+  xr.store(xs, T * H);
+  __syncthreads();
+  if (a.norm_weight) {  // residual block: RMSNorm per token in fp32, then bf16, in place
+    if (wave < T) {
+      const uint16_t* xrow = xs + wave * H;
+      float ss = 0.f;
+      for (int k = lane * 8; k < H; k += 64 * 8) {
+        const uint4 v = *(const uint4*)(xrow + k);
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_bits_to_f32(d[q] & 0xFFFFu), hi = bf16_bits_to_f32(d[q] >> 16);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) rstd[wave] = 1.0f / sqrtf(ss / (float)H + a.norm_eps);
+    }
+    __syncthreads();
+    for (int i = tid * 8; i < T * H; i += kDecThreads * 8) {
+      const int tt = i / H, k = i % H;
+      const uint4 v = *(const uint4*)(xs + i);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = pack_bf16x2(bf16_bits_to_f32(d[q] & 0xFFFFu) * rstd[tt] * a.norm_weight[k + 2 * q],
+                           bf16_bits_to_f32(d[q] >> 16) * rstd[tt] * a.norm_weight[k + 2 * q + 1]);
+      *(uint4*)(xs + i) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  wr.mma(t < T ? xs + t * H : nullptr, kb, g, acc);
+  const f32x4 tot = reduce_waves(acc, red);
+  if (wave == 0 && t < T) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = row0 + g * 4 + r;
+      if (n < L) {
+        const uint16_t hi = f32_to_bf16_bits(tot[r]);
+        a.hhi[(size_t)t * L + n] = hi;
+        a.hlo[(size_t)t * L + n] = f32_to_bf16_bits(tot[r] - bf16_bits_to_f32(hi));
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ top-k
+
+// (value, expert) keys ordered so that a larger value wins and equal values
+// go to the lower expert: key = (order-preserving value bits << 32) | ~expert.
+__device__ __forceinline__ uint64_t order_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  uint32_t u = (uint32_t)(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ int key_expert(uint64_t k) { return (int)(~(uint32_t)k); }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max64(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t lo2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, CTRL, 0xF, 0xF, false);
+  const uint32_t hi2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, CTRL, 0xF, 0xF, false);
+  const uint64_t o = ((uint64_t)hi2 << 32) | lo2;
+  return o > v ? o : v;
+}
+
+// Largest key over the 64 lanes (same value in every lane): DPP steps inside
+// each 16-lane row, then the four row results through readlane.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+  v = dpp_max64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max64<0x141>(v);  // row_half_mirror: max over 8 lanes
+  v = dpp_max64<0x140>(v);  // row_mirror: max over 16 lanes
+  uint64_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, r * 16);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), r * 16);
+    const uint64_t k = ((uint64_t)hi << 32) | lo;
+    best = k > best ? k : best;
+  }
+  return best;
+}
+
+// Top-k of one token's logits by this wave; lane j < k ends with choice j
+// (descending). Renormalised weights: exp(l_j - l_0) / sum over the k.
+template <int EPL>
+__device__ __forceinline__ void wave_topk(const float* logits_row, int E, int k, int* out_e,
+                                          float* out_w) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? order_key(__hip_atomic_load(logits_row + e, __ATOMIC_RELAXED, AGENT), e)
+                   : 0ull;
+  }
+  uint64_t mine = 0;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    const uint64_t win = wave_max64(best);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) key[i] = key[i] == win ? 0ull : key[i];
+    if (lane == r) mine = win;
+  }
+  const uint32_t lo0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, 0);
+  const uint32_t hi0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), 0);
+  const float top = key_value(((uint64_t)hi0 << 32) | lo0);
+  const float ex = lane < k ? expf(key_value(mine) - top) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    out_e[lane] = key_expert(mine);
+    out_w[lane] = ex / sum;
+  }
+}
+
+// ------------------------------------------------------------------ 2. router + shared gate/up
+
+// SiLU(gate) * up of a 16-row tile, to act[t][n0 + rows] (bf16, t < T).
+__device__ __forceinline__ void store_gateup(const f32x4& g4, const f32x4& u4, float gsg,
+                                             float gsu, uint16_t* act, int I, int T, int n0,
+                                             int lane) {
+  const int t = lane & 15, g = lane >> 4;
+  if (t >= T) return;
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float gg = gsg * g4[r], uu = gsu * u4[r];
+    v[r] = gg / (1.0f + expf(-gg)) * uu;
+  }
+  *(uint2*)(act + (size_t)t * I + n0 + g * 4) =
+      make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
+// Gate/up of one expert for two 16-row tiles per workgroup: wave w handles
+// tile w/4, matrix (w/2)%2 (gate, up), K half w%2. The halves and matrices
+// meet in LDS; waves 0 and 4 apply SiLU*mul and store.
+template <int NCH_H>
+struct GateUpTask {
+  Fp4Rows<NCH_H> wr;
+  __device__ __forceinline__ void load(const Fp4Mat& gate, const Fp4Mat& up, int e, int I, int L,
+                                       int n0, int wave, int lane) {
+    const int mat = (wave >> 1) & 1, half = wave & 1, g = lane >> 4;
+    const Fp4Mat& m = mat ? up : gate;
+    const size_t row = ((size_t)e * I + n0 + (lane & 15)) * L;
+    wr.load(m.codes + row / 2, m.scales + row / 16, half * (L / 2), g);
+  }
+  __device__ __forceinline__ f32x4 mma(const uint16_t* act, int L, int wave, int lane) const {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    wr.mma(act, (wave & 1) * (L / 2), lane >> 4, acc);
+    return acc;
+  }
+};
+
+// Writes this wave's tile, then (waves 0 and 4) combines the four partial
+// tiles of its row tile: gate = half0 + half1, up = half0 + half1.
+__device__ __forceinline__ void finish_gateup(f32x4 acc, float* red, bool tile_busy, float gsg,
+                                              float gsu, uint16_t* act, int I, int T, int n0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  *(f32x4*)(red + (wave * 64 + lane) * 4) = acc;
+  __syncthreads();
+  if ((wave & 3) == 0 && tile_busy) {
+    const f32x4 g0 = *(const f32x4*)(red + ((wave + 0) * 64 + lane) * 4);
+    const f32x4 g1 = *(const f32x4*)(red + ((wave + 1) * 64 + lane) * 4);
+    const f32x4 u0 = *(const f32x4*)(red + ((wave + 2) * 64 + lane) * 4);
+    const f32x4 u1 = *(const f32x4*)(red + ((wave + 3) * 64 + lane) * 4);
+    store_gateup(g0 + g1, u0 + u1, gsg, gsu, act, I, T, n0, lane);
+  }
+}
+
+struct RouteLds {
+  int idx[kDecodeMaxT * 16];
+  float w[kDecodeMaxT * 16];
+  uint32_t flags[kMaxExperts / 32];
+  int list[kDecodeMaxT * 16];
+  int n_act;
+};
+
+// Routing table from the T x k choices in `rl` (one workgroup): the active
+// experts in ascending order, each token's gate weight per slot (slot 0 is the
+// shared expert with weight 1, slot s >= 1 the s-th active expert), and the
+// optional debug copies.
+__device__ void publish_routing(const DecodeArgs& a, RouteLds& rl) {
+  const int E = a.n_experts, T = a.T, k = a.top_k, P = T * k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
+  __syncthreads();
+  for (int p = tid; p < P; p += kDecThreads)
+    atomicOr(&rl.flags[rl.idx[p] >> 5], 1u << (rl.idx[p] & 31));
+  __syncthreads();
+  if (wave == 0) {  // compact the set bits in ascending order (E <= 1024 bits)
+    const int nw = (E + 31) / 32;
+    const uint32_t bits = lane < nw ? rl.flags[lane] : 0u;
+    const int cnt = __popc(bits);
+    const int inc = wave_inclusive_scan(cnt);
+    int pos = inc - cnt;
+    for (uint32_t b = bits; b; b &= b - 1) rl.list[pos++] = lane * 32 + __ffs(b) - 1;
+    if (lane == 63) rl.n_act = inc;
+  }
+  __syncthreads();
+  const int n_act = rl.n_act;
+  if (tid == 0) a.route_n_act[0] = n_act;
+  for (int i = tid; i < n_act; i += kDecThreads) a.route_list[i] = rl.list[i];
+  for (int i = tid; i < (n_act + 1) * T; i += kDecThreads) {
+    const int slot = i / T, t = i % T;
+    float w = 0.0f;
+    if (slot == 0) {
+      w = a.n_shared ? 1.0f : 0.0f;
+    } else {
+      const int e = rl.list[slot - 1];
+      for (int j = 0; j < k; ++j)
+        if (rl.idx[t * k + j] == e) w = rl.w[t * k + j];
+    }
+    a.route_wtab[i] = w;
+  }
+  if (a.dbg_idx)
+    for (int i = tid; i < P; i += kDecThreads) a.dbg_idx[i] = rl.idx[i];
+  if (a.dbg_w)
+    for (int i = tid; i < P; i += kDecThreads) a.dbg_w[i] = rl.w[i];
+  if (a.dbg_logits)
+    for (int i = tid; i < T * E; i += kDecThreads)
+      a.dbg_logits[i] = __hip_atomic_load(a.logits + i, __ATOMIC_RELAXED, AGENT);
+  // counts, offsets and the stable permutation of the P pairs (pair p of
+  // expert e goes after the pairs of smaller experts and the earlier pairs of e)
+  if (a.dbg_counts)
+    for (int e = tid; e < E; e += kDecThreads) {
+      int c = 0;
+      for (int p = 0; p < P; ++p) c += rl.idx[p] == e;
+      a.dbg_counts[e] = c;
+    }
+  if (a.dbg_offsets)
+    for (int e = tid; e <= E; e += kDecThreads) {
+      int o = 0;
+      for (int p = 0; p < P; ++p) o += rl.idx[p] < e;
+      a.dbg_offsets[e] = o;
+    }
+  if (a.dbg_perm)
+    for (int p = tid; p < P; p += kDecThreads) {
+      const int e = rl.idx[p];
+      int pos = 0;
+      for (int q = 0; q < P; ++q) pos += (rl.idx[q] < e) || (rl.idx[q] == e && q < p);
+      a.dbg_perm[pos] = p;
+    }
+}
+
+template <int NCH_R, int NCH_H>
+__global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  __shared__ RouteLds rl;
+  __shared__ unsigned last_flag;
+  const int L = a.latent, T = a.T, E = a.n_experts, I = a.inter;
+  uint16_t* hi = lds;                    // [T][L]
+  uint16_t* lo = lds + kDecodeMaxT * L;  // [T][L]
+  float* red = (float*)(lo + kDecodeMaxT * L);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, t = lane & 15;
+  const int nrb = (E + 15) / 16;
+
+  if ((int)blockIdx.x < nrb) {
+    const int e0 = blockIdx.x * 16;
+    const int e = min(e0 + (lane & 15), E - 1);
+    const int kb = wave * (L / kDecWaves);
+    RowStage sh_hi, sh_lo;
+    sh_hi.load(a.hhi, T * L);
+    sh_lo.load(a.hlo, T * L);
+    Bf16Rows<NCH_R> wr;
+    wr.load(a.R + (size_t)e * L, kb, g);
+    sh_hi.store(hi, T * L);
+    sh_lo.store(lo, T * L);
+    __syncthreads();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    wr.mma2(t < T ? hi + t * L : nullptr, t < T ? lo + t * L : nullptr, kb, g, acc);
+    const f32x4 tot = reduce_waves(acc, red);
+    if (wave == 0 && t < T) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ee = e0 + g * 4 + r;
+        if (ee < E)
+          __hip_atomic_store(a.logits + (size_t)t * E + ee, tot[r] + (a.bias ? a.bias[ee] : 0.0f),
+                             __ATOMIC_RELAXED, AGENT);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the logits stores complete before the arrival count
+    __syncthreads();
+    if (tid == 0)
+      last_flag = __hip_atomic_fetch_add(a.route_counter, 1u, __ATOMIC_RELAXED, AGENT) ==
+                  (unsigned)(nrb - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    // the last router workgroup: top-k of every token, then the routing table
+    if (wave < T) {
+      if (E <= 512)
+        wave_topk<8>(a.logits + (size_t)wave * E, E, a.top_k, rl.idx + wave * a.top_k,
+                     rl.w + wave * a.top_k);
+      else
+        wave_topk<16>(a.logits + (size_t)wave * E, E, a.top_k, rl.idx + wave * a.top_k,
+                      rl.w + wave * a.top_k);
+    }
+    __syncthreads();
+    publish_routing(a, rl);
+    return;
+  }
+  // shared expert gate/up: two 16-row tiles per workgroup (see GateUpTask)
+  if (!a.n_shared) return;
+  const int tile = (blockIdx.x - nrb) * 2 + (wave >> 2);
+  const bool busy = tile * 16 < I;
+  const int n0 = busy ? tile * 16 : 0;
+  RowStage st;
+  st.load(a.hhi, T * L);
+  GateUpTask<NCH_H> task;
+  if (busy) task.load(a.sh_gate, a.sh_up, 0, I, L, n0, wave, lane);
+  st.store(hi, T * L);
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (busy) acc = task.mma(t < T ? hi + t * L : nullptr, L, wave, lane);
+  finish_gateup(acc, red, busy, a.sh_gate.gscale[0], a.sh_up.gscale[0], a.act, I, T, n0);
+}
+
+// ------------------------------------------------------------------ 3. routed gate/up
+
+template <int NCH_H>
+__global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int L = a.latent, T = a.T, I = a.inter;
+  uint16_t* hi = lds;  // [T][L]
+  float* red = (float*)(lds + kDecodeMaxT * L);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = lane & 15;
+  const int tiles = I / 16;
+  const int tile = blockIdx.x * 2 + (wave >> 2);  // (slot - 1) * tiles + row tile
+  // the routing table: entry count and this tile's expert, read together
+  const int n_act = a.route_n_act[0];
+  const int e_guess = a.route_list[min(tile / tiles, a.max_active - 1)];
+  if (blockIdx.x == 0 && tid < (a.latent + 15) / 16) a.down_counter[tid] = 0u;
+  const bool busy = tile < n_act * tiles;
+  if (__syncthreads_or(busy ? 1 : 0) == 0) return;
+  const int slot = 1 + tile / tiles;
+  const int n0 = (tile % tiles) * 16;
+  RowStage st;
+  st.load(a.hhi, T * L);
+  GateUpTask<NCH_H> task;
+  if (busy) task.load(a.gate, a.up, e_guess, I, L, n0, wave, lane);
+  st.store(hi, T * L);
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (busy) acc = task.mma(t < T ? hi + t * L : nullptr, L, wave, lane);
+  finish_gateup(acc, red, busy, busy ? a.gate.gscale[e_guess] : 0.f,
+                busy ? a.up.gscale[e_guess] : 0.f, a.act + (size_t)slot * T * I, I, T, n0);
+}
+
+// ------------------------------------------------------------------ 4. down + combine
+
+// Workgroup (row block rb, slot group sg): wave w takes slot sg*8 + w (slot
+// 0 is the shared expert) and adds weight(t, slot) * gscale * y; the waves
+// are summed in order into zpart[sg]. The last workgroup of a row block to
+// finish sums the groups in order and writes z (bf16) for those rows.
+template <int NCH_D>
+__global__ __launch_bounds__(kDecThreads) void k_dec_down(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) float red[kDecWaves * 64 * 4];
+  __shared__ unsigned last_flag;
+  const int L = a.latent, T = a.T, I = a.inter;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, t = lane & 15;
+  const int rb = blockIdx.x / a.n_zpart, sgrp = blockIdx.x % a.n_zpart;
+  const int s = sgrp * kSlotsPerGroup + wave;
+  const int n_act = a.route_n_act[0];
+  const int e_guess = s >= 1 ? a.route_list[min(s - 1, a.max_active - 1)] : 0;
+  const float w_guess = t < T ? a.route_wtab[min(s, a.max_active) * T + t] : 0.f;
+  const bool sh = s == 0;
+  const bool busy = s <= n_act && (!sh || a.n_shared);
+  const int row0 = rb * 16;
+  const int row = min(row0 + (lane & 15), L - 1);
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  if (busy) {
+    const int e = sh ? 0 : e_guess;
+    const Fp4Mat& m = sh ? a.sh_down : a.down;
+    uint4 b[NCH_D * 4];
+    const uint16_t* act = a.act + ((size_t)s * T + (t < T ? t : 0)) * I;
+#pragma unroll
+    for (int i = 0; i < NCH_D; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        b[i * 4 + q] = t < T ? *(const uint4*)(act + (i * 4 + g) * 32 + q * 8)
+                             : make_uint4(0u, 0u, 0u, 0u);
+    const size_t rowd = ((size_t)e * L + row) * I;
+    Fp4Rows<NCH_D> wd;
+    wd.load(m.codes + rowd / 2, m.scales + rowd / 16, 0, g);
+    const float wt = w_guess * m.gscale[e];
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    wd.mma_regs(b, y);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = wt * y[r];
+  }
+  const f32x4 tot = reduce_waves(z, red);
+  if (wave == 0 && t < T) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = row0 + g * 4 + r;
+      if (n < L)
+        __hip_atomic_store(a.zpart + ((size_t)sgrp * T + t) * L + n, tot[r], __ATOMIC_RELAXED,
+                           AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // partial sums complete before the arrival count
+  __syncthreads();
+  if (tid == 0)
+    last_flag = __hip_atomic_fetch_add(a.down_counter + rb, 1u, __ATOMIC_RELAXED, AGENT) ==
+                (unsigned)(a.n_zpart - 1);
+  __syncthreads();
+  if (!last_flag) return;
+  // last workgroup of the row block: z[t][rows] = sum of the groups in order
+  if (tid < 16 * T) {
+    const int tt = tid / 16, n = row0 + tid % 16;
+    if (n < L) {
+      float v = 0.f;
+      for (int gi = 0; gi < a.n_zpart; ++gi)
+        v += __hip_atomic_load(a.zpart + ((size_t)gi * T + tt) * L + n, __ATOMIC_RELAXED, AGENT);
+      a.z[(size_t)tt * L + n] = f32_to_bf16_bits(v);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 5. U
+
+template <int NCH>
+__global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int L = a.latent, H = a.hidden, T = a.T;
+  uint16_t* zs = lds;  // [T][L] bf16
+  float* red = (float*)(lds + kDecodeMaxT * L);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, t = lane & 15;
+  const int m0 = blockIdx.x * 16;
+  const int m = min(m0 + (lane & 15), H - 1);
+  const int kb = wave * (L / kDecWaves);
+  RowStage st;
+  st.load(a.z, T * L);
+  Bf16Rows<NCH> wr;
+  wr.load(a.U + (size_t)m * L, kb, g);
+  st.store(zs, T * L);
+  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  wr.mma(t < T ? zs + t * L : nullptr, kb, g, acc);
+  const f32x4 tot = reduce_waves(acc, red);
+  if (wave == 0 && t < T) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = m0 + g * 4 + r;
+      if (n < H) {
+        float o = tot[r];
+        if (a.norm_weight) o += bf16_bits_to_f32(a.x[(size_t)t * H + n]);
+        a.out[(size_t)t * H + n] = f32_to_bf16_bits(o);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+static hipError_t set_lds(const void* fn, size_t bytes) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// Calls f(std::integral_constant<int, N>) for the chunk counts the kernels
+// are instantiated for.
+template <class F>
+static hipError_t with_nch(int n, F&& f) {
+  switch (n) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 5: return f(std::integral_constant<int, 5>{});
+    case 7: return f(std::integral_constant<int, 7>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    case 10: return f(std::integral_constant<int, 10>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static bool nch_ok(int n) {
+  return n == 1 || n == 2 || n == 4 || n == 5 || n == 7 || n == 8 || n == 10;
+}
+
+int decode_zpart_groups(int n_experts, int top_k, int T) {
+  const int max_act = n_experts < T * top_k ? n_experts : T * top_k;
+  return (1 + max_act + kSlotsPerGroup - 1) / kSlotsPerGroup;
+}
+
+bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int T) {
+  if (T < 1 || T > kDecodeMaxT || n_experts > kMaxExperts || top_k > 16) return false;
+  // D, U and the router split K over 8 waves x 4 lane groups x 8 bf16;
+  // expert rows are consumed in 32-weight chunks by 4 lane groups.
+  if (hidden % 256 || latent % 256 || inter % 128) return false;
+  if (!nch_ok(hidden / 256) || !nch_ok(latent / 256) || !nch_ok(inter / 128)) return false;
+  if (latent / 128 > 14 || inter / 128 > 5) return false;  // register budget per wave
+  if (kDecodeMaxT * (hidden > latent ? hidden : latent) > kDecThreads * kStageVec * 8)
+    return false;  // activation staging (each staged array is at most T x max(hidden, latent))
+  const size_t red = kDecWaves * 64 * 4 * sizeof(float);
+  return (size_t)2 * kDecodeMaxT * latent * 2 + red <= 96 * 1024 &&
+         (size_t)kDecodeMaxT * hidden * 2 + red + 64 <= 96 * 1024;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& mk) {
+  const int H = a.hidden, L = a.latent, I = a.inter, E = a.n_experts;
+  const size_t red = kDecWaves * 64 * 4 * sizeof(float);
+  const dim3 block(kDecThreads);
+  hipError_t err;
+  // 1. h = x D^T
+  err = with_nch(H / 256, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    const size_t lds = (size_t)kDecodeMaxT * H * 2 + red + kDecodeMaxT * 4;
+    hipError_t e = set_lds((const void*)k_dec_dproj<n>, lds);
+    if (e == hipSuccess) e = mk.mark(kStageDproj, 0);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_dec_dproj<n>, dim3((L + 15) / 16), block, lds, st, a);
+      e = hipGetLastError();
+    }
+    return e == hipSuccess ? mk.mark(kStageDproj, 1) : e;
+  });
+  if (err != hipSuccess) return err;
+  // 2. router logits + top-k (last router workgroup) + shared expert gate/up
+  err = with_nch(L / 256, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    const size_t lds = (size_t)2 * kDecodeMaxT * L * 2 + red;
+    const int nrb = (E + 15) / 16;
+    const int nsh = a.n_shared ? (I / 16 + 1) / 2 : 0;
+    hipError_t e = set_lds((const void*)k_dec_router<n, n>, lds);
+    if (e == hipSuccess) e = mk.mark(kStageRouter, 0);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL((k_dec_router<n, n>), dim3(nrb + nsh), block, lds, st, a);
+      e = hipGetLastError();
+    }
+    return e == hipSuccess ? mk.mark(kStageRouter, 1) : e;
+  });
+  if (err != hipSuccess) return err;
+  // 3. routed gate/up
+  err = with_nch(L / 256, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    const size_t lds = (size_t)kDecodeMaxT * L * 2 + red;
+    const int nblk = (a.max_active * (I / 16) + 1) / 2;
+    hipError_t e = set_lds((const void*)k_dec_gateup<n>, lds);
+    if (e == hipSuccess) e = mk.mark(kStageGateup, 0);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_dec_gateup<n>, dim3(nblk), block, lds, st, a);
+      e = hipGetLastError();
+    }
+    return e == hipSuccess ? mk.mark(kStageGateup, 1) : e;
+  });
+  if (err != hipSuccess) return err;
+  // 4. down + combine
+  err = with_nch(I / 128, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    hipError_t e = mk.mark(kStageDown, 0);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_dec_down<n>, dim3(((L + 15) / 16) * a.n_zpart), block, 0, st, a);
+      e = hipGetLastError();
+    }
+    return e == hipSuccess ? mk.mark(kStageDown, 1) : e;
+  });
+  if (err != hipSuccess) return err;
+  // 5. out = z U^T (+ x)
+  return with_nch(L / 256, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    const size_t lds = (size_t)kDecodeMaxT * L * 2 + red;
+    hipError_t e = set_lds((const void*)k_dec_uproj<n>, lds);
+    if (e == hipSuccess) e = mk.mark(kStageUproj, 0);
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(k_dec_uproj<n>, dim3((H + 15) / 16), block, lds, st, a);
+      e = hipGetLastError();
+    }
+    return e == hipSuccess ? mk.mark(kStageUproj, 1) : e;
+  });
+}
+
+}  // namespace moe

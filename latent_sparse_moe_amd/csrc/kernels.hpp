@@ -77,4 +77,64 @@ hipError_t launch_route_permute(const int32_t* idx, int pairs, int E,
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w, int T, int k,
                           int pairs, int latent, int n_shared, uint16_t* z, hipStream_t stream);
 
+// ------------------------------------------------------------------ decode path
+
+constexpr int kDecodeMaxT = 8;   // tokens the weight-streaming decode kernels take
+
+// Stage ids for optional timing events (match MOE_LATENT_STAGE_* in the header).
+enum { kStageNorm = 0, kStageDproj = 1, kStageRouter = 2, kStageTopk = 3, kStageRoute = 4,
+       kStageGateup = 5, kStageDown = 6, kStageCombine = 7, kStageUproj = 8 };
+
+// Records the caller's event pair of a stage on the stream (no-op when absent).
+struct StageMarks {
+  void* const* ev;
+  hipStream_t st;
+  hipError_t mark(int stage, int end) const {
+    if (!ev) return hipSuccess;
+    void* e = ev[2 * stage + end];
+    return e ? hipEventRecord((hipEvent_t)e, st) : hipSuccess;
+  }
+};
+
+struct DecodeArgs {
+  // inputs
+  const uint16_t* x;
+  const uint16_t* D;
+  const uint16_t* R;
+  const uint16_t* U;
+  const float* bias;         // or null
+  const float* norm_weight;  // residual block when non-null
+  float norm_eps;
+  Fp4Mat gate, up, down;           // routed experts
+  Fp4Mat sh_gate, sh_up, sh_down;  // shared expert (count 1)
+  int hidden, latent, inter, n_experts, top_k, n_shared, T;
+  // scratch (workspace)
+  uint16_t* hhi;       // [T][latent]
+  uint16_t* hlo;       // [T][latent]
+  float* logits;       // [T][E]
+  uint16_t* act;       // [1 + max_active][T][inter]   slot 0: shared expert
+  float* zpart;        // [n_zpart][T][latent]  per expert-slot group
+  int n_zpart;         // decode_zpart_groups(...)
+  int max_active;      // min(n_experts, T * top_k): capacity of the routing table
+  unsigned* down_counter;  // [latent/16] finished down workgroups per row block
+  uint16_t* z;         // [T][latent] combined expert output (bf16)
+  unsigned* route_counter;  // router workgroups that finished (zeroed by dec_dproj)
+  int* route_n_act;    // [1]
+  int* route_list;     // [max_active]
+  float* route_wtab;   // [1 + max_active][T]
+  // output
+  uint16_t* out;
+  // optional routing copies
+  int32_t* dbg_idx;
+  float* dbg_w;
+  int32_t* dbg_counts;
+  int32_t* dbg_offsets;
+  int32_t* dbg_perm;
+  float* dbg_logits;
+};
+
+bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int T);
+int decode_zpart_groups(int n_experts, int top_k, int T);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& mk);
+
 }  // namespace moe

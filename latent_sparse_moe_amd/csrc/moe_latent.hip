@@ -41,6 +41,12 @@ struct Layout {
   size_t act;       // bf16 [P + T*n_shared][inter]
   size_t y;         // bf16 [P + T*n_shared][latent]
   size_t z;         // bf16 [T][latent]
+  // decode path (T <= kDecodeMaxT)
+  size_t d_hhi, d_hlo;   // bf16 [T][latent]
+  size_t d_logits;       // fp32 [T][E]
+  size_t d_act;          // bf16 [1 + max_active][T][inter]
+  size_t d_zpart;        // fp32 [groups][T][latent]
+  size_t d_n_act, d_list, d_wtab, d_counter, d_down_counter, d_z;
   size_t total;
 };
 
@@ -69,6 +75,23 @@ Layout layout_of(const moe_latent_dims& d, int64_t T) {
   L.act = take(rows * d.inter * 2);
   L.y = take(rows * d.latent * 2);
   L.z = take(T * d.latent * 2);
+  if (T <= moe::kDecodeMaxT) {
+    const int64_t max_act = d.n_experts < T * d.top_k ? d.n_experts : T * d.top_k;
+    L.d_hhi = take(T * d.latent * 2);
+    L.d_hlo = take(T * d.latent * 2);
+    L.d_logits = take(T * d.n_experts * 4);
+    L.d_act = take((1 + max_act) * T * d.inter * 2);
+    L.d_zpart = take((int64_t)moe::decode_zpart_groups(d.n_experts, d.top_k, (int)T) * T * d.latent * 4);
+    L.d_n_act = take(4);
+    L.d_list = take(max_act * 4);
+    L.d_wtab = take((1 + max_act) * T * 4);
+    L.d_counter = take(4);
+    L.d_down_counter = take((d.latent + 15) / 16 * 4);
+    L.d_z = take(T * d.latent * 2);
+  } else {
+    L.d_hhi = L.d_hlo = L.d_logits = L.d_act = L.d_zpart = L.d_n_act = L.d_list = L.d_wtab = 0;
+    L.d_counter = L.d_down_counter = L.d_z = 0;
+  }
   L.total = at;
   return L;
 }
@@ -121,17 +144,6 @@ moe::Fp4Set to_set(const moe_fp4_experts* s) {
   return r;
 }
 
-// Records stage_events[2*stage + end] on the stream when the caller asked.
-struct StageMarks {
-  void* const* ev;
-  hipStream_t st;
-  hipError_t mark(int stage, int end) const {
-    if (!ev) return hipSuccess;
-    void* e = ev[2 * stage + end];
-    return e ? hipEventRecord((hipEvent_t)e, st) : hipSuccess;
-  }
-};
-
 #define HIP_TRY(expr)                                                                 \
   do {                                                                                \
     hipError_t e_ = (expr);                                                           \
@@ -161,13 +173,13 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   uint16_t* y = (uint16_t*)(ws + L.y);
   uint16_t* z = (uint16_t*)(ws + L.z);
 
-  const StageMarks sm{o.stage_events, st};
+  const moe::StageMarks sm{o.stage_events, st};
   // S0 (residual block only): pre-norm.
   const uint16_t* a_in = x;
   if (o.residual) {
-    HIP_TRY(sm.mark(MOE_LATENT_STAGE_NORM, 0));
+    HIP_TRY(sm.mark(moe::kStageNorm, 0));
     HIP_TRY(moe::launch_rmsnorm(x, o.norm_weight, o.norm_eps, u, T, H, st));
-    HIP_TRY(sm.mark(MOE_LATENT_STAGE_NORM, 1));
+    HIP_TRY(sm.mark(moe::kStageNorm, 1));
     a_in = u;
   }
   // S1: h = x D^T, stored as bf16 hi | lo.
@@ -175,44 +187,44 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   ep.out = hcat;
   ep.ldo = 2 * Lat;
   ep.lo_off = Lat;
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_DPROJ, 0));
+  HIP_TRY(sm.mark(moe::kStageDproj, 0));
   HIP_TRY(moe::launch_gemm_dense(moe::kEpiSplit, a_in, H, D, H, H, T, Lat, H, ep, st));
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_DPROJ, 1));
+  HIP_TRY(sm.mark(moe::kStageDproj, 1));
   // S2: logits = (hi + lo) R^T + b, as a GEMM over K = 2*latent with R read twice.
   ep = moe::DenseEpilogue{};
   ep.out = logits;
   ep.ldo = E;
   ep.bias = router->bias;
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_ROUTER, 0));
+  HIP_TRY(sm.mark(moe::kStageRouter, 0));
   HIP_TRY(moe::launch_gemm_dense(moe::kEpiLogits, hcat, 2 * Lat, router->w, Lat, Lat, T, E,
                                  2 * Lat, ep, st));
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_ROUTER, 1));
+  HIP_TRY(sm.mark(moe::kStageRouter, 1));
   // S3: top-k + renormalised softmax weights.
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_TOPK, 0));
+  HIP_TRY(sm.mark(moe::kStageTopk, 0));
   HIP_TRY(moe::launch_topk(logits, T, E, k, idx, w, st));
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_TOPK, 1));
+  HIP_TRY(sm.mark(moe::kStageTopk, 1));
   // S4-S6: histogram, prefix sums, stable permutation.
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_ROUTE, 0));
+  HIP_TRY(sm.mark(moe::kStageRoute, 0));
   HIP_TRY(moe::launch_route_hist(idx, P, E, chunk, st));
   HIP_TRY(moe::launch_route_scan(chunk, nch, E, P, T, d.n_shared, counts, off, tile_off, st));
   HIP_TRY(moe::launch_route_permute(idx, P, E, chunk, perm, slot, st));
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_ROUTE, 1));
+  HIP_TRY(sm.mark(moe::kStageRoute, 1));
   // S7-S9: grouped expert GEMMs (routed groups, then the shared expert).
   moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k};
   moe::ExpertsView ex{};
   ex.routed = to_set(experts);
   if (d.n_shared) ex.shared = to_set(shared);
   const int max_mtiles = (P + 127) / 128 + (E < P ? E : P) + d.n_shared * ((T + 127) / 128);
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_GATEUP, 0));
+  HIP_TRY(sm.mark(moe::kStageGateup, 0));
   HIP_TRY(moe::launch_expert_gateup(hcat, 2 * Lat, rv, ex, act, I, Lat, max_mtiles, st));
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_GATEUP, 1));
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_DOWN, 0));
+  HIP_TRY(sm.mark(moe::kStageGateup, 1));
+  HIP_TRY(sm.mark(moe::kStageDown, 0));
   HIP_TRY(moe::launch_expert_down(act, rv, ex, y, I, Lat, max_mtiles, st));
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_DOWN, 1));
+  HIP_TRY(sm.mark(moe::kStageDown, 1));
   // S10: weighted combine in fixed order.
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_COMBINE, 0));
+  HIP_TRY(sm.mark(moe::kStageCombine, 0));
   HIP_TRY(moe::launch_combine(y, slot, w, T, k, P, Lat, d.n_shared, z, st));
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_COMBINE, 1));
+  HIP_TRY(sm.mark(moe::kStageCombine, 1));
   // S11: out = z U^T (+ x for the residual block).
   ep = moe::DenseEpilogue{};
   ep.out = out;
@@ -221,9 +233,9 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
     ep.resid = x;
     ep.ldr = H;
   }
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_UPROJ, 0));
+  HIP_TRY(sm.mark(moe::kStageUproj, 0));
   HIP_TRY(moe::launch_gemm_dense(moe::kEpiOut, z, Lat, U, Lat, Lat, T, H, Lat, ep, st));
-  HIP_TRY(sm.mark(MOE_LATENT_STAGE_UPROJ, 1));
+  HIP_TRY(sm.mark(moe::kStageUproj, 1));
 
   if (dbg) {
     if (dbg->topk_idx) HIP_TRY(hipMemcpyAsync(dbg->topk_idx, idx, (size_t)P * 4, hipMemcpyDeviceToDevice, st));
@@ -233,6 +245,61 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
     if (dbg->perm) HIP_TRY(hipMemcpyAsync(dbg->perm, perm, (size_t)P * 4, hipMemcpyDeviceToDevice, st));
     if (dbg->logits) HIP_TRY(hipMemcpyAsync(dbg->logits, logits, (size_t)T * E * 4, hipMemcpyDeviceToDevice, st));
   }
+  return 0;
+}
+
+int run_decode(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_t* D,
+               const uint16_t* U, const moe_router* router, const moe_fp4_experts* experts,
+               const moe_fp4_experts* shared, uint16_t* out, char* ws, const Layout& L,
+               moe_route_debug* dbg, const moe_latent_opts& o, hipStream_t st) {
+  moe::DecodeArgs a{};
+  a.x = x;
+  a.D = D;
+  a.R = router->w;
+  a.U = U;
+  a.bias = router->bias;
+  a.norm_weight = o.residual ? o.norm_weight : nullptr;
+  a.norm_eps = o.norm_eps;
+  const moe::Fp4Set rs = to_set(experts);
+  a.gate = rs.gate;
+  a.up = rs.up;
+  a.down = rs.down;
+  if (d.n_shared) {
+    const moe::Fp4Set ss = to_set(shared);
+    a.sh_gate = ss.gate;
+    a.sh_up = ss.up;
+    a.sh_down = ss.down;
+  }
+  a.hidden = d.hidden;
+  a.latent = d.latent;
+  a.inter = d.inter;
+  a.n_experts = d.n_experts;
+  a.top_k = d.top_k;
+  a.n_shared = d.n_shared;
+  a.T = T;
+  a.hhi = (uint16_t*)(ws + L.d_hhi);
+  a.hlo = (uint16_t*)(ws + L.d_hlo);
+  a.logits = (float*)(ws + L.d_logits);
+  a.act = (uint16_t*)(ws + L.d_act);
+  a.zpart = (float*)(ws + L.d_zpart);
+  a.route_n_act = (int*)(ws + L.d_n_act);
+  a.route_list = (int*)(ws + L.d_list);
+  a.route_wtab = (float*)(ws + L.d_wtab);
+  a.route_counter = (unsigned*)(ws + L.d_counter);
+  a.n_zpart = moe::decode_zpart_groups(d.n_experts, d.top_k, T);
+  a.max_active = d.n_experts < T * d.top_k ? d.n_experts : T * d.top_k;
+  a.down_counter = (unsigned*)(ws + L.d_down_counter);
+  a.z = (uint16_t*)(ws + L.d_z);
+  a.out = out;
+  if (dbg) {
+    a.dbg_idx = dbg->topk_idx;
+    a.dbg_w = dbg->topk_w;
+    a.dbg_counts = dbg->counts;
+    a.dbg_offsets = dbg->offsets;
+    a.dbg_perm = dbg->perm;
+    a.dbg_logits = dbg->logits;
+  }
+  HIP_TRY(moe::launch_decode(a, st, moe::StageMarks{o.stage_events, st}));
   return 0;
 }
 
@@ -292,6 +359,14 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
   if (overlaps(workspace, L.total, out, xbytes) || overlaps(workspace, L.total, x, xbytes))
     return fail(MOE_LATENT_EINVAL, "workspace overlaps x or out");
 
+  const bool dec_ok = moe::decode_supported(d.hidden, d.latent, d.inter, d.n_experts, d.top_k,
+                                            (int)T);
+  if (o.path == MOE_LATENT_PATH_DECODE && !dec_ok)
+    return fail(MOE_LATENT_EUNSUPPORTED, "the decode path does not take these dims / T");
+  if (o.path == MOE_LATENT_PATH_DECODE || (o.path == MOE_LATENT_PATH_AUTO && dec_ok))
+    return run_decode(d, (int)T, (const uint16_t*)x, (const uint16_t*)D, (const uint16_t*)U,
+                      router, experts, shared, (uint16_t*)out, (char*)workspace, L, debug, o,
+                      (hipStream_t)stream);
   return run_grouped(d, (int)T, (const uint16_t*)x, (const uint16_t*)D, (const uint16_t*)U,
                      router, experts, shared, (uint16_t*)out, (char*)workspace, L, debug, o,
                      (hipStream_t)stream);

@@ -146,3 +146,88 @@ def test_residual_block():
     err = rel_l2(gpu["out"][~near] - xv[~near], want[~near] - xv[~near])
     say(f"[ok] residual block moe-part rel_l2={err:.3e} full={rel_l2(gpu['out'], want):.3e}")
     assert err <= 2e-2
+
+
+# ------------------------------------------------------------------ decode path (T <= 8)
+
+DEC_SMALL = synth.Dims(hidden=512, latent=256, n_experts=64, inter=128, top_k=4, n_shared=1)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 5, 8])
+def test_decode_path_145b(T):
+    cfg, host, dl = layer_for("decode145")
+    x = synth.make_x(T, cfg.dims.hidden, cfg.seed if T == 4 else 300 + T)
+    run_case(f"decode145 decode-path T={T}", host, dl, x, lsm.PATH_DECODE)
+
+
+def test_decode_path_120b():
+    cfg, host, dl = layer_for("prefill120")
+    x = synth.make_x(4, cfg.dims.hidden, 41)
+    run_case("120b decode-path T=4", host, dl, x, lsm.PATH_DECODE)
+
+
+@pytest.mark.parametrize("variant", ["small", "small_no_shared", "small_hot", "small_k1"])
+def test_decode_path_variants(variant):
+    d, bias, zs = DEC_SMALL, "none", 1.1
+    if variant == "small_no_shared":
+        d = synth.replace(d, n_shared=0)
+    elif variant == "small_hot":
+        bias, zs = "zipf", 40.0
+    elif variant == "small_k1":
+        d = synth.replace(d, top_k=1)
+    host = synth.make_layer(d, 17, bias, zs)
+    dl = lsm.DeviceLayer.from_host(host, device())
+    for T in (1, 7):
+        x = synth.make_x(T, d.hidden, 17 + T)
+        run_case(f"{variant} decode-path T={T}", host, dl, x, lsm.PATH_DECODE)
+
+
+def test_decode_path_matches_grouped_routing():
+    """Both paths on the same input: identical routing bookkeeping, outputs
+    within the oracle bar of each other."""
+    cfg, host, dl = layer_for("decode145")
+    x = synth.make_x(4, cfg.dims.hidden, cfg.seed)
+    say("[case] decode vs grouped path, decode145 T=4")
+    a = run_gpu(dl, x, path=lsm.PATH_DECODE)
+    b = run_gpu(dl, x, path=lsm.PATH_GROUPED)
+    ref = oracle.forward(host, x)
+    ok = ref.gap >= 1e-4
+    for t in np.nonzero(ok)[0]:
+        assert set(a["topk_idx"][t]) == set(b["topk_idx"][t])
+    from gpu_helpers import rel_l2
+    assert rel_l2(a["out"], b["out"]) < 2e-2
+
+
+def test_decode_path_residual_block():
+    d = synth.replace(synth.E145, n_experts=64)
+    host = synth.make_layer(d, 21, "zipf")
+    dl = lsm.DeviceLayer.from_host(host, device())
+    x = synth.make_x(8, d.hidden, 21)
+    say("[case] residual block, decode path, 145B shapes, 64 experts")
+    gpu = run_gpu(dl, x, path=lsm.PATH_DECODE, residual=True)
+    want, ref = oracle.block_forward(host, x, 1e-6)
+    check_routing(ref, gpu, d.top_k, d.n_experts)
+    from gpu_helpers import rel_l2
+    near = ref.gap < 1e-4
+    xv = oracle.bf16_value(x)
+    err = rel_l2(gpu["out"][~near] - xv[~near], want[~near] - xv[~near])
+    say(f"[ok] residual block decode path moe-part rel_l2={err:.3e}")
+    assert err <= 2e-2
+
+
+def test_decode_path_deterministic():
+    cfg, host, dl = layer_for("decode145")
+    x = synth.make_x(4, cfg.dims.hidden, cfg.seed)
+    say("[case] determinism decode path")
+    a = run_gpu(dl, x, path=lsm.PATH_DECODE)
+    b = run_gpu(dl, x, path=lsm.PATH_DECODE)
+    for f in ("out_bits", "topk_idx", "topk_w", "perm", "counts", "logits"):
+        assert np.array_equal(a[f], b[f]), f
+
+
+def test_auto_path_picks_decode_and_rejects_unsupported():
+    cfg, host, dl = layer_for("tiny")
+    x = torch.zeros((4, cfg.dims.hidden), dtype=torch.bfloat16, device=device())
+    say("[case] PATH_DECODE on unsupported dims raises")
+    with pytest.raises(lsm.MoeLatentError):
+        lsm.forward(x, dl, path=lsm.PATH_DECODE)
