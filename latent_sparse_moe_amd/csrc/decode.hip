@@ -1,10 +1,10 @@
 // Weight-streaming decode path of the latent-MoE layer (T <= 8 tokens).
 //
 // At a handful of tokens every weight byte feeds only T multiply-adds, so the
-// layer is bound by HBM bandwidth. Five kernels; in each, every wave issues
-// all of its weight loads before anything else (a kernel boundary is the
-// cheapest grid-wide synchronisation on this chip and needs no co-residency
-// assumption):
+// layer is bound by HBM bandwidth and by the fixed latency of each dependent
+// step. Five kernels; in each, every wave issues its loads before anything
+// else, and a kernel boundary is the only grid-wide synchronisation (no
+// workgroup ever waits for another one to be scheduled):
 //
 //   1. dec_dproj   h = x D^T (RMSNorm fused for the residual block); K split
 //                  over the 8 waves; h leaves as bf16 hi + lo
@@ -12,13 +12,14 @@
 //                  last router workgroup to finish takes the top-k of every
 //                  token and publishes the routing table. The shared expert's
 //                  gate/up (routing-independent) runs in the same launch.
-//   3. dec_gateup  one wave per (routed expert, 16 intermediate rows):
-//                  silu(gate) * up
-//   4. dec_down    one workgroup per (16 latent rows, 8 expert slots), one
-//                  expert per wave: down rows, weighted by the gate weights
-//                  and summed over the waves in a fixed order
-//   5. dec_uproj   z = sum of the per-group partials (fixed order);
-//                  out = z U^T (+ x)
+//   3. dec_gateup  one wave per (routed expert, 16 intermediate rows, matrix,
+//                  K half): silu(gate) * up
+//   4. dec_down    one workgroup per (expert slot, 128 latent rows): the slot's
+//                  activations are staged once in LDS, each wave takes 16 rows;
+//                  partial rows, weighted by the gate weights, go to a per-slot
+//                  buffer. The last workgroup of a row range to finish sums the
+//                  slots in a fixed order and writes z (bf16).
+//   5. dec_uproj   out = z U^T (+ x)
 //
 // Matrix-core tiles are v_mfma_f32_16x16x32_bf16 with weight rows as the M
 // operand (16 rows) and tokens as the N operand (16 columns, T used; the rest
@@ -28,13 +29,21 @@
 // inside a dot product is free; the token operand is read with the same
 // chunk mapping.
 //
+// The top-k runs once per call, in one workgroup: every wave of it executes
+// some hundreds of dependent instructions per token, which would cost several
+// microseconds if every gate/up workgroup repeated it.
+//
 // Cross-workgroup data inside one launch (router logits -> the last router
-// workgroup) moves through agent-scope relaxed atomic accesses, which are
-// coherent across the chip's XCDs without flushing the L2 caches; everything
-// else crosses kernel boundaries.
+// workgroup, per-slot partial rows -> the last down workgroup of a row range)
+// moves through agent-scope relaxed atomic accesses, which are coherent across
+// the chip's XCDs without flushing the L2 caches; everything else crosses
+// kernel boundaries.
 #include <limits.h>
 
+#include <mutex>
+#include <set>
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -43,7 +52,8 @@ namespace moe {
 
 constexpr int kDecThreads = 512;  // 8 waves
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kSlotsPerGroup = kDecWaves;  // down kernel: one expert slot per wave
+constexpr int kDownRows = kDecodeDownRows;
+static_assert(kDownRows == kDecWaves * 16, "one 16-row tile per wave");
 
 #define AGENT __HIP_MEMORY_SCOPE_AGENT
 
@@ -96,7 +106,7 @@ struct Fp4Rows {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) s[i] = *(const uint16_t*)(srow + (kb + (i * 4 + g) * 32) / 16);
   }
-  // token operand from a row in memory (LDS or global), or null (zero column)
+  // token operand from a row in LDS, or null (zero column)
   __device__ __forceinline__ void mma(const uint16_t* act, int kb, int g, f32x4& acc) const {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -108,18 +118,6 @@ struct Fp4Rows {
         if (act) b = *(const bf16x8*)(act + kb + (i * 4 + g) * 32 + q * 8);
         acc = mfma16x16x32(dequant8(d[q], q < 2 ? s0 : s1), b, acc);
       }
-    }
-  }
-  // token operand already in registers (4 x 8 bf16 per chunk)
-  __device__ __forceinline__ void mma_regs(const uint4 (&b)[NCH * 4], f32x4& acc) const {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const float s0 = e4m3_to_f32(s[i] & 0xFFu), s1 = e4m3_to_f32((s[i] >> 8) & 0xFFu);
-      const uint32_t d[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        acc = mfma16x16x32(dequant8(d[q], q < 2 ? s0 : s1),
-                           __builtin_bit_cast(bf16x8, b[i * 4 + q]), acc);
     }
   }
 };
@@ -160,15 +158,23 @@ struct RowStage {
   }
 };
 
+// Dynamic LDS layouts (bytes), sized by the call's T.
+constexpr size_t kRedBytes = kDecWaves * 64 * 4 * sizeof(float);
+inline size_t dproj_lds(int T, int H) { return (size_t)T * H * 2 + kRedBytes + kDecodeMaxT * 4; }
+inline size_t router_lds(int T, int L) { return (size_t)2 * T * L * 2 + kRedBytes; }
+inline size_t gateup_lds(int T, int L) { return (size_t)T * L * 2 + kRedBytes; }
+inline size_t down_lds(int T, int I) { return (size_t)T * I * 2; }
+inline size_t uproj_lds(int T, int L) { return (size_t)T * L * 2 + kRedBytes; }
+
 // ------------------------------------------------------------------ 1. D
 
 template <int NCH>
 __global__ __launch_bounds__(kDecThreads) void k_dec_dproj(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int H = a.hidden, L = a.latent, T = a.T;
-  uint16_t* xs = lds;                                // [T][H] bf16
-  float* red = (float*)(lds + kDecodeMaxT * H);      // [8][64][4]
-  float* rstd = red + kDecWaves * 64 * 4;            // [T]
+  uint16_t* xs = lds;                       // [T][H] bf16
+  float* red = (float*)(lds + T * H);       // [8][64][4]
+  float* rstd = red + kDecWaves * 64 * 4;   // [T]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
   const int row0 = blockIdx.x * 16;
@@ -228,83 +234,6 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_dproj(DecodeArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ top-k
-
-// (value, expert) keys ordered so that a larger value wins and equal values
-// go to the lower expert: key = (order-preserving value bits << 32) | ~expert.
-__device__ __forceinline__ uint64_t order_key(float v, int e) {
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)e);
-}
-__device__ __forceinline__ float key_value(uint64_t k) {
-  uint32_t u = (uint32_t)(k >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-  return __uint_as_float(u);
-}
-__device__ __forceinline__ int key_expert(uint64_t k) { return (int)(~(uint32_t)k); }
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max64(uint64_t v) {
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  const uint32_t lo2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, CTRL, 0xF, 0xF, false);
-  const uint32_t hi2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, CTRL, 0xF, 0xF, false);
-  const uint64_t o = ((uint64_t)hi2 << 32) | lo2;
-  return o > v ? o : v;
-}
-
-// Largest key over the 64 lanes (same value in every lane): DPP steps inside
-// each 16-lane row, then the four row results through readlane.
-__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
-  v = dpp_max64<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_max64<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_max64<0x141>(v);  // row_half_mirror: max over 8 lanes
-  v = dpp_max64<0x140>(v);  // row_mirror: max over 16 lanes
-  uint64_t best = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, r * 16);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), r * 16);
-    const uint64_t k = ((uint64_t)hi << 32) | lo;
-    best = k > best ? k : best;
-  }
-  return best;
-}
-
-// Top-k of one token's logits by this wave; lane j < k ends with choice j
-// (descending). Renormalised weights: exp(l_j - l_0) / sum over the k.
-template <int EPL>
-__device__ __forceinline__ void wave_topk(const float* logits_row, int E, int k, int* out_e,
-                                          float* out_w) {
-  const int lane = threadIdx.x & 63;
-  uint64_t key[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? order_key(__hip_atomic_load(logits_row + e, __ATOMIC_RELAXED, AGENT), e)
-                   : 0ull;
-  }
-  uint64_t mine = 0;
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-    const uint64_t win = wave_max64(best);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) key[i] = key[i] == win ? 0ull : key[i];
-    if (lane == r) mine = win;
-  }
-  const uint32_t lo0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, 0);
-  const uint32_t hi0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), 0);
-  const float top = key_value(((uint64_t)hi0 << 32) | lo0);
-  const float ex = lane < k ? expf(key_value(mine) - top) : 0.0f;
-  const float sum = wave_sum(ex);
-  if (lane < k) {
-    out_e[lane] = key_expert(mine);
-    out_w[lane] = ex / sum;
-  }
-}
-
 // ------------------------------------------------------------------ 2. router + shared gate/up
 
 // SiLU(gate) * up of a 16-row tile, to act[t][n0 + rows] (bf16, t < T).
@@ -332,9 +261,10 @@ struct GateUpTask {
   __device__ __forceinline__ void load(const Fp4Mat& gate, const Fp4Mat& up, int e, int I, int L,
                                        int n0, int wave, int lane) {
     const int mat = (wave >> 1) & 1, half = wave & 1, g = lane >> 4;
-    const Fp4Mat& m = mat ? up : gate;
+    const uint8_t* codes = mat ? up.codes : gate.codes;
+    const uint8_t* scales = mat ? up.scales : gate.scales;
     const size_t row = ((size_t)e * I + n0 + (lane & 15)) * L;
-    wr.load(m.codes + row / 2, m.scales + row / 16, half * (L / 2), g);
+    wr.load(codes + row / 2, scales + row / 16, half * (L / 2), g);
   }
   __device__ __forceinline__ f32x4 mma(const uint16_t* act, int L, int wave, int lane) const {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -359,6 +289,104 @@ __device__ __forceinline__ void finish_gateup(f32x4 acc, float* red, bool tile_b
   }
 }
 
+// ------------------------------------------------------------------ top-k
+
+// Order-preserving 32-bit key of an fp32 value (larger value, larger key;
+// 0 is below every non-NaN value and marks an empty or taken entry).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+  return o > v ? o : v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umin(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+  return o < v ? o : v;
+}
+
+// Largest / smallest value over the 64 lanes (wave-uniform): DPP steps
+// inside each 16-lane row, then the four row results through readlane.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = dpp_umax<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_umax<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_umax<0x141>(v);  // row_half_mirror: over 8 lanes
+  v = dpp_umax<0x140>(v);  // row_mirror: over 16 lanes
+  uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, r * 16);
+    m = o > m ? o : m;
+  }
+  return m;
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = dpp_umin<0xB1>(v);
+  v = dpp_umin<0x4E>(v);
+  v = dpp_umin<0x141>(v);
+  v = dpp_umin<0x140>(v);
+  uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, r * 16);
+    m = o < m ? o : m;
+  }
+  return m;
+}
+
+// Top-k of one token's logits by this wave; lane j < k ends with choice j
+// (descending value, equal values to the lower expert). Renormalised
+// weights: exp(l_j - l_0) / sum over the k chosen. The logits were written
+// by other workgroups of this launch: agent-scope loads.
+template <int EPL>
+__device__ __forceinline__ void wave_topk(const float* row, int E, int k, int* out_e,
+                                          float* out_w) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? order_key(__hip_atomic_load(row + min(e, E - 1), __ATOMIC_RELAXED, AGENT))
+                   : 0u;
+  }
+  uint32_t my_key = 0u;
+  int my_e = 0;
+  for (int r = 0; r < k; ++r) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    const uint32_t m = wave_umax(best);
+    // the lowest expert holding m (expert = lane + 64 i)
+    uint32_t first = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = EPL - 1; i >= 0; --i) first = key[i] == m ? (uint32_t)(lane + 64 * i) : first;
+    const int win = (int)min(wave_umin(first), (uint32_t)(E - 1));  // in range even for NaN
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i == win ? 0u : key[i];
+    if (lane == r) {
+      my_key = m;
+      my_e = win;
+    }
+  }
+  const float top = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
+  const float ex = lane < k ? expf(key_value(my_key) - top) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    out_e[lane] = my_e;
+    out_w[lane] = ex / sum;
+  }
+}
+
+// ------------------------------------------------------------------ routing table
+
 struct RouteLds {
   int idx[kDecodeMaxT * 16];
   float w[kDecodeMaxT * 16];
@@ -367,15 +395,10 @@ struct RouteLds {
   int n_act;
 };
 
-// Routing table from the T x k choices in `rl` (one workgroup): the active
-// experts in ascending order, each token's gate weight per slot (slot 0 is the
-// shared expert with weight 1, slot s >= 1 the s-th active expert), and the
-// optional debug copies.
-__device__ void publish_routing(const DecodeArgs& a, RouteLds& rl) {
-  const int E = a.n_experts, T = a.T, k = a.top_k, P = T * k;
+// The active experts of the T x k choices in ascending order (rl.list,
+// rl.n_act). rl.flags must be zero and rl.idx complete (barrier) on entry.
+__device__ __forceinline__ void build_active_list(int E, int P, RouteLds& rl) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
-  __syncthreads();
   for (int p = tid; p < P; p += kDecThreads)
     atomicOr(&rl.flags[rl.idx[p] >> 5], 1u << (rl.idx[p] & 31));
   __syncthreads();
@@ -389,6 +412,14 @@ __device__ void publish_routing(const DecodeArgs& a, RouteLds& rl) {
     if (lane == 63) rl.n_act = inc;
   }
   __syncthreads();
+}
+
+// Routing table for the down kernel: the active list, each token's gate
+// weight per slot (slot 0 is the shared expert with weight 1, slot s >= 1
+// the s-th active expert), and the optional debug copies.
+__device__ __forceinline__ void publish_routing(const DecodeArgs& a, const RouteLds& rl) {
+  const int E = a.n_experts, T = a.T, k = a.top_k, P = T * k;
+  const int tid = threadIdx.x;
   const int n_act = rl.n_act;
   if (tid == 0) a.route_n_act[0] = n_act;
   for (int i = tid; i < n_act; i += kDecThreads) a.route_list[i] = rl.list[i];
@@ -440,9 +471,9 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
   __shared__ RouteLds rl;
   __shared__ unsigned last_flag;
   const int L = a.latent, T = a.T, E = a.n_experts, I = a.inter;
-  uint16_t* hi = lds;                    // [T][L]
-  uint16_t* lo = lds + kDecodeMaxT * L;  // [T][L]
-  float* red = (float*)(lo + kDecodeMaxT * L);
+  uint16_t* hi = lds;           // [T][L]
+  uint16_t* lo = lds + T * L;   // [T][L]
+  float* red = (float*)(lo + T * L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
   const int nrb = (E + 15) / 16;
@@ -456,6 +487,11 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
     sh_lo.load(a.hlo, T * L);
     Bf16Rows<NCH_R> wr;
     wr.load(a.R + (size_t)e * L, kb, g);
+    float bias[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.bias && wave == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bias[r] = a.bias[min(e0 + g * 4 + r, E - 1)];
+    }
     sh_hi.store(hi, T * L);
     sh_lo.store(lo, T * L);
     __syncthreads();
@@ -467,8 +503,8 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int ee = e0 + g * 4 + r;
         if (ee < E)
-          __hip_atomic_store(a.logits + (size_t)t * E + ee, tot[r] + (a.bias ? a.bias[ee] : 0.0f),
-                             __ATOMIC_RELAXED, AGENT);
+          __hip_atomic_store(a.logits + (size_t)t * E + ee, tot[r] + bias[r], __ATOMIC_RELAXED,
+                             AGENT);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // the logits stores complete before the arrival count
@@ -479,6 +515,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
     __syncthreads();
     if (!last_flag) return;
     // the last router workgroup: top-k of every token, then the routing table
+    for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
     if (wave < T) {
       if (E <= 512)
         wave_topk<8>(a.logits + (size_t)wave * E, E, a.top_k, rl.idx + wave * a.top_k,
@@ -488,6 +525,8 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
                       rl.w + wave * a.top_k);
     }
     __syncthreads();
+    build_active_list(E, T * a.top_k, rl);
+    for (int i = tid; i < decode_row_ranges(L); i += kDecThreads) a.down_counter[i] = 0u;
     publish_routing(a, rl);
     return;
   }
@@ -500,11 +539,12 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
   st.load(a.hhi, T * L);
   GateUpTask<NCH_H> task;
   if (busy) task.load(a.sh_gate, a.sh_up, 0, I, L, n0, wave, lane);
+  const float gsg = a.sh_gate.gscale[0], gsu = a.sh_up.gscale[0];
   st.store(hi, T * L);
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (busy) acc = task.mma(t < T ? hi + t * L : nullptr, L, wave, lane);
-  finish_gateup(acc, red, busy, a.sh_gate.gscale[0], a.sh_up.gscale[0], a.act, I, T, n0);
+  finish_gateup(acc, red, busy, gsg, gsu, a.act, I, T, n0);
 }
 
 // ------------------------------------------------------------------ 3. routed gate/up
@@ -514,7 +554,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int L = a.latent, T = a.T, I = a.inter;
   uint16_t* hi = lds;  // [T][L]
-  float* red = (float*)(lds + kDecodeMaxT * L);
+  float* red = (float*)(lds + T * L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = lane & 15;
   const int tiles = I / 16;
@@ -522,92 +562,92 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   // the routing table: entry count and this tile's expert, read together
   const int n_act = a.route_n_act[0];
   const int e_guess = a.route_list[min(tile / tiles, a.max_active - 1)];
-  if (blockIdx.x == 0 && tid < (a.latent + 15) / 16) a.down_counter[tid] = 0u;
+  if ((int)blockIdx.x * 2 >= n_act * tiles) return;  // both tiles idle (uniform)
   const bool busy = tile < n_act * tiles;
-  if (__syncthreads_or(busy ? 1 : 0) == 0) return;
-  const int slot = 1 + tile / tiles;
-  const int n0 = (tile % tiles) * 16;
+  const int e = busy ? e_guess : 0;
+  const int n0 = busy ? (tile % tiles) * 16 : 0;
   RowStage st;
   st.load(a.hhi, T * L);
   GateUpTask<NCH_H> task;
-  if (busy) task.load(a.gate, a.up, e_guess, I, L, n0, wave, lane);
+  if (busy) task.load(a.gate, a.up, e, I, L, n0, wave, lane);
+  const float gsg = a.gate.gscale[e], gsu = a.up.gscale[e];
   st.store(hi, T * L);
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (busy) acc = task.mma(t < T ? hi + t * L : nullptr, L, wave, lane);
-  finish_gateup(acc, red, busy, busy ? a.gate.gscale[e_guess] : 0.f,
-                busy ? a.up.gscale[e_guess] : 0.f, a.act + (size_t)slot * T * I, I, T, n0);
+  finish_gateup(acc, red, busy, gsg, gsu,
+                a.act + (size_t)(1 + (busy ? tile / tiles : 0)) * T * I, I, T, n0);
 }
 
 // ------------------------------------------------------------------ 4. down + combine
 
-// Workgroup (row block rb, slot group sg): wave w takes slot sg*8 + w (slot
-// 0 is the shared expert) and adds weight(t, slot) * gscale * y; the waves
-// are summed in order into zpart[sg]. The last workgroup of a row block to
-// finish sums the groups in order and writes z (bf16) for those rows.
 template <int NCH_D>
 __global__ __launch_bounds__(kDecThreads) void k_dec_down(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) float red[kDecWaves * 64 * 4];
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [T][I] activations
   __shared__ unsigned last_flag;
   const int L = a.latent, T = a.T, I = a.inter;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
-  const int rb = blockIdx.x / a.n_zpart, sgrp = blockIdx.x % a.n_zpart;
-  const int s = sgrp * kSlotsPerGroup + wave;
+  const int nrr = decode_row_ranges(L);
+  const int s = blockIdx.x / nrr, rr = blockIdx.x % nrr;
+  // the routing table, read together (the guesses are clamped in range)
   const int n_act = a.route_n_act[0];
-  const int e_guess = s >= 1 ? a.route_list[min(s - 1, a.max_active - 1)] : 0;
-  const float w_guess = t < T ? a.route_wtab[min(s, a.max_active) * T + t] : 0.f;
+  const int e_guess = a.route_list[min(max(s - 1, 0), a.max_active - 1)];
+  const float w_guess = a.route_wtab[min(s, a.max_active) * T + min(t, T - 1)];
   const bool sh = s == 0;
-  const bool busy = s <= n_act && (!sh || a.n_shared);
-  const int row0 = rb * 16;
+  if (sh ? a.n_shared == 0 : s > n_act) return;  // uniform over the workgroup
+  const int e = sh ? 0 : e_guess;
+  const uint8_t* codes = sh ? a.sh_down.codes : a.down.codes;
+  const uint8_t* scales = sh ? a.sh_down.scales : a.down.scales;
+  const float* gscale = sh ? a.sh_down.gscale : a.down.gscale;
+  RowStage st;
+  st.load(a.act + (size_t)s * T * I, T * I);
+  const int row0 = rr * kDownRows + wave * 16;
   const int row = min(row0 + (lane & 15), L - 1);
-  f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  if (busy) {
-    const int e = sh ? 0 : e_guess;
-    const Fp4Mat& m = sh ? a.sh_down : a.down;
-    uint4 b[NCH_D * 4];
-    const uint16_t* act = a.act + ((size_t)s * T + (t < T ? t : 0)) * I;
-#pragma unroll
-    for (int i = 0; i < NCH_D; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        b[i * 4 + q] = t < T ? *(const uint4*)(act + (i * 4 + g) * 32 + q * 8)
-                             : make_uint4(0u, 0u, 0u, 0u);
-    const size_t rowd = ((size_t)e * L + row) * I;
-    Fp4Rows<NCH_D> wd;
-    wd.load(m.codes + rowd / 2, m.scales + rowd / 16, 0, g);
-    const float wt = w_guess * m.gscale[e];
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-    wd.mma_regs(b, y);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = wt * y[r];
-  }
-  const f32x4 tot = reduce_waves(z, red);
-  if (wave == 0 && t < T) {
+  const size_t rowd = ((size_t)e * L + row) * I;
+  Fp4Rows<NCH_D> wd;
+  wd.load(codes + rowd / 2, scales + rowd / 16, 0, g);
+  const float gs = gscale[e];
+  st.store(lds, T * I);
+  __syncthreads();
+  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+  wd.mma(t < T ? lds + t * I : nullptr, 0, g, y);
+  if (t < T) {
+    const float wt = w_guess * gs;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int n = row0 + g * 4 + r;
       if (n < L)
-        __hip_atomic_store(a.zpart + ((size_t)sgrp * T + t) * L + n, tot[r], __ATOMIC_RELAXED,
+        __hip_atomic_store(a.zpart + ((size_t)s * T + t) * L + n, wt * y[r], __ATOMIC_RELAXED,
                            AGENT);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // partial sums complete before the arrival count
+  __builtin_amdgcn_s_waitcnt(0);  // partial rows complete before the arrival count
   __syncthreads();
+  const int s0 = a.n_shared ? 0 : 1;
   if (tid == 0)
-    last_flag = __hip_atomic_fetch_add(a.down_counter + rb, 1u, __ATOMIC_RELAXED, AGENT) ==
-                (unsigned)(a.n_zpart - 1);
+    last_flag = __hip_atomic_fetch_add(a.down_counter + rr, 1u, __ATOMIC_RELAXED, AGENT) ==
+                (unsigned)(n_act - s0);
   __syncthreads();
   if (!last_flag) return;
-  // last workgroup of the row block: z[t][rows] = sum of the groups in order
-  if (tid < 16 * T) {
-    const int tt = tid / 16, n = row0 + tid % 16;
-    if (n < L) {
-      float v = 0.f;
-      for (int gi = 0; gi < a.n_zpart; ++gi)
-        v += __hip_atomic_load(a.zpart + ((size_t)gi * T + tt) * L + n, __ATOMIC_RELAXED, AGENT);
-      a.z[(size_t)tt * L + n] = f32_to_bf16_bits(v);
+  // last workgroup of the row range: z[t][rows] = sum over the slots in order
+  const size_t step = (size_t)T * L;
+  for (int i = tid; i < T * kDownRows; i += kDecThreads) {
+    const int tt = i / kDownRows, n = rr * kDownRows + i % kDownRows;
+    if (n >= L) continue;
+    const float* src = a.zpart + (size_t)tt * L + n;
+    float v = 0.f;
+    int ss = s0;
+    for (; ss + 8 <= n_act + 1; ss += 8) {  // eight loads in flight, summed in order
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        p[j] = __hip_atomic_load(src + (ss + j) * step, __ATOMIC_RELAXED, AGENT);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += p[j];
     }
+    for (; ss <= n_act; ++ss) v += __hip_atomic_load(src + ss * step, __ATOMIC_RELAXED, AGENT);
+    a.z[(size_t)tt * L + n] = f32_to_bf16_bits(v);
   }
 }
 
@@ -618,7 +658,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int L = a.latent, H = a.hidden, T = a.T;
   uint16_t* zs = lds;  // [T][L] bf16
-  float* red = (float*)(lds + kDecodeMaxT * L);
+  float* red = (float*)(lds + T * L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
   const int m0 = blockIdx.x * 16;
@@ -648,8 +688,20 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
 
 // ------------------------------------------------------------------ launch
 
-static hipError_t set_lds(const void* fn, size_t bytes) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+// Raises a kernel's dynamic-LDS limit once per device (to what the largest
+// supported T needs) instead of on every call.
+static hipError_t ensure_lds(const void* fn, size_t bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({fn, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) done.insert({fn, dev});
+  return e;
 }
 
 // Calls f(std::integral_constant<int, N>) for the chunk counts the kernels
@@ -672,53 +724,49 @@ static bool nch_ok(int n) {
   return n == 1 || n == 2 || n == 4 || n == 5 || n == 7 || n == 8 || n == 10;
 }
 
-int decode_zpart_groups(int n_experts, int top_k, int T) {
-  const int max_act = n_experts < T * top_k ? n_experts : T * top_k;
-  return (1 + max_act + kSlotsPerGroup - 1) / kSlotsPerGroup;
-}
-
 bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int T) {
   if (T < 1 || T > kDecodeMaxT || n_experts > kMaxExperts || top_k > 16) return false;
   // D, U and the router split K over 8 waves x 4 lane groups x 8 bf16;
   // expert rows are consumed in 32-weight chunks by 4 lane groups.
   if (hidden % 256 || latent % 256 || inter % 128) return false;
   if (!nch_ok(hidden / 256) || !nch_ok(latent / 256) || !nch_ok(inter / 128)) return false;
-  if (latent / 128 > 14 || inter / 128 > 5) return false;  // register budget per wave
-  if (kDecodeMaxT * (hidden > latent ? hidden : latent) > kDecThreads * kStageVec * 8)
-    return false;  // activation staging (each staged array is at most T x max(hidden, latent))
-  const size_t red = kDecWaves * 64 * 4 * sizeof(float);
-  return (size_t)2 * kDecodeMaxT * latent * 2 + red <= 96 * 1024 &&
-         (size_t)kDecodeMaxT * hidden * 2 + red + 64 <= 96 * 1024;
+  if (latent / 128 > 14) return false;  // register budget of the gate/up waves
+  // activation staging: each staged array is at most T x max(hidden, latent, inter)
+  int widest = hidden > latent ? hidden : latent;
+  widest = widest > inter ? widest : inter;
+  if (kDecodeMaxT * widest > kDecThreads * kStageVec * 8) return false;
+  const size_t lim = 96 * 1024;
+  return dproj_lds(kDecodeMaxT, hidden) <= lim && router_lds(kDecodeMaxT, latent) <= lim &&
+         router_lds(kDecodeMaxT, latent) + sizeof(RouteLds) <= lim &&
+         gateup_lds(kDecodeMaxT, latent) <= lim &&
+         down_lds(kDecodeMaxT, inter) <= lim && uproj_lds(kDecodeMaxT, latent) <= lim;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& mk) {
-  const int H = a.hidden, L = a.latent, I = a.inter, E = a.n_experts;
-  const size_t red = kDecWaves * 64 * 4 * sizeof(float);
+  const int H = a.hidden, L = a.latent, I = a.inter, E = a.n_experts, T = a.T;
   const dim3 block(kDecThreads);
   hipError_t err;
   // 1. h = x D^T
   err = with_nch(H / 256, [&](auto N) {
     constexpr int n = decltype(N)::value;
-    const size_t lds = (size_t)kDecodeMaxT * H * 2 + red + kDecodeMaxT * 4;
-    hipError_t e = set_lds((const void*)k_dec_dproj<n>, lds);
+    hipError_t e = ensure_lds((const void*)k_dec_dproj<n>, dproj_lds(kDecodeMaxT, H));
     if (e == hipSuccess) e = mk.mark(kStageDproj, 0);
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_dec_dproj<n>, dim3((L + 15) / 16), block, lds, st, a);
+      hipLaunchKernelGGL(k_dec_dproj<n>, dim3((L + 15) / 16), block, dproj_lds(T, H), st, a);
       e = hipGetLastError();
     }
     return e == hipSuccess ? mk.mark(kStageDproj, 1) : e;
   });
   if (err != hipSuccess) return err;
-  // 2. router logits + top-k (last router workgroup) + shared expert gate/up
+  // 2. router logits + top-k + routing table, shared expert gate/up
   err = with_nch(L / 256, [&](auto N) {
     constexpr int n = decltype(N)::value;
-    const size_t lds = (size_t)2 * kDecodeMaxT * L * 2 + red;
     const int nrb = (E + 15) / 16;
     const int nsh = a.n_shared ? (I / 16 + 1) / 2 : 0;
-    hipError_t e = set_lds((const void*)k_dec_router<n, n>, lds);
+    hipError_t e = ensure_lds((const void*)k_dec_router<n, n>, router_lds(kDecodeMaxT, L));
     if (e == hipSuccess) e = mk.mark(kStageRouter, 0);
     if (e == hipSuccess) {
-      hipLaunchKernelGGL((k_dec_router<n, n>), dim3(nrb + nsh), block, lds, st, a);
+      hipLaunchKernelGGL((k_dec_router<n, n>), dim3(nrb + nsh), block, router_lds(T, L), st, a);
       e = hipGetLastError();
     }
     return e == hipSuccess ? mk.mark(kStageRouter, 1) : e;
@@ -727,12 +775,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
   // 3. routed gate/up
   err = with_nch(L / 256, [&](auto N) {
     constexpr int n = decltype(N)::value;
-    const size_t lds = (size_t)kDecodeMaxT * L * 2 + red;
     const int nblk = (a.max_active * (I / 16) + 1) / 2;
-    hipError_t e = set_lds((const void*)k_dec_gateup<n>, lds);
+    hipError_t e = ensure_lds((const void*)k_dec_gateup<n>, gateup_lds(kDecodeMaxT, L));
     if (e == hipSuccess) e = mk.mark(kStageGateup, 0);
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_dec_gateup<n>, dim3(nblk), block, lds, st, a);
+      hipLaunchKernelGGL(k_dec_gateup<n>, dim3(nblk), block, gateup_lds(T, L), st, a);
       e = hipGetLastError();
     }
     return e == hipSuccess ? mk.mark(kStageGateup, 1) : e;
@@ -741,9 +788,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
   // 4. down + combine
   err = with_nch(I / 128, [&](auto N) {
     constexpr int n = decltype(N)::value;
-    hipError_t e = mk.mark(kStageDown, 0);
+    hipError_t e = ensure_lds((const void*)k_dec_down<n>, down_lds(kDecodeMaxT, I));
+    if (e == hipSuccess) e = mk.mark(kStageDown, 0);
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_dec_down<n>, dim3(((L + 15) / 16) * a.n_zpart), block, 0, st, a);
+      hipLaunchKernelGGL(k_dec_down<n>, dim3((1 + a.max_active) * decode_row_ranges(L)), block,
+                         down_lds(T, I), st, a);
       e = hipGetLastError();
     }
     return e == hipSuccess ? mk.mark(kStageDown, 1) : e;
@@ -752,11 +801,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
   // 5. out = z U^T (+ x)
   return with_nch(L / 256, [&](auto N) {
     constexpr int n = decltype(N)::value;
-    const size_t lds = (size_t)kDecodeMaxT * L * 2 + red;
-    hipError_t e = set_lds((const void*)k_dec_uproj<n>, lds);
+    hipError_t e = ensure_lds((const void*)k_dec_uproj<n>, uproj_lds(kDecodeMaxT, L));
     if (e == hipSuccess) e = mk.mark(kStageUproj, 0);
     if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_dec_uproj<n>, dim3((H + 15) / 16), block, lds, st, a);
+      hipLaunchKernelGGL(k_dec_uproj<n>, dim3((H + 15) / 16), block, uproj_lds(T, L), st, a);
       e = hipGetLastError();
     }
     return e == hipSuccess ? mk.mark(kStageUproj, 1) : e;

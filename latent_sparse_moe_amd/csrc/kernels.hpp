@@ -113,10 +113,9 @@ struct DecodeArgs {
   uint16_t* hlo;       // [T][latent]
   float* logits;       // [T][E]
   uint16_t* act;       // [1 + max_active][T][inter]   slot 0: shared expert
-  float* zpart;        // [n_zpart][T][latent]  per expert-slot group
-  int n_zpart;         // decode_zpart_groups(...)
+  float* zpart;        // [1 + max_active][T][latent]  per-slot weighted down rows
   int max_active;      // min(n_experts, T * top_k): capacity of the routing table
-  unsigned* down_counter;  // [latent/16] finished down workgroups per row block
+  unsigned* down_counter;  // [decode_row_ranges(latent)] finished down slots per row range
   uint16_t* z;         // [T][latent] combined expert output (bf16)
   unsigned* route_counter;  // router workgroups that finished (zeroed by dec_dproj)
   int* route_n_act;    // [1]
@@ -134,7 +133,10 @@ struct DecodeArgs {
 };
 
 bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int T);
-int decode_zpart_groups(int n_experts, int top_k, int T);
+constexpr int kDecodeDownRows = 128;  // latent rows per down workgroup (8 waves x 16)
+__host__ __device__ inline int decode_row_ranges(int latent) {
+  return (latent + kDecodeDownRows - 1) / kDecodeDownRows;
+}
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& mk);
 
 }  // namespace moe
