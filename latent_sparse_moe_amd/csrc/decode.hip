@@ -750,12 +750,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
   err = with_nch(H / 256, [&](auto N) {
     constexpr int n = decltype(N)::value;
     hipError_t e = ensure_lds((const void*)k_dec_dproj<n>, dproj_lds(kDecodeMaxT, H));
-    if (e == hipSuccess) e = mk.mark(kStageDproj, 0);
-    if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_dec_dproj<n>, dim3((L + 15) / 16), block, dproj_lds(T, H), st, a);
-      e = hipGetLastError();
-    }
-    return e == hipSuccess ? mk.mark(kStageDproj, 1) : e;
+    if (e == hipSuccess)
+      e = mk.launch(kStageDproj, k_dec_dproj<n>, dim3((L + 15) / 16), block, dproj_lds(T, H), a);
+    return e;
   });
   if (err != hipSuccess) return err;
   // 2. router logits + top-k + routing table, shared expert gate/up
@@ -764,12 +761,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
     const int nrb = (E + 15) / 16;
     const int nsh = a.n_shared ? (I / 16 + 1) / 2 : 0;
     hipError_t e = ensure_lds((const void*)k_dec_router<n, n>, router_lds(kDecodeMaxT, L));
-    if (e == hipSuccess) e = mk.mark(kStageRouter, 0);
-    if (e == hipSuccess) {
-      hipLaunchKernelGGL((k_dec_router<n, n>), dim3(nrb + nsh), block, router_lds(T, L), st, a);
-      e = hipGetLastError();
-    }
-    return e == hipSuccess ? mk.mark(kStageRouter, 1) : e;
+    if (e == hipSuccess)
+      e = mk.launch(kStageRouter, k_dec_router<n, n>, dim3(nrb + nsh), block, router_lds(T, L), a);
+    return e;
   });
   if (err != hipSuccess) return err;
   // 3. routed gate/up
@@ -777,37 +771,28 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
     constexpr int n = decltype(N)::value;
     const int nblk = (a.max_active * (I / 16) + 1) / 2;
     hipError_t e = ensure_lds((const void*)k_dec_gateup<n>, gateup_lds(kDecodeMaxT, L));
-    if (e == hipSuccess) e = mk.mark(kStageGateup, 0);
-    if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_dec_gateup<n>, dim3(nblk), block, gateup_lds(T, L), st, a);
-      e = hipGetLastError();
-    }
-    return e == hipSuccess ? mk.mark(kStageGateup, 1) : e;
+    if (e == hipSuccess)
+      e = mk.launch(kStageGateup, k_dec_gateup<n>, dim3(nblk), block, gateup_lds(T, L), a);
+    return e;
   });
   if (err != hipSuccess) return err;
   // 4. down + combine
   err = with_nch(I / 128, [&](auto N) {
     constexpr int n = decltype(N)::value;
     hipError_t e = ensure_lds((const void*)k_dec_down<n>, down_lds(kDecodeMaxT, I));
-    if (e == hipSuccess) e = mk.mark(kStageDown, 0);
-    if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_dec_down<n>, dim3((1 + a.max_active) * decode_row_ranges(L)), block,
-                         down_lds(T, I), st, a);
-      e = hipGetLastError();
-    }
-    return e == hipSuccess ? mk.mark(kStageDown, 1) : e;
+    if (e == hipSuccess)
+      e = mk.launch(kStageDown, k_dec_down<n>, dim3((1 + a.max_active) * decode_row_ranges(L)),
+                    block, down_lds(T, I), a);
+    return e;
   });
   if (err != hipSuccess) return err;
   // 5. out = z U^T (+ x)
   return with_nch(L / 256, [&](auto N) {
     constexpr int n = decltype(N)::value;
     hipError_t e = ensure_lds((const void*)k_dec_uproj<n>, uproj_lds(kDecodeMaxT, L));
-    if (e == hipSuccess) e = mk.mark(kStageUproj, 0);
-    if (e == hipSuccess) {
-      hipLaunchKernelGGL(k_dec_uproj<n>, dim3((H + 15) / 16), block, uproj_lds(T, L), st, a);
-      e = hipGetLastError();
-    }
-    return e == hipSuccess ? mk.mark(kStageUproj, 1) : e;
+    if (e == hipSuccess)
+      e = mk.launch(kStageUproj, k_dec_uproj<n>, dim3((H + 15) / 16), block, uproj_lds(T, L), a);
+    return e;
   });
 }
 

@@ -13,6 +13,12 @@
 // matrix cores work on step k. Expert weights arrive as 4-bit codes and are
 // dequantised in registers (exactly, to bf16) on their way into LDS, so the
 // HBM traffic for weights is the 4.5-bit format, not bf16.
+//
+// Grids are one-dimensional over (m-tile, n-tile) with n fastest, and the
+// block id is permuted so that the workgroups the hardware places on one XCD
+// (consecutive ids go to the 8 XCDs in turn) take a contiguous range of
+// tiles: the n-tiles of one m-tile then run together on one XCD and share its
+// A rows through that XCD's L2 instead of fetching them once per n-tile.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,6 +26,14 @@ namespace moe {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;
+
+// Logical tile of workgroup b among n: XCD x = b % 8 takes the contiguous
+// range [x*q + min(x, r), ...) of q or q+1 tiles (q = n / 8, r = n % 8).
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  const int x = b % kXcds, q = n / kXcds, r = n % kXcds;
+  return x * q + min(x, r) + b / kXcds;
+}
 
 template <int BK>
 struct TileShape {
@@ -190,7 +204,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
                                                          int kwrap, int M, int N, int K,
                                                          DenseEpilogue ep) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[smem_elems<BK>()];
-  const int m0 = blockIdx.y * kTile, n0 = blockIdx.x * kTile;
+  const int nt = (N + kTile - 1) / kTile;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (tile / nt) * kTile, n0 = (tile % nt) * kTile;
   RowLoader<BK> al, bl;
   al.init([&](int r) { return A + (size_t)min(m0 + r, M - 1) * lda; }, K);
   bl.init([&](int r) { return B + (size_t)min(n0 + r, N - 1) * ldb; }, kwrap);
@@ -277,9 +293,11 @@ __global__ __launch_bounds__(kThreads) void k_expert_gateup(const uint16_t* __re
                                                             ExpertsView ex, uint16_t* __restrict__ act,
                                                             int inter, int latent) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[smem_elems<BK>()];
+  const int nt = (inter + 63) / 64;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
   TileWork tw;
-  if (!tile_work(rv, blockIdx.x, &tw)) return;
-  const int n0 = blockIdx.y * 64;
+  if (!tile_work(rv, tile / nt, &tw)) return;
+  const int n0 = (tile % nt) * 64;
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   const int P = rv.pairs;
@@ -325,9 +343,11 @@ __global__ __launch_bounds__(kThreads) void k_expert_down(const uint16_t* __rest
                                                           uint16_t* __restrict__ y, int inter,
                                                           int latent) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[smem_elems<BK>()];
+  const int nt = (latent + kTile - 1) / kTile;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
   TileWork tw;
-  if (!tile_work(rv, blockIdx.x, &tw)) return;
-  const int n0 = blockIdx.y * kTile;
+  if (!tile_work(rv, tile / nt, &tw)) return;
+  const int n0 = (tile % nt) * kTile;
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   RowLoader<BK> al;
@@ -366,7 +386,7 @@ static inline int pick_bk(int K, int kwrap) { return (K % 64 == 0 && kwrap % 64 
 hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t* B, int ldb,
                              int kwrap, int M, int N, int K, const DenseEpilogue& ep,
                              hipStream_t stream) {
-  dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile), block(kThreads);
+  dim3 grid(((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile)), block(kThreads);
   const int bk = pick_bk(K, kwrap);
 #define MOE_LAUNCH_DENSE(BKV, EPIV)                                                           \
   hipLaunchKernelGGL((k_gemm_dense<BKV, EPIV>), grid, block, 0, stream, A, lda, B, ldb, kwrap, \
@@ -387,8 +407,7 @@ hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t
 hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& rv,
                                 const ExpertsView& ex, uint16_t* act, int inter, int latent,
                                 int max_mtiles, hipStream_t stream) {
-  // m-tiles on x (unbounded), output-column tiles on y
-  dim3 grid(max_mtiles, (inter + 63) / 64), block(kThreads);
+  dim3 grid(max_mtiles * ((inter + 63) / 64)), block(kThreads);
   if (latent % 64 == 0)
     hipLaunchKernelGGL(k_expert_gateup<64>, grid, block, 0, stream, hcat, ldh, rv, ex, act, inter,
                        latent);
@@ -401,7 +420,7 @@ hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& 
 hipError_t launch_expert_down(const uint16_t* act, const RouteView& rv, const ExpertsView& ex,
                               uint16_t* y, int inter, int latent, int max_mtiles,
                               hipStream_t stream) {
-  dim3 grid(max_mtiles, (latent + kTile - 1) / kTile), block(kThreads);
+  dim3 grid(max_mtiles * ((latent + kTile - 1) / kTile)), block(kThreads);
   if (inter % 64 == 0)
     hipLaunchKernelGGL(k_expert_down<64>, grid, block, 0, stream, act, rv, ex, y, inter, latent);
   else

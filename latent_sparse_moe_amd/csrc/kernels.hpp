@@ -1,6 +1,7 @@
 // Kernel-side views and launcher declarations of the latent-MoE layer.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -93,6 +94,19 @@ struct StageMarks {
     if (!ev) return hipSuccess;
     void* e = ev[2 * stage + end];
     return e ? hipEventRecord((hipEvent_t)e, st) : hipSuccess;
+  }
+  // Launches `kernel` as the whole of `stage`: the stage's events (when
+  // given) are recorded by the dispatch itself, so they time the kernel
+  // alone rather than the kernel plus two extra queue packets.
+  template <typename K, typename... Args>
+  hipError_t launch(int stage, K kernel, dim3 grid, dim3 block, size_t lds, Args... args) const {
+    hipEvent_t e0 = ev ? (hipEvent_t)ev[2 * stage] : nullptr;
+    hipEvent_t e1 = ev ? (hipEvent_t)ev[2 * stage + 1] : nullptr;
+    if (e0 || e1)
+      hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u, args...);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+    return hipGetLastError();
   }
 };
 
