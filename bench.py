@@ -92,8 +92,11 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--only", choices=["decode", "prefill", "copy"], default=None,
-                   help="run one workload and print its object (profiling)")
+    p.add_argument("--only", choices=["decode", "prefill", "copy", "stack"], default=None,
+                   help="run one workload and print its object (profiling; 'stack' is the "
+                        "48-block residual stack at T = 8, reported only this way)")
+    p.add_argument("--stack-steps", type=int, default=20)
+    p.add_argument("--stack-warmup", type=int, default=3)
     p.add_argument("--summarize-pmc", metavar="CSV", default=None,
                    help="print per-kernel averages of a rocprofv3 counter_collection.csv")
     p.add_argument("--write-traffic", metavar="DIR", default=None,
@@ -410,6 +413,79 @@ def bench_prefill(args, torch, lsm, synth, dev):
     }
 
 
+def bench_stack(args, torch, lsm, synth, dev):
+    """48 residual blocks (RMSNorm + latent MoE) of 145B shapes, all resident
+    (~48 GB, far beyond the Infinity Cache), T = 8 with Zipf routing bias;
+    one step runs the blocks in order, each block's output feeding the next."""
+    cfg = synth.CONFIGS["stack145"]
+    d, T, nl = cfg.dims, cfg.T, cfg.n_layers
+    t0 = time.time()
+    dls = []
+    for l in range(nl):
+        h = synth.make_layer(d, cfg.seed + l, cfg.bias, cfg.zipf_s)
+        dls.append(lsm.DeviceLayer.from_host(h, dev))
+        del h
+    log(f"[stack] generated and uploaded {nl} blocks in {time.time() - t0:.1f}s")
+    x = torch.from_numpy(synth.make_x(T, d.hidden, cfg.seed).view("int16")).view(torch.bfloat16).to(dev)
+    bufs = [torch.empty_like(x), torch.empty_like(x)]
+    ws = lsm.alloc_workspace(d, T, dev)
+
+    # experts touched by each block on this input (untimed pass, debug copies)
+    n_touched, cur = [], x
+    for l in range(nl):
+        dbg = lsm.RouteDebug.alloc(d, T, dev)
+        out = bufs[l % 2]
+        lsm.forward(cur, dls[l], out=out, workspace=ws, debug=dbg, residual=True)
+        torch.cuda.synchronize()
+        n_touched.append(int((dbg.counts > 0).sum().item()))
+        cur = out
+    rec = REC_BYTES_CODES(d.latent, d.inter)
+    per_block_dense = (2 * d.latent * d.hidden * 2 + d.n_experts * d.latent * 2 + d.n_experts * 4
+                       + d.hidden * 4 + 2 * T * d.hidden * 2)
+    step_bytes = sum((n + d.n_shared) * (rec + 12) + per_block_dense for n in n_touched)
+
+    def step():
+        cur = x
+        for l in range(nl):
+            out = bufs[l % 2]
+            lsm.forward(cur, dls[l], out=out, workspace=ws, residual=True)
+            cur = out
+
+    for _ in range(args.stack_warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.stack_steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.stack_steps
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    return {"metric": "48-block stack decode step (T = 8), tokens/s", "value": T / (ms * 1e-3),
+            "unit": "tokens/s", "ms_per_step": ms, "steps": args.stack_steps,
+            "warmup": args.stack_warmup, "bytes_per_step": step_bytes, "GBps": gbps,
+            "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS, "us_per_block": ms * 1e3 / nl,
+            "experts_touched_per_block": n_touched,
+            "config": {"workload": "stack145", "blocks": nl, "T": T, "hidden": d.hidden,
+                       "latent": d.latent, "experts": d.n_experts, "inter": d.inter,
+                       "top_k": d.top_k, "shared": d.n_shared, "router_bias": "zipf(1.1)",
+                       "resident_weight_GB": sum(
+                           sum(t.numel() * t.element_size() for t in _tensors(dl)) for dl in dls) / 1e9}}
+
+
+def _tensors(v):
+    import dataclasses
+    import torch
+    if v is None:
+        return
+    if dataclasses.is_dataclass(v) and not isinstance(v, type):
+        for f in dataclasses.fields(v):
+            yield from _tensors(getattr(v, f.name))
+    elif isinstance(v, torch.Tensor):
+        yield v
+
+
 def cpu_baseline(args, host, x0):
     import numpy as np
     import oracle
@@ -454,6 +530,9 @@ def main():
         return
     if args.only == "prefill":
         print(json.dumps(bench_prefill(args, torch, lsm, synth, dev)), flush=True)
+        return
+    if args.only == "stack":
+        print(json.dumps(bench_stack(args, torch, lsm, synth, dev)), flush=True)
         return
     dec = bench_decode(args, torch, lsm, synth, dev)
     if args.only == "decode":

@@ -375,3 +375,43 @@ def check_bf16_rounding_vs_torch(seed=15):
     got = _to_bf16_bits(v)
     want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(got, want)
+
+
+def _torch_block_bits(layer, x_bits, H):
+    """One residual block by the independent route: torch rms_norm, the
+    per-token brute-force layer, torch's bfloat16 rounding of the sum."""
+    xb = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    u = torch.nn.functional.rms_norm(xb, (H,), torch.from_numpy(layer.norm_w).to(torch.float64), 1e-6)
+    u_bits = u.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    out_b, _, _, _ = brute_forward(layer, u_bits)
+    y = xb.numpy() + out_b
+    return torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def check_stack_zero_up_projection_is_identity(seed=16):
+    """U = 0 in every block makes each block's MoE output exactly zero, so the
+    residual stream passes through unchanged: every x_l equals x bit for bit."""
+    dims = synth.Dims(hidden=64, latent=32, n_experts=8, inter=32, top_k=2, n_shared=1)
+    layers = [synth.make_layer(dims, seed + l, "zipf") for l in range(3)]
+    for layer in layers:
+        layer.U = np.zeros_like(layer.U)
+    x = synth.make_x(5, 64, seed)
+    xs, _ = oracle.stack_forward(layers, x, 1e-6)
+    for xl in xs:
+        assert np.array_equal(xl, x)
+
+
+def check_stack_vs_torch_chain(seed=17):
+    """Three blocks chained by the independent route (torch rms_norm + brute
+    layer + torch bf16 rounding between blocks) equal the oracle's stack bit
+    for bit, including a middle block whose U = 0 (it must return its input)."""
+    dims = synth.Dims(hidden=64, latent=32, n_experts=8, inter=32, top_k=2, n_shared=1)
+    layers = [synth.make_layer(dims, seed + l, "zipf") for l in range(3)]
+    layers[1].U = np.zeros_like(layers[1].U)
+    x = synth.make_x(6, 64, seed)
+    xs, _ = oracle.stack_forward(layers, x, 1e-6)
+    cur = x
+    for l, layer in enumerate(layers):
+        cur = _torch_block_bits(layer, cur, 64)
+        assert np.array_equal(xs[l + 1], cur), l
+    assert np.array_equal(xs[2], xs[1])

@@ -231,3 +231,45 @@ def test_auto_path_picks_decode_and_rejects_unsupported():
     say("[case] PATH_DECODE on unsupported dims raises")
     with pytest.raises(lsm.MoeLatentError):
         lsm.forward(x, dl, path=lsm.PATH_DECODE)
+
+
+# ------------------------------------------------------------------ residual stack
+
+def _stack_layers(n):
+    cfg = synth.CONFIGS["stack145"]
+    key = ("stack145", n)
+    if key not in _cache:
+        say(f"[gen] stack145 first {n} blocks dims={cfg.dims} zipf")
+        hosts = [synth.make_layer(cfg.dims, cfg.seed + l, cfg.bias, cfg.zipf_s) for l in range(n)]
+        _cache[key] = (cfg, hosts, [lsm.DeviceLayer.from_host(h, device()) for h in hosts])
+    return _cache[key]
+
+
+@pytest.mark.parametrize("path", [lsm.PATH_DECODE, lsm.PATH_GROUPED])
+def test_stack145_three_blocks(path):
+    """Blocks 0-2 of the 48-block stack (T = 8, Zipf bias, seed = block).
+    Each block's MoE is checked on the oracle's own bf16 MoE input
+    u = bf16(rmsnorm(x_l) * g), so both sides route identical values (the
+    GPU's fp32 RMSNorm can round an element of u one bf16 ulp away from the
+    float64 one, which moves logits by ~1e-4). The chained GPU blocks, with
+    their own RMSNorm, are checked on the accumulated MoE part (x_3 - x_0) at
+    the layer bar."""
+    from gpu_helpers import rel_l2
+    from oracle.latent_moe import _to_bf16_bits
+    cfg, hosts, dls = _stack_layers(3)
+    x = synth.make_x(cfg.T, cfg.dims.hidden, cfg.seed)
+    xs, results = oracle.stack_forward(hosts, x, 1e-6)
+    cur = x
+    for l, (dl, host, res) in enumerate(zip(dls, hosts, results)):
+        say(f"[case] stack145 block {l} path={path} (MoE on the oracle's u)")
+        u = _to_bf16_bits(oracle.rmsnorm(oracle.bf16_value(xs[l]), host.norm_w, 1e-6))
+        gpu = run_gpu(dl, u, path=path)
+        check_routing(res, gpu, cfg.dims.top_k, cfg.dims.n_experts)
+        n_ok, _ = check_output(res, gpu["out"])
+        say(f"[ok] block {l} MoE rel_l2={n_ok:.3e}")
+        say(f"[case] stack145 block {l} path={path} (chained)")
+        cur = run_gpu(dl, cur, path=path, residual=True)["out_bits"].view(np.uint16)
+    x0 = oracle.bf16_value(x)
+    err = rel_l2(oracle.bf16_value(cur) - x0, oracle.bf16_value(xs[3]) - x0)
+    say(f"[ok] stack145 3 blocks path={path}: accumulated MoE part rel_l2={err:.3e}")
+    assert err <= 2e-2

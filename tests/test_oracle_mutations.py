@@ -156,3 +156,25 @@ def test_transposed_projection_caught(monkeypatch):
         layer = synth.make_layer(dims, 9)
         pins.check_vs_brute(layer, synth.make_x(4, 64, 9))
     assert _fails(check)
+
+
+def test_stack_without_residual_caught(monkeypatch):
+    """Blocks that return the MoE output alone (residual add dropped)."""
+    orig = M.block_forward
+    def bad(layer, x_bits, eps=1e-6, tokens=None):
+        y, res = orig(layer, x_bits, eps, tokens)
+        return y - oracle.bf16_value(x_bits)[res.tokens], res
+    monkeypatch.setattr(M, "block_forward", bad)
+    assert _fails(pins.check_stack_zero_up_projection_is_identity)
+    assert _fails(pins.check_stack_vs_torch_chain)
+
+
+def test_stack_truncating_residual_caught(monkeypatch):
+    """Residual stream rounded toward zero between blocks instead of to nearest."""
+    orig = M.block_forward
+    def bad(layer, x_bits, eps=1e-6, tokens=None):
+        y, res = orig(layer, x_bits, eps, tokens)
+        t = (np.asarray(y, np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32)
+        return t.astype(np.float64), res
+    monkeypatch.setattr(M, "block_forward", bad)
+    assert _fails(pins.check_stack_vs_torch_chain)

@@ -120,3 +120,11 @@ def test_block_residual():
 
 def test_bf16_rounding_vs_torch():
     pins.check_bf16_rounding_vs_torch()
+
+
+def test_stack_zero_up_projection_is_identity():
+    pins.check_stack_zero_up_projection_is_identity()
+
+
+def test_stack_vs_torch_chain():
+    pins.check_stack_vs_torch_chain()
