@@ -5,14 +5,28 @@
 //            W_e in e2m1 codes + E4M3 per-16 block scales (gate/up fused with
 //            SiLU*mul, then down).
 //
-// One 256-thread workgroup computes a 128x128 tile; its four waves each own a
-// 64x64 sub-tile made of 2x2 v_mfma_f32_32x32x16_bf16 products. A and B
-// tiles are staged through LDS (rows padded by 16 bytes so the 16-byte
-// fragment reads of a half-wave hit distinct banks), double-buffered with
-// register prefetch: the global loads of step k+1 are in flight while the
-// matrix cores work on step k. Expert weights arrive as 4-bit codes and are
-// dequantised in registers (exactly, to bf16) on their way into LDS, so the
-// HBM traffic for weights is the 4.5-bit format, not bf16.
+// One 256-thread workgroup computes a 128 x 256 tile: wave w owns all 128
+// rows and columns [64w, 64w + 64), as 4 x 2 v_mfma_f32_32x32x16_bf16
+// products. The operands take different routes, chosen from measured LDS
+// rates on gfx950 (16-byte reads ~200+ B/clk/CU, writes from registers ~64):
+//   - A (activation rows, shared by all four waves) is staged through LDS:
+//     loaded two K steps ahead into registers, written one step ahead into
+//     one of three LDS stages, read as fragments. Rows are BK elements with
+//     their 16-byte chunks XOR-swizzled by row pair (measured: a 16-byte read
+//     is served 16 lanes at a time over 256 bytes of banks, a 16-byte write 8
+//     lanes at a time), so that the fragment reads of 16 consecutive rows at
+//     one chunk and the row-order writes of the loader are conflict-free.
+//   - B (weights, used by exactly one wave) never touches LDS: each lane
+//     loads its own weight row's slice straight into registers, three K
+//     steps deep, and for the experts dequantises the 4-bit codes (exactly,
+//     to bf16) right before its matrix-core op. HBM and L2 traffic for expert
+//     weights is the 4.5-bit format.
+// The workgroup meets once per K step at an LDS-only barrier; nothing in the
+// steady-state loop is conditional, so the compiler's load waits are exact.
+// The expert kernels are held to 256 registers per lane so that two
+// workgroups share a CU (two waves per SIMD): one wave's LDS, barrier and
+// load waits then overlap the other's matrix-core work (measured on the 16K
+// prefill shapes: gate/up 1.51 -> 1.11 ms, down 0.93 -> 0.72 ms).
 //
 // Grids are one-dimensional over (m-tile, n-tile) with n fastest, and the
 // block id is permuted so that the workgroups the hardware places on one XCD
@@ -24,8 +38,9 @@
 
 namespace moe {
 
-constexpr int kTile = 128;
-constexpr int kThreads = 256;
+constexpr int kBM = 128;       // tile rows (tokens)
+constexpr int kBN = 256;       // tile columns (weight rows)
+constexpr int kThreads = 256;  // four waves
 constexpr int kXcds = 8;
 
 // Logical tile of workgroup b among n: XCD x = b % 8 takes the contiguous
@@ -36,165 +51,233 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
 }
 
 template <int BK>
-struct TileShape {
-  static constexpr int kStride = BK + 8;              // bf16 per LDS row
-  static constexpr int kElems = kTile * kStride;      // bf16 per tile
-  static constexpr int kChunksPerRow = BK / 8;        // 16-byte chunks per row
-  static constexpr int kChunksPerThread = kTile * kChunksPerRow / kThreads;
+struct Geo {
+  static constexpr int kCpr = BK / 8;     // 16-byte chunks per A row
+  static constexpr int kRpl = 16 / kCpr;  // A rows per 256 bytes (all 64 banks)
+  static constexpr int kSub = BK / 16;   // K = 16 matrix-core steps per K step
 };
 
-// 128 rows of bf16, row r starting at ptr_r; column index wraps modulo
-// `kwrap` (a multiple of BK) so one physical matrix can stand for two
-// concatenated copies along K.
+// Slot (16-byte unit) of logical chunk c of `row` in a swizzled A tile.
 template <int BK>
-struct RowLoader {
-  static constexpr int CPT = TileShape<BK>::kChunksPerThread;
-  const uint16_t* ptr[CPT];
-  int lds_off[CPT];
-  uint4 reg[CPT];
+__device__ __forceinline__ int swz(int row, int c) {
+  using G = Geo<BK>;
+  return row * G::kCpr + (c ^ ((row / G::kRpl) % G::kCpr));
+}
+
+// Order of K inside a step. The 32x32x16 product takes its K = 16 as two
+// halves of 8, lane l supplying half l / 32. A K step is split the same way
+// at the top level: lane half h covers columns [h*BK/2, (h+1)*BK/2) of the
+// step and matrix-core step ks takes its 8-column chunk ks. A lane's B
+// operand for a whole step is then BK/2 consecutive weights of one row (one
+// 16-byte load of 4-bit codes), and its A fragment for (ks, half h) is
+// logical chunk h * kSub + ks of the row. The order of the products within
+// an fp32 accumulation differs from plain K order; the set of products
+// does not.
+
+// Workgroup barrier that orders LDS accesses only: global loads still in
+// flight (the next steps' operands) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 128 rows of bf16 A into a swizzled [128][BK] LDS tile. Thread t moves
+// 16-byte chunks t, t + 256, ... of the tile (consecutive threads read one
+// row's chunks in order) through register set `set`.
+template <int BK>
+struct ALoader {
+  static constexpr int V = kBM * Geo<BK>::kCpr / kThreads;
+  const uint16_t* src[V];
+  int dst[V];
+  uint4 reg[3][V];
+
+  // rowfn(r) = address of row r's K = 0 element
+  template <class RowFn>
+  __device__ __forceinline__ void init(RowFn rowfn) {
+    using G = Geo<BK>;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int chunk = v * kThreads + (int)threadIdx.x;
+      const int row = chunk / G::kCpr, c = chunk % G::kCpr;
+      src[v] = rowfn(row) + c * 8;
+      dst[v] = swz<BK>(row, c) * 8;
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, int set) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) reg[set][v] = *(const uint4*)(src[v] + kt * BK);
+  }
+  __device__ __forceinline__ void finish(uint16_t* tile, int set) const {
+#pragma unroll
+    for (int v = 0; v < V; ++v) *(uint4*)(tile + dst[v]) = reg[set][v];
+  }
+};
+
+// B operand in registers: expert weights in e2m1 codes + E4M3 block scales.
+// Lane (half h) of sub-tile j holds BK/2 codes and BK/32 scale bytes of its
+// weight row per step.
+template <int BK>
+struct Fp4B {
+  static constexpr int kWords = BK / 16;  // 32-bit code words per lane per step
+  struct Set {
+    uint32_t c[2][kWords];
+    uint32_t s[2];
+  };
+  const uint8_t* cp[2];
+  const uint8_t* sp[2];
+
+  // rowfn(j, &codes_row, &scales_row): the lane's weight row of sub-tile j
+  template <class RowFn>
+  __device__ __forceinline__ void init(RowFn rowfn, int) {
+    const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* c;
+      const uint8_t* s;
+      rowfn(j, &c, &s);
+      cp[j] = c + h * (BK / 4);
+      sp[j] = s + h * (BK / 32);
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, Set& st) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (BK == 64) {
+        const uint4 v = *(const uint4*)(cp[j] + kt * (BK / 2));
+        st.c[j][0] = v.x; st.c[j][1] = v.y; st.c[j][2] = v.z; st.c[j][3] = v.w;
+        st.s[j] = *(const uint16_t*)(sp[j] + kt * (BK / 16));
+      } else {
+        const uint2 v = *(const uint2*)(cp[j] + kt * (BK / 2));
+        st.c[j][0] = v.x; st.c[j][1] = v.y;
+        st.s[j] = *(const uint8_t*)(sp[j] + kt * (BK / 16));
+      }
+    }
+  }
+  // chunk ks (8 weights) of sub-tile j; scale block ks / 2 of the lane's half
+  __device__ __forceinline__ bf16x8 frag(const Set& st, int j, int ks) const {
+    const float sc = e4m3_to_f32((st.s[j] >> (8 * (ks >> 1))) & 0xFFu);
+    return dequant8(st.c[j][ks], sc);
+  }
+};
+
+// B operand in registers: bf16 weights (dense GEMMs). Column index wraps
+// modulo kwrap (a multiple of BK), so one physical matrix can stand for two
+// copies concatenated along K.
+template <int BK>
+struct Bf16B {
+  static constexpr int kSub = Geo<BK>::kSub;
+  struct Set {
+    uint4 c[2][kSub];
+  };
+  const uint16_t* p[2];
   int kwrap;
 
+  // rowfn(j): the lane's weight row of sub-tile j (K = 0 element)
   template <class RowFn>
   __device__ __forceinline__ void init(RowFn rowfn, int kwrap_) {
     kwrap = kwrap_;
+    const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int row = c / TileShape<BK>::kChunksPerRow;
-      const int col8 = c % TileShape<BK>::kChunksPerRow;
-      ptr[i] = rowfn(row) + col8 * 8;
-      lds_off[i] = row * TileShape<BK>::kStride + col8 * 8;
-    }
+    for (int j = 0; j < 2; ++j) p[j] = rowfn(j) + h * (BK / 2);
   }
-  __device__ __forceinline__ void load(int kt) {
+  __device__ __forceinline__ void issue(int kt, Set& st) const {
     int kc = kt * BK;
     if (kc >= kwrap) kc -= kwrap;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) reg[i] = *(const uint4*)(ptr[i] + kc);
-  }
-  __device__ __forceinline__ void store(uint16_t* lds) const {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) *(uint4*)(lds + lds_off[i]) = reg[i];
+      for (int ks = 0; ks < kSub; ++ks) st.c[j][ks] = *(const uint4*)(p[j] + kc + ks * 8);
+  }
+  __device__ __forceinline__ bf16x8 frag(const Set& st, int j, int ks) const {
+    return __builtin_bit_cast(bf16x8, st.c[j][ks]);
   }
 };
 
-// 128 rows of 4-bit codes + E4M3 block scales; each active thread moves 32
-// consecutive weights (16 bytes of codes, 2 scale bytes) per K step.
-template <int BK>
-struct Fp4Loader {
-  static constexpr int kParts = BK / 32;
-  static constexpr int kActive = kTile * kParts;
-  bool active;
-  const uint8_t* cptr;
-  const uint8_t* sptr;
-  int lds_off;
-  uint4 creg;
-  uint32_t sreg;
-
-  // rowfn(row, &codes_row, &scales_row)
-  template <class RowFn>
-  __device__ __forceinline__ void init(RowFn rowfn) {
-    const int t = threadIdx.x;
-    active = t < kActive;
-    const int row = active ? t / kParts : 0;
-    const int part = active ? t % kParts : 0;
-    const uint8_t* c;
-    const uint8_t* s;
-    rowfn(row, &c, &s);
-    cptr = c + part * 16;
-    sptr = s + part * 2;
-    lds_off = row * TileShape<BK>::kStride + part * 32;
-  }
-  __device__ __forceinline__ void load(int kt) {
-    if (!active) return;
-    creg = *(const uint4*)(cptr + kt * (BK / 2));
-    sreg = *(const uint16_t*)(sptr + kt * (BK / 16));
-  }
-  __device__ __forceinline__ void store(uint16_t* lds) const {
-    if (!active) return;
-    const float s0 = e4m3_to_f32(sreg & 0xFFu);
-    const float s1 = e4m3_to_f32((sreg >> 8) & 0xFFu);
-    bf16x8* dst = (bf16x8*)(lds + lds_off);
-    dst[0] = dequant8(creg.x, s0);
-    dst[1] = dequant8(creg.y, s0);
-    dst[2] = dequant8(creg.z, s1);
-    dst[3] = dequant8(creg.w, s1);
-  }
+// The three LDS stages of the A tile, each its own array.
+struct Pipe {
+  uint16_t* a[3];
 };
 
-// Wave w of the workgroup owns rows [wm*64, wm*64+64) of the tile, wm = w/2.
-// Its two B sub-tiles are tile rows brow(wn, j) .. +32 (wn = w%2): adjacent
-// 32-row groups for a plain GEMM; for gate/up the tile holds 64 gate rows
-// then 64 up rows, and sub-tile j = 0 (gate) and j = 1 (up) cover the same
-// 32 output columns so SiLU*mul can pair them in registers.
-template <bool GATEUP>
-__device__ __forceinline__ int b_subtile_row(int wn, int j) {
-  return GATEUP ? (j * 64 + wn * 32) : (wn * 64 + j * 32);
+// One K step on stage S = kt % 3: issue the loads of step kt + 2 (A into
+// register set (S+2)%3, B into B set (S+2)%3), run the matrix cores on A
+// stage S and B set S, and write A of step kt + 1 (loaded one step ago) into
+// stage (S+1)%3, which was read last in step kt - 2. Past the last step the
+// loads repeat step KT - 1 and the writes go to a stage nobody reads.
+template <int BK, int S, class BL>
+__device__ __forceinline__ void gemm_step(int kt, int KT, ALoader<BK>& al, const BL& bl,
+                                          const Pipe& p, typename BL::Set (&bs)[3],
+                                          const int (&frag)[Geo<BK>::kSub],
+                                          f32x16 (&acc)[4][2]) {
+  using G = Geo<BK>;
+  constexpr int N1 = (S + 1) % 3, N2 = (S + 2) % 3;
+  const int kl = min(kt + 2, KT - 1);
+  al.issue(kl, N2);
+  bl.issue(kl, bs[N2]);
+  const uint16_t* ca = p.a[S];
+#pragma unroll
+  for (int ks = 0; ks < G::kSub; ++ks) {
+    bf16x8 a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(ca + i * 32 * BK + frag[ks]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = bl.frag(bs[S], j, ks);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+    if (ks == 0) al.finish(p.a[N1], N1);
+  }
+  lds_barrier();
 }
 
-template <int BK, bool GATEUP, class AL, class BL>
-__device__ __forceinline__ void mainloop(AL& al, BL& bl, int KT, uint16_t* smem,
-                                         f32x16 (&acc)[2][2]) {
-  using TS = TileShape<BK>;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  uint16_t* As[2] = {smem, smem + 2 * TS::kElems};
-  uint16_t* Bs[2] = {smem + TS::kElems, smem + 3 * TS::kElems};
+template <int BK, class BL>
+__device__ __forceinline__ void mainloop(ALoader<BK>& al, const BL& bl, int KT, const Pipe& p,
+                                         f32x16 (&acc)[4][2]) {
+  using G = Geo<BK>;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // this lane's A fragment slot (in elements) for each matrix-core step,
+  // relative to the first row of its 32-row block
+  const int lane = threadIdx.x & 63;
+  int frag[G::kSub];
+#pragma unroll
+  for (int ks = 0; ks < G::kSub; ++ks)
+    frag[ks] = swz<BK>(lane & 31, (lane >> 5) * G::kSub + ks) * 8;
 
-  al.load(0);
-  bl.load(0);
-  al.store(As[0]);
-  bl.store(Bs[0]);
-  __syncthreads();
-  const int arow = wm * 64 + (lane & 31);
-  const int kof = (lane >> 5) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) {
-      al.load(kt + 1);
-      bl.load(kt + 1);
-    }
-    const uint16_t* A = As[cur];
-    const uint16_t* B = Bs[cur];
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *(const bf16x8*)(A + (arow + i * 32) * TS::kStride + ks * 16 + kof);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *(const bf16x8*)(B + (b_subtile_row<GATEUP>(wn, j) + (lane & 31)) * TS::kStride +
-                                ks * 16 + kof);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
-    }
-    if (kt + 1 < KT) {
-      al.store(As[cur ^ 1]);
-      bl.store(Bs[cur ^ 1]);
-    }
-    __syncthreads();
+  typename BL::Set bs[3];
+  // prologue: step 0 in LDS and B set 0, step 1 in flight
+  al.issue(0, 0);
+  bl.issue(0, bs[0]);
+  al.issue(min(1, KT - 1), 1);
+  bl.issue(min(1, KT - 1), bs[1]);
+  al.finish(p.a[0], 0);
+  lds_barrier();
+  int kt = 0;
+  for (; kt + 3 <= KT; kt += 3) {
+    gemm_step<BK, 0>(kt, KT, al, bl, p, bs, frag, acc);
+    gemm_step<BK, 1>(kt + 1, KT, al, bl, p, bs, frag, acc);
+    gemm_step<BK, 2>(kt + 2, KT, al, bl, p, bs, frag, acc);
   }
+  if (kt < KT) gemm_step<BK, 0>(kt, KT, al, bl, p, bs, frag, acc);
+  if (kt + 1 < KT) gemm_step<BK, 1>(kt + 1, KT, al, bl, p, bs, frag, acc);
 }
 
-// Output coordinates of accumulator (i, j, r) for this lane, relative to the tile.
-__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
-  return wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+// Output row of accumulator register r of row block i (relative to the
+// tile); the column is the lane's l % 32 within its 32-column block.
+__device__ __forceinline__ int acc_row(int i, int r, int lane) {
+  return i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
-template <int BK>
-constexpr int smem_elems() {
-  return 4 * TileShape<BK>::kElems;
-}
+#define MOE_GEMM_LDS(BK)                                                        \
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a0[kBM * BK];            \
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a1[kBM * BK];            \
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a2[kBM * BK];            \
+  const Pipe pipe{{lds_a0, lds_a1, lds_a2}}
 
 // ------------------------------------------------------------------ dense
 
@@ -203,29 +286,30 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
                                                          const uint16_t* __restrict__ B, int ldb,
                                                          int kwrap, int M, int N, int K,
                                                          DenseEpilogue ep) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[smem_elems<BK>()];
-  const int nt = (N + kTile - 1) / kTile;
+  MOE_GEMM_LDS(BK);
+  const int nt = (N + kBN - 1) / kBN;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int m0 = (tile / nt) * kTile, n0 = (tile % nt) * kTile;
-  RowLoader<BK> al, bl;
-  al.init([&](int r) { return A + (size_t)min(m0 + r, M - 1) * lda; }, K);
-  bl.init([&](int r) { return B + (size_t)min(n0 + r, N - 1) * ldb; }, kwrap);
-  f32x16 acc[2][2];
-  mainloop<BK, false>(al, bl, K / BK, smem, acc);
-
+  const int m0 = (tile / nt) * kBM, n0 = (tile % nt) * kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int ncol = n0 + wave * 64 + (lane & 31);  // the lane's column in sub-tile 0
+  ALoader<BK> al;
+  al.init([&](int r) { return A + (size_t)min(m0 + r, M - 1) * lda; });
+  Bf16B<BK> bl;
+  bl.init([&](int j) { return B + (size_t)min(ncol + j * 32, N - 1) * ldb; }, kwrap);
+  f32x16 acc[4][2];
+  mainloop<BK>(al, bl, K / BK, pipe, acc);
+
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+    const int n = ncol + j * 32;
     if (n >= N) continue;
     float bias = 0.0f;
     if (EPI == kEpiLogits && ep.bias) bias = ep.bias[n];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + acc_row(wm, i, r, lane);
+        const int m = m0 + acc_row(i, r, lane);
         if (m >= M) continue;
         const float v = acc[i][j][r];
         if (EPI == kEpiSplit) {
@@ -272,7 +356,7 @@ __device__ __forceinline__ bool tile_work(const RouteView& rv, int mt, TileWork*
   if (mt >= total) return false;
   const int g = find_group(rv.tile_off, ngroups, mt);
   w->group = g;
-  w->rbeg = rv.off[g] + (mt - rv.tile_off[g]) * kTile;
+  w->rbeg = rv.off[g] + (mt - rv.tile_off[g]) * kBM;
   w->rend = rv.off[g + 1];
   return true;
 }
@@ -287,48 +371,47 @@ __device__ __forceinline__ const Fp4Set& pick_set(const ExpertsView& ex, int g, 
   return ex.shared;
 }
 
+// Gate/up: a tile covers 128 output columns of the SwiGLU width; wave w
+// takes columns n0 + 32w .. +32 as sub-tile 0 (gate rows) and sub-tile 1 (up
+// rows), so SiLU*mul pairs them in registers.
 template <int BK>
-__global__ __launch_bounds__(kThreads) void k_expert_gateup(const uint16_t* __restrict__ hcat,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_gateup(const uint16_t* __restrict__ hcat,
                                                             int ldh, RouteView rv,
                                                             ExpertsView ex, uint16_t* __restrict__ act,
                                                             int inter, int latent) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[smem_elems<BK>()];
-  const int nt = (inter + 63) / 64;
+  MOE_GEMM_LDS(BK);
+  const int nt = (inter + kBN / 2 - 1) / (kBN / 2);
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   TileWork tw;
   if (!tile_work(rv, tile / nt, &tw)) return;
-  const int n0 = (tile % nt) * 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = (tile % nt) * (kBN / 2) + wave * 32 + (lane & 31);  // the lane's output column
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   const int P = rv.pairs;
-  RowLoader<BK> al;
+  ALoader<BK> al;
   al.init([&](int r) {
     const int row = min(tw.rbeg + r, tw.rend - 1);
     const int tok = row < P ? rv.perm[row] / rv.top_k : row - P;
     return hcat + (size_t)tok * ldh;
-  }, latent);
-  Fp4Loader<BK> bl;
-  bl.init([&](int r, const uint8_t** c, const uint8_t** s) {
-    const bool up = r >= 64;
-    const int n = min(n0 + (r & 63), inter - 1);
-    const Fp4Mat& m = up ? set.up : set.gate;
-    const size_t row = (size_t)le * inter + n;
+  });
+  Fp4B<BK> bl;
+  bl.init([&](int j, const uint8_t** c, const uint8_t** s) {
+    const Fp4Mat& m = j ? set.up : set.gate;
+    const size_t row = (size_t)le * inter + min(n, inter - 1);
     *c = m.codes + row * (latent / 2);
     *s = m.scales + row * (latent / 16);
-  });
-  f32x16 acc[2][2];
-  mainloop<BK, true>(al, bl, latent / BK, smem, acc);
+  }, 0);
+  f32x16 acc[4][2];
+  mainloop<BK>(al, bl, latent / BK, pipe, acc);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n = n0 + wn * 32 + (lane & 31);
   if (n >= inter) return;
   const float gsg = set.gate.gscale[le], gsu = set.up.gscale[le];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = tw.rbeg + acc_row(wm, i, r, lane);
+      const int row = tw.rbeg + acc_row(i, r, lane);
       if (row >= tw.rend) continue;
       const float g = gsg * acc[i][0][r];
       const float u = gsu * acc[i][1][r];
@@ -338,41 +421,40 @@ __global__ __launch_bounds__(kThreads) void k_expert_gateup(const uint16_t* __re
 }
 
 template <int BK>
-__global__ __launch_bounds__(kThreads) void k_expert_down(const uint16_t* __restrict__ act,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_down(const uint16_t* __restrict__ act,
                                                           RouteView rv, ExpertsView ex,
                                                           uint16_t* __restrict__ y, int inter,
                                                           int latent) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[smem_elems<BK>()];
-  const int nt = (latent + kTile - 1) / kTile;
+  MOE_GEMM_LDS(BK);
+  const int nt = (latent + kBN - 1) / kBN;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   TileWork tw;
   if (!tile_work(rv, tile / nt, &tw)) return;
-  const int n0 = (tile % nt) * kTile;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ncol = (tile % nt) * kBN + wave * 64 + (lane & 31);  // column in sub-tile 0
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
-  RowLoader<BK> al;
-  al.init([&](int r) { return act + (size_t)min(tw.rbeg + r, tw.rend - 1) * inter; }, inter);
-  Fp4Loader<BK> bl;
-  bl.init([&](int r, const uint8_t** c, const uint8_t** s) {
-    const size_t row = (size_t)le * latent + min(n0 + r, latent - 1);
+  ALoader<BK> al;
+  al.init([&](int r) { return act + (size_t)min(tw.rbeg + r, tw.rend - 1) * inter; });
+  Fp4B<BK> bl;
+  bl.init([&](int j, const uint8_t** c, const uint8_t** s) {
+    const size_t row = (size_t)le * latent + min(ncol + j * 32, latent - 1);
     *c = set.down.codes + row * (inter / 2);
     *s = set.down.scales + row * (inter / 16);
-  });
-  f32x16 acc[2][2];
-  mainloop<BK, false>(al, bl, inter / BK, smem, acc);
+  }, 0);
+  f32x16 acc[4][2];
+  mainloop<BK>(al, bl, inter / BK, pipe, acc);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const float gsd = set.down.gscale[le];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+    const int n = ncol + j * 32;
     if (n >= latent) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = tw.rbeg + acc_row(wm, i, r, lane);
+        const int row = tw.rbeg + acc_row(i, r, lane);
         if (row >= tw.rend) continue;
         y[(size_t)row * latent + n] = f32_to_bf16_bits(gsd * acc[i][j][r]);
       }
@@ -386,7 +468,7 @@ static inline int pick_bk(int K, int kwrap) { return (K % 64 == 0 && kwrap % 64 
 hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t* B, int ldb,
                              int kwrap, int M, int N, int K, const DenseEpilogue& ep,
                              hipStream_t stream) {
-  dim3 grid(((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile)), block(kThreads);
+  dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), block(kThreads);
   const int bk = pick_bk(K, kwrap);
 #define MOE_LAUNCH_DENSE(BKV, EPIV)                                                           \
   hipLaunchKernelGGL((k_gemm_dense<BKV, EPIV>), grid, block, 0, stream, A, lda, B, ldb, kwrap, \
@@ -407,7 +489,7 @@ hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t
 hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& rv,
                                 const ExpertsView& ex, uint16_t* act, int inter, int latent,
                                 int max_mtiles, hipStream_t stream) {
-  dim3 grid(max_mtiles * ((inter + 63) / 64)), block(kThreads);
+  dim3 grid(max_mtiles * ((inter + kBN / 2 - 1) / (kBN / 2))), block(kThreads);
   if (latent % 64 == 0)
     hipLaunchKernelGGL(k_expert_gateup<64>, grid, block, 0, stream, hcat, ldh, rv, ex, act, inter,
                        latent);
@@ -420,7 +502,7 @@ hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& 
 hipError_t launch_expert_down(const uint16_t* act, const RouteView& rv, const ExpertsView& ex,
                               uint16_t* y, int inter, int latent, int max_mtiles,
                               hipStream_t stream) {
-  dim3 grid(max_mtiles * ((latent + kTile - 1) / kTile)), block(kThreads);
+  dim3 grid(max_mtiles * ((latent + kBN - 1) / kBN)), block(kThreads);
   if (inter % 64 == 0)
     hipLaunchKernelGGL(k_expert_down<64>, grid, block, 0, stream, act, rv, ex, y, inter, latent);
   else
