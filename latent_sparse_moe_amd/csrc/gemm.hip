@@ -225,7 +225,7 @@ __device__ __forceinline__ void gemm_step(int kt, int KT, ALoader<BK>& al, const
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
     if (ks == 0) al.finish(p.a[N1], N1);
   }
   lds_barrier();
@@ -267,10 +267,14 @@ __device__ __forceinline__ void mainloop(ALoader<BK>& al, const BL& bl, int KT, 
   if (kt + 1 < KT) gemm_step<BK, 1>(kt + 1, KT, al, bl, p, bs, frag, acc);
 }
 
-// Output row of accumulator register r of row block i (relative to the
-// tile); the column is the lane's l % 32 within its 32-column block.
-__device__ __forceinline__ int acc_row(int i, int r, int lane) {
-  return i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+// The products are computed transposed (weights as the first matrix-core
+// operand), so accumulator acc[i][j] holds, for token row i*32 + l % 32 of
+// the tile, the four consecutive outputs of column block j starting at
+// acc_col(g, l) in registers 4g .. 4g + 3: one 8-byte store of bf16.
+__device__ __forceinline__ int acc_col(int g, int lane) { return g * 8 + (lane >> 5) * 4; }
+
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return uint2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
 }
 
 #define MOE_GEMM_LDS(BK)                                                        \
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int m0 = (tile / nt) * kBM, n0 = (tile % nt) * kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ncol = n0 + wave * 64 + (lane & 31);  // the lane's column in sub-tile 0
+  const int ncol = n0 + wave * 64 + (lane & 31);  // weight row this lane loads (sub-tile 0)
   ALoader<BK> al;
   al.init([&](int r) { return A + (size_t)min(m0 + r, M - 1) * lda; });
   Bf16B<BK> bl;
@@ -299,33 +303,60 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
   f32x16 acc[4][2];
   mainloop<BK>(al, bl, K / BK, pipe, acc);
 
+  const int nbase = n0 + wave * 64;
+  // 4-wide stores need the row starts 8-byte (16-byte for fp32) aligned
+  const bool vec = (ep.ldo & 3) == 0 && (EPI != kEpiOut || !ep.resid || (ep.ldr & 3) == 0);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = ncol + j * 32;
-    if (n >= N) continue;
-    float bias = 0.0f;
-    if (EPI == kEpiLogits && ep.bias) bias = ep.bias[n];
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + i * 32 + (lane & 31);
+    if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + acc_row(i, r, lane);
-        if (m >= M) continue;
-        const float v = acc[i][j][r];
+      for (int g = 0; g < 4; ++g) {
+        const int n = nbase + j * 32 + acc_col(g, lane);
+        if (n >= N) continue;
+        float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                      acc[i][j][4 * g + 3]};
+        const int nv = min(4, N - n);
         if (EPI == kEpiSplit) {
           // latent vector as bf16 hi + bf16 lo: hi feeds the experts, hi + lo
           // (about 16 significant bits) feeds the router
-          uint16_t* o = (uint16_t*)ep.out + (size_t)m * ep.ldo;
-          const uint16_t hi = f32_to_bf16_bits(v);
-          const float rest = v - bf16_bits_to_f32(hi);
-          o[n] = hi;
-          o[ep.lo_off + n] = f32_to_bf16_bits(rest);
+          uint16_t* o = (uint16_t*)ep.out + (size_t)m * ep.ldo + n;
+          float lo[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) lo[q] = v[q] - bf16_bits_to_f32(f32_to_bf16_bits(v[q]));
+          if (vec && nv == 4) {
+            *(uint2*)o = pack_bf16x4(v[0], v[1], v[2], v[3]);
+            *(uint2*)(o + ep.lo_off) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+          } else {
+            for (int q = 0; q < nv; ++q) {
+              o[q] = f32_to_bf16_bits(v[q]);
+              o[ep.lo_off + q] = f32_to_bf16_bits(lo[q]);
+            }
+          }
         } else if (EPI == kEpiLogits) {
-          ((float*)ep.out)[(size_t)m * ep.ldo + n] = v + bias;
+          float* o = (float*)ep.out + (size_t)m * ep.ldo + n;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] += ep.bias && q < nv ? ep.bias[n + q] : 0.0f;
+          if (vec && nv == 4) *(float4*)o = float4{v[0], v[1], v[2], v[3]};
+          else for (int q = 0; q < nv; ++q) o[q] = v[q];
         } else {  // kEpiOut
-          float o = v;
-          if (ep.resid) o += bf16_bits_to_f32(ep.resid[(size_t)m * ep.ldr + n]);
-          ((uint16_t*)ep.out)[(size_t)m * ep.ldo + n] = f32_to_bf16_bits(o);
+          uint16_t* o = (uint16_t*)ep.out + (size_t)m * ep.ldo + n;
+          if (ep.resid) {
+            const uint16_t* rr = ep.resid + (size_t)m * ep.ldr + n;
+            if (vec && nv == 4) {
+              const uint2 rv = *(const uint2*)rr;
+              v[0] += bf16_bits_to_f32(rv.x & 0xFFFFu);
+              v[1] += bf16_bits_to_f32(rv.x >> 16);
+              v[2] += bf16_bits_to_f32(rv.y & 0xFFFFu);
+              v[3] += bf16_bits_to_f32(rv.y >> 16);
+            } else {
+              for (int q = 0; q < nv; ++q) v[q] += bf16_bits_to_f32(rr[q]);
+            }
+          }
+          if (vec && nv == 4) *(uint2*)o = pack_bf16x4(v[0], v[1], v[2], v[3]);
+          else for (int q = 0; q < nv; ++q) o[q] = f32_to_bf16_bits(v[q]);
         }
       }
   }
@@ -385,7 +416,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   TileWork tw;
   if (!tile_work(rv, tile / nt, &tw)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = (tile % nt) * (kBN / 2) + wave * 32 + (lane & 31);  // the lane's output column
+  const int n = (tile % nt) * (kBN / 2) + wave * 32 + (lane & 31);  // weight row this lane loads
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   const int P = rv.pairs;
@@ -405,19 +436,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   f32x16 acc[4][2];
   mainloop<BK>(al, bl, latent / BK, pipe, acc);
 
-  if (n >= inter) return;
   const float gsg = set.gate.gscale[le], gsu = set.up.gscale[le];
+  const int nbase = (tile % nt) * (kBN / 2) + wave * 32;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int row = tw.rbeg + i * 32 + (lane & 31);
+    if (row >= tw.rend) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = tw.rbeg + acc_row(i, r, lane);
-      if (row >= tw.rend) continue;
-      const float g = gsg * acc[i][0][r];
-      const float u = gsu * acc[i][1][r];
-      const float a = g / (1.0f + expf(-g)) * u;
-      act[(size_t)row * inter + n] = f32_to_bf16_bits(a);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int nc = nbase + acc_col(g4, lane);
+      if (nc >= inter) continue;  // inter is a multiple of 32: all four or none
+      float a[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float g = gsg * acc[i][0][4 * g4 + q];
+        const float u = gsu * acc[i][1][4 * g4 + q];
+        a[q] = g / (1.0f + expf(-g)) * u;
+      }
+      *(uint2*)(act + (size_t)row * inter + nc) = pack_bf16x4(a[0], a[1], a[2], a[3]);
     }
+  }
 }
 
 template <int BK>
@@ -431,7 +469,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   TileWork tw;
   if (!tile_work(rv, tile / nt, &tw)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ncol = (tile % nt) * kBN + wave * 64 + (lane & 31);  // column in sub-tile 0
+  const int ncol = (tile % nt) * kBN + wave * 64 + (lane & 31);  // weight row this lane loads
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   ALoader<BK> al;
@@ -446,17 +484,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   mainloop<BK>(al, bl, inter / BK, pipe, acc);
 
   const float gsd = set.down.gscale[le];
+  const int nbase = (tile % nt) * kBN + wave * 64;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = ncol + j * 32;
-    if (n >= latent) continue;
+  for (int i = 0; i < 4; ++i) {
+    const int row = tw.rbeg + i * 32 + (lane & 31);
+    if (row >= tw.rend) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = tw.rbeg + acc_row(i, r, lane);
-        if (row >= tw.rend) continue;
-        y[(size_t)row * latent + n] = f32_to_bf16_bits(gsd * acc[i][j][r]);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int nc = nbase + j * 32 + acc_col(g4, lane);
+        if (nc >= latent) continue;  // latent is a multiple of 32: all four or none
+        const f32x16& c = acc[i][j];
+        *(uint2*)(y + (size_t)row * latent + nc) =
+            pack_bf16x4(gsd * c[4 * g4], gsd * c[4 * g4 + 1], gsd * c[4 * g4 + 2], gsd * c[4 * g4 + 3]);
       }
   }
 }
