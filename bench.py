@@ -462,10 +462,25 @@ def bench_stack(args, torch, lsm, synth, dev):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.stack_steps
     gbps = step_bytes / (ms * 1e-3) / 1e9
+    # the same step captured once in a HIP graph and replayed (kernel
+    # launches only: the path records no memset, copy or host sync)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.stack_warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.stack_steps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    graph_ms = start.elapsed_time(end) / args.stack_steps
     return {"metric": "48-block stack decode step (T = 8), tokens/s", "value": T / (ms * 1e-3),
             "unit": "tokens/s", "ms_per_step": ms, "steps": args.stack_steps,
             "warmup": args.stack_warmup, "bytes_per_step": step_bytes, "GBps": gbps,
             "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS, "us_per_block": ms * 1e3 / nl,
+            "graph_replay": {"ms_per_step": graph_ms, "us_per_block": graph_ms * 1e3 / nl},
             "experts_touched_per_block": n_touched,
             "config": {"workload": "stack145", "blocks": nl, "T": T, "hidden": d.hidden,
                        "latent": d.latent, "experts": d.n_experts, "inter": d.inter,

@@ -273,3 +273,43 @@ def test_stack145_three_blocks(path):
     err = rel_l2(oracle.bf16_value(cur) - x0, oracle.bf16_value(xs[3]) - x0)
     say(f"[ok] stack145 3 blocks path={path}: accumulated MoE part rel_l2={err:.3e}")
     assert err <= 2e-2
+
+
+@pytest.mark.parametrize("path", [lsm.PATH_DECODE, lsm.PATH_GROUPED])
+def test_graph_replay_matches_eager(path):
+    """Three chained residual blocks (T = 8) captured in one HIP graph: every
+    replay must reproduce the eager result bit for bit, with eager calls on
+    the same buffers between the replays (the path records only kernel
+    launches: no memset, copy or host synchronisation while capturing)."""
+    cfg, hosts, dls = _stack_layers(3)
+    dev = device()
+    x = torch.from_numpy(synth.make_x(cfg.T, cfg.dims.hidden, cfg.seed).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    ws = lsm.alloc_workspace(cfg.dims, cfg.T, dev)
+    bufs = [torch.empty_like(x), torch.empty_like(x)]
+
+    def step():
+        cur = x
+        for l, dl in enumerate(dls):
+            o = bufs[l % 2]
+            lsm.forward(cur, dl, out=o, workspace=ws, path=path, residual=True)
+            cur = o
+        return cur
+
+    say(f"[case] graph replay of 3 residual blocks, path={path}")
+    out = step()
+    torch.cuda.synchronize()
+    ref = out.view(torch.int16).clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        bufs[0].zero_()
+        bufs[1].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref), f"replay {i} differs from the eager result"
+        step()  # eager work on the same buffers between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref), f"eager call after replay {i} differs"
+    say("[ok] graph replays identical to eager")
