@@ -3,8 +3,9 @@
 // At a handful of tokens every weight byte feeds only T multiply-adds, so the
 // layer is bound by HBM bandwidth and by the fixed latency of each dependent
 // step. Five kernels; in each, every wave issues its loads before anything
-// else, and a kernel boundary is the only grid-wide synchronisation (no
-// workgroup ever waits for another one to be scheduled):
+// else (the routed gate/up kernel first stages its activations, see there),
+// and a kernel boundary is the only grid-wide synchronisation (no workgroup
+// ever waits for another one to be scheduled):
 //
 //   1. dec_dproj   h = x D^T (RMSNorm fused for the residual block); K split
 //                  over the 8 waves; h leaves as bf16 hi + lo
@@ -573,13 +574,19 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   const bool busy = tile < n_act * tiles;
   const int e = busy ? e_guess : 0;
   const int n0 = busy ? (tile % tiles) * 16 : 0;
+  // The activations are staged, and waited for, before any weight load is
+  // issued. Four workgroups share a CU and all of them stream weights at
+  // once, so activations loaded behind the weights arrive only when most of
+  // the CU's weights have; every workgroup's compute would then start after
+  // the data window instead of riding on it (measured: 60.3 -> 58.2 us per
+  // decode step at T = 4).
   RowStage<(NCH_H + 1) / 2> st;  // T x latent, latent = 256 NCH_H
   st.load(a.hhi, T * L);
+  st.store(hi, T * L);
+  __syncthreads();
   GateUpTask<NCH_H> task;
   if (busy) task.load(a.gate, a.up, e, I, L, n0, wave, lane);
   const float gsg = a.gate.gscale[e], gsu = a.up.gscale[e];
-  st.store(hi, T * L);
-  __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (busy) acc = task.mma(t < T ? hi + t * L : nullptr, L, wave, lane);
   finish_gateup(acc, red, busy, gsg, gsu,
