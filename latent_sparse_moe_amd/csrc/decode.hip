@@ -3,7 +3,7 @@
 // At a handful of tokens every weight byte feeds only T multiply-adds, so the
 // layer is bound by HBM bandwidth and by the fixed latency of each dependent
 // step. Five kernels; in each, every wave issues its loads before anything
-// else (the routed gate/up kernel first stages its activations, see there),
+// else (the router and routed gate/up kernels first stage their activations),
 // and a kernel boundary is the only grid-wide synchronisation (no workgroup
 // ever waits for another one to be scheduled):
 //
@@ -491,8 +491,13 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
     const int e = min(e0 + (lane & 15), E - 1);
     const int kb = wave * (L / kDecWaves);
     RowStage<(NCH_R + 1) / 2> sh_hi, sh_lo;  // T x latent, latent = 256 NCH_R
+    // latent rows staged (and waited for) before the router rows are loaded,
+    // as in the routed gate/up kernel (measured: 0.6 us less per decode step)
     sh_hi.load(a.hhi, T * L);
     sh_lo.load(a.hlo, T * L);
+    sh_hi.store(hi, T * L);
+    sh_lo.store(lo, T * L);
+    __syncthreads();
     Bf16Rows<NCH_R> wr;
     wr.load(a.R + (size_t)e * L, kb, g);
     float bias[4] = {0.f, 0.f, 0.f, 0.f};
@@ -500,9 +505,6 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) bias[r] = a.bias[min(e0 + g * 4 + r, E - 1)];
     }
-    sh_hi.store(hi, T * L);
-    sh_lo.store(lo, T * L);
-    __syncthreads();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     wr.mma2(t < T ? hi + t * L : nullptr, t < T ? lo + t * L : nullptr, kb, g, acc);
     const f32x4 tot = reduce_waves(acc, red);
