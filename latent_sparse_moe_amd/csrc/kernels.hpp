@@ -73,8 +73,8 @@ hipError_t launch_route_scan(int32_t* chunk_hist, int n_chunks, int E, int pairs
                              int n_shared, int32_t* counts, int32_t* off, int32_t* tile_off,
                              hipStream_t stream);
 hipError_t launch_route_permute(const int32_t* idx, int pairs, int E,
-                                const int32_t* chunk_base, int32_t* perm, int32_t* slot,
-                                hipStream_t stream);
+                                const int32_t* chunk_base, const int32_t* off, int32_t* perm,
+                                int32_t* slot, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w, int T, int k,
                           int pairs, int latent, int n_shared, uint16_t* z, hipStream_t stream);
 

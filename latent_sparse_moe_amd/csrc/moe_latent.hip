@@ -207,7 +207,7 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   HIP_TRY(sm.mark(moe::kStageRoute, 0));
   HIP_TRY(moe::launch_route_hist(idx, P, E, chunk, st));
   HIP_TRY(moe::launch_route_scan(chunk, nch, E, P, T, d.n_shared, counts, off, tile_off, st));
-  HIP_TRY(moe::launch_route_permute(idx, P, E, chunk, perm, slot, st));
+  HIP_TRY(moe::launch_route_permute(idx, P, E, chunk, off, perm, slot, st));
   HIP_TRY(sm.mark(moe::kStageRoute, 1));
   // S7-S9: grouped expert GEMMs (routed groups, then the shared expert).
   moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k};

@@ -182,7 +182,10 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
 //   counts[e]; off[e] = exclusive prefix of counts (off[E] = pairs,
 //   off[E+1] = pairs + n_shared*T for the shared expert's rows);
 //   tile_off likewise over ceil(count/128) (the grouped GEMM m-tiles);
-//   chunk_hist[c][e] becomes the first permuted row of chunk c's pairs of e.
+//   chunk_hist[c][e] becomes the pairs of e in chunks before c (the permute
+//   adds off[e]). A thread's chunk counts are loaded 16 at a time before
+//   any is used, so the walk over the chunks is not one load round trip per
+//   chunk.
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_hist,
                                                      int n_chunks, int E, int pairs, int T,
                                                      int n_shared, int32_t* __restrict__ counts,
@@ -192,10 +195,16 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      const int v = chunk_hist[(size_t)c * E + e];
-      chunk_hist[(size_t)c * E + e] = cnt;
-      cnt += v;
+    for (int c0 = 0; c0 < n_chunks; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        v[j] = c0 + j < n_chunks ? chunk_hist[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (c0 + j < n_chunks) chunk_hist[(size_t)(c0 + j) * E + e] = cnt;
+        cnt += v[j];
+      }
     }
   }
   const int tiles = (cnt + 127) / 128;
@@ -205,7 +214,6 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
     counts[e] = cnt;
     off[e] = ex_cnt;
     tile_off[e] = ex_tiles;
-    for (int c = 0; c < n_chunks; ++c) chunk_hist[(size_t)c * E + e] += ex_cnt;
   }
   if (e == 0) {
     off[E] = pairs;
@@ -225,27 +233,45 @@ hipError_t launch_route_scan(int32_t* chunk_hist, int n_chunks, int E, int pairs
 
 // ------------------------------------------------------------------ permute
 
-// One wave per chunk walks its pairs in order, 64 at a time. Lanes holding
-// the same expert find each other with one ballot per bit of the expert id;
-// a lane's rank among them (lanes below it) gives its position after the
-// chunk's running cursor for that expert, so the result is the stable
-// counting sort: ascending pair index within each expert.
-__global__ __launch_bounds__(64) void k_route_permute(const int32_t* __restrict__ idx, int pairs,
-                                                      int E, const int32_t* __restrict__ chunk_base,
-                                                      int32_t* __restrict__ perm,
-                                                      int32_t* __restrict__ slot) {
+// One 4-wave workgroup per chunk walks its pairs in order, 256 at a time
+// (wave w takes pairs base + 64w .. +64). Lanes of a wave holding the same
+// expert find each other with one ballot per bit of the expert id, and a
+// lane's rank among them (lanes below it) orders them. The waves then meet
+// in LDS: each wave's count per expert, summed over the earlier waves, comes
+// before it. Position = the chunk's cursor for the expert + earlier waves +
+// rank, so the result is the stable counting sort: ascending pair index
+// within each expert. A lane's expert ids for the whole chunk are loaded
+// before the walk.
+constexpr int kPermThreads = 256;
+constexpr int kPermWaves = kPermThreads / 64;
+constexpr int kPermIter = kRouteChunk / kPermThreads;
+
+__global__ __launch_bounds__(kPermThreads) void k_route_permute(
+    const int32_t* __restrict__ idx, int pairs, int E, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ off, int32_t* __restrict__ perm, int32_t* __restrict__ slot) {
   __shared__ int cursor[kMaxExperts + 1];
-  const int lane = threadIdx.x, c = blockIdx.x;
-  for (int e = lane; e < E; e += 64) cursor[e] = chunk_base[(size_t)c * E + e];
-  if (lane == 0) cursor[E] = 0;
-  __syncthreads();
+  __shared__ int wcnt[kPermWaves][kMaxExperts + 1];  // per-wave counts of this step
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = blockIdx.x;
+  for (int e = tid; e <= E; e += kPermThreads) {
+    cursor[e] = e < E ? off[e] + chunk_base[(size_t)c * E + e] : 0;
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) wcnt[w][e] = 0;
+  }
   const int nbits = 32 - __clz(E);  // enough bits for the sentinel value E
   const uint64_t below = lanemask_lt();
   const int p0 = c * kRouteChunk, p1 = min(p0 + kRouteChunk, pairs);
-  for (int base = p0; base < p1; base += 64) {
-    const int p = base + lane;
+  int ev[kPermIter];
+#pragma unroll
+  for (int i = 0; i < kPermIter; ++i) {
+    const int p = p0 + i * kPermThreads + tid;
+    ev[i] = p < p1 ? idx[p] : E;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kPermIter; ++i) {
+    const int p = p0 + i * kPermThreads + tid;
     const bool valid = p < p1;
-    const int e = valid ? idx[p] : E;
+    const int e = ev[i];
     uint64_t peers = ~0ull;
     for (int b = 0; b < nbits; ++b) {
       const int bit = (e >> b) & 1;
@@ -253,22 +279,31 @@ __global__ __launch_bounds__(64) void k_route_permute(const int32_t* __restrict_
       peers &= bit ? m : ~m;
     }
     const int rank = __popcll(peers & below);
-    const int start = cursor[e];
+    const int cnt = __popcll(peers);
+    if (valid && rank == 0) wcnt[wave][e] = cnt;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wcnt[w][e];
     if (valid) {
-      const int pos = start + rank;
+      const int pos = cursor[e] + before + rank;
       perm[pos] = p;
       slot[p] = pos;
-      if (rank == 0) cursor[e] = start + __popcll(peers);
+    }
+    __syncthreads();  // every lane has read this step's cursors and counts
+    if (valid && rank == 0) {
+      atomicAdd(&cursor[e], cnt);  // order-free sum over the waves
+      wcnt[wave][e] = 0;
     }
     __syncthreads();
   }
 }
 
 hipError_t launch_route_permute(const int32_t* idx, int pairs, int E, const int32_t* chunk_base,
-                                int32_t* perm, int32_t* slot, hipStream_t stream) {
+                                const int32_t* off, int32_t* perm, int32_t* slot,
+                                hipStream_t stream) {
   const int nch = (pairs + kRouteChunk - 1) / kRouteChunk;
-  hipLaunchKernelGGL(k_route_permute, dim3(nch), dim3(64), 0, stream, idx, pairs, E, chunk_base,
-                     perm, slot);
+  hipLaunchKernelGGL(k_route_permute, dim3(nch), dim3(kPermThreads), 0, stream, idx, pairs, E,
+                     chunk_base, off, perm, slot);
   return hipGetLastError();
 }
 
