@@ -268,13 +268,28 @@ __device__ __forceinline__ void mainloop(ALoader<BK>& al, const BL& bl, int KT, 
 }
 
 // The products are computed transposed (weights as the first matrix-core
-// operand), so accumulator acc[i][j] holds, for token row i*32 + l % 32 of
-// the tile, the four consecutive outputs of column block j starting at
-// acc_col(g, l) in registers 4g .. 4g + 3: one 8-byte store of bf16.
-__device__ __forceinline__ int acc_col(int g, int lane) { return g * 8 + (lane >> 5) * 4; }
+// operand): result register r of lane l belongs to matrix-core row
+// m = (r/4)*8 + (l/32)*4 + r%4, i.e. to the weight row loaded by lane m of
+// the operand. Lanes do not load weight row m of their 32-row block but row
+// weight_row(m), chosen so that registers 8q .. 8q+7 of lane l hold the eight
+// consecutive output columns starting at acc_col(q, l) = 16q + 8*(l/32). A
+// lane then stores eight outputs (16 bytes of bf16) at once, and the two
+// lanes of a token row fill 32 contiguous bytes per store instruction.
+__device__ __forceinline__ int weight_row(int m) {
+  const int r = (m >> 3) * 4 + (m & 3), h = (m >> 2) & 1;
+  return (r >> 3) * 16 + h * 8 + (r & 7);
+}
+__device__ __forceinline__ int acc_col(int q, int lane) { return q * 16 + (lane >> 5) * 8; }
 
-__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
-  return uint2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+// Registers 8q .. 8q+7 of an accumulator, each times s, as eight bf16.
+__device__ __forceinline__ uint4 pack_bf16x8(const f32x16& c, int q, float s) {
+  return uint4{pack_bf16x2(s * c[8 * q], s * c[8 * q + 1]), pack_bf16x2(s * c[8 * q + 2], s * c[8 * q + 3]),
+               pack_bf16x2(s * c[8 * q + 4], s * c[8 * q + 5]),
+               pack_bf16x2(s * c[8 * q + 6], s * c[8 * q + 7])};
+}
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
+  return uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+               pack_bf16x2(v[6], v[7])};
 }
 
 #define MOE_GEMM_LDS(BK)                                                        \
@@ -295,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int m0 = (tile / nt) * kBM, n0 = (tile % nt) * kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ncol = n0 + wave * 64 + (lane & 31);  // weight row this lane loads (sub-tile 0)
+  const int ncol = n0 + wave * 64 + weight_row(lane & 31);  // weight row this lane loads (sub-tile 0)
   ALoader<BK> al;
   al.init([&](int r) { return A + (size_t)min(m0 + r, M - 1) * lda; });
   Bf16B<BK> bl;
@@ -304,8 +319,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
   mainloop<BK>(al, bl, K / BK, pipe, acc);
 
   const int nbase = n0 + wave * 64;
-  // 4-wide stores need the row starts 8-byte (16-byte for fp32) aligned
-  const bool vec = (ep.ldo & 3) == 0 && (EPI != kEpiOut || !ep.resid || (ep.ldr & 3) == 0);
+  // 8-wide stores need the row starts 16-byte aligned
+  const bool vec = EPI == kEpiLogits
+                       ? (ep.ldo & 3) == 0
+                       : (ep.ldo & 7) == 0 && (EPI != kEpiSplit || (ep.lo_off & 7) == 0) &&
+                             (EPI != kEpiOut || !ep.resid || (ep.ldr & 7) == 0);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + i * 32 + (lane & 31);
@@ -313,50 +331,57 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = nbase + j * 32 + acc_col(g, lane);
+      for (int q = 0; q < 2; ++q) {
+        const int n = nbase + j * 32 + acc_col(q, lane);
         if (n >= N) continue;
-        float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                      acc[i][j][4 * g + 3]};
-        const int nv = min(4, N - n);
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = acc[i][j][8 * q + e];
+        const int nv = min(8, N - n);
         if (EPI == kEpiSplit) {
           // latent vector as bf16 hi + bf16 lo: hi feeds the experts, hi + lo
           // (about 16 significant bits) feeds the router
           uint16_t* o = (uint16_t*)ep.out + (size_t)m * ep.ldo + n;
-          float lo[4];
+          float lo[8];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) lo[q] = v[q] - bf16_bits_to_f32(f32_to_bf16_bits(v[q]));
-          if (vec && nv == 4) {
-            *(uint2*)o = pack_bf16x4(v[0], v[1], v[2], v[3]);
-            *(uint2*)(o + ep.lo_off) = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+          for (int e = 0; e < 8; ++e) lo[e] = v[e] - bf16_bits_to_f32(f32_to_bf16_bits(v[e]));
+          if (vec && nv == 8) {
+            *(uint4*)o = pack_bf16x8(v);
+            *(uint4*)(o + ep.lo_off) = pack_bf16x8(lo);
           } else {
-            for (int q = 0; q < nv; ++q) {
-              o[q] = f32_to_bf16_bits(v[q]);
-              o[ep.lo_off + q] = f32_to_bf16_bits(lo[q]);
+            for (int e = 0; e < nv; ++e) {
+              o[e] = f32_to_bf16_bits(v[e]);
+              o[ep.lo_off + e] = f32_to_bf16_bits(lo[e]);
             }
           }
         } else if (EPI == kEpiLogits) {
           float* o = (float*)ep.out + (size_t)m * ep.ldo + n;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] += ep.bias && q < nv ? ep.bias[n + q] : 0.0f;
-          if (vec && nv == 4) *(float4*)o = float4{v[0], v[1], v[2], v[3]};
-          else for (int q = 0; q < nv; ++q) o[q] = v[q];
+          for (int e = 0; e < 8; ++e) v[e] += ep.bias && e < nv ? ep.bias[n + e] : 0.0f;
+          if (vec && nv == 8) {
+            *(float4*)o = float4{v[0], v[1], v[2], v[3]};
+            *(float4*)(o + 4) = float4{v[4], v[5], v[6], v[7]};
+          } else {
+            for (int e = 0; e < nv; ++e) o[e] = v[e];
+          }
         } else {  // kEpiOut
           uint16_t* o = (uint16_t*)ep.out + (size_t)m * ep.ldo + n;
           if (ep.resid) {
             const uint16_t* rr = ep.resid + (size_t)m * ep.ldr + n;
-            if (vec && nv == 4) {
-              const uint2 rv = *(const uint2*)rr;
-              v[0] += bf16_bits_to_f32(rv.x & 0xFFFFu);
-              v[1] += bf16_bits_to_f32(rv.x >> 16);
-              v[2] += bf16_bits_to_f32(rv.y & 0xFFFFu);
-              v[3] += bf16_bits_to_f32(rv.y >> 16);
+            if (vec && nv == 8) {
+              const uint4 rv = *(const uint4*)rr;
+              const uint32_t d[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v[2 * e] += bf16_bits_to_f32(d[e] & 0xFFFFu);
+                v[2 * e + 1] += bf16_bits_to_f32(d[e] >> 16);
+              }
             } else {
-              for (int q = 0; q < nv; ++q) v[q] += bf16_bits_to_f32(rr[q]);
+              for (int e = 0; e < nv; ++e) v[e] += bf16_bits_to_f32(rr[e]);
             }
           }
-          if (vec && nv == 4) *(uint2*)o = pack_bf16x4(v[0], v[1], v[2], v[3]);
-          else for (int q = 0; q < nv; ++q) o[q] = f32_to_bf16_bits(v[q]);
+          if (vec && nv == 8) *(uint4*)o = pack_bf16x8(v);
+          else for (int e = 0; e < nv; ++e) o[e] = f32_to_bf16_bits(v[e]);
         }
       }
   }
@@ -416,7 +441,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   TileWork tw;
   if (!tile_work(rv, tile / nt, &tw)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = (tile % nt) * (kBN / 2) + wave * 32 + (lane & 31);  // weight row this lane loads
+  const int n = (tile % nt) * (kBN / 2) + wave * 32 + weight_row(lane & 31);  // weight row this lane loads
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   const int P = rv.pairs;
@@ -443,17 +468,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int row = tw.rbeg + i * 32 + (lane & 31);
     if (row >= tw.rend) continue;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int nc = nbase + acc_col(g4, lane);
-      if (nc >= inter) continue;  // inter is a multiple of 32: all four or none
-      float a[4];
+    for (int q = 0; q < 2; ++q) {
+      const int nc = nbase + acc_col(q, lane);
+      if (nc >= inter) continue;  // inter is a multiple of 32: all eight or none
+      float a[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float g = gsg * acc[i][0][4 * g4 + q];
-        const float u = gsu * acc[i][1][4 * g4 + q];
-        a[q] = g / (1.0f + expf(-g)) * u;
+      for (int e = 0; e < 8; ++e) {
+        const float g = gsg * acc[i][0][8 * q + e];
+        const float u = gsu * acc[i][1][8 * q + e];
+        a[e] = g / (1.0f + expf(-g)) * u;
       }
-      *(uint2*)(act + (size_t)row * inter + nc) = pack_bf16x4(a[0], a[1], a[2], a[3]);
+      *(uint4*)(act + (size_t)row * inter + nc) = pack_bf16x8(a);
     }
   }
 }
@@ -469,7 +494,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   TileWork tw;
   if (!tile_work(rv, tile / nt, &tw)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ncol = (tile % nt) * kBN + wave * 64 + (lane & 31);  // weight row this lane loads
+  const int ncol = (tile % nt) * kBN + wave * 64 + weight_row(lane & 31);  // weight row this lane loads
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   ALoader<BK> al;
@@ -492,12 +517,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int nc = nbase + j * 32 + acc_col(g4, lane);
-        if (nc >= latent) continue;  // latent is a multiple of 32: all four or none
-        const f32x16& c = acc[i][j];
-        *(uint2*)(y + (size_t)row * latent + nc) =
-            pack_bf16x4(gsd * c[4 * g4], gsd * c[4 * g4 + 1], gsd * c[4 * g4 + 2], gsd * c[4 * g4 + 3]);
+      for (int q = 0; q < 2; ++q) {
+        const int nc = nbase + j * 32 + acc_col(q, lane);
+        if (nc >= latent) continue;  // latent is a multiple of 32: all eight or none
+        *(uint4*)(y + (size_t)row * latent + nc) = pack_bf16x8(acc[i][j], q, gsd);
       }
   }
 }
