@@ -203,12 +203,14 @@ struct Pipe {
 // register set (S+2)%3, B into B set (S+2)%3), run the matrix cores on A
 // stage S and B set S, and write A of step kt + 1 (loaded one step ago) into
 // stage (S+1)%3, which was read last in step kt - 2. Past the last step the
-// loads repeat step KT - 1 and the writes go to a stage nobody reads.
-template <int BK, int S, class BL>
+// loads repeat step KT - 1 and the writes go to a stage nobody reads. Only
+// the first NI 32-row blocks of the tile are multiplied (the last tile of an
+// expert's rows may hold fewer than 128).
+template <int BK, int S, int NI, class BL>
 __device__ __forceinline__ void gemm_step(int kt, int KT, ALoader<BK>& al, const BL& bl,
                                           const Pipe& p, typename BL::Set (&bs)[3],
                                           const int (&frag)[Geo<BK>::kSub],
-                                          f32x16 (&acc)[4][2]) {
+                                          f32x16 (&acc)[NI][2]) {
   using G = Geo<BK>;
   constexpr int N1 = (S + 1) % 3, N2 = (S + 2) % 3;
   const int kl = min(kt + 2, KT - 1);
@@ -217,13 +219,13 @@ __device__ __forceinline__ void gemm_step(int kt, int KT, ALoader<BK>& al, const
   const uint16_t* ca = p.a[S];
 #pragma unroll
   for (int ks = 0; ks < G::kSub; ++ks) {
-    bf16x8 a[4], b[2];
+    bf16x8 a[NI], b[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(ca + i * 32 * BK + frag[ks]);
+    for (int i = 0; i < NI; ++i) a[i] = *(const bf16x8*)(ca + i * 32 * BK + frag[ks]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) b[j] = bl.frag(bs[S], j, ks);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
     if (ks == 0) al.finish(p.a[N1], N1);
@@ -231,16 +233,21 @@ __device__ __forceinline__ void gemm_step(int kt, int KT, ALoader<BK>& al, const
   lds_barrier();
 }
 
-template <int BK, class BL>
-__device__ __forceinline__ void mainloop(ALoader<BK>& al, const BL& bl, int KT, const Pipe& p,
-                                         f32x16 (&acc)[4][2]) {
-  using G = Geo<BK>;
+template <int NI>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[NI][2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// Accumulates the tile's products into acc (zeroed by the caller).
+template <int BK, int NI, class BL>
+__device__ __forceinline__ void mainloop(ALoader<BK>& al, const BL& bl, int KT, const Pipe& p,
+                                         f32x16 (&acc)[NI][2]) {
+  using G = Geo<BK>;
   // this lane's A fragment slot (in elements) for each matrix-core step,
   // relative to the first row of its 32-row block
   const int lane = threadIdx.x & 63;
@@ -259,12 +266,12 @@ __device__ __forceinline__ void mainloop(ALoader<BK>& al, const BL& bl, int KT, 
   lds_barrier();
   int kt = 0;
   for (; kt + 3 <= KT; kt += 3) {
-    gemm_step<BK, 0>(kt, KT, al, bl, p, bs, frag, acc);
-    gemm_step<BK, 1>(kt + 1, KT, al, bl, p, bs, frag, acc);
-    gemm_step<BK, 2>(kt + 2, KT, al, bl, p, bs, frag, acc);
+    gemm_step<BK, 0, NI>(kt, KT, al, bl, p, bs, frag, acc);
+    gemm_step<BK, 1, NI>(kt + 1, KT, al, bl, p, bs, frag, acc);
+    gemm_step<BK, 2, NI>(kt + 2, KT, al, bl, p, bs, frag, acc);
   }
-  if (kt < KT) gemm_step<BK, 0>(kt, KT, al, bl, p, bs, frag, acc);
-  if (kt + 1 < KT) gemm_step<BK, 1>(kt + 1, KT, al, bl, p, bs, frag, acc);
+  if (kt < KT) gemm_step<BK, 0, NI>(kt, KT, al, bl, p, bs, frag, acc);
+  if (kt + 1 < KT) gemm_step<BK, 1, NI>(kt + 1, KT, al, bl, p, bs, frag, acc);
 }
 
 // The products are computed transposed (weights as the first matrix-core
@@ -316,7 +323,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
   Bf16B<BK> bl;
   bl.init([&](int j) { return B + (size_t)min(ncol + j * 32, N - 1) * ldb; }, kwrap);
   f32x16 acc[4][2];
-  mainloop<BK>(al, bl, K / BK, pipe, acc);
+  zero_acc<4>(acc);
+  mainloop<BK, 4>(al, bl, K / BK, pipe, acc);
 
   const int nbase = n0 + wave * 64;
   // 8-wide stores need the row starts 16-byte aligned
@@ -427,21 +435,27 @@ __device__ __forceinline__ const Fp4Set& pick_set(const ExpertsView& ex, int g, 
   return ex.shared;
 }
 
+// Blocks of 32 rows holding the tile's rows (1..4). The last tile of an
+// expert's rows is usually partial; gate/up runs it with 1, 2 or 4 blocks
+// of matrix-core work (at the 16K-token routing this cuts the padded rows
+// from 15% to 4%). Each count has its own copy of the tile body, so nothing
+// stays live across the dispatch. Down keeps one copy: with more, the
+// register allocator spills inside its K loop, which costs more than the
+// padding.
+__device__ __forceinline__ int row_blocks(const TileWork& tw) {
+  return min(4, (tw.rend - tw.rbeg + 31) / 32);
+}
+
 // Gate/up: a tile covers 128 output columns of the SwiGLU width; wave w
 // takes columns n0 + 32w .. +32 as sub-tile 0 (gate rows) and sub-tile 1 (up
 // rows), so SiLU*mul pairs them in registers.
-template <int BK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_gateup(const uint16_t* __restrict__ hcat,
-                                                            int ldh, RouteView rv,
-                                                            ExpertsView ex, uint16_t* __restrict__ act,
-                                                            int inter, int latent) {
-  MOE_GEMM_LDS(BK);
-  const int nt = (inter + kBN / 2 - 1) / (kBN / 2);
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  TileWork tw;
-  if (!tile_work(rv, tile / nt, &tw)) return;
+template <int BK, int NI>
+__device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, int ldh,
+                                            const RouteView& rv, const ExpertsView& ex,
+                                            uint16_t* __restrict__ act, int inter, int latent,
+                                            const TileWork& tw, int n0, const Pipe& pipe) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = (tile % nt) * (kBN / 2) + wave * 32 + weight_row(lane & 31);  // weight row this lane loads
+  const int n = n0 + wave * 32 + weight_row(lane & 31);  // weight row this lane loads
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   const int P = rv.pairs;
@@ -458,13 +472,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     *c = m.codes + row * (latent / 2);
     *s = m.scales + row * (latent / 16);
   }, 0);
-  f32x16 acc[4][2];
-  mainloop<BK>(al, bl, latent / BK, pipe, acc);
+  f32x16 acc[NI][2];
+  zero_acc<NI>(acc);
+  mainloop<BK, NI>(al, bl, latent / BK, pipe, acc);
 
   const float gsg = set.gate.gscale[le], gsu = set.up.gscale[le];
-  const int nbase = (tile % nt) * (kBN / 2) + wave * 32;
+  const int nbase = n0 + wave * 32;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int row = tw.rbeg + i * 32 + (lane & 31);
     if (row >= tw.rend) continue;
 #pragma unroll
@@ -484,17 +499,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 }
 
 template <int BK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_down(const uint16_t* __restrict__ act,
-                                                          RouteView rv, ExpertsView ex,
-                                                          uint16_t* __restrict__ y, int inter,
-                                                          int latent) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_gateup(
+    const uint16_t* __restrict__ hcat, int ldh, RouteView rv, ExpertsView ex,
+    uint16_t* __restrict__ act, int inter, int latent) {
   MOE_GEMM_LDS(BK);
-  const int nt = (latent + kBN - 1) / kBN;
+  const int nt = (inter + kBN / 2 - 1) / (kBN / 2);
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   TileWork tw;
   if (!tile_work(rv, tile / nt, &tw)) return;
+  const int n0 = (tile % nt) * (kBN / 2);
+  const int nb = row_blocks(tw);
+  if (nb == 1) gateup_tile<BK, 1>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
+  else if (nb == 2) gateup_tile<BK, 2>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
+  else gateup_tile<BK, 4>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
+}
+
+template <int BK, int NI>
+__device__ __forceinline__ void down_tile(const uint16_t* __restrict__ act, const RouteView& rv,
+                                          const ExpertsView& ex, uint16_t* __restrict__ y,
+                                          int inter, int latent, const TileWork& tw, int n0,
+                                          const Pipe& pipe) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ncol = (tile % nt) * kBN + wave * 64 + weight_row(lane & 31);  // weight row this lane loads
+  const int ncol = n0 + wave * 64 + weight_row(lane & 31);  // weight row this lane loads
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   ALoader<BK> al;
@@ -505,13 +531,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     *c = set.down.codes + row * (inter / 2);
     *s = set.down.scales + row * (inter / 16);
   }, 0);
-  f32x16 acc[4][2];
-  mainloop<BK>(al, bl, inter / BK, pipe, acc);
+  f32x16 acc[NI][2];
+  zero_acc<NI>(acc);
+  mainloop<BK, NI>(al, bl, inter / BK, pipe, acc);
 
   const float gsd = set.down.gscale[le];
-  const int nbase = (tile % nt) * kBN + wave * 64;
+  const int nbase = n0 + wave * 64;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int row = tw.rbeg + i * 32 + (lane & 31);
     if (row >= tw.rend) continue;
 #pragma unroll
@@ -523,6 +550,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         *(uint4*)(y + (size_t)row * latent + nc) = pack_bf16x8(acc[i][j], q, gsd);
       }
   }
+}
+
+template <int BK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_down(
+    const uint16_t* __restrict__ act, RouteView rv, ExpertsView ex, uint16_t* __restrict__ y,
+    int inter, int latent) {
+  MOE_GEMM_LDS(BK);
+  const int nt = (latent + kBN - 1) / kBN;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  TileWork tw;
+  if (!tile_work(rv, tile / nt, &tw)) return;
+  const int n0 = (tile % nt) * kBN;
+  down_tile<BK, 4>(act, rv, ex, y, inter, latent, tw, n0, pipe);
 }
 
 // ------------------------------------------------------------------ launchers
