@@ -112,4 +112,97 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
+// ------------------------------------------------------------------ top-k selection
+
+// Order-preserving 32-bit key of an fp32 value (larger value, larger key;
+// -0 and +0 share a key, and 0 is below every non-NaN value and marks an
+// empty or taken entry).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+  return o > v ? o : v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_umin(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+  return o < v ? o : v;
+}
+
+// Largest / smallest value over the 64 lanes (wave-uniform): DPP steps
+// inside each 16-lane row, then the four row results through readlane.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = dpp_umax<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_umax<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_umax<0x141>(v);  // row_half_mirror: over 8 lanes
+  v = dpp_umax<0x140>(v);  // row_mirror: over 16 lanes
+  uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, r * 16);
+    m = o > m ? o : m;
+  }
+  return m;
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = dpp_umin<0xB1>(v);
+  v = dpp_umin<0x4E>(v);
+  v = dpp_umin<0x141>(v);
+  v = dpp_umin<0x140>(v);
+  uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, r * 16);
+    m = o < m ? o : m;
+  }
+  return m;
+}
+
+// k rounds of a wave-wide arg-max over the keys of one token, lane l holding
+// experts l, l + 64, ... (key 0 = absent). Round r takes the largest key
+// left, ties to the lower expert; lane r ends with its key and expert.
+// The largest key comes from one DPP reduction. The lanes holding it are
+// found by a ballot: when exactly one lane does (the usual case) its lowest
+// such expert wins directly; otherwise a second reduction takes the lowest
+// expert over those lanes.
+template <int EPL>
+__device__ __forceinline__ void wave_select_topk(uint32_t (&key)[EPL], int E, int k,
+                                                 uint32_t& my_key, int& my_e) {
+  const int lane = threadIdx.x & 63;
+  my_key = 0u;
+  my_e = 0;
+  for (int r = 0; r < k; ++r) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+    const uint32_t m = wave_umax(best);
+    // this lane's lowest expert holding m (expert = lane + 64 i)
+    uint32_t first = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = EPL - 1; i >= 0; --i) first = key[i] == m ? (uint32_t)(lane + 64 * i) : first;
+    const uint64_t holders = __ballot(best == m);
+    uint32_t win;
+    if (__popcll(holders) == 1)
+      win = (uint32_t)__builtin_amdgcn_readlane((int)first, __ffsll((unsigned long long)holders) - 1);
+    else
+      win = wave_umin(first);
+    const int w = (int)min(win, (uint32_t)(E - 1));  // in range even for NaN
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i == w ? 0u : key[i];
+    if (lane == r) {
+      my_key = m;
+      my_e = w;
+    }
+  }
+}
+
 }  // namespace moe

@@ -299,57 +299,6 @@ __device__ __forceinline__ void finish_gateup(f32x4 acc, float* red, bool tile_b
 
 // ------------------------------------------------------------------ top-k
 
-// Order-preserving 32-bit key of an fp32 value (larger value, larger key;
-// 0 is below every non-NaN value and marks an empty or taken entry).
-__device__ __forceinline__ uint32_t order_key(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_umax(uint32_t v) {
-  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-  return o > v ? o : v;
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_umin(uint32_t v) {
-  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-  return o < v ? o : v;
-}
-
-// Largest / smallest value over the 64 lanes (wave-uniform): DPP steps
-// inside each 16-lane row, then the four row results through readlane.
-__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
-  v = dpp_umax<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = dpp_umax<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = dpp_umax<0x141>(v);  // row_half_mirror: over 8 lanes
-  v = dpp_umax<0x140>(v);  // row_mirror: over 16 lanes
-  uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, r * 16);
-    m = o > m ? o : m;
-  }
-  return m;
-}
-__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
-  v = dpp_umin<0xB1>(v);
-  v = dpp_umin<0x4E>(v);
-  v = dpp_umin<0x141>(v);
-  v = dpp_umin<0x140>(v);
-  uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) {
-    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, r * 16);
-    m = o < m ? o : m;
-  }
-  return m;
-}
-
 // Top-k of one token's logits by this wave; lane j < k ends with choice j
 // (descending value, equal values to the lower expert). Renormalised
 // weights: exp(l_j - l_0) / sum over the k chosen. The logits were written
@@ -365,25 +314,9 @@ __device__ __forceinline__ void wave_topk(const float* row, int E, int k, int* o
     key[i] = e < E ? order_key(__hip_atomic_load(row + min(e, E - 1), __ATOMIC_RELAXED, AGENT))
                    : 0u;
   }
-  uint32_t my_key = 0u;
-  int my_e = 0;
-  for (int r = 0; r < k; ++r) {
-    uint32_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-    const uint32_t m = wave_umax(best);
-    // the lowest expert holding m (expert = lane + 64 i)
-    uint32_t first = 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = EPL - 1; i >= 0; --i) first = key[i] == m ? (uint32_t)(lane + 64 * i) : first;
-    const int win = (int)min(wave_umin(first), (uint32_t)(E - 1));  // in range even for NaN
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i == win ? 0u : key[i];
-    if (lane == r) {
-      my_key = m;
-      my_e = win;
-    }
-  }
+  uint32_t my_key;
+  int my_e;
+  wave_select_topk<EPL>(key, E, k, my_key, my_e);
   const float top = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
   const float ex = lane < k ? expf(key_value(my_key) - top) : 0.0f;
   const float sum = wave_sum(ex);

@@ -68,9 +68,9 @@ hipError_t launch_rmsnorm(const uint16_t* x, const float* w, float eps, uint16_t
 
 // ------------------------------------------------------------------ top-k
 
-// One wave per token; lane l holds logits of experts l, l+64, ... (EPL of
-// them). k rounds of a wave-wide arg-max (larger value wins, ties to the
-// lower expert index); lane j keeps the j-th choice.
+// One wave per token; lane l holds the logits of experts l, l+64, ... (EPL
+// of them) as order-preserving keys; k rounds of a wave-wide arg-max (larger
+// value wins, ties to the lower expert index); lane j keeps the j-th choice.
 template <int EPL>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E,
                                               int k, int32_t* __restrict__ idx,
@@ -79,43 +79,17 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
-  float v[EPL];
+  uint32_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : -INFINITY;
+    key[i] = e < E ? order_key(row[e]) : 0u;
   }
-  uint32_t taken = 0;
-  float my_v = 0.0f;
-  int my_e = 0;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int be = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < be))) {
-        bv = v[i];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m, 64);
-      const int oe = __shfl_xor(be, m, 64);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == r) {
-      my_v = bv;
-      my_e = be;
-    }
-  }
-  const float mx = __shfl(my_v, 0, 64);
-  const float ex = lane < k ? expf(my_v - mx) : 0.0f;
+  uint32_t my_key;
+  int my_e;
+  wave_select_topk<EPL>(key, E, k, my_key, my_e);
+  const float mx = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
+  const float ex = lane < k ? expf(key_value(my_key) - mx) : 0.0f;
   const float sum = wave_sum(ex);
   if (lane < k) {
     idx[(size_t)t * k + lane] = my_e;
