@@ -54,6 +54,17 @@
  *     gscale fp32  [count]
  *   experts.gate, experts.up: N = inter, K = latent;  experts.down: N = latent,
  *   K = inter. The shared expert uses the same layout with count 1.
+ *   packed fp4 set (moe_fp4_pack; N a multiple of 32, K of 64): the same
+ *     bytes reordered for the grouped path's loads. Block (e, t, s) covers
+ *     matrix e, rows [32t, 32t+32), columns [64s, 64s+64); blocks are stored
+ *     in (e, t, s) order, each as 64 lanes L of
+ *       codes  16 bytes: row 32t + r(L % 32), columns 64s + 32(L/32) .. +32
+ *              (plain byte order), at codes + 1024 * block + 16 L
+ *       scales  2 bytes: the two block scales of those 32 columns,
+ *              at scales + 128 * block + 2 L
+ *     where r(m) = 16 (q / 8) + 8 ((m / 4) % 2) + q % 8 with
+ *     q = 4 (m / 8) + m % 4 (a permutation of 0..31: it puts a matrix-core
+ *     lane's results on consecutive output columns). gscale is unchanged.
  *
  * Ownership: the caller allocates every buffer (device memory) and owns it.
  * Calls never allocate or free device memory and keep no pointer after they
@@ -76,7 +87,7 @@
 extern "C" {
 #endif
 
-#define MOE_LATENT_ABI_VERSION 1
+#define MOE_LATENT_ABI_VERSION 2
 
 #define MOE_LATENT_OK 0
 #define MOE_LATENT_EINVAL (-1)       /* null pointer, bad size, misaligned pointer, aliasing */
@@ -160,6 +171,15 @@ typedef struct moe_latent_opts {
    * before and just after stage s's kernels. Stages a path does not run
    * leave their events untouched. */
   void *const *stage_events;
+  /* NULL, or the routed experts (count n_experts) and the shared expert
+   * (count n_shared; NULL when n_shared = 0) in the packed layout, holding
+   * the same weights as `experts` and `shared`. The grouped path then loads
+   * the packed copies: one contiguous 1 KB of codes per wave and K step
+   * instead of 32 rows x 32 bytes; results are bit-identical. Needs latent
+   * and inter multiples of 64 (else MOE_LATENT_EUNSUPPORTED). The decode
+   * path reads the plain sets. */
+  const moe_fp4_experts *packed_experts;
+  const moe_fp4_experts *packed_shared;
 } moe_latent_opts;
 
 /* Device bytes of scratch one call needs for `T` tokens (the maximum over
@@ -196,6 +216,16 @@ const char *moe_latent_last_error(void);
 
 /* MOE_LATENT_ABI_VERSION of the library. */
 int moe_latent_version(void);
+
+/* Writes the packed layout (see "Layouts") of the fp4 matrix set `src`
+ * ([count][N][K] codes and scales; gscale is not read) to dst_codes
+ * (count*N*K/2 bytes) and dst_scales (count*N*K/16 bytes), device memory,
+ * 16-byte aligned, overlapping neither the source nor each other. Enqueued
+ * on `stream`; a one-time step when weights are loaded. Returns
+ * MOE_LATENT_EUNSUPPORTED unless N % 32 == 0 and K % 64 == 0, EINVAL for NULL,
+ * misaligned or overlapping buffers. count = 0 enqueues nothing. */
+int moe_fp4_pack(const moe_fp4_matrix *src, int32_t count, int32_t N, int32_t K,
+                 uint8_t *dst_codes, uint8_t *dst_scales, void *stream);
 
 #ifdef __cplusplus
 }

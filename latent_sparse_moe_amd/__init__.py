@@ -51,7 +51,9 @@ class CRouteDebug(ctypes.Structure):
 
 class COpts(ctypes.Structure):
     _fields_ = [("path", c_i32), ("residual", c_i32), ("norm_weight", c_vp), ("norm_eps", c_f32),
-                ("stage_events", ctypes.POINTER(c_vp))]
+                ("stage_events", ctypes.POINTER(c_vp)),
+                ("packed_experts", ctypes.POINTER(CFp4Experts)),
+                ("packed_shared", ctypes.POINTER(CFp4Experts))]
 
 
 STAGES = ("norm", "dproj", "router", "topk", "route", "gateup", "down", "combine", "uproj")
@@ -59,7 +61,7 @@ N_STAGES = len(STAGES)
 
 
 EXPORTS = ("moe_latent_forward", "moe_latent_forward_ex", "moe_latent_workspace_bytes",
-           "moe_latent_last_error", "moe_latent_version")
+           "moe_latent_last_error", "moe_latent_version", "moe_fp4_pack")
 
 _lib = None
 
@@ -86,6 +88,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_latent_last_error.restype = ctypes.c_char_p
     lib.moe_latent_version.argtypes = []
     lib.moe_latent_version.restype = ctypes.c_int
+    lib.moe_fp4_pack.argtypes = [P(CFp4Matrix), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
+    lib.moe_fp4_pack.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -139,6 +143,19 @@ class DeviceLayer:
     experts: DeviceExperts
     shared: Optional[DeviceExperts]
     norm_w: Optional[torch.Tensor] = None  # float32 [hidden]
+    # the experts again in the packed layout (moe_fp4_pack), read by the
+    # grouped path when present; see pack()
+    packed_experts: Optional[DeviceExperts] = None
+    packed_shared: Optional[DeviceExperts] = None
+
+    def pack(self, stream: Optional[torch.cuda.Stream] = None) -> "DeviceLayer":
+        """Adds packed copies of the routed and shared experts (same bytes,
+        reordered for the grouped kernels' loads). Needs latent and inter
+        multiples of 64."""
+        self.packed_experts = pack_experts(self.experts, self.dims, stream)
+        self.packed_shared = (pack_experts(self.shared, self.dims, stream)
+                              if self.shared is not None else None)
+        return self
 
     @staticmethod
     def from_host(h, device) -> "DeviceLayer":
@@ -163,6 +180,27 @@ class DeviceLayer:
                            bias=None if h.bias is None else f32(h.bias),
                            experts=bank(h.experts), shared=bank(h.shared),
                            norm_w=None if getattr(h, "norm_w", None) is None else f32(h.norm_w))
+
+
+def pack_fp4(m: DeviceFp4, N: int, K: int, stream: Optional[torch.cuda.Stream] = None) -> DeviceFp4:
+    """The packed copy of one fp4 matrix set [count][N][K] (moe_fp4_pack)."""
+    lib = load_library()
+    codes = torch.empty_like(m.codes)
+    scales = torch.empty_like(m.scales)
+    if stream is None:
+        stream = torch.cuda.current_stream(m.codes.device)
+    src = m.c()
+    rc = lib.moe_fp4_pack(ctypes.byref(src), m.codes.shape[0], N, K, codes.data_ptr(),
+                          scales.data_ptr(), stream.cuda_stream)
+    if rc != 0:
+        raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
+    return DeviceFp4(codes, scales, m.gscale)
+
+
+def pack_experts(b: DeviceExperts, dims, stream=None) -> DeviceExperts:
+    L, I = dims.latent, dims.inter
+    return DeviceExperts(pack_fp4(b.gate, I, L, stream), pack_fp4(b.up, I, L, stream),
+                         pack_fp4(b.down, L, I, stream))
 
 
 def workspace_bytes(dims, T: int) -> int:
@@ -226,8 +264,11 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
             i = STAGES.index(name)
             ev_arr[2 * i] = a.cuda_event
             ev_arr[2 * i + 1] = b.cuda_event
+    pex = layer.packed_experts.c() if layer.packed_experts is not None else None
+    psh = layer.packed_shared.c() if layer.packed_shared is not None else None
     opts = COpts(path, 1 if residual else 0, _ptr(layer.norm_w) if residual else None, norm_eps,
-                 ev_arr)
+                 ev_arr, ctypes.pointer(pex) if pex is not None else None,
+                 ctypes.pointer(psh) if psh is not None else None)
     dbg = debug.c() if debug is not None else None
     rc = lib.moe_latent_forward_ex(
         ctypes.byref(_dims(d)), T, x.data_ptr(), layer.D.data_ptr(), layer.U.data_ptr(),
@@ -241,5 +282,6 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
 
 
 __all__ = ["load_library", "DeviceLayer", "DeviceExperts", "DeviceFp4", "RouteDebug", "forward",
+           "pack_fp4", "pack_experts",
            "workspace_bytes", "alloc_workspace", "MoeLatentError", "EXPORTS",
            "PATH_AUTO", "PATH_GROUPED", "PATH_DECODE", "DECODE_MAX_T", "STAGES"]

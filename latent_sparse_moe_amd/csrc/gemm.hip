@@ -116,10 +116,17 @@ struct ALoader {
 
 // B operand in registers: expert weights in e2m1 codes + E4M3 block scales.
 // Lane (half h) of sub-tile j holds BK/2 codes and BK/32 scale bytes of its
-// weight row per step.
-template <int BK>
+// weight row per step. The weights are either in the plain row-major layout
+// (a lane's bytes of one step are 16 of its row's 32; a load instruction
+// touches 32 rows) or packed (PK, BK = 64 only; see launch_pack_fp4): the 64
+// lanes' bytes of one step are contiguous, 1 KB of codes and 128 bytes of
+// scales per load instruction. The values loaded are the same.
+template <int BK, bool PK>
 struct Fp4B {
-  static constexpr int kWords = BK / 16;  // 32-bit code words per lane per step
+  static_assert(!PK || BK == 64, "the packed layout has 64-wide K steps");
+  static constexpr int kWords = BK / 16;              // 32-bit code words per lane per step
+  static constexpr int kCodeStep = PK ? 1024 : BK / 2;  // bytes between a lane's steps
+  static constexpr int kScaleStep = PK ? 128 : BK / 16;
   struct Set {
     uint32_t c[2][kWords];
     uint32_t s[2];
@@ -127,30 +134,22 @@ struct Fp4B {
   const uint8_t* cp[2];
   const uint8_t* sp[2];
 
-  // rowfn(j, &codes_row, &scales_row): the lane's weight row of sub-tile j
-  template <class RowFn>
-  __device__ __forceinline__ void init(RowFn rowfn, int) {
-    const int h = (threadIdx.x & 63) >> 5;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint8_t* c;
-      const uint8_t* s;
-      rowfn(j, &c, &s);
-      cp[j] = c + h * (BK / 4);
-      sp[j] = s + h * (BK / 32);
-    }
+  // this lane's code and scale bytes of sub-tile j at step 0
+  __device__ __forceinline__ void set(int j, const uint8_t* c, const uint8_t* s) {
+    cp[j] = c;
+    sp[j] = s;
   }
   __device__ __forceinline__ void issue(int kt, Set& st) const {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (BK == 64) {
-        const uint4 v = *(const uint4*)(cp[j] + kt * (BK / 2));
+        const uint4 v = *(const uint4*)(cp[j] + kt * kCodeStep);
         st.c[j][0] = v.x; st.c[j][1] = v.y; st.c[j][2] = v.z; st.c[j][3] = v.w;
-        st.s[j] = *(const uint16_t*)(sp[j] + kt * (BK / 16));
+        st.s[j] = *(const uint16_t*)(sp[j] + kt * kScaleStep);
       } else {
-        const uint2 v = *(const uint2*)(cp[j] + kt * (BK / 2));
+        const uint2 v = *(const uint2*)(cp[j] + kt * kCodeStep);
         st.c[j][0] = v.x; st.c[j][1] = v.y;
-        st.s[j] = *(const uint8_t*)(sp[j] + kt * (BK / 16));
+        st.s[j] = *(const uint8_t*)(sp[j] + kt * kScaleStep);
       }
     }
   }
@@ -435,6 +434,60 @@ __device__ __forceinline__ const Fp4Set& pick_set(const ExpertsView& ex, int g, 
   return ex.shared;
 }
 
+// This lane's code and scale bytes at step 0 for the 32-row sub-tile that
+// starts at weight row nb of matrix le of the set m ([count][N][K]); the
+// lane's row is nb + weight_row(lane % 32). Sub-tiles past N read the last
+// one (their results are not stored).
+template <int BK, bool PK>
+__device__ __forceinline__ void fp4_lane_ptrs(const Fp4Mat& m, int le, int nb, int N, int K,
+                                              const uint8_t** c, const uint8_t** s) {
+  const int lane = threadIdx.x & 63;
+  if (PK) {
+    const int st = min(nb, N - 32) / 32;
+    const size_t blk = ((size_t)le * (N / 32) + st) * (K / 64);
+    *c = m.codes + blk * 1024 + lane * 16;
+    *s = m.scales + blk * 128 + lane * 2;
+  } else {
+    const size_t row = (size_t)le * N + min(nb + weight_row(lane & 31), N - 1);
+    const int h = lane >> 5;
+    *c = m.codes + row * (K / 2) + h * (BK / 4);
+    *s = m.scales + row * (K / 16) + h * (BK / 32);
+  }
+}
+
+// Packs an fp4 matrix set [count][N][K] (N % 32 == 0, K % 64 == 0) into the
+// order the grouped kernels load it in. Block (e, t, kt) = matrix e, rows
+// [32t, 32t + 32), columns [64kt, 64kt + 64), blocks in that nesting order.
+// Its codes are 64 lanes x 16 bytes: lane L holds the 32 codes of row
+// 32t + weight_row(L % 32), columns 64kt + 32(L / 32) .. +32, bytes in the
+// plain order. Its scales are 64 lanes x 2 bytes: the two block scales of
+// the same 32 columns. One thread moves one lane's 16 + 2 bytes.
+__global__ __launch_bounds__(256) void k_pack_fp4(const uint8_t* __restrict__ codes,
+                                                  const uint8_t* __restrict__ scales,
+                                                  int64_t n_lanes, int N, int K,
+                                                  uint8_t* __restrict__ pcodes,
+                                                  uint8_t* __restrict__ pscales) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_lanes) return;
+  const int L = (int)(i & 63);
+  const int64_t blk = i >> 6;               // (e * (N / 32) + t) * (K / 64) + kt
+  const int kt = (int)(blk % (K / 64));
+  const int64_t et = blk / (K / 64);        // e * (N / 32) + t
+  const int64_t row = et * 32 + weight_row(L & 31);  // e * N + 32 t + ...
+  const int h = L >> 5;
+  *(uint4*)(pcodes + i * 16) = *(const uint4*)(codes + row * (K / 2) + kt * 32 + h * 16);
+  *(uint16_t*)(pscales + i * 2) = *(const uint16_t*)(scales + row * (K / 16) + kt * 4 + h * 2);
+}
+
+hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int count, int N, int K,
+                           uint8_t* pcodes, uint8_t* pscales, hipStream_t stream) {
+  const int64_t n_lanes = (int64_t)count * (N / 32) * (K / 64) * 64;
+  if (n_lanes == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)((n_lanes + 255) / 256)), dim3(256), 0, stream,
+                     codes, scales, n_lanes, N, K, pcodes, pscales);
+  return hipGetLastError();
+}
+
 // Blocks of 32 rows holding the tile's rows (1..4). The last tile of an
 // expert's rows is usually partial; gate/up runs it with 1, 2 or 4 blocks
 // of matrix-core work (at the 16K-token routing this cuts the padded rows
@@ -449,13 +502,13 @@ __device__ __forceinline__ int row_blocks(const TileWork& tw) {
 // Gate/up: a tile covers 128 output columns of the SwiGLU width; wave w
 // takes columns n0 + 32w .. +32 as sub-tile 0 (gate rows) and sub-tile 1 (up
 // rows), so SiLU*mul pairs them in registers.
-template <int BK, int NI>
+template <int BK, bool PK, int NI>
 __device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, int ldh,
                                             const RouteView& rv, const ExpertsView& ex,
                                             uint16_t* __restrict__ act, int inter, int latent,
                                             const TileWork& tw, int n0, const Pipe& pipe) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = n0 + wave * 32 + weight_row(lane & 31);  // weight row this lane loads
+  const int nb = n0 + wave * 32;  // first weight row of this wave's sub-tiles
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   const int P = rv.pairs;
@@ -465,13 +518,13 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, i
     const int tok = row < P ? rv.perm[row] / rv.top_k : row - P;
     return hcat + (size_t)tok * ldh;
   });
-  Fp4B<BK> bl;
-  bl.init([&](int j, const uint8_t** c, const uint8_t** s) {
-    const Fp4Mat& m = j ? set.up : set.gate;
-    const size_t row = (size_t)le * inter + min(n, inter - 1);
-    *c = m.codes + row * (latent / 2);
-    *s = m.scales + row * (latent / 16);
-  }, 0);
+  Fp4B<BK, PK> bl;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint8_t *c, *s;
+    fp4_lane_ptrs<BK, PK>(j ? set.up : set.gate, le, nb, inter, latent, &c, &s);
+    bl.set(j, c, s);
+  }
   f32x16 acc[NI][2];
   zero_acc<NI>(acc);
   mainloop<BK, NI>(al, bl, latent / BK, pipe, acc);
@@ -498,7 +551,7 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, i
   }
 }
 
-template <int BK>
+template <int BK, bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_gateup(
     const uint16_t* __restrict__ hcat, int ldh, RouteView rv, ExpertsView ex,
     uint16_t* __restrict__ act, int inter, int latent) {
@@ -509,28 +562,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (!tile_work(rv, tile / nt, &tw)) return;
   const int n0 = (tile % nt) * (kBN / 2);
   const int nb = row_blocks(tw);
-  if (nb == 1) gateup_tile<BK, 1>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
-  else if (nb == 2) gateup_tile<BK, 2>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
-  else gateup_tile<BK, 4>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
+  if (nb == 1) gateup_tile<BK, PK, 1>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
+  else if (nb == 2) gateup_tile<BK, PK, 2>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
+  else gateup_tile<BK, PK, 4>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
 }
 
-template <int BK, int NI>
+template <int BK, bool PK, int NI>
 __device__ __forceinline__ void down_tile(const uint16_t* __restrict__ act, const RouteView& rv,
                                           const ExpertsView& ex, uint16_t* __restrict__ y,
                                           int inter, int latent, const TileWork& tw, int n0,
                                           const Pipe& pipe) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ncol = n0 + wave * 64 + weight_row(lane & 31);  // weight row this lane loads
+  const int nb = n0 + wave * 64;  // first weight row of this wave's sub-tiles
   int le;
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   ALoader<BK> al;
   al.init([&](int r) { return act + (size_t)min(tw.rbeg + r, tw.rend - 1) * inter; });
-  Fp4B<BK> bl;
-  bl.init([&](int j, const uint8_t** c, const uint8_t** s) {
-    const size_t row = (size_t)le * latent + min(ncol + j * 32, latent - 1);
-    *c = set.down.codes + row * (inter / 2);
-    *s = set.down.scales + row * (inter / 16);
-  }, 0);
+  Fp4B<BK, PK> bl;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint8_t *c, *s;
+    fp4_lane_ptrs<BK, PK>(set.down, le, nb + j * 32, latent, inter, &c, &s);
+    bl.set(j, c, s);
+  }
   f32x16 acc[NI][2];
   zero_acc<NI>(acc);
   mainloop<BK, NI>(al, bl, inter / BK, pipe, acc);
@@ -552,7 +606,7 @@ __device__ __forceinline__ void down_tile(const uint16_t* __restrict__ act, cons
   }
 }
 
-template <int BK>
+template <int BK, bool PK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_down(
     const uint16_t* __restrict__ act, RouteView rv, ExpertsView ex, uint16_t* __restrict__ y,
     int inter, int latent) {
@@ -562,7 +616,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   TileWork tw;
   if (!tile_work(rv, tile / nt, &tw)) return;
   const int n0 = (tile % nt) * kBN;
-  down_tile<BK, 4>(act, rv, ex, y, inter, latent, tw, n0, pipe);
+  down_tile<BK, PK, 4>(act, rv, ex, y, inter, latent, tw, n0, pipe);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -594,12 +648,16 @@ hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& 
                                 const ExpertsView& ex, uint16_t* act, int inter, int latent,
                                 int max_mtiles, hipStream_t stream) {
   dim3 grid(max_mtiles * ((inter + kBN / 2 - 1) / (kBN / 2))), block(kThreads);
-  if (latent % 64 == 0)
-    hipLaunchKernelGGL(k_expert_gateup<64>, grid, block, 0, stream, hcat, ldh, rv, ex, act, inter,
-                       latent);
+  if (ex.packed && latent % 64 != 0) return hipErrorInvalidValue;
+  if (ex.packed)
+    hipLaunchKernelGGL((k_expert_gateup<64, true>), grid, block, 0, stream, hcat, ldh, rv, ex, act,
+                       inter, latent);
+  else if (latent % 64 == 0)
+    hipLaunchKernelGGL((k_expert_gateup<64, false>), grid, block, 0, stream, hcat, ldh, rv, ex,
+                       act, inter, latent);
   else
-    hipLaunchKernelGGL(k_expert_gateup<32>, grid, block, 0, stream, hcat, ldh, rv, ex, act, inter,
-                       latent);
+    hipLaunchKernelGGL((k_expert_gateup<32, false>), grid, block, 0, stream, hcat, ldh, rv, ex,
+                       act, inter, latent);
   return hipGetLastError();
 }
 
@@ -607,10 +665,16 @@ hipError_t launch_expert_down(const uint16_t* act, const RouteView& rv, const Ex
                               uint16_t* y, int inter, int latent, int max_mtiles,
                               hipStream_t stream) {
   dim3 grid(max_mtiles * ((latent + kBN - 1) / kBN)), block(kThreads);
-  if (inter % 64 == 0)
-    hipLaunchKernelGGL(k_expert_down<64>, grid, block, 0, stream, act, rv, ex, y, inter, latent);
+  if (ex.packed && inter % 64 != 0) return hipErrorInvalidValue;
+  if (ex.packed)
+    hipLaunchKernelGGL((k_expert_down<64, true>), grid, block, 0, stream, act, rv, ex, y, inter,
+                       latent);
+  else if (inter % 64 == 0)
+    hipLaunchKernelGGL((k_expert_down<64, false>), grid, block, 0, stream, act, rv, ex, y, inter,
+                       latent);
   else
-    hipLaunchKernelGGL(k_expert_down<32>, grid, block, 0, stream, act, rv, ex, y, inter, latent);
+    hipLaunchKernelGGL((k_expert_down<32, false>), grid, block, 0, stream, act, rv, ex, y, inter,
+                       latent);
   return hipGetLastError();
 }
 

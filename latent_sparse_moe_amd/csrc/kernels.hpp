@@ -19,10 +19,12 @@ struct Fp4Set {
 };
 
 // Routed experts and the shared expert. Grouped kernels number the groups
-// 0..n_experts-1 (routed) and n_experts (shared, when present).
+// 0..n_experts-1 (routed) and n_experts (shared, when present). packed: both
+// sets are in the layout written by launch_pack_fp4 (K multiples of 64).
 struct ExpertsView {
   Fp4Set routed;
   Fp4Set shared;
+  bool packed;
 };
 
 // Routing as the grouped GEMMs consume it. Rows of the permuted activation
@@ -58,6 +60,11 @@ hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& 
 hipError_t launch_expert_down(const uint16_t* act, const RouteView& rv, const ExpertsView& ex,
                               uint16_t* y, int inter, int latent, int max_mtiles,
                               hipStream_t stream);
+// fp4 matrix set [count][N][K] (N % 32 == 0, K % 64 == 0) -> the packed
+// layout the grouped kernels load with one 1 KB (codes) and one 128-byte
+// (scales) access per wave and K step; same byte counts as the plain layout.
+hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int count, int N, int K,
+                           uint8_t* pcodes, uint8_t* pscales, hipStream_t stream);
 
 // Routing bookkeeping (route.hip).
 constexpr int kRouteChunk = 4096;  // pairs per histogram / permute chunk

@@ -212,8 +212,9 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   // S7-S9: grouped expert GEMMs (routed groups, then the shared expert).
   moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k};
   moe::ExpertsView ex{};
-  ex.routed = to_set(experts);
-  if (d.n_shared) ex.shared = to_set(shared);
+  ex.packed = o.packed_experts != nullptr;
+  ex.routed = to_set(ex.packed ? o.packed_experts : experts);
+  if (d.n_shared) ex.shared = to_set(ex.packed ? o.packed_shared : shared);
   const int max_mtiles = (P + 127) / 128 + (E < P ? E : P) + d.n_shared * ((T + 127) / 128);
   HIP_TRY(sm.mark(moe::kStageGateup, 0));
   HIP_TRY(moe::launch_expert_gateup(hcat, 2 * Lat, rv, ex, act, I, Lat, max_mtiles, st));
@@ -308,6 +309,30 @@ extern "C" {
 
 int moe_latent_version(void) { return MOE_LATENT_ABI_VERSION; }
 
+int moe_fp4_pack(const moe_fp4_matrix* src, int32_t count, int32_t N, int32_t K,
+                 uint8_t* dst_codes, uint8_t* dst_scales, void* stream) {
+  g_err.clear();
+  if (!src || !src->codes || !src->scales || !dst_codes || !dst_scales)
+    return fail(MOE_LATENT_EINVAL, "src, its codes and scales, and the destinations must be non-NULL");
+  if (count < 0 || N <= 0 || K <= 0)
+    return fail(MOE_LATENT_EINVAL, "count must be >= 0 and N, K positive (%d, %d, %d)", count, N, K);
+  if (N % 32 || K % 64)
+    return fail(MOE_LATENT_EUNSUPPORTED, "packing needs N a multiple of 32 and K of 64 (%d, %d)", N,
+                K);
+  if (!aligned(src->codes, 16) || !aligned(src->scales, 16) || !aligned(dst_codes, 16) ||
+      !aligned(dst_scales, 16))
+    return fail(MOE_LATENT_EINVAL, "codes and scales must be 16-byte aligned");
+  const size_t nc = (size_t)count * N * (K / 2), ns = (size_t)count * N * (K / 16);
+  if (overlaps(dst_codes, nc, src->codes, nc) || overlaps(dst_codes, nc, src->scales, ns) ||
+      overlaps(dst_scales, ns, src->codes, nc) || overlaps(dst_scales, ns, src->scales, ns) ||
+      overlaps(dst_codes, nc, dst_scales, ns))
+    return fail(MOE_LATENT_EINVAL, "packed buffers overlap the source or each other");
+  if (count == 0) return 0;
+  HIP_TRY(moe::launch_pack_fp4(src->codes, src->scales, count, N, K, dst_codes, dst_scales,
+                               (hipStream_t)stream));
+  return 0;
+}
+
 const char* moe_latent_last_error(void) { return g_err.c_str(); }
 
 size_t moe_latent_workspace_bytes(const moe_latent_dims* dims, int64_t T) {
@@ -344,6 +369,16 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
     return fail(MOE_LATENT_EINVAL, "router->w must be 16-byte aligned");
   if ((rc = check_set(experts, "experts", d.n_experts))) return rc;
   if (d.n_shared && (rc = check_set(shared, "shared", d.n_shared))) return rc;
+  if (o.packed_experts || o.packed_shared) {
+    if (!o.packed_experts || (d.n_shared && !o.packed_shared))
+      return fail(MOE_LATENT_EINVAL, "packed_experts and (with a shared expert) packed_shared "
+                                     "come together");
+    if (d.latent % 64 || d.inter % 64)
+      return fail(MOE_LATENT_EUNSUPPORTED, "packed experts need latent and inter multiples of 64 "
+                                           "(%d, %d)", d.latent, d.inter);
+    if ((rc = check_set(o.packed_experts, "packed_experts", d.n_experts))) return rc;
+    if (d.n_shared && (rc = check_set(o.packed_shared, "packed_shared", d.n_shared))) return rc;
+  }
   if (o.residual) {
     if (!o.norm_weight) return fail(MOE_LATENT_EINVAL, "residual block needs norm_weight");
     if (!(o.norm_eps >= 0.0f)) return fail(MOE_LATENT_EINVAL, "norm_eps must be >= 0");

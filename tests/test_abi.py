@@ -20,7 +20,7 @@ def declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        for m in re.finditer(r"\b(moe_latent_\w+)\s*\(", text):
+        for m in re.finditer(r"\b(moe_\w+)\s*\(", text):
             names.add(m.group(1))
     return sorted(names)
 
@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert lib.moe_latent_version() == 1
+    assert lib.moe_latent_version() == 2
 
 
 def _dims(**kw):
@@ -130,3 +130,46 @@ def test_binding_fails_loudly_without_library(tmp_path):
             lsm.load_library(str(tmp_path / "missing.so"))
     finally:
         lsm._lib = saved
+
+
+def _packed_opts(n_shared=1):
+    m = lsm.CFp4Matrix(11 * A, 12 * A, 10 * A)
+    pex = lsm.CFp4Experts(m, m, m, 512)
+    psh = lsm.CFp4Experts(m, m, m, 1)
+    o = lsm.COpts(lsm.PATH_GROUPED, 0, None, 0.0, None, ctypes.pointer(pex),
+                  ctypes.pointer(psh) if n_shared else None)
+    return o, (pex, psh)
+
+
+def test_packed_opts_validation(lib):
+    o, keep = _packed_opts(n_shared=0)
+    rc, msg = _call(lib, _dims(), opts=o)             # the shared expert's packed copy is missing
+    assert rc == lsm.EINVAL and "packed" in msg
+    o, keep = _packed_opts()
+    rc, msg = _call(lib, _dims(latent=1760), opts=o)  # latent % 64 != 0
+    assert rc == lsm.EUNSUPPORTED and "64" in msg
+    rc, msg = _call(lib, _dims(inter=608), opts=o)    # inter % 64 != 0
+    assert rc == lsm.EUNSUPPORTED
+    bad = lsm.CFp4Experts(lsm.CFp4Matrix(11 * A + 8, 12 * A, 10 * A), keep[0].up, keep[0].down, 512)
+    o2 = lsm.COpts(lsm.PATH_GROUPED, 0, None, 0.0, None, ctypes.pointer(bad), ctypes.pointer(keep[1]))
+    assert _call(lib, _dims(), opts=o2)[0] == lsm.EINVAL  # misaligned packed codes
+    assert _call(lib, _dims(), T=0, opts=o)[0] == 0
+
+
+def _pack(lib, src=True, count=4, N=64, K=128, dc=20 * A, ds=21 * A, codes=8 * A, scales=9 * A):
+    m = lsm.CFp4Matrix(codes, scales, 10 * A)
+    rc = lib.moe_fp4_pack(ctypes.byref(m) if src else None, count, N, K, dc, ds, None)
+    return rc, lib.moe_latent_last_error().decode()
+
+
+def test_pack_validation(lib):
+    assert _pack(lib, src=False)[0] == lsm.EINVAL
+    assert _pack(lib, dc=0)[0] == lsm.EINVAL
+    assert _pack(lib, N=48)[0] == lsm.EUNSUPPORTED         # N % 32
+    assert _pack(lib, K=96)[0] == lsm.EUNSUPPORTED         # K % 64
+    assert _pack(lib, K=0)[0] == lsm.EINVAL
+    assert _pack(lib, count=-1)[0] == lsm.EINVAL
+    assert _pack(lib, dc=20 * A + 4)[0] == lsm.EINVAL      # misaligned
+    assert _pack(lib, dc=8 * A)[0] == lsm.EINVAL           # packed codes over the source codes
+    assert _pack(lib, ds=20 * A + 64)[0] == lsm.EINVAL     # packed scales inside packed codes
+    assert _pack(lib, count=0) == (0, "")                  # nothing to do
