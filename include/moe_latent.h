@@ -65,6 +65,11 @@
  *     where r(m) = 16 (q / 8) + 8 ((m / 4) % 2) + q % 8 with
  *     q = 4 (m / 8) + m % 4 (a permutation of 0..31: it puts a matrix-core
  *     lane's results on consecutive output columns). gscale is unchanged.
+ *   packed bf16 matrix [N][K] (moe_bf16_pack; N a multiple of 32, K of 64):
+ *     block (t, s) covers rows [32t, 32t+32), columns [64s, 64s+64); blocks
+ *     in (t, s) order, 4096 bytes each: the 16 bytes at 1024 q + 16 L of a
+ *     block (q = 0..3, L = 0..63) are row 32t + r(L % 32), columns
+ *     64s + 32(L/32) + 8q .. +8.
  *
  * Ownership: the caller allocates every buffer (device memory) and owns it.
  * Calls never allocate or free device memory and keep no pointer after they
@@ -180,6 +185,14 @@ typedef struct moe_latent_opts {
    * path reads the plain sets. */
   const moe_fp4_experts *packed_experts;
   const moe_fp4_experts *packed_shared;
+  /* NULL, or D, U, router.w in the packed bf16 layout (moe_bf16_pack), each
+   * on its own: the grouped path's D, U and router GEMMs then load them with
+   * one contiguous 1 KB per wave and load; results are bit-identical.
+   * packed_D needs hidden % 64 == 0, packed_U and packed_R latent % 64 == 0,
+   * packed_R n_experts % 32 == 0 (else MOE_LATENT_EUNSUPPORTED). */
+  const void *packed_D;
+  const void *packed_U;
+  const void *packed_R;
 } moe_latent_opts;
 
 /* Device bytes of scratch one call needs for `T` tokens (the maximum over
@@ -226,6 +239,13 @@ int moe_latent_version(void);
  * misaligned or overlapping buffers. count = 0 enqueues nothing. */
 int moe_fp4_pack(const moe_fp4_matrix *src, int32_t count, int32_t N, int32_t K,
                  uint8_t *dst_codes, uint8_t *dst_scales, void *stream);
+
+/* Writes the packed bf16 layout (see "Layouts") of the matrix `src`
+ * (bf16 [N][K]) to `dst` (N*K*2 bytes), device memory, 16-byte aligned,
+ * not overlapping src. Enqueued on `stream`. MOE_LATENT_EUNSUPPORTED unless
+ * N % 32 == 0 and K % 64 == 0; EINVAL for NULL, misaligned or overlapping
+ * buffers. */
+int moe_bf16_pack(const void *src, int32_t N, int32_t K, void *dst, void *stream);
 
 #ifdef __cplusplus
 }

@@ -53,7 +53,8 @@ class COpts(ctypes.Structure):
     _fields_ = [("path", c_i32), ("residual", c_i32), ("norm_weight", c_vp), ("norm_eps", c_f32),
                 ("stage_events", ctypes.POINTER(c_vp)),
                 ("packed_experts", ctypes.POINTER(CFp4Experts)),
-                ("packed_shared", ctypes.POINTER(CFp4Experts))]
+                ("packed_shared", ctypes.POINTER(CFp4Experts)),
+                ("packed_D", c_vp), ("packed_U", c_vp), ("packed_R", c_vp)]
 
 
 STAGES = ("norm", "dproj", "router", "topk", "route", "gateup", "down", "combine", "uproj")
@@ -61,7 +62,7 @@ N_STAGES = len(STAGES)
 
 
 EXPORTS = ("moe_latent_forward", "moe_latent_forward_ex", "moe_latent_workspace_bytes",
-           "moe_latent_last_error", "moe_latent_version", "moe_fp4_pack")
+           "moe_latent_last_error", "moe_latent_version", "moe_fp4_pack", "moe_bf16_pack")
 
 _lib = None
 
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_latent_version.restype = ctypes.c_int
     lib.moe_fp4_pack.argtypes = [P(CFp4Matrix), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
     lib.moe_fp4_pack.restype = ctypes.c_int
+    lib.moe_bf16_pack.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp]
+    lib.moe_bf16_pack.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -147,14 +150,27 @@ class DeviceLayer:
     # grouped path when present; see pack()
     packed_experts: Optional[DeviceExperts] = None
     packed_shared: Optional[DeviceExperts] = None
+    packed_D: Optional[torch.Tensor] = None
+    packed_U: Optional[torch.Tensor] = None
+    packed_R: Optional[torch.Tensor] = None
 
     def pack(self, stream: Optional[torch.cuda.Stream] = None) -> "DeviceLayer":
-        """Adds packed copies of the routed and shared experts (same bytes,
-        reordered for the grouped kernels' loads). Needs latent and inter
-        multiples of 64."""
-        self.packed_experts = pack_experts(self.experts, self.dims, stream)
-        self.packed_shared = (pack_experts(self.shared, self.dims, stream)
-                              if self.shared is not None else None)
+        """Adds packed copies of the weights the grouped path loads (same
+        bytes, reordered for its loads): the experts (latent and inter
+        multiples of 64), D (hidden % 64 == 0), U, and the router rows
+        (n_experts % 32 == 0); a matrix whose dims do not allow it is left
+        plain."""
+        d = self.dims
+        if d.latent % 64 == 0 and d.inter % 64 == 0:
+            self.packed_experts = pack_experts(self.experts, d, stream)
+            self.packed_shared = (pack_experts(self.shared, d, stream)
+                                  if self.shared is not None else None)
+        if d.hidden % 64 == 0:
+            self.packed_D = pack_bf16(self.D, stream)
+        if d.latent % 64 == 0:
+            self.packed_U = pack_bf16(self.U, stream)
+            if d.n_experts % 32 == 0:
+                self.packed_R = pack_bf16(self.R, stream)
         return self
 
     @staticmethod
@@ -195,6 +211,18 @@ def pack_fp4(m: DeviceFp4, N: int, K: int, stream: Optional[torch.cuda.Stream] =
     if rc != 0:
         raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
     return DeviceFp4(codes, scales, m.gscale)
+
+
+def pack_bf16(w: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The packed copy of a bf16 matrix [N][K] (moe_bf16_pack)."""
+    lib = load_library()
+    out = torch.empty_like(w)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device)
+    rc = lib.moe_bf16_pack(w.data_ptr(), w.shape[0], w.shape[1], out.data_ptr(), stream.cuda_stream)
+    if rc != 0:
+        raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
+    return out
 
 
 def pack_experts(b: DeviceExperts, dims, stream=None) -> DeviceExperts:
@@ -268,7 +296,8 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
     psh = layer.packed_shared.c() if layer.packed_shared is not None else None
     opts = COpts(path, 1 if residual else 0, _ptr(layer.norm_w) if residual else None, norm_eps,
                  ev_arr, ctypes.pointer(pex) if pex is not None else None,
-                 ctypes.pointer(psh) if psh is not None else None)
+                 ctypes.pointer(psh) if psh is not None else None,
+                 _ptr(layer.packed_D), _ptr(layer.packed_U), _ptr(layer.packed_R))
     dbg = debug.c() if debug is not None else None
     rc = lib.moe_latent_forward_ex(
         ctypes.byref(_dims(d)), T, x.data_ptr(), layer.D.data_ptr(), layer.U.data_ptr(),
@@ -282,6 +311,6 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
 
 
 __all__ = ["load_library", "DeviceLayer", "DeviceExperts", "DeviceFp4", "RouteDebug", "forward",
-           "pack_fp4", "pack_experts",
+           "pack_fp4", "pack_experts", "pack_bf16",
            "workspace_bytes", "alloc_workspace", "MoeLatentError", "EXPORTS",
            "PATH_AUTO", "PATH_GROUPED", "PATH_DECODE", "DECODE_MAX_T", "STAGES"]

@@ -162,9 +162,12 @@ struct Fp4B {
 
 // B operand in registers: bf16 weights (dense GEMMs). Column index wraps
 // modulo kwrap (a multiple of BK), so one physical matrix can stand for two
-// copies concatenated along K.
-template <int BK>
+// copies concatenated along K. Plain row-major weights (a load instruction
+// touches 32 rows) or packed (PK, BK = 64 only; see launch_pack_bf16: the
+// 64 lanes' 16 bytes of one load are contiguous). The values are the same.
+template <int BK, bool PK>
 struct Bf16B {
+  static_assert(!PK || BK == 64, "the packed layout has 64-wide K steps");
   static constexpr int kSub = Geo<BK>::kSub;
   struct Set {
     uint4 c[2][kSub];
@@ -172,21 +175,17 @@ struct Bf16B {
   const uint16_t* p[2];
   int kwrap;
 
-  // rowfn(j): the lane's weight row of sub-tile j (K = 0 element)
-  template <class RowFn>
-  __device__ __forceinline__ void init(RowFn rowfn, int kwrap_) {
-    kwrap = kwrap_;
-    const int h = (threadIdx.x & 63) >> 5;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) p[j] = rowfn(j) + h * (BK / 2);
-  }
+  // this lane's first element of sub-tile j (K = 0)
+  __device__ __forceinline__ void set(int j, const uint16_t* q) { p[j] = q; }
   __device__ __forceinline__ void issue(int kt, Set& st) const {
     int kc = kt * BK;
     if (kc >= kwrap) kc -= kwrap;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int ks = 0; ks < kSub; ++ks) st.c[j][ks] = *(const uint4*)(p[j] + kc + ks * 8);
+      for (int ks = 0; ks < kSub; ++ks)
+        st.c[j][ks] = PK ? *(const uint4*)(p[j] + kc * 32 + ks * 512)
+                         : *(const uint4*)(p[j] + kc + ks * 8);
   }
   __device__ __forceinline__ bf16x8 frag(const Set& st, int j, int ks) const {
     return __builtin_bit_cast(bf16x8, st.c[j][ks]);
@@ -306,7 +305,7 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
 
 // ------------------------------------------------------------------ dense
 
-template <int BK, int EPI>
+template <int BK, int EPI, bool PK>
 __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restrict__ A, int lda,
                                                          const uint16_t* __restrict__ B, int ldb,
                                                          int kwrap, int M, int N, int K,
@@ -316,11 +315,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int m0 = (tile / nt) * kBM, n0 = (tile % nt) * kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ncol = n0 + wave * 64 + weight_row(lane & 31);  // weight row this lane loads (sub-tile 0)
   ALoader<BK> al;
   al.init([&](int r) { return A + (size_t)min(m0 + r, M - 1) * lda; });
-  Bf16B<BK> bl;
-  bl.init([&](int j) { return B + (size_t)min(ncol + j * 32, N - 1) * ldb; }, kwrap);
+  Bf16B<BK, PK> bl;
+  bl.kwrap = kwrap;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int nb = n0 + wave * 64 + j * 32;  // first weight row of sub-tile j
+    if (PK) {  // block (t, 0) of sub-tile t; N % 32 == 0
+      const int t = min(nb, N - 32) / 32;
+      bl.set(j, B + (size_t)t * 32 * kwrap + lane * 8);
+    } else {   // the lane's row (rows past N read the last one; never stored)
+      bl.set(j, B + (size_t)min(nb + weight_row(lane & 31), N - 1) * ldb + (lane >> 5) * (BK / 2));
+    }
+  }
   f32x16 acc[4][2];
   zero_acc<4>(acc);
   mainloop<BK, 4>(al, bl, K / BK, pipe, acc);
@@ -479,6 +487,31 @@ __global__ __launch_bounds__(256) void k_pack_fp4(const uint8_t* __restrict__ co
   *(uint16_t*)(pscales + i * 2) = *(const uint16_t*)(scales + row * (K / 16) + kt * 4 + h * 2);
 }
 
+// Packs a bf16 matrix [N][K] (N % 32 == 0, K % 64 == 0) into the order the
+// dense kernels load it in. Block (t, s) = rows [32t, 32t + 32), columns
+// [64s, 64s + 64), blocks in that nesting order, 4 KB each: load ks (0..3)
+// of lane L is 16 bytes at 1024 ks + 16 L: row 32t + weight_row(L % 32),
+// columns 64s + 32(L / 32) + 8ks .. +8. One thread moves 16 bytes.
+__global__ __launch_bounds__(256) void k_pack_bf16(const uint16_t* __restrict__ w, int64_t n_chunks,
+                                                   int K, uint16_t* __restrict__ pw) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_chunks) return;
+  const int L = (int)(i & 63), ks = (int)((i >> 6) & 3);
+  const int64_t blk = i >> 8;  // t * (K / 64) + s
+  const int s = (int)(blk % (K / 64));
+  const int64_t t = blk / (K / 64);
+  const int64_t row = t * 32 + weight_row(L & 31);
+  *(uint4*)(pw + i * 8) = *(const uint4*)(w + row * K + s * 64 + (L >> 5) * 32 + ks * 8);
+}
+
+hipError_t launch_pack_bf16(const uint16_t* w, int N, int K, uint16_t* pw, hipStream_t stream) {
+  const int64_t n_chunks = (int64_t)N * K / 8;
+  if (n_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_bf16, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, stream,
+                     w, n_chunks, K, pw);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int count, int N, int K,
                            uint8_t* pcodes, uint8_t* pscales, hipStream_t stream) {
   const int64_t n_lanes = (int64_t)count * (N / 32) * (K / 64) * 64;
@@ -625,20 +658,25 @@ static inline int pick_bk(int K, int kwrap) { return (K % 64 == 0 && kwrap % 64 
 
 hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t* B, int ldb,
                              int kwrap, int M, int N, int K, const DenseEpilogue& ep,
-                             hipStream_t stream) {
+                             hipStream_t stream, bool packed) {
   dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), block(kThreads);
   const int bk = pick_bk(K, kwrap);
-#define MOE_LAUNCH_DENSE(BKV, EPIV)                                                           \
-  hipLaunchKernelGGL((k_gemm_dense<BKV, EPIV>), grid, block, 0, stream, A, lda, B, ldb, kwrap, \
-                     M, N, K, ep)
-  if (bk == 64) {
-    if (epi == kEpiSplit) MOE_LAUNCH_DENSE(64, kEpiSplit);
-    else if (epi == kEpiLogits) MOE_LAUNCH_DENSE(64, kEpiLogits);
-    else MOE_LAUNCH_DENSE(64, kEpiOut);
+  if (packed && (bk != 64 || N % 32)) return hipErrorInvalidValue;
+#define MOE_LAUNCH_DENSE(BKV, EPIV, PKV)                                                      \
+  hipLaunchKernelGGL((k_gemm_dense<BKV, EPIV, PKV>), grid, block, 0, stream, A, lda, B, ldb,  \
+                     kwrap, M, N, K, ep)
+  if (packed) {
+    if (epi == kEpiSplit) MOE_LAUNCH_DENSE(64, kEpiSplit, true);
+    else if (epi == kEpiLogits) MOE_LAUNCH_DENSE(64, kEpiLogits, true);
+    else MOE_LAUNCH_DENSE(64, kEpiOut, true);
+  } else if (bk == 64) {
+    if (epi == kEpiSplit) MOE_LAUNCH_DENSE(64, kEpiSplit, false);
+    else if (epi == kEpiLogits) MOE_LAUNCH_DENSE(64, kEpiLogits, false);
+    else MOE_LAUNCH_DENSE(64, kEpiOut, false);
   } else {
-    if (epi == kEpiSplit) MOE_LAUNCH_DENSE(32, kEpiSplit);
-    else if (epi == kEpiLogits) MOE_LAUNCH_DENSE(32, kEpiLogits);
-    else MOE_LAUNCH_DENSE(32, kEpiOut);
+    if (epi == kEpiSplit) MOE_LAUNCH_DENSE(32, kEpiSplit, false);
+    else if (epi == kEpiLogits) MOE_LAUNCH_DENSE(32, kEpiLogits, false);
+    else MOE_LAUNCH_DENSE(32, kEpiOut, false);
   }
 #undef MOE_LAUNCH_DENSE
   return hipGetLastError();

@@ -51,9 +51,11 @@ struct DenseEpilogue {
   int ldr;
 };
 
+// packed: B is in the layout written by launch_pack_bf16 ([N][kwrap] packed;
+// N % 32 == 0, K and kwrap multiples of 64).
 hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t* B, int ldb,
                              int kwrap, int M, int N, int K, const DenseEpilogue& ep,
-                             hipStream_t stream);
+                             hipStream_t stream, bool packed = false);
 hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& rv,
                                 const ExpertsView& ex, uint16_t* act, int inter, int latent,
                                 int max_mtiles, hipStream_t stream);
@@ -65,6 +67,9 @@ hipError_t launch_expert_down(const uint16_t* act, const RouteView& rv, const Ex
 // (scales) access per wave and K step; same byte counts as the plain layout.
 hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int count, int N, int K,
                            uint8_t* pcodes, uint8_t* pscales, hipStream_t stream);
+// bf16 matrix [N][K] (N % 32 == 0, K % 64 == 0) -> the packed layout the
+// dense kernels load with one contiguous 1 KB access per wave.
+hipError_t launch_pack_bf16(const uint16_t* w, int N, int K, uint16_t* pw, hipStream_t stream);
 
 // Routing bookkeeping (route.hip).
 constexpr int kRouteChunk = 4096;  // pairs per histogram / permute chunk

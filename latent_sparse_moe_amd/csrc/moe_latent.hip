@@ -188,7 +188,8 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   ep.ldo = 2 * Lat;
   ep.lo_off = Lat;
   HIP_TRY(sm.mark(moe::kStageDproj, 0));
-  HIP_TRY(moe::launch_gemm_dense(moe::kEpiSplit, a_in, H, D, H, H, T, Lat, H, ep, st));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiSplit, a_in, H, o.packed_D ? (const uint16_t*)o.packed_D : D,
+                                 H, H, T, Lat, H, ep, st, o.packed_D != nullptr));
   HIP_TRY(sm.mark(moe::kStageDproj, 1));
   // S2: logits = (hi + lo) R^T + b, as a GEMM over K = 2*latent with R read twice.
   ep = moe::DenseEpilogue{};
@@ -196,8 +197,9 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   ep.ldo = E;
   ep.bias = router->bias;
   HIP_TRY(sm.mark(moe::kStageRouter, 0));
-  HIP_TRY(moe::launch_gemm_dense(moe::kEpiLogits, hcat, 2 * Lat, router->w, Lat, Lat, T, E,
-                                 2 * Lat, ep, st));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiLogits, hcat, 2 * Lat,
+                                 o.packed_R ? (const uint16_t*)o.packed_R : router->w, Lat, Lat, T,
+                                 E, 2 * Lat, ep, st, o.packed_R != nullptr));
   HIP_TRY(sm.mark(moe::kStageRouter, 1));
   // S3: top-k + renormalised softmax weights.
   HIP_TRY(sm.mark(moe::kStageTopk, 0));
@@ -235,7 +237,8 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
     ep.ldr = H;
   }
   HIP_TRY(sm.mark(moe::kStageUproj, 0));
-  HIP_TRY(moe::launch_gemm_dense(moe::kEpiOut, z, Lat, U, Lat, Lat, T, H, Lat, ep, st));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiOut, z, Lat, o.packed_U ? (const uint16_t*)o.packed_U : U,
+                                 Lat, Lat, T, H, Lat, ep, st, o.packed_U != nullptr));
   HIP_TRY(sm.mark(moe::kStageUproj, 1));
 
   if (dbg) {
@@ -309,6 +312,21 @@ extern "C" {
 
 int moe_latent_version(void) { return MOE_LATENT_ABI_VERSION; }
 
+int moe_bf16_pack(const void* src, int32_t N, int32_t K, void* dst, void* stream) {
+  g_err.clear();
+  if (!src || !dst) return fail(MOE_LATENT_EINVAL, "src and dst must be non-NULL");
+  if (N <= 0 || K <= 0) return fail(MOE_LATENT_EINVAL, "N and K must be positive (%d, %d)", N, K);
+  if (N % 32 || K % 64)
+    return fail(MOE_LATENT_EUNSUPPORTED, "packing needs N a multiple of 32 and K of 64 (%d, %d)", N,
+                K);
+  if (!aligned(src, 16) || !aligned(dst, 16))
+    return fail(MOE_LATENT_EINVAL, "src and dst must be 16-byte aligned");
+  const size_t n = (size_t)N * K * 2;
+  if (overlaps(src, n, dst, n)) return fail(MOE_LATENT_EINVAL, "dst overlaps src");
+  HIP_TRY(moe::launch_pack_bf16((const uint16_t*)src, N, K, (uint16_t*)dst, (hipStream_t)stream));
+  return 0;
+}
+
 int moe_fp4_pack(const moe_fp4_matrix* src, int32_t count, int32_t N, int32_t K,
                  uint8_t* dst_codes, uint8_t* dst_scales, void* stream) {
   g_err.clear();
@@ -379,6 +397,17 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
     if ((rc = check_set(o.packed_experts, "packed_experts", d.n_experts))) return rc;
     if (d.n_shared && (rc = check_set(o.packed_shared, "packed_shared", d.n_shared))) return rc;
   }
+  if ((o.packed_D && !aligned(o.packed_D, 16)) || (o.packed_U && !aligned(o.packed_U, 16)) ||
+      (o.packed_R && !aligned(o.packed_R, 16)))
+    return fail(MOE_LATENT_EINVAL, "packed D, U and R must be 16-byte aligned");
+  if (o.packed_D && d.hidden % 64)
+    return fail(MOE_LATENT_EUNSUPPORTED, "packed D needs hidden a multiple of 64 (%d)", d.hidden);
+  if ((o.packed_U || o.packed_R) && d.latent % 64)
+    return fail(MOE_LATENT_EUNSUPPORTED, "packed U and R need latent a multiple of 64 (%d)",
+                d.latent);
+  if (o.packed_R && d.n_experts % 32)
+    return fail(MOE_LATENT_EUNSUPPORTED, "packed R needs n_experts a multiple of 32 (%d)",
+                d.n_experts);
   if (o.residual) {
     if (!o.norm_weight) return fail(MOE_LATENT_EINVAL, "residual block needs norm_weight");
     if (!(o.norm_eps >= 0.0f)) return fail(MOE_LATENT_EINVAL, "norm_eps must be >= 0");

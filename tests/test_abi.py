@@ -173,3 +173,29 @@ def test_pack_validation(lib):
     assert _pack(lib, dc=8 * A)[0] == lsm.EINVAL           # packed codes over the source codes
     assert _pack(lib, ds=20 * A + 64)[0] == lsm.EINVAL     # packed scales inside packed codes
     assert _pack(lib, count=0) == (0, "")                  # nothing to do
+
+
+def test_bf16_pack_validation(lib):
+    def pk(src=8 * A, N=64, K=128, dst=20 * A):
+        return lib.moe_bf16_pack(src, N, K, dst, None)
+    assert pk(src=0) == lsm.EINVAL
+    assert pk(dst=0) == lsm.EINVAL
+    assert pk(N=48) == lsm.EUNSUPPORTED
+    assert pk(K=96) == lsm.EUNSUPPORTED
+    assert pk(N=-32) == lsm.EINVAL
+    assert pk(dst=20 * A + 2) == lsm.EINVAL
+    assert pk(dst=8 * A + 4096) == lsm.EINVAL      # overlaps the source
+
+
+def test_packed_dense_opts_validation(lib):
+    def with_packed(**kw):
+        f = dict(packed_D=None, packed_U=None, packed_R=None)
+        f.update(kw)
+        return lsm.COpts(lsm.PATH_GROUPED, 0, None, 0.0, None, None, None,
+                         f["packed_D"], f["packed_U"], f["packed_R"])
+    assert _call(lib, _dims(n_experts=24, top_k=4), opts=with_packed(packed_R=30 * A))[0] == lsm.EUNSUPPORTED
+    assert _call(lib, _dims(hidden=2528), opts=with_packed(packed_D=30 * A))[0] == lsm.EUNSUPPORTED
+    assert _call(lib, _dims(latent=1760), opts=with_packed(packed_U=30 * A))[0] == lsm.EUNSUPPORTED
+    assert _call(lib, _dims(), opts=with_packed(packed_U=30 * A + 8))[0] == lsm.EINVAL
+    assert _call(lib, _dims(), T=0, opts=with_packed(packed_D=30 * A, packed_U=31 * A,
+                                                      packed_R=32 * A))[0] == 0

@@ -401,12 +401,38 @@ def test_pack_layout(count, N, K):
     assert np.array_equal(p.scales.cpu().numpy().reshape(count, -1), ps)
 
 
-@pytest.mark.parametrize("name,T", [("dec_small", 300), ("decode145", 513), ("prefill145", 4096)])
+@pytest.mark.parametrize("N,K", [(32, 64), (96, 192), (1792, 2560)])
+def test_pack_bf16_layout(N, K):
+    say(f"[case] bf16 pack layout N={N} K={K}")
+    rng = np.random.default_rng(N * K)
+    w = rng.integers(0, 65536, (N, K), dtype=np.uint16)
+    t = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(device())
+    p = lsm.pack_bf16(t)
+    torch.cuda.synchronize()
+    got = p.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+    m = np.arange(32)
+    q = 4 * (m // 8) + m % 4
+    r = 16 * (q // 8) + 8 * ((m // 4) % 2) + q % 8
+    ref = np.empty((N // 32, K // 64, 4, 64, 8), np.uint16)
+    for L in range(64):
+        for qq in range(4):
+            for s_ in range(K // 64):
+                c0 = 64 * s_ + 32 * (L // 32) + 8 * qq
+                ref[:, s_, qq, L, :] = w[np.arange(N // 32) * 32 + r[L % 32], c0:c0 + 8]
+    assert np.array_equal(got, ref.reshape(-1))
+
+
+E24 = synth.Dims(hidden=512, latent=256, n_experts=24, inter=128, top_k=3, n_shared=1)
+
+
+@pytest.mark.parametrize("name,T", [("dec_small", 300), ("e24", 200), ("decode145", 513),
+                                    ("prefill145", 4096)])
 def test_packed_experts_bit_exact(name, T):
-    """The grouped path on packed experts loads the same bytes per lane as on
-    the plain layout: outputs and routing are bit-identical."""
-    if name == "dec_small":
-        host = synth.make_layer(DEC_SMALL, 31, "zipf", 1.1)
+    """The grouped path on packed weights (experts, D, U, router rows) loads
+    the same bytes per lane as on the plain layout: outputs and routing are
+    bit-identical. With 24 experts the router rows stay plain."""
+    if name in ("dec_small", "e24"):
+        host = synth.make_layer(DEC_SMALL if name == "dec_small" else E24, 31, "zipf", 1.1)
         dl = lsm.DeviceLayer.from_host(host, device())
     else:
         cfg, host, dl = layer_for(name)
@@ -415,11 +441,13 @@ def test_packed_experts_bit_exact(name, T):
     plain = run_gpu(dl, x, path=lsm.PATH_GROUPED)
     packed_layer = lsm.DeviceLayer(**{**dl.__dict__})
     packed_layer.pack()
+    assert packed_layer.packed_experts is not None and packed_layer.packed_D is not None
+    assert (packed_layer.packed_R is None) == (name == "e24")
     packed = run_gpu(packed_layer, x, path=lsm.PATH_GROUPED)
     assert np.array_equal(packed["out_bits"], plain["out_bits"])
     for f in ("topk_idx", "counts", "perm"):
         assert np.array_equal(packed[f], plain[f]), f
-    if name == "dec_small":
+    if name in ("dec_small", "e24"):
         ref = oracle.forward(host, x)
         n_near = check_routing(ref, packed, host.dims.top_k, host.dims.n_experts)
         err_ok, _ = check_output(ref, packed["out"])
