@@ -252,7 +252,10 @@ def bench_decode(args, torch, lsm, synth, dev):
     t0 = time.time()
     host = synth.make_layer(d, cfg.seed, cfg.bias, cfg.zipf_s)
     log(f"[decode] generated layer in {time.time() - t0:.1f}s")
-    base = lsm.DeviceLayer.from_host(host, dev)
+    # weights also in the decode-packed layout the decode kernels load from
+    # (a one-time reorder at load time, outside the timed region); each
+    # rotating copy has its own
+    base = lsm.DeviceLayer.from_host(host, dev).pack(grouped=False)
     layers = [base] + [clone_layer(lsm, base) for _ in range(args.copies - 1)]
     xs_host = [synth.make_x(T, d.hidden, cfg.seed + i) for i in range(args.copies)]
     xs = [torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev) for x in xs_host]
@@ -350,7 +353,7 @@ def bench_prefill(args, torch, lsm, synth, dev):
     log(f"[prefill] generated layer in {time.time() - t0:.1f}s")
     # experts also in the packed layout the grouped kernels load from (a
     # one-time reorder at load time, outside the timed region)
-    dl = lsm.DeviceLayer.from_host(host, dev).pack()
+    dl = lsm.DeviceLayer.from_host(host, dev).pack(decode=False)
     torch.cuda.synchronize()
     del host
     x = torch.from_numpy(synth.make_x(T, d.hidden, cfg.seed).view("int16")).view(torch.bfloat16).to(dev)
@@ -426,7 +429,7 @@ def bench_stack(args, torch, lsm, synth, dev):
     dls = []
     for l in range(nl):
         h = synth.make_layer(d, cfg.seed + l, cfg.bias, cfg.zipf_s)
-        dls.append(lsm.DeviceLayer.from_host(h, dev))
+        dls.append(lsm.DeviceLayer.from_host(h, dev).pack(grouped=False))
         del h
     log(f"[stack] generated and uploaded {nl} blocks in {time.time() - t0:.1f}s")
     x = torch.from_numpy(synth.make_x(T, d.hidden, cfg.seed).view("int16")).view(torch.bfloat16).to(dev)

@@ -54,8 +54,10 @@
  *     gscale fp32  [count]
  *   experts.gate, experts.up: N = inter, K = latent;  experts.down: N = latent,
  *   K = inter. The shared expert uses the same layout with count 1.
- *   packed fp4 set (moe_fp4_pack; N a multiple of 32, K of 64): the same
- *     bytes reordered for the grouped path's loads. Block (e, t, s) covers
+ *   Packed copies (moe_fp4_pack / moe_bf16_pack) hold the same bytes
+ *   reordered so that each wave's weight loads are contiguous 1 KB runs; a
+ *   path reading them gives bit-identical results. One layout per path:
+ *   grouped-packed fp4 set (N a multiple of 32, K of 64): block (e, t, s) covers
  *     matrix e, rows [32t, 32t+32), columns [64s, 64s+64); blocks are stored
  *     in (e, t, s) order, each as 64 lanes L of
  *       codes  16 bytes: row 32t + r(L % 32), columns 64s + 32(L/32) .. +32
@@ -65,11 +67,21 @@
  *     where r(m) = 16 (q / 8) + 8 ((m / 4) % 2) + q % 8 with
  *     q = 4 (m / 8) + m % 4 (a permutation of 0..31: it puts a matrix-core
  *     lane's results on consecutive output columns). gscale is unchanged.
- *   packed bf16 matrix [N][K] (moe_bf16_pack; N a multiple of 32, K of 64):
+ *   grouped-packed bf16 matrix [N][K] (N a multiple of 32, K of 64):
  *     block (t, s) covers rows [32t, 32t+32), columns [64s, 64s+64); blocks
  *     in (t, s) order, 4096 bytes each: the 16 bytes at 1024 q + 16 L of a
  *     block (q = 0..3, L = 0..63) are row 32t + r(L % 32), columns
  *     64s + 32(L/32) + 8q .. +8.
+ *   decode-packed fp4 set (N a multiple of 16, K of 128): block (e, t, c)
+ *     covers matrix e, rows [16t, 16t+16), columns [128c, 128c+128), blocks
+ *     in (e, t, c) order; codes 1 KB per block, the 16 bytes at 16 l
+ *     (l = 0..63) being row 16t + l % 16, columns 128c + 32(l/16) .. +32;
+ *     scales 128 bytes per block, row 16t + i's eight block scales of the
+ *     128 columns at 8 i.
+ *   decode-packed bf16 matrix [N][K] (N a multiple of 16, K of 32): block
+ *     (t, c) covers rows [16t, 16t+16), columns [32c, 32c+32), blocks in
+ *     (t, c) order, 1 KB each, the 16 bytes at 16 l being row 16t + l % 16,
+ *     columns 32c + 8(l/16) .. +8.
  *
  * Ownership: the caller allocates every buffer (device memory) and owns it.
  * Calls never allocate or free device memory and keep no pointer after they
@@ -125,6 +137,19 @@ typedef struct moe_fp4_experts {
   int32_t count;       /* n_experts for the routed set, n_shared for the shared one */
 } moe_fp4_experts;
 
+/* Packed copies of a layer's weights for one path (NULL members: not given). */
+typedef struct moe_packed_weights {
+  const moe_fp4_experts *experts; /* routed experts (count n_experts) */
+  const moe_fp4_experts *shared;  /* shared expert (count n_shared); with experts */
+  const void *D;                  /* bf16 [latent][hidden] */
+  const void *U;                  /* bf16 [hidden][latent] */
+  const void *R;                  /* bf16 router.w [n_experts][latent] */
+} moe_packed_weights;
+
+/* Packing layouts (moe_fp4_pack, moe_bf16_pack). */
+#define MOE_LATENT_PACK_GROUPED 1
+#define MOE_LATENT_PACK_DECODE 2
+
 typedef struct moe_router {
   const uint16_t *w; /* bf16 [n_experts][latent], 16-byte aligned */
   const float *bias; /* fp32 [n_experts], or NULL for no bias */
@@ -176,23 +201,17 @@ typedef struct moe_latent_opts {
    * before and just after stage s's kernels. Stages a path does not run
    * leave their events untouched. */
   void *const *stage_events;
-  /* NULL, or the routed experts (count n_experts) and the shared expert
-   * (count n_shared; NULL when n_shared = 0) in the packed layout, holding
-   * the same weights as `experts` and `shared`. The grouped path then loads
-   * the packed copies: one contiguous 1 KB of codes per wave and K step
-   * instead of 32 rows x 32 bytes; results are bit-identical. Needs latent
-   * and inter multiples of 64 (else MOE_LATENT_EUNSUPPORTED). The decode
-   * path reads the plain sets. */
-  const moe_fp4_experts *packed_experts;
-  const moe_fp4_experts *packed_shared;
-  /* NULL, or D, U, router.w in the packed bf16 layout (moe_bf16_pack), each
-   * on its own: the grouped path's D, U and router GEMMs then load them with
-   * one contiguous 1 KB per wave and load; results are bit-identical.
-   * packed_D needs hidden % 64 == 0, packed_U and packed_R latent % 64 == 0,
-   * packed_R n_experts % 32 == 0 (else MOE_LATENT_EUNSUPPORTED). */
-  const void *packed_D;
-  const void *packed_U;
-  const void *packed_R;
+  /* NULL, or grouped-packed copies of the same weights: the grouped path
+   * reads each member given instead of the plain argument (experts and,
+   * with n_shared = 1, shared come together; each of D, U, R on its own).
+   * Needs latent and inter multiples of 64 for experts, U and R, hidden for
+   * D, n_experts % 32 == 0 for R (else MOE_LATENT_EUNSUPPORTED). */
+  const moe_packed_weights *grouped_packed;
+  /* NULL, or decode-packed copies: all of experts, shared (n_shared = 1),
+   * D, U and R, read by the decode path instead of the plain arguments.
+   * Needs n_experts % 16 == 0 (the decode path's dims rules give the rest).
+   * Neither path reads the other's copies. */
+  const moe_packed_weights *decode_packed;
 } moe_latent_opts;
 
 /* Device bytes of scratch one call needs for `T` tokens (the maximum over
@@ -230,22 +249,23 @@ const char *moe_latent_last_error(void);
 /* MOE_LATENT_ABI_VERSION of the library. */
 int moe_latent_version(void);
 
-/* Writes the packed layout (see "Layouts") of the fp4 matrix set `src`
- * ([count][N][K] codes and scales; gscale is not read) to dst_codes
- * (count*N*K/2 bytes) and dst_scales (count*N*K/16 bytes), device memory,
- * 16-byte aligned, overlapping neither the source nor each other. Enqueued
- * on `stream`; a one-time step when weights are loaded. Returns
- * MOE_LATENT_EUNSUPPORTED unless N % 32 == 0 and K % 64 == 0, EINVAL for NULL,
- * misaligned or overlapping buffers. count = 0 enqueues nothing. */
-int moe_fp4_pack(const moe_fp4_matrix *src, int32_t count, int32_t N, int32_t K,
+/* Writes `layout` (MOE_LATENT_PACK_GROUPED or _DECODE, see "Layouts") of
+ * the fp4 matrix set `src` ([count][N][K] codes and scales; gscale is not
+ * read) to dst_codes (count*N*K/2 bytes) and dst_scales (count*N*K/16
+ * bytes), device memory, 16-byte aligned, overlapping neither the source nor
+ * each other. Enqueued on `stream`; a one-time step when weights are loaded.
+ * Returns MOE_LATENT_EUNSUPPORTED when N, K do not fit the layout (grouped:
+ * N % 32, K % 64; decode: N % 16, K % 128), EINVAL for an unknown layout,
+ * NULL, misaligned or overlapping buffers. count = 0 enqueues nothing. */
+int moe_fp4_pack(const moe_fp4_matrix *src, int32_t count, int32_t N, int32_t K, int32_t layout,
                  uint8_t *dst_codes, uint8_t *dst_scales, void *stream);
 
-/* Writes the packed bf16 layout (see "Layouts") of the matrix `src`
- * (bf16 [N][K]) to `dst` (N*K*2 bytes), device memory, 16-byte aligned,
- * not overlapping src. Enqueued on `stream`. MOE_LATENT_EUNSUPPORTED unless
- * N % 32 == 0 and K % 64 == 0; EINVAL for NULL, misaligned or overlapping
- * buffers. */
-int moe_bf16_pack(const void *src, int32_t N, int32_t K, void *dst, void *stream);
+/* Writes `layout` of the bf16 matrix `src` [N][K] to `dst` (N*K*2 bytes),
+ * device memory, 16-byte aligned, not overlapping src. Enqueued on `stream`.
+ * MOE_LATENT_EUNSUPPORTED when N, K do not fit the layout (grouped: N % 32,
+ * K % 64; decode: N % 16, K % 32); EINVAL for an unknown layout, NULL,
+ * misaligned or overlapping buffers. */
+int moe_bf16_pack(const void *src, int32_t N, int32_t K, int32_t layout, void *dst, void *stream);
 
 #ifdef __cplusplus
 }

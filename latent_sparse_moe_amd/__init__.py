@@ -49,12 +49,19 @@ class CRouteDebug(ctypes.Structure):
                 ("perm", c_vp), ("logits", c_vp)]
 
 
+class CPackedWeights(ctypes.Structure):
+    _fields_ = [("experts", ctypes.POINTER(CFp4Experts)), ("shared", ctypes.POINTER(CFp4Experts)),
+                ("D", c_vp), ("U", c_vp), ("R", c_vp)]
+
+
 class COpts(ctypes.Structure):
     _fields_ = [("path", c_i32), ("residual", c_i32), ("norm_weight", c_vp), ("norm_eps", c_f32),
                 ("stage_events", ctypes.POINTER(c_vp)),
-                ("packed_experts", ctypes.POINTER(CFp4Experts)),
-                ("packed_shared", ctypes.POINTER(CFp4Experts)),
-                ("packed_D", c_vp), ("packed_U", c_vp), ("packed_R", c_vp)]
+                ("grouped_packed", ctypes.POINTER(CPackedWeights)),
+                ("decode_packed", ctypes.POINTER(CPackedWeights))]
+
+
+PACK_GROUPED, PACK_DECODE = 1, 2
 
 
 STAGES = ("norm", "dproj", "router", "topk", "route", "gateup", "down", "combine", "uproj")
@@ -89,9 +96,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_latent_last_error.restype = ctypes.c_char_p
     lib.moe_latent_version.argtypes = []
     lib.moe_latent_version.restype = ctypes.c_int
-    lib.moe_fp4_pack.argtypes = [P(CFp4Matrix), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
+    lib.moe_fp4_pack.argtypes = [P(CFp4Matrix), c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
     lib.moe_fp4_pack.restype = ctypes.c_int
-    lib.moe_bf16_pack.argtypes = [c_vp, c_i32, c_i32, c_vp, c_vp]
+    lib.moe_bf16_pack.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]
     lib.moe_bf16_pack.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -146,31 +153,39 @@ class DeviceLayer:
     experts: DeviceExperts
     shared: Optional[DeviceExperts]
     norm_w: Optional[torch.Tensor] = None  # float32 [hidden]
-    # the experts again in the packed layout (moe_fp4_pack), read by the
-    # grouped path when present; see pack()
-    packed_experts: Optional[DeviceExperts] = None
-    packed_shared: Optional[DeviceExperts] = None
-    packed_D: Optional[torch.Tensor] = None
-    packed_U: Optional[torch.Tensor] = None
-    packed_R: Optional[torch.Tensor] = None
+    # packed copies of the weights for each path (moe_fp4_pack / moe_bf16_pack);
+    # see pack()
+    grouped_packed: Optional["PackedWeights"] = None
+    decode_packed: Optional["PackedWeights"] = None
 
-    def pack(self, stream: Optional[torch.cuda.Stream] = None) -> "DeviceLayer":
-        """Adds packed copies of the weights the grouped path loads (same
-        bytes, reordered for its loads): the experts (latent and inter
-        multiples of 64), D (hidden % 64 == 0), U, and the router rows
-        (n_experts % 32 == 0); a matrix whose dims do not allow it is left
-        plain."""
+    def pack(self, grouped: bool = True, decode: bool = True,
+             stream: Optional[torch.cuda.Stream] = None) -> "DeviceLayer":
+        """Adds packed copies of the weights (same bytes, reordered so each
+        wave's loads are contiguous). Grouped: each matrix whose dims allow
+        it (experts: latent and inter % 64; D: hidden % 64; U: latent % 64;
+        router rows: also n_experts % 32). Decode: every matrix, when the
+        decode kernels take these dims and n_experts % 16 == 0."""
         d = self.dims
-        if d.latent % 64 == 0 and d.inter % 64 == 0:
-            self.packed_experts = pack_experts(self.experts, d, stream)
-            self.packed_shared = (pack_experts(self.shared, d, stream)
-                                  if self.shared is not None else None)
-        if d.hidden % 64 == 0:
-            self.packed_D = pack_bf16(self.D, stream)
-        if d.latent % 64 == 0:
-            self.packed_U = pack_bf16(self.U, stream)
-            if d.n_experts % 32 == 0:
-                self.packed_R = pack_bf16(self.R, stream)
+        if grouped:
+            g = PackedWeights()
+            if d.latent % 64 == 0 and d.inter % 64 == 0:
+                g.experts = pack_experts(self.experts, d, PACK_GROUPED, stream)
+                g.shared = (pack_experts(self.shared, d, PACK_GROUPED, stream)
+                            if self.shared is not None else None)
+            if d.hidden % 64 == 0:
+                g.D = pack_bf16(self.D, PACK_GROUPED, stream)
+            if d.latent % 64 == 0:
+                g.U = pack_bf16(self.U, PACK_GROUPED, stream)
+                if d.n_experts % 32 == 0:
+                    g.R = pack_bf16(self.R, PACK_GROUPED, stream)
+            self.grouped_packed = g
+        if decode and d.hidden % 256 == 0 and d.latent % 256 == 0 and d.inter % 128 == 0 \
+                and d.n_experts % 16 == 0:
+            self.decode_packed = PackedWeights(
+                pack_experts(self.experts, d, PACK_DECODE, stream),
+                pack_experts(self.shared, d, PACK_DECODE, stream) if self.shared is not None else None,
+                pack_bf16(self.D, PACK_DECODE, stream), pack_bf16(self.U, PACK_DECODE, stream),
+                pack_bf16(self.R, PACK_DECODE, stream))
         return self
 
     @staticmethod
@@ -198,37 +213,59 @@ class DeviceLayer:
                            norm_w=None if getattr(h, "norm_w", None) is None else f32(h.norm_w))
 
 
-def pack_fp4(m: DeviceFp4, N: int, K: int, stream: Optional[torch.cuda.Stream] = None) -> DeviceFp4:
-    """The packed copy of one fp4 matrix set [count][N][K] (moe_fp4_pack)."""
+@dataclass
+class PackedWeights:
+    """Packed copies for one path (members None when not packed)."""
+    experts: Optional[DeviceExperts] = None
+    shared: Optional[DeviceExperts] = None
+    D: Optional[torch.Tensor] = None
+    U: Optional[torch.Tensor] = None
+    R: Optional[torch.Tensor] = None
+
+    def c(self):
+        """(CPackedWeights, objects to keep alive while it is used)."""
+        ex = self.experts.c() if self.experts is not None else None
+        sh = self.shared.c() if self.shared is not None else None
+        cp = CPackedWeights(ctypes.pointer(ex) if ex is not None else None,
+                            ctypes.pointer(sh) if sh is not None else None,
+                            _ptr(self.D), _ptr(self.U), _ptr(self.R))
+        return cp, (ex, sh)
+
+
+def pack_fp4(m: DeviceFp4, N: int, K: int, layout: int = PACK_GROUPED,
+             stream: Optional[torch.cuda.Stream] = None) -> DeviceFp4:
+    """A packed copy of one fp4 matrix set [count][N][K] (moe_fp4_pack)."""
     lib = load_library()
     codes = torch.empty_like(m.codes)
     scales = torch.empty_like(m.scales)
     if stream is None:
         stream = torch.cuda.current_stream(m.codes.device)
     src = m.c()
-    rc = lib.moe_fp4_pack(ctypes.byref(src), m.codes.shape[0], N, K, codes.data_ptr(),
+    rc = lib.moe_fp4_pack(ctypes.byref(src), m.codes.shape[0], N, K, layout, codes.data_ptr(),
                           scales.data_ptr(), stream.cuda_stream)
     if rc != 0:
         raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
     return DeviceFp4(codes, scales, m.gscale)
 
 
-def pack_bf16(w: torch.Tensor, stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """The packed copy of a bf16 matrix [N][K] (moe_bf16_pack)."""
+def pack_bf16(w: torch.Tensor, layout: int = PACK_GROUPED,
+              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """A packed copy of a bf16 matrix [N][K] (moe_bf16_pack)."""
     lib = load_library()
     out = torch.empty_like(w)
     if stream is None:
         stream = torch.cuda.current_stream(w.device)
-    rc = lib.moe_bf16_pack(w.data_ptr(), w.shape[0], w.shape[1], out.data_ptr(), stream.cuda_stream)
+    rc = lib.moe_bf16_pack(w.data_ptr(), w.shape[0], w.shape[1], layout, out.data_ptr(),
+                           stream.cuda_stream)
     if rc != 0:
         raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
     return out
 
 
-def pack_experts(b: DeviceExperts, dims, stream=None) -> DeviceExperts:
+def pack_experts(b: DeviceExperts, dims, layout: int = PACK_GROUPED, stream=None) -> DeviceExperts:
     L, I = dims.latent, dims.inter
-    return DeviceExperts(pack_fp4(b.gate, I, L, stream), pack_fp4(b.up, I, L, stream),
-                         pack_fp4(b.down, L, I, stream))
+    return DeviceExperts(pack_fp4(b.gate, I, L, layout, stream), pack_fp4(b.up, I, L, layout, stream),
+                         pack_fp4(b.down, L, I, layout, stream))
 
 
 def workspace_bytes(dims, T: int) -> int:
@@ -292,12 +329,11 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
             i = STAGES.index(name)
             ev_arr[2 * i] = a.cuda_event
             ev_arr[2 * i + 1] = b.cuda_event
-    pex = layer.packed_experts.c() if layer.packed_experts is not None else None
-    psh = layer.packed_shared.c() if layer.packed_shared is not None else None
+    gp = layer.grouped_packed.c() if layer.grouped_packed is not None else None
+    dp = layer.decode_packed.c() if layer.decode_packed is not None else None
     opts = COpts(path, 1 if residual else 0, _ptr(layer.norm_w) if residual else None, norm_eps,
-                 ev_arr, ctypes.pointer(pex) if pex is not None else None,
-                 ctypes.pointer(psh) if psh is not None else None,
-                 _ptr(layer.packed_D), _ptr(layer.packed_U), _ptr(layer.packed_R))
+                 ev_arr, ctypes.pointer(gp[0]) if gp is not None else None,
+                 ctypes.pointer(dp[0]) if dp is not None else None)
     dbg = debug.c() if debug is not None else None
     rc = lib.moe_latent_forward_ex(
         ctypes.byref(_dims(d)), T, x.data_ptr(), layer.D.data_ptr(), layer.U.data_ptr(),
@@ -311,6 +347,6 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
 
 
 __all__ = ["load_library", "DeviceLayer", "DeviceExperts", "DeviceFp4", "RouteDebug", "forward",
-           "pack_fp4", "pack_experts", "pack_bf16",
+           "pack_fp4", "pack_experts", "pack_bf16", "PackedWeights", "PACK_GROUPED", "PACK_DECODE",
            "workspace_bytes", "alloc_workspace", "MoeLatentError", "EXPORTS",
            "PATH_AUTO", "PATH_GROUPED", "PATH_DECODE", "DECODE_MAX_T", "STAGES"]

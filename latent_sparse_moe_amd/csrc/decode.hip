@@ -58,15 +58,57 @@ static_assert(kDownRows == kDecWaves * 16, "one 16-row tile per wave");
 
 #define AGENT __HIP_MEMORY_SCOPE_AGENT
 
+// ------------------------------------------------------------------ weight addressing
+
+// A wave streams a 16-row tile (rows r0 .. r0+15, r0 % 16 == 0) of a weight
+// matrix over the K range [kb, ...): lane l serves row r0 + l % 16 and lane
+// group g = l / 16 takes chunk 4i + g at step i. Plain row-major weights put
+// a lane's successive chunks 64 (fp4) or 32 (bf16) elements apart within its
+// row. The decode-packed layout (launch_pack_*_decode) stores each step's
+// 64 lane chunks contiguously (1 KB), so that the wave's loads are too.
+struct Fp4Lane {
+  const uint8_t* c;
+  int cstep;
+  const uint8_t* s;
+  int sstep;
+};
+
+// fp4 matrix e of a set [count][N][K]; kb % 128 == 0.
+__device__ __forceinline__ Fp4Lane fp4_lane(const Fp4Mat& m, bool packed, int e, int N, int K,
+                                            int r0, int kb) {
+  const int lane = threadIdx.x & 63;
+  if (packed) {  // block (e, t, c): 1 KB codes [lane][16], 128 B scales [row][8]
+    const size_t blk = ((size_t)e * (N / 16) + min(r0, N - 16) / 16) * (K / 128) + kb / 128;
+    return {m.codes + blk * 1024 + lane * 16, 1024, m.scales + blk * 128 + (lane & 15) * 8, 128};
+  }
+  const size_t row = (size_t)e * N + min(r0 + (lane & 15), N - 1);
+  return {m.codes + row * (K / 2) + kb / 2 + (lane >> 4) * 16, 64,
+          m.scales + row * (K / 16) + kb / 16, 8};
+}
+
+// Lane base and step (elements) of a bf16 matrix [N][K]; kb % 32 == 0.
+__device__ __forceinline__ const uint16_t* bf16_lane(const uint16_t* w, bool packed, int N, int K,
+                                                    int r0, int kb, int* step) {
+  const int lane = threadIdx.x & 63;
+  if (packed) {  // block (t, c): 1 KB [lane][8 elements]
+    *step = 512;
+    const size_t blk = (size_t)(min(r0, N - 16) / 16) * (K / 32) + kb / 32;
+    return w + blk * 512 + lane * 8;
+  }
+  *step = 32;
+  return w + (size_t)min(r0 + (lane & 15), N - 1) * K + kb + (lane >> 4) * 8;
+}
+
 // ------------------------------------------------------------------ wave tiles
 
 // NCH chunks of 8 bf16 per lane group: the wave's K range is [kb, kb + 32*NCH).
+// Chunk c of the lane sits at base + c * step (elements); see bf16_lane.
 template <int NCH>
 struct Bf16Rows {
   uint4 w[NCH];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ row, int kb, int g) {
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int step) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) w[c] = *(const uint4*)(row + kb + (c * 4 + g) * 8);
+    for (int c = 0; c < NCH; ++c) w[c] = *(const uint4*)(base + c * step);
   }
   // acc += W . act over the range; act = token row (LDS) or null (zero column)
   __device__ __forceinline__ void mma(const uint16_t* act, int kb, int g, f32x4& acc) const {
@@ -104,13 +146,9 @@ template <int NCH>
 struct Fp4Rows {
   uint4 c[NCH];
   uint2 s[NCH];
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ crow,
-                                       const uint8_t* __restrict__ srow, int kb, int g) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) c[i] = *(const uint4*)(crow + (kb + (i * 4 + g) * 32) / 2);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) s[i] = *(const uint2*)(srow + (kb + i * 4 * 32) / 16);
-  }
+  // chunk i of the lane at l.c + i * l.cstep, its row's 8 scale bytes at
+  // l.s + i * l.sstep (see fp4_lane)
+  __device__ __forceinline__ void load(const Fp4Lane& l);
   // token operand from a row in LDS, or null (zero column)
   __device__ __forceinline__ void mma(const uint16_t* act, int kb, int g, f32x4& acc) const {
 #pragma unroll
@@ -127,6 +165,14 @@ struct Fp4Rows {
     }
   }
 };
+
+template <int NCH>
+__device__ __forceinline__ void Fp4Rows<NCH>::load(const Fp4Lane& l) {
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) c[i] = *(const uint4*)(l.c + i * l.cstep);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) s[i] = *(const uint2*)(l.s + i * l.sstep);
+}
 
 // Sum the per-wave partial tiles through LDS in wave order; lane l of wave 0
 // returns the totals of rows (l/16)*4 + r, token l%16.
@@ -186,13 +232,14 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_dproj(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
   const int row0 = blockIdx.x * 16;
-  const int row = min(row0 + (lane & 15), L - 1);
   const int kb = wave * (H / kDecWaves);
   if (blockIdx.x == 0 && tid == 0) *a.route_counter = 0u;  // for the router's last workgroup
   RowStage<(NCH + 1) / 2> xr;  // T x hidden, hidden = 256 NCH
   xr.load(a.x, T * H);
   Bf16Rows<NCH> wr;
-  wr.load(a.D + (size_t)row * H, kb, g);
+  int step;
+  const uint16_t* wb = bf16_lane(a.D, a.packed, L, H, row0, kb, &step);
+  wr.load(wb, step);
   xr.store(xs, T * H);
   __syncthreads();
   if (a.norm_weight) {  // residual block: RMSNorm per token in fp32, then bf16, in place
@@ -266,13 +313,11 @@ __device__ __forceinline__ void store_gateup(const f32x4& g4, const f32x4& u4, f
 template <int NCH_H>
 struct GateUpTask {
   Fp4Rows<NCH_H> wr;
-  __device__ __forceinline__ void load(const Fp4Mat& gate, const Fp4Mat& up, int e, int I, int L,
-                                       int n0, int wave, int lane) {
-    const int mat = (wave >> 1) & 1, half = wave & 1, g = lane >> 4;
-    const uint8_t* codes = mat ? up.codes : gate.codes;
-    const uint8_t* scales = mat ? up.scales : gate.scales;
-    const size_t row = ((size_t)e * I + n0 + (lane & 15)) * L;
-    wr.load(codes + row / 2, scales + row / 16, half * (L / 2), g);
+  __device__ __forceinline__ void load(const Fp4Mat& gate, const Fp4Mat& up, bool packed, int e,
+                                       int I, int L, int n0, int wave, int lane) {
+    const int mat = (wave >> 1) & 1, half = wave & 1;
+    (void)lane;
+    wr.load(fp4_lane(mat ? up : gate, packed, e, I, L, n0, half * (L / 2)));
   }
   __device__ __forceinline__ f32x4 mma(const uint16_t* act, int L, int wave, int lane) const {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -421,7 +466,6 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
 
   if ((int)blockIdx.x < nrb) {
     const int e0 = blockIdx.x * 16;
-    const int e = min(e0 + (lane & 15), E - 1);
     const int kb = wave * (L / kDecWaves);
     RowStage<(NCH_R + 1) / 2> sh_hi, sh_lo;  // T x latent, latent = 256 NCH_R
     // latent rows staged (and waited for) before the router rows are loaded,
@@ -432,7 +476,9 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
     sh_lo.store(lo, T * L);
     __syncthreads();
     Bf16Rows<NCH_R> wr;
-    wr.load(a.R + (size_t)e * L, kb, g);
+    int step;
+    const uint16_t* wb = bf16_lane(a.R, a.packed, E, L, e0, kb, &step);
+    wr.load(wb, step);
     float bias[4] = {0.f, 0.f, 0.f, 0.f};
     if (a.bias && wave == 0) {
 #pragma unroll
@@ -481,7 +527,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
   RowStage<(NCH_H + 1) / 2> st;  // T x latent, latent = 256 NCH_H
   st.load(a.hhi, T * L);
   GateUpTask<NCH_H> task;
-  if (busy) task.load(a.sh_gate, a.sh_up, 0, I, L, n0, wave, lane);
+  if (busy) task.load(a.sh_gate, a.sh_up, a.packed, 0, I, L, n0, wave, lane);
   const float gsg = a.sh_gate.gscale[0], gsu = a.sh_up.gscale[0];
   st.store(hi, T * L);
   __syncthreads();
@@ -520,7 +566,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   st.store(hi, T * L);
   __syncthreads();
   GateUpTask<NCH_H> task;
-  if (busy) task.load(a.gate, a.up, e, I, L, n0, wave, lane);
+  if (busy) task.load(a.gate, a.up, a.packed, e, I, L, n0, wave, lane);
   const float gsg = a.gate.gscale[e], gsu = a.up.gscale[e];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (busy) acc = task.mma(t < T ? hi + t * L : nullptr, L, wave, lane);
@@ -546,16 +592,13 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_down(DecodeArgs a) {
   const bool sh = s == 0;
   if (sh ? a.n_shared == 0 : s > n_act) return;  // uniform over the workgroup
   const int e = sh ? 0 : e_guess;
-  const uint8_t* codes = sh ? a.sh_down.codes : a.down.codes;
-  const uint8_t* scales = sh ? a.sh_down.scales : a.down.scales;
-  const float* gscale = sh ? a.sh_down.gscale : a.down.gscale;
+  const Fp4Mat& dm = sh ? a.sh_down : a.down;
+  const float* gscale = dm.gscale;
   RowStage<(NCH_D + 3) / 4> st;  // T x inter, inter = 128 NCH_D
   st.load(a.act + (size_t)s * T * I, T * I);
   const int row0 = rr * kDownRows + wave * 16;
-  const int row = min(row0 + (lane & 15), L - 1);
-  const size_t rowd = ((size_t)e * L + row) * I;
   Fp4Rows<NCH_D> wd;
-  wd.load(codes + rowd / 2, scales + rowd / 16, 0, g);
+  wd.load(fp4_lane(dm, a.packed, e, L, I, row0, 0));
   const float gs = gscale[e];
   st.store(lds, T * I);
   __syncthreads();
@@ -611,12 +654,13 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
   const int m0 = blockIdx.x * 16;
-  const int m = min(m0 + (lane & 15), H - 1);
   const int kb = wave * (L / kDecWaves);
   RowStage<(NCH + 1) / 2> st;  // T x latent, latent = 256 NCH
   st.load(a.z, T * L);
   Bf16Rows<NCH> wr;
-  wr.load(a.U + (size_t)m * L, kb, g);
+  int step;
+  const uint16_t* wb = bf16_lane(a.U, a.packed, H, L, m0, kb, &step);
+  wr.load(wb, step);
   st.store(zs, T * L);
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -687,6 +731,63 @@ bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_
          router_lds(kDecodeMaxT, latent) + sizeof(RouteLds) <= lim &&
          gateup_lds(kDecodeMaxT, latent) <= lim &&
          down_lds(kDecodeMaxT, inter) <= lim && uproj_lds(kDecodeMaxT, latent) <= lim;
+}
+
+// ------------------------------------------------------------------ decode-packed layouts
+
+// fp4 set [count][N][K] (N % 16 == 0, K % 128 == 0): block (e, t, c) = matrix
+// e, rows [16t, 16t + 16), columns [128c, 128c + 128), in (e, t, c) order.
+// Codes: 1 KB, lane l's 16 bytes at 16 l = row 16t + l % 16, columns
+// 128c + 32 (l / 16) .. +32. Scales: 128 bytes, row 16t + r's eight block
+// scales of the 128 columns at 8 r. One thread moves one lane's 16 bytes and
+// (lanes 0..15) its row's 8 scale bytes.
+__global__ __launch_bounds__(256) void k_pack_fp4_decode(const uint8_t* __restrict__ codes,
+                                                         const uint8_t* __restrict__ scales,
+                                                         int64_t n_lanes, int K,
+                                                         uint8_t* __restrict__ pcodes,
+                                                         uint8_t* __restrict__ pscales) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_lanes) return;
+  const int l = (int)(i & 63);
+  const int64_t blk = i >> 6;
+  const int c = (int)(blk % (K / 128));
+  const int64_t row = (blk / (K / 128)) * 16 + (l & 15);  // e * N + 16 t + l % 16
+  *(uint4*)(pcodes + i * 16) = *(const uint4*)(codes + row * (K / 2) + c * 64 + (l >> 4) * 16);
+  if (l < 16)
+    *(uint2*)(pscales + blk * 128 + l * 8) = *(const uint2*)(scales + row * (K / 16) + c * 8);
+}
+
+// bf16 [N][K] (N % 16 == 0, K % 32 == 0): block (t, c) = rows [16t, 16t + 16),
+// columns [32c, 32c + 32), in (t, c) order, 1 KB: lane l's 16 bytes at 16 l =
+// row 16t + l % 16, columns 32c + 8 (l / 16) .. +8.
+__global__ __launch_bounds__(256) void k_pack_bf16_decode(const uint16_t* __restrict__ w,
+                                                          int64_t n_lanes, int K,
+                                                          uint16_t* __restrict__ pw) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_lanes) return;
+  const int l = (int)(i & 63);
+  const int64_t blk = i >> 6;
+  const int c = (int)(blk % (K / 32));
+  const int64_t row = (blk / (K / 32)) * 16 + (l & 15);
+  *(uint4*)(pw + i * 8) = *(const uint4*)(w + row * K + c * 32 + (l >> 4) * 8);
+}
+
+hipError_t launch_pack_fp4_decode(const uint8_t* codes, const uint8_t* scales, int count, int N,
+                                  int K, uint8_t* pcodes, uint8_t* pscales, hipStream_t stream) {
+  const int64_t n_lanes = (int64_t)count * (N / 16) * (K / 128) * 64;
+  if (n_lanes == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_fp4_decode, dim3((unsigned)((n_lanes + 255) / 256)), dim3(256), 0,
+                     stream, codes, scales, n_lanes, K, pcodes, pscales);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_bf16_decode(const uint16_t* w, int N, int K, uint16_t* pw,
+                                   hipStream_t stream) {
+  const int64_t n_lanes = (int64_t)N * K / 8;
+  if (n_lanes == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_bf16_decode, dim3((unsigned)((n_lanes + 255) / 256)), dim3(256), 0,
+                     stream, w, n_lanes, K, pw);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& mk) {

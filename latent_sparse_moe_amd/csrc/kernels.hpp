@@ -134,6 +134,7 @@ struct DecodeArgs {
   Fp4Mat gate, up, down;           // routed experts
   Fp4Mat sh_gate, sh_up, sh_down;  // shared expert (count 1)
   int hidden, latent, inter, n_experts, top_k, n_shared, T;
+  bool packed;  // D, U, R and the expert sets above are in the decode-packed layouts
   // scratch (workspace)
   uint16_t* hhi;       // [T][latent]
   uint16_t* hlo;       // [T][latent]
@@ -164,5 +165,11 @@ __host__ __device__ inline int decode_row_ranges(int latent) {
   return (latent + kDecodeDownRows - 1) / kDecodeDownRows;
 }
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& mk);
+// Decode-packed layouts (decode.hip): fp4 set [count][N][K] with N % 16 == 0,
+// K % 128 == 0; bf16 [N][K] with N % 16 == 0, K % 32 == 0.
+hipError_t launch_pack_fp4_decode(const uint8_t* codes, const uint8_t* scales, int count, int N,
+                                  int K, uint8_t* pcodes, uint8_t* pscales, hipStream_t stream);
+hipError_t launch_pack_bf16_decode(const uint16_t* w, int N, int K, uint16_t* pw,
+                                   hipStream_t stream);
 
 }  // namespace moe

@@ -188,8 +188,12 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   ep.ldo = 2 * Lat;
   ep.lo_off = Lat;
   HIP_TRY(sm.mark(moe::kStageDproj, 0));
-  HIP_TRY(moe::launch_gemm_dense(moe::kEpiSplit, a_in, H, o.packed_D ? (const uint16_t*)o.packed_D : D,
-                                 H, H, T, Lat, H, ep, st, o.packed_D != nullptr));
+  const moe_packed_weights* gp = o.grouped_packed;
+  const uint16_t* pD = gp ? (const uint16_t*)gp->D : nullptr;
+  const uint16_t* pU = gp ? (const uint16_t*)gp->U : nullptr;
+  const uint16_t* pR = gp ? (const uint16_t*)gp->R : nullptr;
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiSplit, a_in, H, pD ? pD : D, H, H, T, Lat, H, ep, st,
+                                 pD != nullptr));
   HIP_TRY(sm.mark(moe::kStageDproj, 1));
   // S2: logits = (hi + lo) R^T + b, as a GEMM over K = 2*latent with R read twice.
   ep = moe::DenseEpilogue{};
@@ -197,9 +201,8 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   ep.ldo = E;
   ep.bias = router->bias;
   HIP_TRY(sm.mark(moe::kStageRouter, 0));
-  HIP_TRY(moe::launch_gemm_dense(moe::kEpiLogits, hcat, 2 * Lat,
-                                 o.packed_R ? (const uint16_t*)o.packed_R : router->w, Lat, Lat, T,
-                                 E, 2 * Lat, ep, st, o.packed_R != nullptr));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiLogits, hcat, 2 * Lat, pR ? pR : router->w, Lat, Lat, T,
+                                 E, 2 * Lat, ep, st, pR != nullptr));
   HIP_TRY(sm.mark(moe::kStageRouter, 1));
   // S3: top-k + renormalised softmax weights.
   HIP_TRY(sm.mark(moe::kStageTopk, 0));
@@ -214,9 +217,9 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   // S7-S9: grouped expert GEMMs (routed groups, then the shared expert).
   moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k};
   moe::ExpertsView ex{};
-  ex.packed = o.packed_experts != nullptr;
-  ex.routed = to_set(ex.packed ? o.packed_experts : experts);
-  if (d.n_shared) ex.shared = to_set(ex.packed ? o.packed_shared : shared);
+  ex.packed = gp && gp->experts;
+  ex.routed = to_set(ex.packed ? gp->experts : experts);
+  if (d.n_shared) ex.shared = to_set(ex.packed ? gp->shared : shared);
   const int max_mtiles = (P + 127) / 128 + (E < P ? E : P) + d.n_shared * ((T + 127) / 128);
   HIP_TRY(sm.mark(moe::kStageGateup, 0));
   HIP_TRY(moe::launch_expert_gateup(hcat, 2 * Lat, rv, ex, act, I, Lat, max_mtiles, st));
@@ -237,8 +240,8 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
     ep.ldr = H;
   }
   HIP_TRY(sm.mark(moe::kStageUproj, 0));
-  HIP_TRY(moe::launch_gemm_dense(moe::kEpiOut, z, Lat, o.packed_U ? (const uint16_t*)o.packed_U : U,
-                                 Lat, Lat, T, H, Lat, ep, st, o.packed_U != nullptr));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiOut, z, Lat, pU ? pU : U, Lat, Lat, T, H, Lat, ep, st,
+                                 pU != nullptr));
   HIP_TRY(sm.mark(moe::kStageUproj, 1));
 
   if (dbg) {
@@ -257,9 +260,17 @@ int run_decode(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_
                const moe_fp4_experts* shared, uint16_t* out, char* ws, const Layout& L,
                moe_route_debug* dbg, const moe_latent_opts& o, hipStream_t st) {
   moe::DecodeArgs a{};
+  const moe_packed_weights* dp = o.decode_packed;
+  a.packed = dp != nullptr;
+  if (dp) {  // all members present (validated)
+    D = (const uint16_t*)dp->D;
+    U = (const uint16_t*)dp->U;
+    experts = dp->experts;
+    shared = dp->shared;
+  }
   a.x = x;
   a.D = D;
-  a.R = router->w;
+  a.R = dp ? (const uint16_t*)dp->R : router->w;
   a.U = U;
   a.bias = router->bias;
   a.norm_weight = o.residual ? o.norm_weight : nullptr;
@@ -312,31 +323,43 @@ extern "C" {
 
 int moe_latent_version(void) { return MOE_LATENT_ABI_VERSION; }
 
-int moe_bf16_pack(const void* src, int32_t N, int32_t K, void* dst, void* stream) {
+int moe_bf16_pack(const void* src, int32_t N, int32_t K, int32_t layout, void* dst, void* stream) {
   g_err.clear();
+  if (layout != MOE_LATENT_PACK_GROUPED && layout != MOE_LATENT_PACK_DECODE)
+    return fail(MOE_LATENT_EINVAL, "unknown packing layout %d", layout);
   if (!src || !dst) return fail(MOE_LATENT_EINVAL, "src and dst must be non-NULL");
   if (N <= 0 || K <= 0) return fail(MOE_LATENT_EINVAL, "N and K must be positive (%d, %d)", N, K);
-  if (N % 32 || K % 64)
-    return fail(MOE_LATENT_EUNSUPPORTED, "packing needs N a multiple of 32 and K of 64 (%d, %d)", N,
-                K);
+  const int nm = layout == MOE_LATENT_PACK_GROUPED ? 32 : 16;
+  const int km = layout == MOE_LATENT_PACK_GROUPED ? 64 : 32;
+  if (N % nm || K % km)
+    return fail(MOE_LATENT_EUNSUPPORTED, "this layout needs N a multiple of %d and K of %d (%d, %d)",
+                nm, km, N, K);
   if (!aligned(src, 16) || !aligned(dst, 16))
     return fail(MOE_LATENT_EINVAL, "src and dst must be 16-byte aligned");
   const size_t n = (size_t)N * K * 2;
   if (overlaps(src, n, dst, n)) return fail(MOE_LATENT_EINVAL, "dst overlaps src");
-  HIP_TRY(moe::launch_pack_bf16((const uint16_t*)src, N, K, (uint16_t*)dst, (hipStream_t)stream));
+  if (layout == MOE_LATENT_PACK_GROUPED)
+    HIP_TRY(moe::launch_pack_bf16((const uint16_t*)src, N, K, (uint16_t*)dst, (hipStream_t)stream));
+  else
+    HIP_TRY(moe::launch_pack_bf16_decode((const uint16_t*)src, N, K, (uint16_t*)dst,
+                                         (hipStream_t)stream));
   return 0;
 }
 
-int moe_fp4_pack(const moe_fp4_matrix* src, int32_t count, int32_t N, int32_t K,
+int moe_fp4_pack(const moe_fp4_matrix* src, int32_t count, int32_t N, int32_t K, int32_t layout,
                  uint8_t* dst_codes, uint8_t* dst_scales, void* stream) {
   g_err.clear();
+  if (layout != MOE_LATENT_PACK_GROUPED && layout != MOE_LATENT_PACK_DECODE)
+    return fail(MOE_LATENT_EINVAL, "unknown packing layout %d", layout);
   if (!src || !src->codes || !src->scales || !dst_codes || !dst_scales)
     return fail(MOE_LATENT_EINVAL, "src, its codes and scales, and the destinations must be non-NULL");
   if (count < 0 || N <= 0 || K <= 0)
     return fail(MOE_LATENT_EINVAL, "count must be >= 0 and N, K positive (%d, %d, %d)", count, N, K);
-  if (N % 32 || K % 64)
-    return fail(MOE_LATENT_EUNSUPPORTED, "packing needs N a multiple of 32 and K of 64 (%d, %d)", N,
-                K);
+  const int nm = layout == MOE_LATENT_PACK_GROUPED ? 32 : 16;
+  const int km = layout == MOE_LATENT_PACK_GROUPED ? 64 : 128;
+  if (N % nm || K % km)
+    return fail(MOE_LATENT_EUNSUPPORTED, "this layout needs N a multiple of %d and K of %d (%d, %d)",
+                nm, km, N, K);
   if (!aligned(src->codes, 16) || !aligned(src->scales, 16) || !aligned(dst_codes, 16) ||
       !aligned(dst_scales, 16))
     return fail(MOE_LATENT_EINVAL, "codes and scales must be 16-byte aligned");
@@ -346,8 +369,12 @@ int moe_fp4_pack(const moe_fp4_matrix* src, int32_t count, int32_t N, int32_t K,
       overlaps(dst_codes, nc, dst_scales, ns))
     return fail(MOE_LATENT_EINVAL, "packed buffers overlap the source or each other");
   if (count == 0) return 0;
-  HIP_TRY(moe::launch_pack_fp4(src->codes, src->scales, count, N, K, dst_codes, dst_scales,
-                               (hipStream_t)stream));
+  if (layout == MOE_LATENT_PACK_GROUPED)
+    HIP_TRY(moe::launch_pack_fp4(src->codes, src->scales, count, N, K, dst_codes, dst_scales,
+                                 (hipStream_t)stream));
+  else
+    HIP_TRY(moe::launch_pack_fp4_decode(src->codes, src->scales, count, N, K, dst_codes,
+                                        dst_scales, (hipStream_t)stream));
   return 0;
 }
 
@@ -387,27 +414,43 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
     return fail(MOE_LATENT_EINVAL, "router->w must be 16-byte aligned");
   if ((rc = check_set(experts, "experts", d.n_experts))) return rc;
   if (d.n_shared && (rc = check_set(shared, "shared", d.n_shared))) return rc;
-  if (o.packed_experts || o.packed_shared) {
-    if (!o.packed_experts || (d.n_shared && !o.packed_shared))
-      return fail(MOE_LATENT_EINVAL, "packed_experts and (with a shared expert) packed_shared "
-                                     "come together");
-    if (d.latent % 64 || d.inter % 64)
-      return fail(MOE_LATENT_EUNSUPPORTED, "packed experts need latent and inter multiples of 64 "
-                                           "(%d, %d)", d.latent, d.inter);
-    if ((rc = check_set(o.packed_experts, "packed_experts", d.n_experts))) return rc;
-    if (d.n_shared && (rc = check_set(o.packed_shared, "packed_shared", d.n_shared))) return rc;
+  if (const moe_packed_weights* gp = o.grouped_packed) {
+    if (gp->experts || gp->shared) {
+      if (!gp->experts || (d.n_shared && !gp->shared))
+        return fail(MOE_LATENT_EINVAL, "grouped_packed: experts and (with a shared expert) shared "
+                                       "come together");
+      if (d.latent % 64 || d.inter % 64)
+        return fail(MOE_LATENT_EUNSUPPORTED, "grouped-packed experts need latent and inter "
+                                             "multiples of 64 (%d, %d)", d.latent, d.inter);
+      if ((rc = check_set(gp->experts, "grouped_packed->experts", d.n_experts))) return rc;
+      if (d.n_shared && (rc = check_set(gp->shared, "grouped_packed->shared", d.n_shared)))
+        return rc;
+    }
+    if ((gp->D && !aligned(gp->D, 16)) || (gp->U && !aligned(gp->U, 16)) ||
+        (gp->R && !aligned(gp->R, 16)))
+      return fail(MOE_LATENT_EINVAL, "grouped-packed D, U and R must be 16-byte aligned");
+    if (gp->D && d.hidden % 64)
+      return fail(MOE_LATENT_EUNSUPPORTED, "grouped-packed D needs hidden a multiple of 64 (%d)",
+                  d.hidden);
+    if ((gp->U || gp->R) && d.latent % 64)
+      return fail(MOE_LATENT_EUNSUPPORTED, "grouped-packed U and R need latent a multiple of 64 "
+                                           "(%d)", d.latent);
+    if (gp->R && d.n_experts % 32)
+      return fail(MOE_LATENT_EUNSUPPORTED, "grouped-packed R needs n_experts a multiple of 32 (%d)",
+                  d.n_experts);
   }
-  if ((o.packed_D && !aligned(o.packed_D, 16)) || (o.packed_U && !aligned(o.packed_U, 16)) ||
-      (o.packed_R && !aligned(o.packed_R, 16)))
-    return fail(MOE_LATENT_EINVAL, "packed D, U and R must be 16-byte aligned");
-  if (o.packed_D && d.hidden % 64)
-    return fail(MOE_LATENT_EUNSUPPORTED, "packed D needs hidden a multiple of 64 (%d)", d.hidden);
-  if ((o.packed_U || o.packed_R) && d.latent % 64)
-    return fail(MOE_LATENT_EUNSUPPORTED, "packed U and R need latent a multiple of 64 (%d)",
-                d.latent);
-  if (o.packed_R && d.n_experts % 32)
-    return fail(MOE_LATENT_EUNSUPPORTED, "packed R needs n_experts a multiple of 32 (%d)",
-                d.n_experts);
+  if (const moe_packed_weights* dp = o.decode_packed) {
+    if (!dp->experts || (d.n_shared && !dp->shared) || !dp->D || !dp->U || !dp->R)
+      return fail(MOE_LATENT_EINVAL, "decode_packed needs experts, shared (n_shared = 1), D, U "
+                                     "and R");
+    if (d.n_experts % 16)
+      return fail(MOE_LATENT_EUNSUPPORTED, "decode-packed weights need n_experts a multiple of 16 "
+                                           "(%d)", d.n_experts);
+    if (!aligned(dp->D, 16) || !aligned(dp->U, 16) || !aligned(dp->R, 16))
+      return fail(MOE_LATENT_EINVAL, "decode-packed D, U and R must be 16-byte aligned");
+    if ((rc = check_set(dp->experts, "decode_packed->experts", d.n_experts))) return rc;
+    if (d.n_shared && (rc = check_set(dp->shared, "decode_packed->shared", d.n_shared))) return rc;
+  }
   if (o.residual) {
     if (!o.norm_weight) return fail(MOE_LATENT_EINVAL, "residual block needs norm_weight");
     if (!(o.norm_eps >= 0.0f)) return fail(MOE_LATENT_EINVAL, "norm_eps must be >= 0");

@@ -132,70 +132,102 @@ def test_binding_fails_loudly_without_library(tmp_path):
         lsm._lib = saved
 
 
-def _packed_opts(n_shared=1):
-    m = lsm.CFp4Matrix(11 * A, 12 * A, 10 * A)
-    pex = lsm.CFp4Experts(m, m, m, 512)
-    psh = lsm.CFp4Experts(m, m, m, 1)
-    o = lsm.COpts(lsm.PATH_GROUPED, 0, None, 0.0, None, ctypes.pointer(pex),
-                  ctypes.pointer(psh) if n_shared else None)
-    return o, (pex, psh)
+def _opts_with(grouped=None, decode=None):
+    return lsm.COpts(lsm.PATH_AUTO, 0, None, 0.0, None,
+                     ctypes.pointer(grouped) if grouped is not None else None,
+                     ctypes.pointer(decode) if decode is not None else None)
 
 
-def test_packed_opts_validation(lib):
-    o, keep = _packed_opts(n_shared=0)
-    rc, msg = _call(lib, _dims(), opts=o)             # the shared expert's packed copy is missing
-    assert rc == lsm.EINVAL and "packed" in msg
-    o, keep = _packed_opts()
-    rc, msg = _call(lib, _dims(latent=1760), opts=o)  # latent % 64 != 0
+_M = lsm.CFp4Matrix(11 * A, 12 * A, 10 * A)
+_PEX = lsm.CFp4Experts(_M, _M, _M, 512)
+_PSH = lsm.CFp4Experts(_M, _M, _M, 1)
+
+
+def _pw(experts=True, shared=True, D=None, U=None, R=None):
+    return lsm.CPackedWeights(ctypes.pointer(_PEX) if experts else None,
+                              ctypes.pointer(_PSH) if shared else None, D, U, R)
+
+
+def test_grouped_packed_validation(lib):
+    rc, msg = _call(lib, _dims(), opts=_opts_with(_pw(shared=False)))  # shared copy missing
+    assert rc == lsm.EINVAL and "shared" in msg
+    rc, msg = _call(lib, _dims(latent=1760), opts=_opts_with(_pw()))  # latent % 64 != 0
     assert rc == lsm.EUNSUPPORTED and "64" in msg
-    rc, msg = _call(lib, _dims(inter=608), opts=o)    # inter % 64 != 0
-    assert rc == lsm.EUNSUPPORTED
-    bad = lsm.CFp4Experts(lsm.CFp4Matrix(11 * A + 8, 12 * A, 10 * A), keep[0].up, keep[0].down, 512)
-    o2 = lsm.COpts(lsm.PATH_GROUPED, 0, None, 0.0, None, ctypes.pointer(bad), ctypes.pointer(keep[1]))
-    assert _call(lib, _dims(), opts=o2)[0] == lsm.EINVAL  # misaligned packed codes
-    assert _call(lib, _dims(), T=0, opts=o)[0] == 0
+    assert _call(lib, _dims(inter=608), opts=_opts_with(_pw()))[0] == lsm.EUNSUPPORTED
+    bad = lsm.CFp4Experts(lsm.CFp4Matrix(11 * A + 8, 12 * A, 10 * A), _M, _M, 512)
+    g = lsm.CPackedWeights(ctypes.pointer(bad), ctypes.pointer(_PSH), None, None, None)
+    assert _call(lib, _dims(), opts=_opts_with(g))[0] == lsm.EINVAL    # misaligned codes
+    dense = _pw(experts=False, shared=False, R=30 * A)
+    assert _call(lib, _dims(n_experts=24, top_k=4), opts=_opts_with(dense))[0] == lsm.EUNSUPPORTED
+    dense = _pw(experts=False, shared=False, D=30 * A)
+    assert _call(lib, _dims(hidden=2528), opts=_opts_with(dense))[0] == lsm.EUNSUPPORTED
+    dense = _pw(experts=False, shared=False, U=30 * A)
+    assert _call(lib, _dims(latent=1760), opts=_opts_with(dense))[0] == lsm.EUNSUPPORTED
+    dense = _pw(experts=False, shared=False, U=30 * A + 8)
+    assert _call(lib, _dims(), opts=_opts_with(dense))[0] == lsm.EINVAL
+    full = _pw(D=30 * A, U=31 * A, R=32 * A)
+    assert _call(lib, _dims(), T=0, opts=_opts_with(full))[0] == 0
 
 
-def _pack(lib, src=True, count=4, N=64, K=128, dc=20 * A, ds=21 * A, codes=8 * A, scales=9 * A):
+def test_decode_packed_validation(lib):
+    full = _pw(D=30 * A, U=31 * A, R=32 * A)
+    assert _call(lib, _dims(), T=0, opts=_opts_with(decode=full))[0] == 0
+    for missing in (dict(D=None), dict(U=None), dict(R=None)):
+        kw = dict(D=30 * A, U=31 * A, R=32 * A)
+        kw.update(missing)
+        rc, msg = _call(lib, _dims(), opts=_opts_with(decode=_pw(**kw)))
+        assert rc == lsm.EINVAL and "decode_packed" in msg
+    assert _call(lib, _dims(), opts=_opts_with(decode=_pw(experts=False, D=30 * A, U=31 * A,
+                                                              R=32 * A)))[0] == lsm.EINVAL
+    rc, msg = _call(lib, _dims(n_experts=24, top_k=4), opts=_opts_with(decode=full))
+    assert rc == lsm.EUNSUPPORTED and "16" in msg
+    assert _call(lib, _dims(), opts=_opts_with(decode=_pw(D=30 * A + 2, U=31 * A,
+                                                          R=32 * A)))[0] == lsm.EINVAL
+
+
+def _pack(lib, src=True, count=4, N=64, K=128, layout=1, dc=20 * A, ds=21 * A, codes=8 * A,
+          scales=9 * A):
     m = lsm.CFp4Matrix(codes, scales, 10 * A)
-    rc = lib.moe_fp4_pack(ctypes.byref(m) if src else None, count, N, K, dc, ds, None)
+    rc = lib.moe_fp4_pack(ctypes.byref(m) if src else None, count, N, K, layout, dc, ds, None)
     return rc, lib.moe_latent_last_error().decode()
 
 
 def test_pack_validation(lib):
     assert _pack(lib, src=False)[0] == lsm.EINVAL
     assert _pack(lib, dc=0)[0] == lsm.EINVAL
-    assert _pack(lib, N=48)[0] == lsm.EUNSUPPORTED         # N % 32
-    assert _pack(lib, K=96)[0] == lsm.EUNSUPPORTED         # K % 64
+    assert _pack(lib, layout=3)[0] == lsm.EINVAL
+    assert _pack(lib, N=48)[0] == lsm.EUNSUPPORTED                 # grouped: N % 32
+    assert _pack(lib, K=96)[0] == lsm.EUNSUPPORTED                 # grouped: K % 64
+    assert _pack(lib, K=192, layout=2)[0] == lsm.EUNSUPPORTED      # decode: K % 128
     assert _pack(lib, K=0)[0] == lsm.EINVAL
     assert _pack(lib, count=-1)[0] == lsm.EINVAL
-    assert _pack(lib, dc=20 * A + 4)[0] == lsm.EINVAL      # misaligned
-    assert _pack(lib, dc=8 * A)[0] == lsm.EINVAL           # packed codes over the source codes
-    assert _pack(lib, ds=20 * A + 64)[0] == lsm.EINVAL     # packed scales inside packed codes
-    assert _pack(lib, count=0) == (0, "")                  # nothing to do
+    assert _pack(lib, dc=20 * A + 4)[0] == lsm.EINVAL              # misaligned
+    assert _pack(lib, dc=8 * A)[0] == lsm.EINVAL                   # over the source codes
+    assert _pack(lib, ds=20 * A + 64)[0] == lsm.EINVAL             # scales inside packed codes
+    assert _pack(lib, count=0) == (0, "")                          # nothing to do
+    assert _pack(lib, count=0, layout=2) == (0, "")
 
 
 def test_bf16_pack_validation(lib):
-    def pk(src=8 * A, N=64, K=128, dst=20 * A):
-        return lib.moe_bf16_pack(src, N, K, dst, None)
+    def pk(src=8 * A, N=64, K=128, layout=1, dst=20 * A):
+        return lib.moe_bf16_pack(src, N, K, layout, dst, None)
     assert pk(src=0) == lsm.EINVAL
     assert pk(dst=0) == lsm.EINVAL
+    assert pk(layout=0) == lsm.EINVAL
     assert pk(N=48) == lsm.EUNSUPPORTED
+    assert pk(N=40, layout=2) == lsm.EUNSUPPORTED      # decode: N % 16
     assert pk(K=96) == lsm.EUNSUPPORTED
+    assert pk(K=80, layout=2) == lsm.EUNSUPPORTED      # decode: K % 32
     assert pk(N=-32) == lsm.EINVAL
     assert pk(dst=20 * A + 2) == lsm.EINVAL
-    assert pk(dst=8 * A + 4096) == lsm.EINVAL      # overlaps the source
+    assert pk(dst=8 * A + 4096) == lsm.EINVAL          # overlaps the source
 
 
-def test_packed_dense_opts_validation(lib):
-    def with_packed(**kw):
-        f = dict(packed_D=None, packed_U=None, packed_R=None)
-        f.update(kw)
-        return lsm.COpts(lsm.PATH_GROUPED, 0, None, 0.0, None, None, None,
-                         f["packed_D"], f["packed_U"], f["packed_R"])
-    assert _call(lib, _dims(n_experts=24, top_k=4), opts=with_packed(packed_R=30 * A))[0] == lsm.EUNSUPPORTED
-    assert _call(lib, _dims(hidden=2528), opts=with_packed(packed_D=30 * A))[0] == lsm.EUNSUPPORTED
-    assert _call(lib, _dims(latent=1760), opts=with_packed(packed_U=30 * A))[0] == lsm.EUNSUPPORTED
-    assert _call(lib, _dims(), opts=with_packed(packed_U=30 * A + 8))[0] == lsm.EINVAL
-    assert _call(lib, _dims(), T=0, opts=with_packed(packed_D=30 * A, packed_U=31 * A,
-                                                      packed_R=32 * A))[0] == 0
+def test_binding_api_present():
+    """The binding's public entry points exist (the GPU tests depend on them)."""
+    for name in ("load_library", "forward", "pack_fp4", "pack_bf16", "pack_experts",
+                 "workspace_bytes", "alloc_workspace"):
+        assert callable(getattr(lsm, name)), name
+    assert callable(lsm.DeviceLayer.from_host) and callable(lsm.DeviceLayer.pack)
+    assert callable(lsm.RouteDebug.alloc)
+    assert {f for f, _ in lsm.COpts._fields_} >= {"grouped_packed", "decode_packed"}

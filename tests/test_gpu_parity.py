@@ -427,10 +427,11 @@ E24 = synth.Dims(hidden=512, latent=256, n_experts=24, inter=128, top_k=3, n_sha
 
 @pytest.mark.parametrize("name,T", [("dec_small", 300), ("e24", 200), ("decode145", 513),
                                     ("prefill145", 4096)])
-def test_packed_experts_bit_exact(name, T):
-    """The grouped path on packed weights (experts, D, U, router rows) loads
-    the same bytes per lane as on the plain layout: outputs and routing are
-    bit-identical. With 24 experts the router rows stay plain."""
+def test_packed_weights_bit_exact(name, T):
+    """Either path on packed weights loads the same bytes per lane as on the
+    plain layouts: outputs and routing are bit-identical. With 24 experts the
+    grouped router rows stay plain and there are no decode-packed copies
+    (n_experts % 16 != 0)."""
     if name in ("dec_small", "e24"):
         host = synth.make_layer(DEC_SMALL if name == "dec_small" else E24, 31, "zipf", 1.1)
         dl = lsm.DeviceLayer.from_host(host, device())
@@ -441,8 +442,10 @@ def test_packed_experts_bit_exact(name, T):
     plain = run_gpu(dl, x, path=lsm.PATH_GROUPED)
     packed_layer = lsm.DeviceLayer(**{**dl.__dict__})
     packed_layer.pack()
-    assert packed_layer.packed_experts is not None and packed_layer.packed_D is not None
-    assert (packed_layer.packed_R is None) == (name == "e24")
+    gp = packed_layer.grouped_packed
+    assert gp.experts is not None and gp.D is not None and gp.U is not None
+    assert (gp.R is None) == (name == "e24")
+    assert (packed_layer.decode_packed is None) == (name == "e24")
     packed = run_gpu(packed_layer, x, path=lsm.PATH_GROUPED)
     assert np.array_equal(packed["out_bits"], plain["out_bits"])
     for f in ("topk_idx", "counts", "perm"):
@@ -452,8 +455,54 @@ def test_packed_experts_bit_exact(name, T):
         n_near = check_routing(ref, packed, host.dims.top_k, host.dims.n_experts)
         err_ok, _ = check_output(ref, packed["out"])
         say(f"[ok] packed {name}: rel_l2={err_ok:.3e} near_ties={n_near}")
-    # the decode path ignores the packed copies
-    xd = synth.make_x(4, host.dims.hidden, 58)
-    a = run_gpu(dl, xd, path=lsm.PATH_AUTO)
-    b = run_gpu(packed_layer, xd, path=lsm.PATH_AUTO)
-    assert np.array_equal(a["out_bits"], b["out_bits"])
+    # the decode path on its own packed copies (AUTO picks it at T <= 8)
+    for Td in (1, 4, 8):
+        xd = synth.make_x(Td, host.dims.hidden, 58 + Td)
+        say(f"[case] decode packed vs plain {name} T={Td}")
+        a = run_gpu(dl, xd, path=lsm.PATH_AUTO)
+        b = run_gpu(packed_layer, xd, path=lsm.PATH_AUTO)
+        assert np.array_equal(a["out_bits"], b["out_bits"])
+        assert np.array_equal(a["topk_idx"], b["topk_idx"])
+
+
+@pytest.mark.parametrize("count,N,K", [(1, 16, 128), (3, 48, 384), (2, 640, 1792)])
+def test_pack_fp4_decode_layout(count, N, K):
+    say(f"[case] decode fp4 pack layout count={count} N={N} K={K}")
+    rng = np.random.default_rng(3 * N + K)
+    codes = rng.integers(0, 256, (count, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (count, N, K // 16), dtype=np.uint8)
+    dev = device()
+    m = lsm.DeviceFp4(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev),
+                      torch.ones(count, dtype=torch.float32, device=dev))
+    p = lsm.pack_fp4(m, N, K, lsm.PACK_DECODE)
+    torch.cuda.synchronize()
+    pc = np.empty((count, N // 16, K // 128, 64, 16), np.uint8)
+    ps = np.empty((count, N // 16, K // 128, 16, 8), np.uint8)
+    rows = np.arange(N // 16) * 16
+    for l in range(64):
+        for c in range(K // 128):
+            c0 = 128 * c + 32 * (l // 16)
+            pc[:, :, c, l, :] = codes[:, rows + l % 16, c0 // 2:c0 // 2 + 16]
+    for i in range(16):
+        for c in range(K // 128):
+            ps[:, :, c, i, :] = scales[:, rows + i, 8 * c:8 * c + 8]
+    assert np.array_equal(p.codes.cpu().numpy().reshape(count, -1), pc.reshape(count, -1))
+    assert np.array_equal(p.scales.cpu().numpy().reshape(count, -1), ps.reshape(count, -1))
+
+
+@pytest.mark.parametrize("N,K", [(16, 32), (48, 96), (2560, 1792)])
+def test_pack_bf16_decode_layout(N, K):
+    say(f"[case] decode bf16 pack layout N={N} K={K}")
+    rng = np.random.default_rng(N + 7 * K)
+    w = rng.integers(0, 65536, (N, K), dtype=np.uint16)
+    t = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(device())
+    p = lsm.pack_bf16(t, lsm.PACK_DECODE)
+    torch.cuda.synchronize()
+    got = p.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+    ref = np.empty((N // 16, K // 32, 64, 8), np.uint16)
+    rows = np.arange(N // 16) * 16
+    for l in range(64):
+        for c in range(K // 32):
+            c0 = 32 * c + 8 * (l // 16)
+            ref[:, c, l, :] = w[rows + l % 16, c0:c0 + 8]
+    assert np.array_equal(got, ref.reshape(-1))
