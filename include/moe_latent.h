@@ -233,7 +233,12 @@ int moe_latent_forward(const moe_latent_dims *dims, int64_t T, const void *x, co
                        moe_route_debug *debug, void *stream);
 
 /* As moe_latent_forward, with options (NULL = defaults: AUTO path, no
- * residual). With opts->residual = 1 this is the residual block
+ * residual). D, U, router->w, experts and shared may be NULL when the path
+ * that runs (decided from opts->path, T and dims before any pointer is
+ * checked) has packed copies of them in opts: a decode-packed set stands in
+ * for all of them on the decode path, and each member of a grouped-packed
+ * set for its plain argument on the grouped path. router->bias is always
+ * read from `router`. With opts->residual = 1 this is the residual block
  * out = x + MoE(rmsnorm(x) * norm_weight): the RMSNorm runs in fp32 and its
  * result is rounded to bf16 before D; the residual add is fp32, then rounded. */
 int moe_latent_forward_ex(const moe_latent_dims *dims, int64_t T, const void *x, const void *D,

@@ -188,6 +188,14 @@ class DeviceLayer:
                 pack_bf16(self.R, PACK_DECODE, stream))
         return self
 
+    def drop_plain(self) -> "DeviceLayer":
+        """Frees the plain weights once packed copies cover every path that
+        will run (calls on a path without such copies then fail with
+        EINVAL). The router bias and norm weight stay."""
+        self.D = self.U = self.R = None
+        self.experts = self.shared = None
+        return self
+
     @staticmethod
     def from_host(h, device) -> "DeviceLayer":
         """Copy a host layer (numpy: bf16 as uint16 bits, fp4 codes/scales as
@@ -319,8 +327,8 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
         workspace = alloc_workspace(d, T, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device)
-    router = CRouter(layer.R.data_ptr(), _ptr(layer.bias))
-    ex = layer.experts.c()
+    router = CRouter(_ptr(layer.R), _ptr(layer.bias))
+    ex = layer.experts.c() if layer.experts is not None else None
     sh = layer.shared.c() if layer.shared is not None else None
     ev_arr = None
     if stage_events:
@@ -336,8 +344,9 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
                  ctypes.pointer(dp[0]) if dp is not None else None)
     dbg = debug.c() if debug is not None else None
     rc = lib.moe_latent_forward_ex(
-        ctypes.byref(_dims(d)), T, x.data_ptr(), layer.D.data_ptr(), layer.U.data_ptr(),
-        ctypes.byref(router), ctypes.byref(ex), ctypes.byref(sh) if sh is not None else None,
+        ctypes.byref(_dims(d)), T, x.data_ptr(), _ptr(layer.D), _ptr(layer.U),
+        ctypes.byref(router), ctypes.byref(ex) if ex is not None else None,
+        ctypes.byref(sh) if sh is not None else None,
         out.data_ptr(), workspace.data_ptr() if workspace is not None else None,
         workspace.numel() if workspace is not None else 0,
         ctypes.byref(dbg) if dbg is not None else None, ctypes.byref(opts), stream.cuda_stream)

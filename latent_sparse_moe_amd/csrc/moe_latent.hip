@@ -406,14 +406,34 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
     return fail(MOE_LATENT_EUNSUPPORTED, "the decode path takes T <= %d (got %lld)",
                 MOE_LATENT_DECODE_MAX_T, (long long)T);
   if (T == 0) return 0;  // nothing to do; buffers may be empty (NULL)
-  if (!x || !D || !U || !out) return fail(MOE_LATENT_EINVAL, "x, D, U and out must be non-NULL");
-  if (!aligned(x, 16) || !aligned(D, 16) || !aligned(U, 16) || !aligned(out, 16))
+  const bool dec_ok = moe::decode_supported(d.hidden, d.latent, d.inter, d.n_experts, d.top_k,
+                                            (int)T);
+  if (o.path == MOE_LATENT_PATH_DECODE && !dec_ok)
+    return fail(MOE_LATENT_EUNSUPPORTED, "the decode path does not take these dims / T");
+  const bool use_decode =
+      o.path == MOE_LATENT_PATH_DECODE || (o.path == MOE_LATENT_PATH_AUTO && dec_ok);
+  // plain weights the chosen path reads (the rest may be NULL: packed copies
+  // stand in for them)
+  const moe_packed_weights* gpk = use_decode ? nullptr : o.grouped_packed;
+  const bool all_packed = use_decode && o.decode_packed;
+  const bool need_D = !all_packed && !(gpk && gpk->D);
+  const bool need_U = !all_packed && !(gpk && gpk->U);
+  const bool need_R = !all_packed && !(gpk && gpk->R);
+  const bool need_ex = !all_packed && !(gpk && gpk->experts);
+  if (!x || !out) return fail(MOE_LATENT_EINVAL, "x and out must be non-NULL");
+  if ((need_D && !D) || (need_U && !U))
+    return fail(MOE_LATENT_EINVAL, "D and U must be non-NULL (no packed copy for this path)");
+  if (!aligned(x, 16) || !aligned(out, 16) || (D && !aligned(D, 16)) || (U && !aligned(U, 16)))
     return fail(MOE_LATENT_EINVAL, "x, D, U and out must be 16-byte aligned");
-  if (!router || !router->w) return fail(MOE_LATENT_EINVAL, "router and router->w must be non-NULL");
-  if (!aligned(router->w, 16) || (router->bias && !aligned(router->bias, 4)))
+  if (!router) return fail(MOE_LATENT_EINVAL, "router must be non-NULL");
+  if (need_R && !router->w)
+    return fail(MOE_LATENT_EINVAL, "router->w must be non-NULL (no packed copy for this path)");
+  if ((router->w && !aligned(router->w, 16)) || (router->bias && !aligned(router->bias, 4)))
     return fail(MOE_LATENT_EINVAL, "router->w must be 16-byte aligned");
-  if ((rc = check_set(experts, "experts", d.n_experts))) return rc;
-  if (d.n_shared && (rc = check_set(shared, "shared", d.n_shared))) return rc;
+  if (need_ex || experts) {
+    if ((rc = check_set(experts, "experts", d.n_experts))) return rc;
+    if (d.n_shared && (rc = check_set(shared, "shared", d.n_shared))) return rc;
+  }
   if (const moe_packed_weights* gp = o.grouped_packed) {
     if (gp->experts || gp->shared) {
       if (!gp->experts || (d.n_shared && !gp->shared))
@@ -465,11 +485,7 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
   if (overlaps(workspace, L.total, out, xbytes) || overlaps(workspace, L.total, x, xbytes))
     return fail(MOE_LATENT_EINVAL, "workspace overlaps x or out");
 
-  const bool dec_ok = moe::decode_supported(d.hidden, d.latent, d.inter, d.n_experts, d.top_k,
-                                            (int)T);
-  if (o.path == MOE_LATENT_PATH_DECODE && !dec_ok)
-    return fail(MOE_LATENT_EUNSUPPORTED, "the decode path does not take these dims / T");
-  if (o.path == MOE_LATENT_PATH_DECODE || (o.path == MOE_LATENT_PATH_AUTO && dec_ok))
+  if (use_decode)
     return run_decode(d, (int)T, (const uint16_t*)x, (const uint16_t*)D, (const uint16_t*)U,
                       router, experts, shared, (uint16_t*)out, (char*)workspace, L, debug, o,
                       (hipStream_t)stream);

@@ -285,32 +285,45 @@ hipError_t launch_route_permute(const int32_t* idx, int pairs, int E, const int3
 
 // z[t] = sum_j w[t][j] * y[slot(t, j)] (+ y[pairs + t], the shared expert),
 // summed in the fixed order j = 0..k-1 then shared, fp32, one bf16 rounding.
+// A thread owns 8 columns of one token. It reads the token's K slots and
+// weights first, then issues all K + 1 row loads before summing, so that
+// each thread has K + 1 loads in flight rather than one at a time.
+template <int K>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                                                  const int32_t* __restrict__ slot,
-                                                 const float* __restrict__ w, int T, int k,
-                                                 int pairs, int latent, int n_shared,
+                                                 const float* __restrict__ w, int T, int pairs,
+                                                 int latent, int n_shared,
                                                  uint16_t* __restrict__ z) {
   const int cpt = latent / 8;
   const int gid = blockIdx.x * 256 + threadIdx.x;
   const int t = gid / cpt, c8 = gid % cpt;
   if (t >= T) return;
+  int r[K];
+  float wt[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    r[j] = slot[(size_t)t * K + j];
+    wt[j] = w[(size_t)t * K + j];
+  }
+  uint4 v[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) v[j] = *(const uint4*)(y + (size_t)r[j] * latent + c8 * 8);
+  uint4 vs = make_uint4(0u, 0u, 0u, 0u);
+  if (n_shared) vs = *(const uint4*)(y + (size_t)(pairs + t) * latent + c8 * 8);
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int r = slot[(size_t)t * k + j];
-    const float wt = w[(size_t)t * k + j];
-    const uint4 v = *(const uint4*)(y + (size_t)r * latent + c8 * 8);
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = fmaf(wt, bf16_bits_to_f32(d[q] & 0xFFFFu), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(wt, bf16_bits_to_f32(d[q] >> 16), acc[2 * q + 1]);
+      acc[2 * q] = fmaf(wt[j], bf16_bits_to_f32(d[q] & 0xFFFFu), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(wt[j], bf16_bits_to_f32(d[q] >> 16), acc[2 * q + 1]);
     }
   }
   if (n_shared) {
-    const uint4 v = *(const uint4*)(y + (size_t)(pairs + t) * latent + c8 * 8);
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t d[4] = {vs.x, vs.y, vs.z, vs.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       acc[2 * q] += bf16_bits_to_f32(d[q] & 0xFFFFu);
@@ -322,11 +335,28 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                  pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
 }
 
+template <int K>
+static void launch_combine_k(dim3 grid, hipStream_t stream, const uint16_t* y, const int32_t* slot,
+                             const float* w, int T, int pairs, int latent, int n_shared,
+                             uint16_t* z) {
+  hipLaunchKernelGGL(k_combine<K>, grid, dim3(256), 0, stream, y, slot, w, T, pairs, latent,
+                     n_shared, z);
+}
+
 hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w, int T, int k,
                           int pairs, int latent, int n_shared, uint16_t* z, hipStream_t stream) {
   const long total = (long)T * (latent / 8);
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, y,
-                     slot, w, T, k, pairs, latent, n_shared, z);
+  const dim3 grid((unsigned)((total + 255) / 256));
+  switch (k) {
+#define MOE_COMBINE_CASE(KV) \
+    case KV: launch_combine_k<KV>(grid, stream, y, slot, w, T, pairs, latent, n_shared, z); break;
+    MOE_COMBINE_CASE(1) MOE_COMBINE_CASE(2) MOE_COMBINE_CASE(3) MOE_COMBINE_CASE(4)
+    MOE_COMBINE_CASE(5) MOE_COMBINE_CASE(6) MOE_COMBINE_CASE(7) MOE_COMBINE_CASE(8)
+    MOE_COMBINE_CASE(9) MOE_COMBINE_CASE(10) MOE_COMBINE_CASE(11) MOE_COMBINE_CASE(12)
+    MOE_COMBINE_CASE(13) MOE_COMBINE_CASE(14) MOE_COMBINE_CASE(15) MOE_COMBINE_CASE(16)
+#undef MOE_COMBINE_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

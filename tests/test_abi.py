@@ -231,3 +231,20 @@ def test_binding_api_present():
     assert callable(lsm.DeviceLayer.from_host) and callable(lsm.DeviceLayer.pack)
     assert callable(lsm.RouteDebug.alloc)
     assert {f for f, _ in lsm.COpts._fields_} >= {"grouped_packed", "decode_packed"}
+
+
+def test_plain_weights_needed_without_packed_copies(lib):
+    d = _dims()
+    g = lsm.COpts(lsm.PATH_GROUPED, 0, None, 0.0, None, None, None)
+    rc, msg = _call(lib, d, D=0, opts=g)
+    assert rc == lsm.EINVAL and "packed" in msg
+    assert _call(lib, d, U=0, opts=g)[0] == lsm.EINVAL
+    assert _call(lib, d, experts=False, opts=g)[0] == lsm.EINVAL
+    # a grouped-packed D does not stand in for the experts
+    dense = _pw(experts=False, shared=False, D=30 * A)
+    o = lsm.COpts(lsm.PATH_GROUPED, 0, None, 0.0, None, ctypes.pointer(dense), None)
+    assert _call(lib, d, experts=False, opts=o)[0] == lsm.EINVAL
+    # decode-packed copies do not serve the grouped path (T = 64 runs grouped)
+    full = _pw(D=30 * A, U=31 * A, R=32 * A)
+    o = lsm.COpts(lsm.PATH_AUTO, 0, None, 0.0, None, None, ctypes.pointer(full))
+    assert _call(lib, d, T=64, D=0, opts=o)[0] == lsm.EINVAL

@@ -456,6 +456,7 @@ def test_packed_weights_bit_exact(name, T):
         err_ok, _ = check_output(ref, packed["out"])
         say(f"[ok] packed {name}: rel_l2={err_ok:.3e} near_ties={n_near}")
     # the decode path on its own packed copies (AUTO picks it at T <= 8)
+    decode_plain = {}
     for Td in (1, 4, 8):
         xd = synth.make_x(Td, host.dims.hidden, 58 + Td)
         say(f"[case] decode packed vs plain {name} T={Td}")
@@ -463,6 +464,16 @@ def test_packed_weights_bit_exact(name, T):
         b = run_gpu(packed_layer, xd, path=lsm.PATH_AUTO)
         assert np.array_equal(a["out_bits"], b["out_bits"])
         assert np.array_equal(a["topk_idx"], b["topk_idx"])
+        decode_plain[Td] = (xd, a["out_bits"])
+    if name == "e24":
+        return
+    # with the plain weights gone, both paths run on their packed copies alone
+    only = lsm.DeviceLayer(**{**packed_layer.__dict__}).drop_plain()
+    say(f"[case] packed copies only {name}")
+    c = run_gpu(only, x, path=lsm.PATH_GROUPED)
+    assert np.array_equal(c["out_bits"], plain["out_bits"])
+    xd, bits = decode_plain[4]
+    assert np.array_equal(run_gpu(only, xd, path=lsm.PATH_AUTO)["out_bits"], bits)
 
 
 @pytest.mark.parametrize("count,N,K", [(1, 16, 128), (3, 48, 384), (2, 640, 1792)])
