@@ -421,7 +421,8 @@ def bench_prefill(args, torch, lsm, synth, dev):
 
 def bench_stack(args, torch, lsm, synth, dev):
     """48 residual blocks (RMSNorm + latent MoE) of 145B shapes, all resident
-    (~48 GB, far beyond the Infinity Cache), T = 8 with Zipf routing bias;
+    (~48 GB of decode-packed weights, far beyond the Infinity Cache), T = 8
+    with Zipf routing bias;
     one step runs the blocks in order, each block's output feeding the next."""
     cfg = synth.CONFIGS["stack145"]
     d, T, nl = cfg.dims, cfg.T, cfg.n_layers
@@ -429,7 +430,8 @@ def bench_stack(args, torch, lsm, synth, dev):
     dls = []
     for l in range(nl):
         h = synth.make_layer(d, cfg.seed + l, cfg.bias, cfg.zipf_s)
-        dls.append(lsm.DeviceLayer.from_host(h, dev).pack(grouped=False))
+        # decode-packed copies only: the plain weights are freed once packed
+        dls.append(lsm.DeviceLayer.from_host(h, dev).pack(grouped=False).drop_plain())
         del h
     log(f"[stack] generated and uploaded {nl} blocks in {time.time() - t0:.1f}s")
     x = torch.from_numpy(synth.make_x(T, d.hidden, cfg.seed).view("int16")).view(torch.bfloat16).to(dev)
