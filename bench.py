@@ -339,10 +339,41 @@ def bench_decode(args, torch, lsm, synth, dev):
             "path": "decode" if use_decode else "grouped",
             "copies": args.copies,
             "step_us_with_events": {k: round(v, 2) for k, v in percentiles(step_us).items()},
+            "shape_family": decode_family(args, torch, lsm, synth, d, layers, path, dev),
         },
         "host": host, "x0": xs_host[0],
     }
     return res
+
+
+def decode_family(args, torch, lsm, synth, d, layers, path, dev, Ts=(1, 2, 3, 5, 8)):
+    """Step time of the same layer copies at other token counts: T = 1 (chat
+    decode) to T = 5 (a verify window of 4 drafted tokens + 1), and T = 8
+    (the decode kernels' limit). Same rotation and timing as the headline
+    pass, without events inside the timed region."""
+    out = {}
+    for T in Ts:
+        xs = [torch.from_numpy(synth.make_x(T, d.hidden, 1000 + T + i).view("int16"))
+              .view(torch.bfloat16).to(dev) for i in range(args.copies)]
+        outs = [torch.empty_like(x) for x in xs]
+        ws = lsm.alloc_workspace(d, T, dev)
+
+        def step(i):
+            c = i % args.copies
+            lsm.forward(xs[c], layers[c], out=outs[c], workspace=ws, path=path)
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            step(i)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / args.steps
+        out[f"T={T}"] = {"us_per_step": round(us, 2), "tok_s": round(T / (us * 1e-6), 1)}
+    log("[decode] shape family: " + ", ".join(f"{k} {v['us_per_step']:.1f}us" for k, v in out.items()))
+    return out
 
 
 def bench_prefill(args, torch, lsm, synth, dev):
