@@ -33,7 +33,7 @@ Arithmetic is float64 throughout. The one decision taken in another
 precision is the top-k choice, made on router logits rounded to float32, the
 precision in which the GPU kernel makes the same choice.
 """
-from .formats import bf16_value, e2m1_value, e4m3fn_value, dequant_fp4
+from .formats import bf16_value, dequant_e1m1, dequant_fp4, e1m1_value, e2m1_value, e4m3fn_value, unpack_e1m1
 from .latent_moe import (
     OracleResult,
     block_forward,
@@ -49,7 +49,8 @@ from .latent_moe import (
 )
 
 __all__ = [
-    "bf16_value", "e2m1_value", "e4m3fn_value", "dequant_fp4", "OracleResult",
+    "bf16_value", "e2m1_value", "e4m3fn_value", "dequant_fp4", "e1m1_value", "unpack_e1m1",
+    "dequant_e1m1", "OracleResult",
     "forward", "gate_topk", "route_bookkeeping", "swiglu_expert", "silu", "rmsnorm",
     "block_forward", "stack_forward", "expert_record_bytes", "param_counts",
 ]

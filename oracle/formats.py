@@ -13,6 +13,21 @@ definitions below are the OCP ones:
   with bias 7, 3 mantissa bits, no infinities; S.1111.111 is NaN. Exponent
   field 0 is subnormal: magnitude = mantissa/8 * 2^-6.
 * bf16: the upper 16 bits of an IEEE binary32.
+
+The mixed 3/4-bit record: the card's Q3_K build is "only partly 3-bit" and
+its experts are fixed-size records (Hugging Face card "Edge0-145B . Q3_K",
+section "Architecture", the paragraph on the 1,630,720-byte expert record),
+but no page defines a 3-bit element format or its layout. The format below is
+this repository's own design:
+
+* E1M1 (3 bits): 1 sign bit, 1 exponent bit with bias 1, 1 mantissa bit;
+  exponent 0 is subnormal. Magnitudes 0, 0.5, 1, 1.5 (so each value is the
+  e2m1 value of the same sign and the low two bits). Gate and up use it with
+  the same E4M3 per-16 block scales and fp32 matrix scale; down stays e2m1.
+* Storage: per matrix row, one 12-byte chunk per 32 consecutive elements: a
+  little-endian 64-bit word whose bits 2i, 2i+1 are element i's exponent and
+  mantissa bits (the magnitude index), then a little-endian 32-bit word
+  whose bit i is element i's sign.
 """
 from __future__ import annotations
 
@@ -57,6 +72,43 @@ def unpack_codes(codes: np.ndarray) -> np.ndarray:
     out[..., 0::2] = codes & 0xF
     out[..., 1::2] = codes >> 4
     return out
+
+
+def e1m1_value(code) -> np.ndarray:
+    """Value of 3-bit E1M1 codes (bit 2 sign, bit 1 exponent, bit 0 mantissa),
+    float64: sign * (exponent ? 1 + mantissa/2 : mantissa/2)."""
+    c = np.asarray(code).astype(np.int64) & 7
+    sign = np.where((c >> 2) & 1, -1.0, 1.0)
+    e = (c >> 1) & 1
+    m = c & 1
+    return sign * np.where(e == 0, m * 0.5, 1.0 + m * 0.5)
+
+
+def unpack_e1m1(codes: np.ndarray) -> np.ndarray:
+    """[..., n, 3k/8] chunked bytes -> [..., n, k] 3-bit codes (sign << 2 |
+    magnitude index), from the 12-byte chunks described above."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    lead, nb = codes.shape[:-1], codes.shape[-1]
+    ch = codes.reshape(lead + (nb // 12, 12)).astype(np.uint64)
+    mag_word = np.zeros(lead + (nb // 12,), dtype=np.uint64)
+    sign_word = np.zeros(lead + (nb // 12,), dtype=np.uint64)
+    for b in range(8):
+        mag_word |= ch[..., b] << np.uint64(8 * b)
+    for b in range(4):
+        sign_word |= ch[..., 8 + b] << np.uint64(8 * b)
+    i = np.arange(32, dtype=np.uint64)
+    mag = (mag_word[..., None] >> (np.uint64(2) * i)) & np.uint64(3)
+    sgn = (sign_word[..., None] >> i) & np.uint64(1)
+    out = (sgn << np.uint64(2)) | mag
+    return out.reshape(lead + (nb // 12 * 32,)).astype(np.uint8)
+
+
+def dequant_e1m1(codes: np.ndarray, scales: np.ndarray, gscale) -> np.ndarray:
+    """One E1M1 matrix [n][k] -> float64 weights:
+    W[n, k] = e1m1(code[n, k]) * e4m3(scale[n, k // 16]) * gscale."""
+    q = e1m1_value(unpack_e1m1(codes))
+    s = np.repeat(e4m3fn_value(scales), 16, axis=-1)
+    return q * s * np.float64(np.float32(gscale))
 
 
 def dequant_fp4(codes: np.ndarray, scales: np.ndarray, gscale) -> np.ndarray:

@@ -24,7 +24,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from .formats import bf16_value, dequant_fp4
+from .formats import bf16_value, dequant_e1m1, dequant_fp4
 
 
 def silu(v: np.ndarray) -> np.ndarray:
@@ -35,7 +35,8 @@ def silu(v: np.ndarray) -> np.ndarray:
 
 def _bank_matrix(bank, proj: str, e: int) -> np.ndarray:
     m = getattr(bank, proj)
-    return dequant_fp4(m.codes[e], m.scales[e], m.gscale[e])
+    dq = dequant_e1m1 if getattr(m, "bits", 4) == 3 else dequant_fp4
+    return dq(m.codes[e], m.scales[e], m.gscale[e])
 
 
 def swiglu_expert(v: np.ndarray, bank, e: int) -> np.ndarray:
@@ -220,12 +221,13 @@ def stack_forward(layers: List, x_bits: np.ndarray, eps: float = 1e-6):
 
 
 def expert_record_bytes(latent: int, inter: int, block: int = 16,
-                        with_matrix_scales: bool = False) -> int:
-    """Bytes of one expert (gate, up, down) in this format: 4-bit codes plus
-    one E4M3 byte per ``block`` weights; optionally the three fp32 matrix
-    scales."""
+                        with_matrix_scales: bool = False, gateup_bits: int = 4) -> int:
+    """Bytes of one expert (gate, up, down): gate and up codes of
+    ``gateup_bits`` (4: e2m1, 3: E1M1) and 4-bit down codes, plus one E4M3
+    byte per ``block`` weights; optionally the three fp32 matrix scales."""
     n = 3 * latent * inter
-    return n // 2 + n // block + (12 if with_matrix_scales else 0)
+    code_bits = 2 * latent * inter * gateup_bits + latent * inter * 4
+    return code_bits // 8 + n // block + (12 if with_matrix_scales else 0)
 
 
 def param_counts(n_layers: int, n_experts: int, top_k: int, latent: int, inter: int):

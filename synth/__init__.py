@@ -14,6 +14,12 @@ Recipe (every stream is independent, so any tensor can be drawn alone):
 * Expert gate/up ~ N(0, 1/latent), down ~ N(0, 1/inter), fp32, then quantised:
   ``gscale = amax / (6 * 448)``, block scale ``s = E4M3_rne(amax_b / (6 gscale))``,
   code ``= e2m1_rne(w / (s gscale))``.
+* With ``Dims.gateup_bits = 3`` (the mixed 3/4-bit record) gate and up use
+  3-bit E1M1 codes instead (magnitudes 0, 0.5, 1, 1.5; 6 replaced by 1.5 in
+  the recipe above); down stays e2m1. Codes are stored per row as K/32
+  chunks of 12 bytes: a 64-bit little-endian word of 2-bit magnitude indices
+  (element i at bits 2i, 2i+1), then a 32-bit word of signs (element i at
+  bit i).
 * Router bias: zero, or the log of an unnormalised Zipf(s) prior,
   ``b_e = -s * ln(e + 1)`` ("hot experts").
 """
@@ -67,6 +73,9 @@ def _load():
         lib.synth_fp4_bank.argtypes = [u64, u32, ctypes.c_int32, i64, i64, f32,
                                        vp, vp, vp, ci]
         lib.synth_quantize_fp4.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.synth_e1m1_bank.argtypes = [u64, u32, ctypes.c_int32, i64, i64, f32,
+                                        vp, vp, vp, ci]
+        lib.synth_quantize_e1m1.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.synth_f32_to_bf16.argtypes = [vp, vp, i64]
         lib.synth_philox4x32_10.argtypes = [vp, vp, vp]
         _lib = lib
@@ -119,13 +128,16 @@ def f32_to_bf16(a: np.ndarray) -> np.ndarray:
 class Fp4Mat:
     """``count`` quantised matrices of shape [n][k].
 
-    codes  uint8 [count][n][k/2] (element 2j low nibble, 2j+1 high nibble)
+    codes  uint8 [count][n][k/2] (bits 4: element 2j low nibble, 2j+1 high
+           nibble) or [count][n][3k/8] (bits 3: E1M1, 12-byte chunks of 32
+           elements, see the module docstring)
     scales uint8 [count][n][k/16] (E4M3fn bits, one per 16 consecutive k)
     gscale fp32  [count]
     """
     codes: np.ndarray
     scales: np.ndarray
     gscale: np.ndarray
+    bits: int = 4
 
     @property
     def count(self) -> int:
@@ -151,6 +163,7 @@ class Dims:
     inter: int
     top_k: int
     n_shared: int = 1
+    gateup_bits: int = 4   # 4: e2m1 gate/up; 3: E1M1 gate/up (down is e2m1 either way)
 
 
 @dataclass
@@ -184,20 +197,27 @@ class Config:
     description: str = ""
 
 
-def fp4_bank(seed: int, tags, count: int, latent: int, inter: int) -> Fp4Bank:
+def fp4_bank(seed: int, tags, count: int, latent: int, inter: int,
+             gateup_bits: int = 4) -> Fp4Bank:
     tg, tu, td = tags
     lib = _load()
 
-    def one(tag, n, k, std):
-        codes = np.empty((count, n, k // 2), dtype=np.uint8)
+    def one(tag, n, k, std, bits=4):
         scales = np.empty((count, n, k // 16), dtype=np.uint8)
         gs = np.empty((count,), dtype=np.float32)
-        lib.synth_fp4_bank(seed, tag, count, n, k, std, _ptr(codes), _ptr(scales),
-                           _ptr(gs), _threads())
-        return Fp4Mat(codes, scales, gs)
+        if bits == 4:
+            codes = np.empty((count, n, k // 2), dtype=np.uint8)
+            lib.synth_fp4_bank(seed, tag, count, n, k, std, _ptr(codes), _ptr(scales),
+                               _ptr(gs), _threads())
+        else:
+            assert bits == 3 and k % 32 == 0
+            codes = np.empty((count, n, k // 32 * 12), dtype=np.uint8)
+            lib.synth_e1m1_bank(seed, tag, count, n, k, std, _ptr(codes), _ptr(scales),
+                                _ptr(gs), _threads())
+        return Fp4Mat(codes, scales, gs, bits)
 
-    return Fp4Bank(gate=one(tg, inter, latent, latent ** -0.5),
-                   up=one(tu, inter, latent, latent ** -0.5),
+    return Fp4Bank(gate=one(tg, inter, latent, latent ** -0.5, gateup_bits),
+                   up=one(tu, inter, latent, latent ** -0.5, gateup_bits),
                    down=one(td, latent, inter, inter ** -0.5))
 
 
@@ -219,6 +239,24 @@ def quantize_fp4(w: np.ndarray) -> Fp4Mat:
     return Fp4Mat(codes, scales, gs)
 
 
+def quantize_e1m1(w: np.ndarray) -> Fp4Mat:
+    """Quantise fp32 matrices [count][n][k] (or one [n][k]) to E1M1 codes."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    single = w.ndim == 2
+    if single:
+        w = w[None]
+    count, n, k = w.shape
+    assert k % 32 == 0
+    codes = np.empty((count, n, k // 32 * 12), dtype=np.uint8)
+    scales = np.empty((count, n, k // 16), dtype=np.uint8)
+    gs = np.empty((count,), dtype=np.float32)
+    lib = _load()
+    for m in range(count):
+        lib.synth_quantize_e1m1(_ptr(w[m]), n, k, _ptr(codes[m]), _ptr(scales[m]),
+                                gs[m:].ctypes.data)
+    return Fp4Mat(codes, scales, gs, 3)
+
+
 def zipf_bias(n_experts: int, s: float) -> np.ndarray:
     return (-s * np.log(np.arange(1, n_experts + 1, dtype=np.float64))).astype(np.float32)
 
@@ -230,8 +268,9 @@ def make_layer(dims: Dims, seed: int = 0, bias: str = "none", zipf_s: float = 1.
     U = normal_bf16(seed, TAG_U, 0, (H, L), L ** -0.5)
     R = normal_bf16(seed, TAG_R, 0, (E, L), L ** -0.5)
     b = zipf_bias(E, zipf_s) if bias == "zipf" else None
-    experts = fp4_bank(seed, (TAG_GATE, TAG_UP, TAG_DOWN), E, L, I)
-    shared = (fp4_bank(seed, (TAG_SH_GATE, TAG_SH_UP, TAG_SH_DOWN), 1, L, I)
+    gb = dims.gateup_bits
+    experts = fp4_bank(seed, (TAG_GATE, TAG_UP, TAG_DOWN), E, L, I, gb)
+    shared = (fp4_bank(seed, (TAG_SH_GATE, TAG_SH_UP, TAG_SH_DOWN), 1, L, I, gb)
               if dims.n_shared else None)
     return Layer(dims=dims, D=D, U=U, R=R, bias=b, experts=experts, shared=shared,
                  norm_w=np.ones((H,), dtype=np.float32), seed=seed)
@@ -273,6 +312,6 @@ def make_config(name_or_cfg, T: Optional[int] = None):
 
 __all__ = [
     "Dims", "Config", "Layer", "Fp4Mat", "Fp4Bank", "CONFIGS", "E145", "E120", "TINY",
-    "make_layer", "make_x", "make_config", "quantize_fp4", "normal_f32", "normal_bf16",
+    "make_layer", "make_x", "make_config", "quantize_fp4", "quantize_e1m1", "normal_f32", "normal_bf16",
     "f32_to_bf16", "philox4x32_10", "zipf_bias", "fp4_bank", "build_library", "replace",
 ]

@@ -186,10 +186,65 @@ void synth_quantize_fp4(const float *w, int64_t N, int64_t K, uint8_t *codes,
   }
 }
 
+/* E1M1 (3-bit: sign, 1 exponent bit with bias 1, 1 mantissa bit; magnitudes
+ * 0, 0.5, 1, 1.5): magnitude index = round-to-nearest-even of 2|v|, clamped
+ * to 3. A zero magnitude is stored with sign 0. */
+static inline uint8_t e1m1_encode_rne(float v) {
+  float a = fabsf(v);
+  uint8_t m = (uint8_t)((a > 0.25f) + (a >= 0.75f) + (a > 1.25f));
+  return (uint8_t)(m ? m | ((v < 0.0f) << 2) : 0);
+}
+
+/* Quantise one [N][K] matrix to E1M1 codes with E4M3 per-16 block scales and
+ * an fp32 matrix scale (the recipe of synth_quantize_fp4 with 1.5 as the
+ * largest code magnitude). Codes: per row, K/32 chunks of 12 bytes, chunk c
+ * holding elements 32c .. 32c+31: bytes 0..7 a little-endian 64-bit word with
+ * element i's magnitude index at bits 2i, 2i+1; bytes 8..11 a 32-bit word
+ * with element i's sign at bit i. */
+void synth_quantize_e1m1(const float *w, int64_t N, int64_t K, uint8_t *codes,
+                         uint8_t *scales, float *gscale_out) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < N * K; ++i) {
+    float a = fabsf(w[i]);
+    if (a > amax) amax = a;
+  }
+  float gscale = (amax > 0.0f) ? amax / (1.5f * 448.0f) : 1.0f;
+  *gscale_out = gscale;
+  const int64_t nb = K / 16;
+  for (int64_t n = 0; n < N; ++n) {
+    const float *row = w + n * K;
+    for (int64_t c = 0; c < K / 32; ++c) {
+      uint64_t mag = 0;
+      uint32_t sgn = 0;
+      for (int h = 0; h < 2; ++h) {
+        const int64_t b = 2 * c + h;
+        const float *blk = row + b * 16;
+        float bmax = 0.0f;
+        for (int j = 0; j < 16; ++j) {
+          float a = fabsf(blk[j]);
+          if (a > bmax) bmax = a;
+        }
+        uint8_t s = e4m3_encode_rne(bmax / (1.5f * gscale));
+        scales[n * nb + b] = s;
+        float denom = e4m3_value(s) * gscale;
+        for (int j = 0; j < 16; ++j) {
+          uint8_t q = denom > 0.0f ? e1m1_encode_rne(blk[j] / denom) : 0;
+          const int i = 16 * h + j;
+          mag |= (uint64_t)(q & 3) << (2 * i);
+          sgn |= (uint32_t)((q >> 2) & 1) << i;
+        }
+      }
+      uint8_t *dst = codes + n * (K / 32) * 12 + c * 12;
+      for (int i = 0; i < 8; ++i) dst[i] = (uint8_t)(mag >> (8 * i));
+      for (int i = 0; i < 4; ++i) dst[8 + i] = (uint8_t)(sgn >> (8 * i));
+    }
+  }
+}
+
 /* ------------------------------------------------------------- threading */
 
 typedef struct {
-  int kind; /* 0: f32 normals, 1: bf16 normals, 2: fp4 bank */
+  int kind; /* 0: f32 normals, 1: bf16 normals, 2: fp4 bank, 3: e1m1 bank */
   uint64_t seed;
   uint32_t tag;
   uint32_t sub;
@@ -233,9 +288,12 @@ static void *run_job(void *arg) {
     for (int32_t m = j->tid; m < j->count; m += j->nthreads) {
       fill_normal_f32(j->seed, j->tag, (uint32_t)m, j->stddev, buf, 0,
                       j->N * j->K);
-      synth_quantize_fp4(buf, j->N, j->K, j->codes + (int64_t)m * j->N * (j->K / 2),
-                         j->scales + (int64_t)m * j->N * (j->K / 16),
-                         j->gscales + m);
+      if (j->kind == 2)
+        synth_quantize_fp4(buf, j->N, j->K, j->codes + (int64_t)m * j->N * (j->K / 2),
+                           j->scales + (int64_t)m * j->N * (j->K / 16), j->gscales + m);
+      else
+        synth_quantize_e1m1(buf, j->N, j->K, j->codes + (int64_t)m * j->N * (j->K / 32) * 12,
+                            j->scales + (int64_t)m * j->N * (j->K / 16), j->gscales + m);
     }
     free(buf);
   }
@@ -284,6 +342,18 @@ void synth_fp4_bank(uint64_t seed, uint32_t tag, int32_t count, int64_t N,
   job_t j;
   memset(&j, 0, sizeof j);
   j.kind = 2; j.seed = seed; j.tag = tag; j.stddev = stddev;
+  j.count = count; j.N = N; j.K = K;
+  j.codes = codes; j.scales = scales; j.gscales = gscales;
+  if (nthreads > count) nthreads = count;
+  run_parallel(j, nthreads);
+}
+
+void synth_e1m1_bank(uint64_t seed, uint32_t tag, int32_t count, int64_t N,
+                     int64_t K, float stddev, uint8_t *codes, uint8_t *scales,
+                     float *gscales, int nthreads) {
+  job_t j;
+  memset(&j, 0, sizeof j);
+  j.kind = 3; j.seed = seed; j.tag = tag; j.stddev = stddev;
   j.count = count; j.N = N; j.K = K;
   j.codes = codes; j.scales = scales; j.gscales = gscales;
   if (nthreads > count) nthreads = count;

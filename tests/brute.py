@@ -38,6 +38,35 @@ def fp4_matrix(codes: np.ndarray, scales: np.ndarray, gscale: float) -> torch.Te
     return vals * sc * float(gscale)
 
 
+E1M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5]
+
+
+def e1m1_matrix(codes: np.ndarray, scales: np.ndarray, gscale: float) -> torch.Tensor:
+    """[n][3k/8] 12-byte chunks (64-bit magnitude word, 32-bit sign word, both
+    little-endian) -> float64 [n][k], decoded element by element with
+    Python integers."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    n, nb = c.shape
+    k = nb // 12 * 32
+    vals = torch.empty((n, k), dtype=torch.float64)
+    for r in range(n):
+        row = bytes(c[r])
+        for ch in range(nb // 12):
+            mag = int.from_bytes(row[12 * ch:12 * ch + 8], "little")
+            sgn = int.from_bytes(row[12 * ch + 8:12 * ch + 12], "little")
+            for i in range(32):
+                v = E1M1_MAGNITUDES[(mag >> (2 * i)) & 3]
+                vals[r, 32 * ch + i] = -v if (sgn >> i) & 1 else v
+    sc = e4m3_to_f64(scales).repeat_interleave(16, dim=1)
+    return vals * sc * float(gscale)
+
+
+def quant_matrix(m, e: int) -> torch.Tensor:
+    """Matrix e of a quantised set, in whichever element format it holds."""
+    f = e1m1_matrix if getattr(m, "bits", 4) == 3 else fp4_matrix
+    return f(m.codes[e], m.scales[e], float(m.gscale[e]))
+
+
 class BruteLayer:
     def __init__(self, layer):
         self.layer = layer
@@ -49,8 +78,7 @@ class BruteLayer:
             bank = getattr(self.layer, bank_name)
             mats = []
             for proj in ("gate", "up", "down"):
-                m = getattr(bank, proj)
-                mats.append(fp4_matrix(m.codes[e], m.scales[e], float(m.gscale[e])))
+                mats.append(quant_matrix(getattr(bank, proj), e))
             self._cache[key] = mats
         return self._cache[key]
 

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import synth
-from brute import E2M1_MAGNITUDES, brute_forward, fp4_matrix
+from brute import E2M1_MAGNITUDES, brute_forward, e1m1_matrix, fp4_matrix
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -83,6 +83,57 @@ def check_dequant_vs_brute(seed=3):
 
 # --------------------------------------------------------------- page dims
 
+def check_e1m1_table():
+    """E1M1 (this repository's 3-bit format): sign, exponent bit (bias 1),
+    mantissa bit -> 0, .5, 1, 1.5 and their negatives; each value equals the
+    OCP e2m1 value with the same sign and mantissa and the top exponent bit
+    clear."""
+    got = oracle.e1m1_value(np.arange(8))
+    want = np.array([0.0, 0.5, 1.0, 1.5, -0.0, -0.5, -1.0, -1.5])
+    assert np.array_equal(got, want), got
+    widened = [((c >> 2) << 3) | (c & 3) for c in range(8)]
+    assert np.array_equal(got, oracle.e2m1_value(np.array(widened)))
+
+
+def check_e1m1_chunk_layout():
+    """A hand-built 12-byte chunk: element i carries code i % 8, so its
+    magnitude index i % 4 sits at bits 2i of the first word and its sign
+    (i % 8) // 4 at bit i of the second."""
+    mag = sum((i % 4) << (2 * i) for i in range(32))
+    sgn = sum(((i % 8) // 4) << i for i in range(32))
+    chunk = np.frombuffer(mag.to_bytes(8, "little") + sgn.to_bytes(4, "little"), dtype=np.uint8)
+    codes = oracle.unpack_e1m1(np.concatenate([chunk, chunk[::-1]])[None])[0]
+    assert codes[:32].tolist() == [i % 8 for i in range(32)], codes[:32]
+    rev = np.frombuffer(bytes(chunk[::-1]), dtype=np.uint8)
+    m2 = int.from_bytes(bytes(rev[:8]), "little")
+    s2 = int.from_bytes(bytes(rev[8:12]), "little")
+    want2 = [(((s2 >> i) & 1) << 2) | ((m2 >> (2 * i)) & 3) for i in range(32)]
+    assert codes[32:].tolist() == want2
+
+
+def check_e1m1_dequant_vs_brute(seed=4):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(3, 24), dtype=np.uint8)   # k = 64
+    scales = rng.integers(0, 0x7F, size=(3, 4), dtype=np.uint8)
+    g = np.float32(0.0123)
+    got = oracle.dequant_e1m1(codes, scales, g)
+    want = e1m1_matrix(codes, scales, float(g)).numpy()
+    assert np.array_equal(got, want)
+
+
+def check_e1m1_quantiser_error(seed=9):
+    """The input generator's E1M1 quantiser, decoded by the oracle, is within
+    half a step (0.25 s g) of the fp32 weights wherever the block maximum fits
+    under 1.5 s g, and within the clamp elsewhere."""
+    w = synth.normal_f32(seed, 77, 0, (8, 256), 1.0)
+    m = synth.quantize_e1m1(w)
+    dq = oracle.dequant_e1m1(m.codes[0], m.scales[0], m.gscale[0])
+    step = np.repeat(oracle.e4m3fn_value(m.scales[0]), 16, axis=-1) * float(m.gscale[0]) * 0.5
+    over = np.maximum(np.abs(w) - 3.0 * step, 0.0)
+    assert np.all(np.abs(dq - w) <= 0.5 * step * (1 + 1e-6) + over)
+    assert np.mean(np.abs(dq - w) / step) < 0.35
+
+
 def check_page_dimensions():
     p = page_pins()
     for dims, lat in ((synth.E145, p["latent_145b"]["value"]), (synth.E120, p["latent_120b"]["value"])):
@@ -114,6 +165,13 @@ def check_record_bytes():
     assert q145 * 1280 == q120 * 1792
     assert sig_round(48 * 512 * q145 / 1e9, 3) == p["q3k_experts_bin_gb"]["value"]
     assert oracle.expert_record_bytes(1280, 640) * 1792 == rec * 1280
+    # the mixed 3/4-bit record (3-bit gate/up, 4-bit down): within 1.2% of the
+    # pages' Q3_K record for both latent widths
+    m145 = oracle.expert_record_bytes(1792, 640, gateup_bits=3)
+    m120 = oracle.expert_record_bytes(1280, 640, gateup_bits=3)
+    assert m145 == 2 * 1792 * 640 * 3 // 8 + 1792 * 640 // 2 + 3 * 1792 * 640 // 16 == 1_648_640
+    assert m120 == 1_177_600
+    assert abs(m145 / q145 - 1) < 0.012 and abs(m120 / q120 - 1) < 0.012
 
 
 # --------------------------------------------------------------- gating

@@ -178,3 +178,44 @@ def test_stack_truncating_residual_caught(monkeypatch):
         return t.astype(np.float64), res
     monkeypatch.setattr(M, "block_forward", bad)
     assert _fails(pins.check_stack_vs_torch_chain)
+
+
+def _tiny_mixed_vs_brute():
+    d = synth.replace(synth.TINY, gateup_bits=3)
+    layer = synth.make_layer(d, 21)
+    pins.check_vs_brute(layer, synth.make_x(4, d.hidden, 21))
+
+
+def test_e1m1_planes_swapped_caught(monkeypatch):
+    orig = F.unpack_e1m1
+    def bad(codes):   # reads the sign word from the first 4 bytes instead of the last
+        c = np.asarray(codes, dtype=np.uint8)
+        lead, nb = c.shape[:-1], c.shape[-1]
+        ch = c.reshape(lead + (nb // 12, 12))
+        ch = np.concatenate([ch[..., 4:12], ch[..., 0:4]], axis=-1)
+        return orig(ch.reshape(lead + (nb,)))
+    monkeypatch.setattr(F, "unpack_e1m1", bad)
+    monkeypatch.setattr(oracle, "unpack_e1m1", bad)
+    assert _fails(pins.check_e1m1_chunk_layout)
+    assert _fails(pins.check_e1m1_dequant_vs_brute)
+    assert _fails(_tiny_mixed_vs_brute)
+
+
+def test_e1m1_subnormal_caught(monkeypatch):
+    orig = F.e1m1_value
+    def bad(c):   # the exponent-0 codes read as normal
+        c = np.asarray(c).astype(np.int64)
+        v = orig(c)
+        return np.where(((c >> 1) & 1) == 0, np.sign(v) * (1.0 + (c & 1) * 0.5) * ((c & 1) > 0), v)
+    monkeypatch.setattr(F, "e1m1_value", bad)
+    monkeypatch.setattr(oracle, "e1m1_value", bad)
+    assert _fails(pins.check_e1m1_table)
+    assert _fails(pins.check_e1m1_dequant_vs_brute)
+
+
+def test_mixed_record_gateup_read_as_fp4_caught(monkeypatch):
+    def bad_bank_matrix(bank, proj, e):
+        m = getattr(bank, proj)
+        return F.dequant_fp4(m.codes[e][..., : m.scales.shape[-1] * 8], m.scales[e], m.gscale[e])
+    monkeypatch.setattr(M, "_bank_matrix", bad_bank_matrix)
+    assert _fails(_tiny_mixed_vs_brute)

@@ -128,3 +128,27 @@ def test_stack_zero_up_projection_is_identity():
 
 def test_stack_vs_torch_chain():
     pins.check_stack_vs_torch_chain()
+
+
+def test_e1m1_table():
+    pins.check_e1m1_table()
+
+
+def test_e1m1_chunk_layout():
+    pins.check_e1m1_chunk_layout()
+
+
+def test_e1m1_dequant_vs_brute():
+    pins.check_e1m1_dequant_vs_brute()
+
+
+def test_e1m1_quantiser_error():
+    pins.check_e1m1_quantiser_error()
+
+
+def test_vs_brute_tiny_mixed_record():
+    """A tiny layer with 3-bit E1M1 gate/up experts (and e2m1 down)."""
+    d = synth.replace(synth.TINY, gateup_bits=3)
+    layer = synth.make_layer(d, 21)
+    x = synth.make_x(6, d.hidden, 21)
+    pins.check_vs_brute(layer, x)
