@@ -54,6 +54,19 @@
  *     gscale fp32  [count]
  *   experts.gate, experts.up: N = inter, K = latent;  experts.down: N = latent,
  *   K = inter. The shared expert uses the same layout with count 1.
+ *   Mixed 3/4-bit expert record (moe_fp4_matrix.bits = 3 on gate and up;
+ *   down stays e2m1). The card's Q3_K build is only partly 3-bit and keeps
+ *   its experts in fixed-size records (Hugging Face card "Edge0-145B . Q3_K",
+ *   section "Architecture"); no page defines the 3-bit element, so this
+ *   format is this library's own. E1M1: 1 sign bit, 1 exponent bit (bias 1,
+ *   exponent 0 subnormal), 1 mantissa bit, so magnitudes 0, 0.5, 1, 1.5 (the
+ *   e2m1 values whose top exponent bit is clear), with the same E4M3 block
+ *   scales and fp32 matrix scale as e2m1:
+ *     codes  uint8 [count][N][K/32][12]   one 12-byte chunk per 32 elements:
+ *            a little-endian u64 whose bits 2i, 2i+1 are element i's
+ *            mantissa and exponent bits (mantissa low), then a little-endian
+ *            u32 whose bit i is element i's sign
+ *     scales, gscale as above.
  *   Packed copies (moe_fp4_pack / moe_bf16_pack) hold the same bytes
  *   reordered so that each wave's weight loads are contiguous 1 KB runs; a
  *   path reading them gives bit-identical results. One layout per path:
@@ -78,6 +91,10 @@
  *     (l = 0..63) being row 16t + l % 16, columns 128c + 32(l/16) .. +32;
  *     scales 128 bytes per block, row 16t + i's eight block scales of the
  *     128 columns at 8 i.
+ *   E1M1 sets pack the same way with each lane's 32 columns as one 12-byte
+ *     chunk instead of 16 bytes: grouped blocks are 768 bytes of codes, lane
+ *     L's chunk at 12 L; decode blocks 768 bytes, lane l's chunk at 12 l.
+ *     Scales are packed as for e2m1.
  *   decode-packed bf16 matrix [N][K] (N a multiple of 16, K of 32): block
  *     (t, c) covers rows [16t, 16t+16), columns [32c, 32c+32), blocks in
  *     (t, c) order, 1 KB each, the 16 bytes at 16 l being row 16t + l % 16,
@@ -104,7 +121,7 @@
 extern "C" {
 #endif
 
-#define MOE_LATENT_ABI_VERSION 2
+#define MOE_LATENT_ABI_VERSION 3
 
 #define MOE_LATENT_OK 0
 #define MOE_LATENT_EINVAL (-1)       /* null pointer, bad size, misaligned pointer, aliasing */
@@ -125,11 +142,15 @@ typedef struct moe_latent_dims {
 } moe_latent_dims;
 
 typedef struct moe_fp4_matrix {
-  const uint8_t *codes;  /* [count][N][K/2], 16-byte aligned */
+  const uint8_t *codes;  /* [count][N][K/2] (E1M1: [count][N][K/32][12]), 16-byte aligned */
   const uint8_t *scales; /* [count][N][K/16], 16-byte aligned */
   const float *gscale;   /* [count] */
+  int32_t bits;          /* element format: 0 or 4 = e2m1, 3 = E1M1 (gate and up only) */
 } moe_fp4_matrix;
 
+/* gate and up have one format (bits), the routed and shared sets of a
+ * layer the same one, and down is e2m1; else MOE_LATENT_EUNSUPPORTED. E1M1
+ * gate/up need latent a multiple of 64. */
 typedef struct moe_fp4_experts {
   moe_fp4_matrix gate; /* N = inter,  K = latent */
   moe_fp4_matrix up;   /* N = inter,  K = latent */
@@ -255,10 +276,11 @@ const char *moe_latent_last_error(void);
 int moe_latent_version(void);
 
 /* Writes `layout` (MOE_LATENT_PACK_GROUPED or _DECODE, see "Layouts") of
- * the fp4 matrix set `src` ([count][N][K] codes and scales; gscale is not
- * read) to dst_codes (count*N*K/2 bytes) and dst_scales (count*N*K/16
- * bytes), device memory, 16-byte aligned, overlapping neither the source nor
- * each other. Enqueued on `stream`; a one-time step when weights are loaded.
+ * the fp4 matrix set `src` ([count][N][K] codes and scales in the format
+ * src->bits names; gscale is not read) to dst_codes (as many bytes as the
+ * source codes: count*N*K/2, or count*N*K*3/8 for E1M1) and dst_scales
+ * (count*N*K/16 bytes), device memory, 16-byte aligned, overlapping neither
+ * the source nor each other. The packed set keeps the source's bits. Enqueued on `stream`; a one-time step when weights are loaded.
  * Returns MOE_LATENT_EUNSUPPORTED when N, K do not fit the layout (grouped:
  * N % 32, K % 64; decode: N % 16, K % 128), EINVAL for an unknown layout,
  * NULL, misaligned or overlapping buffers. count = 0 enqueues nothing. */

@@ -33,7 +33,7 @@ class CDims(ctypes.Structure):
 
 
 class CFp4Matrix(ctypes.Structure):
-    _fields_ = [("codes", c_vp), ("scales", c_vp), ("gscale", c_vp)]
+    _fields_ = [("codes", c_vp), ("scales", c_vp), ("gscale", c_vp), ("bits", c_i32)]
 
 
 class CFp4Experts(ctypes.Structure):
@@ -120,12 +120,14 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 @dataclass
 class DeviceFp4:
-    codes: torch.Tensor   # uint8 [count][N][K/2]
+    codes: torch.Tensor   # uint8 [count][N][K/2] (E1M1: [count][N][3K/8])
     scales: torch.Tensor  # uint8 [count][N][K/16]
     gscale: torch.Tensor  # float32 [count]
+    bits: int = 4         # 4: e2m1 codes, 3: E1M1
 
     def c(self) -> CFp4Matrix:
-        return CFp4Matrix(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr())
+        return CFp4Matrix(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr(),
+                          self.bits)
 
 
 @dataclass
@@ -213,7 +215,8 @@ class DeviceLayer:
             if b is None:
                 return None
             return DeviceExperts(*[DeviceFp4(u8(getattr(b, p).codes), u8(getattr(b, p).scales),
-                                             f32(getattr(b, p).gscale)) for p in ("gate", "up", "down")])
+                                             f32(getattr(b, p).gscale), getattr(b, p).bits)
+                                   for p in ("gate", "up", "down")])
 
         return DeviceLayer(dims=h.dims, D=bf16(h.D), U=bf16(h.U), R=bf16(h.R),
                            bias=None if h.bias is None else f32(h.bias),
@@ -253,7 +256,7 @@ def pack_fp4(m: DeviceFp4, N: int, K: int, layout: int = PACK_GROUPED,
                           scales.data_ptr(), stream.cuda_stream)
     if rc != 0:
         raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
-    return DeviceFp4(codes, scales, m.gscale)
+    return DeviceFp4(codes, scales, m.gscale, m.bits)
 
 
 def pack_bf16(w: torch.Tensor, layout: int = PACK_GROUPED,

@@ -67,6 +67,25 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float s) {
   return r;
 }
 
+// Eight 3-bit E1M1 codes (sign, exponent bit, mantissa bit; magnitudes 0,
+// 0.5, 1, 1.5) -> the eight e2m1 codes of the same values, in dequant8's
+// nibble order. m16 holds the 2-bit magnitude indices (element i at bits 2i,
+// 2i+1), s8 the signs (element i at bit i). An E1M1 value is the e2m1 value
+// with the top exponent bit clear, so nibble i = sign_i << 3 | index_i. The
+// indices and signs are spread to 4-bit slots by three shift/or/mask steps
+// each.
+__device__ __forceinline__ uint32_t e1m1x8_to_e2m1(uint32_t m16, uint32_t s8) {
+  uint32_t x = m16 & 0xFFFFu;
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  uint32_t y = s8 & 0xFFu;
+  y = (y | (y << 12)) & 0x000F000Fu;
+  y = (y | (y << 6)) & 0x03030303u;
+  y = (y | (y << 3)) & 0x11111111u;
+  return x | (y << 3);
+}
+
 // Eight e2m1 codes -> their plain values as bf16 (exact; no block scale).
 __device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t codes) {
   bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 0);

@@ -73,16 +73,19 @@ struct Fp4Lane {
   int sstep;
 };
 
-// fp4 matrix e of a set [count][N][K]; kb % 128 == 0.
+// fp4 matrix e of a set [count][N][K]; kb % 128 == 0. bits 4: e2m1 codes,
+// 16 bytes per 32 weights; bits 3: E1M1 codes, one 12-byte chunk per 32.
 __device__ __forceinline__ Fp4Lane fp4_lane(const Fp4Mat& m, bool packed, int e, int N, int K,
-                                            int r0, int kb) {
+                                            int r0, int kb, int bits = 4) {
   const int lane = threadIdx.x & 63;
-  if (packed) {  // block (e, t, c): 1 KB codes [lane][16], 128 B scales [row][8]
+  const int cb = bits == 4 ? 16 : 12;  // code bytes of 32 weights
+  if (packed) {  // block (e, t, c): 64 lanes x cb code bytes, 128 B scales [row][8]
     const size_t blk = ((size_t)e * (N / 16) + min(r0, N - 16) / 16) * (K / 128) + kb / 128;
-    return {m.codes + blk * 1024 + lane * 16, 1024, m.scales + blk * 128 + (lane & 15) * 8, 128};
+    return {m.codes + blk * 64 * cb + lane * cb, 64 * cb, m.scales + blk * 128 + (lane & 15) * 8,
+            128};
   }
   const size_t row = (size_t)e * N + min(r0 + (lane & 15), N - 1);
-  return {m.codes + row * (K / 2) + kb / 2 + (lane >> 4) * 16, 64,
+  return {m.codes + row * ((size_t)K / 32 * cb) + (kb / 32 + (lane >> 4)) * cb, 4 * cb,
           m.scales + row * (K / 16) + kb / 16, 8};
 }
 
@@ -142,34 +145,51 @@ struct Bf16Rows {
 // contiguous: every lane of the row loads those eight bytes (16 distinct
 // addresses per instruction instead of 64 two-byte ones; measured 12.7 ->
 // 11.3 us for the routed gate/up weight stream) and keeps its two.
-template <int NCH>
+// BITS = 3: E1M1 codes, a lane's chunk of 32 weights being 12 bytes (a 2-bit
+// magnitude plane and a sign plane), widened to e2m1 nibbles in mma.
+template <int NCH, int BITS = 4>
 struct Fp4Rows {
-  uint4 c[NCH];
+  static constexpr int kW = BITS == 4 ? 4 : 3;  // code words per chunk
+  uint32_t c[NCH][kW];
   uint2 s[NCH];
   // chunk i of the lane at l.c + i * l.cstep, its row's 8 scale bytes at
   // l.s + i * l.sstep (see fp4_lane)
   __device__ __forceinline__ void load(const Fp4Lane& l);
+  // e2m1 nibbles of elements 8q .. 8q+7 of chunk i
+  __device__ __forceinline__ uint32_t codes8(int i, int q) const {
+    if constexpr (BITS == 4)
+      return c[i][q];
+    else
+      return e1m1x8_to_e2m1(c[i][q >> 1] >> (16 * (q & 1)), c[i][2] >> (8 * q));
+  }
   // token operand from a row in LDS, or null (zero column)
   __device__ __forceinline__ void mma(const uint16_t* act, int kb, int g, f32x4& acc) const {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const uint32_t sp = ((g & 2) ? s[i].y : s[i].x) >> (16 * (g & 1));
       const float s0 = e4m3_to_f32(sp & 0xFFu), s1 = e4m3_to_f32((sp >> 8) & 0xFFu);
-      const uint32_t d[4] = {c[i].x, c[i].y, c[i].z, c[i].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         bf16x8 b = {};
         if (act) b = *(const bf16x8*)(act + kb + (i * 4 + g) * 32 + q * 8);
-        acc = mfma16x16x32(dequant8(d[q], q < 2 ? s0 : s1), b, acc);
+        acc = mfma16x16x32(dequant8(codes8(i, q), q < 2 ? s0 : s1), b, acc);
       }
     }
   }
 };
 
-template <int NCH>
-__device__ __forceinline__ void Fp4Rows<NCH>::load(const Fp4Lane& l) {
+template <int NCH, int BITS>
+__device__ __forceinline__ void Fp4Rows<NCH, BITS>::load(const Fp4Lane& l) {
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) c[i] = *(const uint4*)(l.c + i * l.cstep);
+  for (int i = 0; i < NCH; ++i) {
+    if constexpr (BITS == 4) {
+      const uint4 v = *(const uint4*)(l.c + i * l.cstep);
+      c[i][0] = v.x; c[i][1] = v.y; c[i][2] = v.z; c[i][3] = v.w;
+    } else {
+      const uint3 v = *(const uint3*)(l.c + i * l.cstep);
+      c[i][0] = v.x; c[i][1] = v.y; c[i][2] = v.z;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) s[i] = *(const uint2*)(l.s + i * l.sstep);
 }
@@ -310,14 +330,14 @@ __device__ __forceinline__ void store_gateup(const f32x4& g4, const f32x4& u4, f
 // Gate/up of one expert for two 16-row tiles per workgroup: wave w handles
 // tile w/4, matrix (w/2)%2 (gate, up), K half w%2. The halves and matrices
 // meet in LDS; waves 0 and 4 apply SiLU*mul and store.
-template <int NCH_H>
+template <int NCH_H, int BITS>
 struct GateUpTask {
-  Fp4Rows<NCH_H> wr;
+  Fp4Rows<NCH_H, BITS> wr;
   __device__ __forceinline__ void load(const Fp4Mat& gate, const Fp4Mat& up, bool packed, int e,
                                        int I, int L, int n0, int wave, int lane) {
     const int mat = (wave >> 1) & 1, half = wave & 1;
     (void)lane;
-    wr.load(fp4_lane(mat ? up : gate, packed, e, I, L, n0, half * (L / 2)));
+    wr.load(fp4_lane(mat ? up : gate, packed, e, I, L, n0, half * (L / 2), BITS));
   }
   __device__ __forceinline__ f32x4 mma(const uint16_t* act, int L, int wave, int lane) const {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -451,7 +471,7 @@ __device__ __forceinline__ void publish_routing(const DecodeArgs& a, const Route
     }
 }
 
-template <int NCH_R, int NCH_H>
+template <int NCH_R, int NCH_H, int BITS>
 __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ RouteLds rl;
@@ -526,7 +546,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
   const int n0 = busy ? tile * 16 : 0;
   RowStage<(NCH_H + 1) / 2> st;  // T x latent, latent = 256 NCH_H
   st.load(a.hhi, T * L);
-  GateUpTask<NCH_H> task;
+  GateUpTask<NCH_H, BITS> task;
   if (busy) task.load(a.sh_gate, a.sh_up, a.packed, 0, I, L, n0, wave, lane);
   const float gsg = a.sh_gate.gscale[0], gsu = a.sh_up.gscale[0];
   st.store(hi, T * L);
@@ -538,7 +558,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
 
 // ------------------------------------------------------------------ 3. routed gate/up
 
-template <int NCH_H>
+template <int NCH_H, int BITS>
 __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int L = a.latent, T = a.T, I = a.inter;
@@ -565,7 +585,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   st.load(a.hhi, T * L);
   st.store(hi, T * L);
   __syncthreads();
-  GateUpTask<NCH_H> task;
+  GateUpTask<NCH_H, BITS> task;
   if (busy) task.load(a.gate, a.up, a.packed, e, I, L, n0, wave, lane);
   const float gsg = a.gate.gscale[e], gsu = a.up.gscale[e];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -737,22 +757,28 @@ bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_
 
 // fp4 set [count][N][K] (N % 16 == 0, K % 128 == 0): block (e, t, c) = matrix
 // e, rows [16t, 16t + 16), columns [128c, 128c + 128), in (e, t, c) order.
-// Codes: 1 KB, lane l's 16 bytes at 16 l = row 16t + l % 16, columns
-// 128c + 32 (l / 16) .. +32. Scales: 128 bytes, row 16t + r's eight block
-// scales of the 128 columns at 8 r. One thread moves one lane's 16 bytes and
-// (lanes 0..15) its row's 8 scale bytes.
+// Codes: 64 lanes x CB bytes (CB = 16 for e2m1, 12 for an E1M1 chunk), lane
+// l's at CB l = row 16t + l % 16, columns 128c + 32 (l / 16) .. +32. Scales:
+// 128 bytes, row 16t + r's eight block scales of the 128 columns at 8 r. One
+// thread moves one lane's code bytes and (lanes 0..15) its row's 8 scale bytes.
+template <int BITS>
 __global__ __launch_bounds__(256) void k_pack_fp4_decode(const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales,
                                                          int64_t n_lanes, int K,
                                                          uint8_t* __restrict__ pcodes,
                                                          uint8_t* __restrict__ pscales) {
+  constexpr int CB = BITS == 4 ? 16 : 12;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n_lanes) return;
   const int l = (int)(i & 63);
   const int64_t blk = i >> 6;
   const int c = (int)(blk % (K / 128));
   const int64_t row = (blk / (K / 128)) * 16 + (l & 15);  // e * N + 16 t + l % 16
-  *(uint4*)(pcodes + i * 16) = *(const uint4*)(codes + row * (K / 2) + c * 64 + (l >> 4) * 16);
+  const uint8_t* src = codes + row * ((int64_t)K / 32 * CB) + (c * 4 + (l >> 4)) * CB;
+  if (BITS == 4)
+    *(uint4*)(pcodes + i * CB) = *(const uint4*)src;
+  else
+    *(uint3*)(pcodes + i * CB) = *(const uint3*)src;
   if (l < 16)
     *(uint2*)(pscales + blk * 128 + l * 8) = *(const uint2*)(scales + row * (K / 16) + c * 8);
 }
@@ -773,11 +799,17 @@ __global__ __launch_bounds__(256) void k_pack_bf16_decode(const uint16_t* __rest
 }
 
 hipError_t launch_pack_fp4_decode(const uint8_t* codes, const uint8_t* scales, int count, int N,
-                                  int K, uint8_t* pcodes, uint8_t* pscales, hipStream_t stream) {
+                                  int K, int bits, uint8_t* pcodes, uint8_t* pscales,
+                                  hipStream_t stream) {
   const int64_t n_lanes = (int64_t)count * (N / 16) * (K / 128) * 64;
   if (n_lanes == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pack_fp4_decode, dim3((unsigned)((n_lanes + 255) / 256)), dim3(256), 0,
-                     stream, codes, scales, n_lanes, K, pcodes, pscales);
+  const dim3 grid((unsigned)((n_lanes + 255) / 256));
+  if (bits == 3)
+    hipLaunchKernelGGL(k_pack_fp4_decode<3>, grid, dim3(256), 0, stream, codes, scales, n_lanes,
+                       K, pcodes, pscales);
+  else
+    hipLaunchKernelGGL(k_pack_fp4_decode<4>, grid, dim3(256), 0, stream, codes, scales, n_lanes,
+                       K, pcodes, pscales);
   return hipGetLastError();
 }
 
@@ -804,24 +836,33 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
   });
   if (err != hipSuccess) return err;
   // 2. router logits + top-k + routing table, shared expert gate/up
-  err = with_nch(L / 256, [&](auto N) {
-    constexpr int n = decltype(N)::value;
+  const auto router = [&](auto N, auto B) {
+    constexpr int n = decltype(N)::value, bits = decltype(B)::value;
     const int nrb = (E + 15) / 16;
     const int nsh = a.n_shared ? (I / 16 + 1) / 2 : 0;
-    hipError_t e = ensure_lds((const void*)k_dec_router<n, n>, router_lds(kDecodeMaxT, L));
+    const auto fn = k_dec_router<n, n, bits>;
+    hipError_t e = ensure_lds((const void*)fn, router_lds(kDecodeMaxT, L));
     if (e == hipSuccess)
-      e = mk.launch(kStageRouter, k_dec_router<n, n>, dim3(nrb + nsh), block, router_lds(T, L), a);
+      e = mk.launch(kStageRouter, fn, dim3(nrb + nsh), block, router_lds(T, L), a);
     return e;
+  };
+  err = with_nch(L / 256, [&](auto N) {
+    return a.gateup_bits == 3 ? router(N, std::integral_constant<int, 3>{})
+                              : router(N, std::integral_constant<int, 4>{});
   });
   if (err != hipSuccess) return err;
   // 3. routed gate/up
-  err = with_nch(L / 256, [&](auto N) {
-    constexpr int n = decltype(N)::value;
+  const auto gateup = [&](auto N, auto B) {
+    constexpr int n = decltype(N)::value, bits = decltype(B)::value;
     const int nblk = (a.max_active * (I / 16) + 1) / 2;
-    hipError_t e = ensure_lds((const void*)k_dec_gateup<n>, gateup_lds(kDecodeMaxT, L));
-    if (e == hipSuccess)
-      e = mk.launch(kStageGateup, k_dec_gateup<n>, dim3(nblk), block, gateup_lds(T, L), a);
+    const auto fn = k_dec_gateup<n, bits>;
+    hipError_t e = ensure_lds((const void*)fn, gateup_lds(kDecodeMaxT, L));
+    if (e == hipSuccess) e = mk.launch(kStageGateup, fn, dim3(nblk), block, gateup_lds(T, L), a);
     return e;
+  };
+  err = with_nch(L / 256, [&](auto N) {
+    return a.gateup_bits == 3 ? gateup(N, std::integral_constant<int, 3>{})
+                              : gateup(N, std::integral_constant<int, 4>{});
   });
   if (err != hipSuccess) return err;
   // 4. down + combine

@@ -121,11 +121,17 @@ struct ALoader {
 // touches 32 rows) or packed (PK, BK = 64 only; see launch_pack_fp4): the 64
 // lanes' bytes of one step are contiguous, 1 KB of codes and 128 bytes of
 // scales per load instruction. The values loaded are the same.
-template <int BK, bool PK>
+//
+// BITS = 3 reads 3-bit E1M1 codes (BK = 64): a lane's 32 weights of a step
+// are one 12-byte chunk (a 2-bit magnitude plane and a sign plane), widened
+// to e2m1 nibbles right before the dequantisation.
+template <int BK, bool PK, int BITS = 4>
 struct Fp4B {
   static_assert(!PK || BK == 64, "the packed layout has 64-wide K steps");
-  static constexpr int kWords = BK / 16;              // 32-bit code words per lane per step
-  static constexpr int kCodeStep = PK ? 1024 : BK / 2;  // bytes between a lane's steps
+  static_assert(BITS == 4 || (BITS == 3 && BK == 64), "3-bit codes need 64-wide K steps");
+  static constexpr int kWords = BITS == 4 ? BK / 16 : 3;  // code words per lane per step
+  static constexpr int kCodeStep =                        // bytes between a lane's steps
+      PK ? 64 * 4 * kWords : (BITS == 4 ? BK / 2 : 24);
   static constexpr int kScaleStep = PK ? 128 : BK / 16;
   struct Set {
     uint32_t c[2][kWords];
@@ -142,7 +148,11 @@ struct Fp4B {
   __device__ __forceinline__ void issue(int kt, Set& st) const {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      if (BK == 64) {
+      if (BITS == 3) {
+        const uint3 v = *(const uint3*)(cp[j] + kt * kCodeStep);
+        st.c[j][0] = v.x; st.c[j][1] = v.y; st.c[j][2] = v.z;
+        st.s[j] = *(const uint16_t*)(sp[j] + kt * kScaleStep);
+      } else if (BK == 64) {
         const uint4 v = *(const uint4*)(cp[j] + kt * kCodeStep);
         st.c[j][0] = v.x; st.c[j][1] = v.y; st.c[j][2] = v.z; st.c[j][3] = v.w;
         st.s[j] = *(const uint16_t*)(sp[j] + kt * kScaleStep);
@@ -156,6 +166,11 @@ struct Fp4B {
   // chunk ks (8 weights) of sub-tile j; scale block ks / 2 of the lane's half
   __device__ __forceinline__ bf16x8 frag(const Set& st, int j, int ks) const {
     const float sc = e4m3_to_f32((st.s[j] >> (8 * (ks >> 1))) & 0xFFu);
+    if (BITS == 3) {  // elements 8ks .. 8ks+7 of the chunk
+      const uint32_t m16 = st.c[j][ks >> 1] >> (16 * (ks & 1));
+      const uint32_t s8 = st.c[j][2] >> (8 * ks);
+      return dequant8(e1m1x8_to_e2m1(m16, s8), sc);
+    }
     return dequant8(st.c[j][ks], sc);
   }
 };
@@ -446,19 +461,20 @@ __device__ __forceinline__ const Fp4Set& pick_set(const ExpertsView& ex, int g, 
 // starts at weight row nb of matrix le of the set m ([count][N][K]); the
 // lane's row is nb + weight_row(lane % 32). Sub-tiles past N read the last
 // one (their results are not stored).
-template <int BK, bool PK>
+template <int BK, bool PK, int BITS = 4>
 __device__ __forceinline__ void fp4_lane_ptrs(const Fp4Mat& m, int le, int nb, int N, int K,
                                               const uint8_t** c, const uint8_t** s) {
   const int lane = threadIdx.x & 63;
+  constexpr int kLaneBytes = BITS == 4 ? 16 : 12;  // a lane's codes of one 64-wide step
   if (PK) {
     const int st = min(nb, N - 32) / 32;
     const size_t blk = ((size_t)le * (N / 32) + st) * (K / 64);
-    *c = m.codes + blk * 1024 + lane * 16;
+    *c = m.codes + blk * 64 * kLaneBytes + lane * kLaneBytes;
     *s = m.scales + blk * 128 + lane * 2;
   } else {
     const size_t row = (size_t)le * N + min(nb + weight_row(lane & 31), N - 1);
     const int h = lane >> 5;
-    *c = m.codes + row * (K / 2) + h * (BK / 4);
+    *c = m.codes + row * ((size_t)K * BITS / 8) + h * (BITS == 4 ? BK / 4 : 12);
     *s = m.scales + row * (K / 16) + h * (BK / 32);
   }
 }
@@ -470,6 +486,9 @@ __device__ __forceinline__ void fp4_lane_ptrs(const Fp4Mat& m, int le, int nb, i
 // 32t + weight_row(L % 32), columns 64kt + 32(L / 32) .. +32, bytes in the
 // plain order. Its scales are 64 lanes x 2 bytes: the two block scales of
 // the same 32 columns. One thread moves one lane's 16 + 2 bytes.
+// With 3-bit E1M1 codes (BITS = 3) a lane's codes are its 12-byte chunk
+// (chunk 2s + L / 32 of the row) at 12 L of a 768-byte block.
+template <int BITS>
 __global__ __launch_bounds__(256) void k_pack_fp4(const uint8_t* __restrict__ codes,
                                                   const uint8_t* __restrict__ scales,
                                                   int64_t n_lanes, int N, int K,
@@ -483,7 +502,11 @@ __global__ __launch_bounds__(256) void k_pack_fp4(const uint8_t* __restrict__ co
   const int64_t et = blk / (K / 64);        // e * (N / 32) + t
   const int64_t row = et * 32 + weight_row(L & 31);  // e * N + 32 t + ...
   const int h = L >> 5;
-  *(uint4*)(pcodes + i * 16) = *(const uint4*)(codes + row * (K / 2) + kt * 32 + h * 16);
+  if (BITS == 4)
+    *(uint4*)(pcodes + i * 16) = *(const uint4*)(codes + row * (K / 2) + kt * 32 + h * 16);
+  else
+    *(uint3*)(pcodes + i * 12) =
+        *(const uint3*)(codes + row * ((int64_t)K * 3 / 8) + (2 * kt + h) * 12);
   *(uint16_t*)(pscales + i * 2) = *(const uint16_t*)(scales + row * (K / 16) + kt * 4 + h * 2);
 }
 
@@ -513,11 +536,16 @@ hipError_t launch_pack_bf16(const uint16_t* w, int N, int K, uint16_t* pw, hipSt
 }
 
 hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int count, int N, int K,
-                           uint8_t* pcodes, uint8_t* pscales, hipStream_t stream) {
+                           int bits, uint8_t* pcodes, uint8_t* pscales, hipStream_t stream) {
   const int64_t n_lanes = (int64_t)count * (N / 32) * (K / 64) * 64;
   if (n_lanes == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)((n_lanes + 255) / 256)), dim3(256), 0, stream,
-                     codes, scales, n_lanes, N, K, pcodes, pscales);
+  const dim3 grid((unsigned)((n_lanes + 255) / 256));
+  if (bits == 3)
+    hipLaunchKernelGGL(k_pack_fp4<3>, grid, dim3(256), 0, stream, codes, scales, n_lanes, N, K,
+                       pcodes, pscales);
+  else
+    hipLaunchKernelGGL(k_pack_fp4<4>, grid, dim3(256), 0, stream, codes, scales, n_lanes, N, K,
+                       pcodes, pscales);
   return hipGetLastError();
 }
 
@@ -535,7 +563,7 @@ __device__ __forceinline__ int row_blocks(const TileWork& tw) {
 // Gate/up: a tile covers 128 output columns of the SwiGLU width; wave w
 // takes columns n0 + 32w .. +32 as sub-tile 0 (gate rows) and sub-tile 1 (up
 // rows), so SiLU*mul pairs them in registers.
-template <int BK, bool PK, int NI>
+template <int BK, bool PK, int BITS, int NI>
 __device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, int ldh,
                                             const RouteView& rv, const ExpertsView& ex,
                                             uint16_t* __restrict__ act, int inter, int latent,
@@ -551,11 +579,11 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, i
     const int tok = row < P ? rv.perm[row] / rv.top_k : row - P;
     return hcat + (size_t)tok * ldh;
   });
-  Fp4B<BK, PK> bl;
+  Fp4B<BK, PK, BITS> bl;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const uint8_t *c, *s;
-    fp4_lane_ptrs<BK, PK>(j ? set.up : set.gate, le, nb, inter, latent, &c, &s);
+    fp4_lane_ptrs<BK, PK, BITS>(j ? set.up : set.gate, le, nb, inter, latent, &c, &s);
     bl.set(j, c, s);
   }
   f32x16 acc[NI][2];
@@ -584,7 +612,7 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, i
   }
 }
 
-template <int BK, bool PK>
+template <int BK, bool PK, int BITS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_gateup(
     const uint16_t* __restrict__ hcat, int ldh, RouteView rv, ExpertsView ex,
     uint16_t* __restrict__ act, int inter, int latent) {
@@ -595,9 +623,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (!tile_work(rv, tile / nt, &tw)) return;
   const int n0 = (tile % nt) * (kBN / 2);
   const int nb = row_blocks(tw);
-  if (nb == 1) gateup_tile<BK, PK, 1>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
-  else if (nb == 2) gateup_tile<BK, PK, 2>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
-  else gateup_tile<BK, PK, 4>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
+  if (nb == 1) gateup_tile<BK, PK, BITS, 1>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
+  else if (nb == 2) gateup_tile<BK, PK, BITS, 2>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
+  else gateup_tile<BK, PK, BITS, 4>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
 }
 
 template <int BK, bool PK, int NI>
@@ -686,16 +714,21 @@ hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& 
                                 const ExpertsView& ex, uint16_t* act, int inter, int latent,
                                 int max_mtiles, hipStream_t stream) {
   dim3 grid(max_mtiles * ((inter + kBN / 2 - 1) / (kBN / 2))), block(kThreads);
-  if (ex.packed && latent % 64 != 0) return hipErrorInvalidValue;
-  if (ex.packed)
-    hipLaunchKernelGGL((k_expert_gateup<64, true>), grid, block, 0, stream, hcat, ldh, rv, ex, act,
-                       inter, latent);
-  else if (latent % 64 == 0)
-    hipLaunchKernelGGL((k_expert_gateup<64, false>), grid, block, 0, stream, hcat, ldh, rv, ex,
-                       act, inter, latent);
-  else
-    hipLaunchKernelGGL((k_expert_gateup<32, false>), grid, block, 0, stream, hcat, ldh, rv, ex,
-                       act, inter, latent);
+  if ((ex.packed || ex.gateup_bits == 3) && latent % 64 != 0) return hipErrorInvalidValue;
+#define MOE_LAUNCH_GU(BKV, PKV, BITSV)                                                           \
+  hipLaunchKernelGGL((k_expert_gateup<BKV, PKV, BITSV>), grid, block, 0, stream, hcat, ldh, rv, ex, \
+                     act, inter, latent)
+  if (ex.gateup_bits == 3) {
+    if (ex.packed) MOE_LAUNCH_GU(64, true, 3);
+    else MOE_LAUNCH_GU(64, false, 3);
+  } else if (ex.packed) {
+    MOE_LAUNCH_GU(64, true, 4);
+  } else if (latent % 64 == 0) {
+    MOE_LAUNCH_GU(64, false, 4);
+  } else {
+    MOE_LAUNCH_GU(32, false, 4);
+  }
+#undef MOE_LAUNCH_GU
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@ struct ExpertsView {
   Fp4Set routed;
   Fp4Set shared;
   bool packed;
+  int gateup_bits;  // 4: e2m1 gate/up codes; 3: E1M1 (down is e2m1 either way)
 };
 
 // Routing as the grouped GEMMs consume it. Rows of the permuted activation
@@ -65,8 +66,9 @@ hipError_t launch_expert_down(const uint16_t* act, const RouteView& rv, const Ex
 // fp4 matrix set [count][N][K] (N % 32 == 0, K % 64 == 0) -> the packed
 // layout the grouped kernels load with one 1 KB (codes) and one 128-byte
 // (scales) access per wave and K step; same byte counts as the plain layout.
+// bits: 4 (e2m1 codes) or 3 (E1M1 codes, 12-byte chunks per 32 elements).
 hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int count, int N, int K,
-                           uint8_t* pcodes, uint8_t* pscales, hipStream_t stream);
+                           int bits, uint8_t* pcodes, uint8_t* pscales, hipStream_t stream);
 // bf16 matrix [N][K] (N % 32 == 0, K % 64 == 0) -> the packed layout the
 // dense kernels load with one contiguous 1 KB access per wave.
 hipError_t launch_pack_bf16(const uint16_t* w, int N, int K, uint16_t* pw, hipStream_t stream);
@@ -135,6 +137,7 @@ struct DecodeArgs {
   Fp4Mat sh_gate, sh_up, sh_down;  // shared expert (count 1)
   int hidden, latent, inter, n_experts, top_k, n_shared, T;
   bool packed;  // D, U, R and the expert sets above are in the decode-packed layouts
+  int gateup_bits;  // 4: e2m1 gate/up codes (routed and shared); 3: E1M1
   // scratch (workspace)
   uint16_t* hhi;       // [T][latent]
   uint16_t* hlo;       // [T][latent]
@@ -168,7 +171,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
 // Decode-packed layouts (decode.hip): fp4 set [count][N][K] with N % 16 == 0,
 // K % 128 == 0; bf16 [N][K] with N % 16 == 0, K % 32 == 0.
 hipError_t launch_pack_fp4_decode(const uint8_t* codes, const uint8_t* scales, int count, int N,
-                                  int K, uint8_t* pcodes, uint8_t* pscales, hipStream_t stream);
+                                  int K, int bits, uint8_t* pcodes, uint8_t* pscales,
+                                  hipStream_t stream);
 hipError_t launch_pack_bf16_decode(const uint16_t* w, int N, int K, uint16_t* pw,
                                    hipStream_t stream);
 

@@ -131,6 +131,26 @@ int check_set(const moe_fp4_experts* s, const char* name, int count) {
   return 0;
 }
 
+// Element format of a matrix: 4 (e2m1; 0 means 4) or 3 (E1M1); -1 otherwise.
+int fmt_bits(const moe_fp4_matrix& m) {
+  const int b = m.bits == 0 ? 4 : m.bits;
+  return b == 3 || b == 4 ? b : -1;
+}
+
+// The gate/up format of an expert set (gate and up alike, down e2m1), or an
+// error return.
+int set_bits(const moe_fp4_experts* s, const char* name, int* bits) {
+  const int g = fmt_bits(s->gate), u = fmt_bits(s->up), dn = fmt_bits(s->down);
+  if (g < 0 || u < 0 || dn < 0)
+    return fail(MOE_LATENT_EUNSUPPORTED, "%s: bits must be 0, 3 or 4 (gate %d, up %d, down %d)",
+                name, s->gate.bits, s->up.bits, s->down.bits);
+  if (g != u || dn != 4)
+    return fail(MOE_LATENT_EUNSUPPORTED, "%s: gate and up need one format and down e2m1 "
+                                         "(gate %d, up %d, down %d bits)", name, g, u, dn);
+  *bits = g;
+  return 0;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
   return pa < pb + nb && pb < pa + na;
@@ -153,7 +173,7 @@ moe::Fp4Set to_set(const moe_fp4_experts* s) {
 
 int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_t* D,
                 const uint16_t* U, const moe_router* router, const moe_fp4_experts* experts,
-                const moe_fp4_experts* shared, uint16_t* out, char* ws, const Layout& L,
+                const moe_fp4_experts* shared, int gu_bits, uint16_t* out, char* ws, const Layout& L,
                 moe_route_debug* dbg, const moe_latent_opts& o, hipStream_t st) {
   const int H = d.hidden, Lat = d.latent, E = d.n_experts, I = d.inter, k = d.top_k;
   const int P = T * k;
@@ -218,6 +238,7 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k};
   moe::ExpertsView ex{};
   ex.packed = gp && gp->experts;
+  ex.gateup_bits = gu_bits;
   ex.routed = to_set(ex.packed ? gp->experts : experts);
   if (d.n_shared) ex.shared = to_set(ex.packed ? gp->shared : shared);
   const int max_mtiles = (P + 127) / 128 + (E < P ? E : P) + d.n_shared * ((T + 127) / 128);
@@ -257,11 +278,12 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
 
 int run_decode(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_t* D,
                const uint16_t* U, const moe_router* router, const moe_fp4_experts* experts,
-               const moe_fp4_experts* shared, uint16_t* out, char* ws, const Layout& L,
+               const moe_fp4_experts* shared, int gu_bits, uint16_t* out, char* ws, const Layout& L,
                moe_route_debug* dbg, const moe_latent_opts& o, hipStream_t st) {
   moe::DecodeArgs a{};
   const moe_packed_weights* dp = o.decode_packed;
   a.packed = dp != nullptr;
+  a.gateup_bits = gu_bits;
   if (dp) {  // all members present (validated)
     D = (const uint16_t*)dp->D;
     U = (const uint16_t*)dp->U;
@@ -355,6 +377,8 @@ int moe_fp4_pack(const moe_fp4_matrix* src, int32_t count, int32_t N, int32_t K,
     return fail(MOE_LATENT_EINVAL, "src, its codes and scales, and the destinations must be non-NULL");
   if (count < 0 || N <= 0 || K <= 0)
     return fail(MOE_LATENT_EINVAL, "count must be >= 0 and N, K positive (%d, %d, %d)", count, N, K);
+  const int bits = fmt_bits(*src);
+  if (bits < 0) return fail(MOE_LATENT_EUNSUPPORTED, "src->bits must be 0, 3 or 4 (%d)", src->bits);
   const int nm = layout == MOE_LATENT_PACK_GROUPED ? 32 : 16;
   const int km = layout == MOE_LATENT_PACK_GROUPED ? 64 : 128;
   if (N % nm || K % km)
@@ -363,17 +387,18 @@ int moe_fp4_pack(const moe_fp4_matrix* src, int32_t count, int32_t N, int32_t K,
   if (!aligned(src->codes, 16) || !aligned(src->scales, 16) || !aligned(dst_codes, 16) ||
       !aligned(dst_scales, 16))
     return fail(MOE_LATENT_EINVAL, "codes and scales must be 16-byte aligned");
-  const size_t nc = (size_t)count * N * (K / 2), ns = (size_t)count * N * (K / 16);
+  const size_t nc = (size_t)count * N * (K / 32) * (bits == 4 ? 16 : 12);
+  const size_t ns = (size_t)count * N * (K / 16);
   if (overlaps(dst_codes, nc, src->codes, nc) || overlaps(dst_codes, nc, src->scales, ns) ||
       overlaps(dst_scales, ns, src->codes, nc) || overlaps(dst_scales, ns, src->scales, ns) ||
       overlaps(dst_codes, nc, dst_scales, ns))
     return fail(MOE_LATENT_EINVAL, "packed buffers overlap the source or each other");
   if (count == 0) return 0;
   if (layout == MOE_LATENT_PACK_GROUPED)
-    HIP_TRY(moe::launch_pack_fp4(src->codes, src->scales, count, N, K, dst_codes, dst_scales,
-                                 (hipStream_t)stream));
+    HIP_TRY(moe::launch_pack_fp4(src->codes, src->scales, count, N, K, bits, dst_codes,
+                                 dst_scales, (hipStream_t)stream));
   else
-    HIP_TRY(moe::launch_pack_fp4_decode(src->codes, src->scales, count, N, K, dst_codes,
+    HIP_TRY(moe::launch_pack_fp4_decode(src->codes, src->scales, count, N, K, bits, dst_codes,
                                         dst_scales, (hipStream_t)stream));
   return 0;
 }
@@ -471,6 +496,34 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
     if ((rc = check_set(dp->experts, "decode_packed->experts", d.n_experts))) return rc;
     if (d.n_shared && (rc = check_set(dp->shared, "decode_packed->shared", d.n_shared))) return rc;
   }
+  // one gate/up format over every expert set given (routed, shared, copies)
+  int gu_bits = 0;
+  {
+    const moe_fp4_experts* sets[6] = {experts, d.n_shared ? shared : nullptr};
+    const char* names[6] = {"experts", "shared", "grouped_packed->experts",
+                            "grouped_packed->shared", "decode_packed->experts",
+                            "decode_packed->shared"};
+    if (const moe_packed_weights* gp = o.grouped_packed) {
+      sets[2] = gp->experts;
+      sets[3] = d.n_shared ? gp->shared : nullptr;
+    }
+    if (const moe_packed_weights* dp = o.decode_packed) {
+      sets[4] = dp->experts;
+      sets[5] = d.n_shared ? dp->shared : nullptr;
+    }
+    for (int i = 0; i < 6; ++i) {
+      if (!sets[i]) continue;
+      int b = 0;
+      if ((rc = set_bits(sets[i], names[i], &b))) return rc;
+      if (gu_bits && b != gu_bits)
+        return fail(MOE_LATENT_EUNSUPPORTED, "%s has %d-bit gate/up, an earlier set %d-bit",
+                    names[i], b, gu_bits);
+      gu_bits = b;
+    }
+    if (gu_bits == 3 && d.latent % 64)
+      return fail(MOE_LATENT_EUNSUPPORTED, "E1M1 gate/up need latent a multiple of 64 (%d)",
+                  d.latent);
+  }
   if (o.residual) {
     if (!o.norm_weight) return fail(MOE_LATENT_EINVAL, "residual block needs norm_weight");
     if (!(o.norm_eps >= 0.0f)) return fail(MOE_LATENT_EINVAL, "norm_eps must be >= 0");
@@ -487,11 +540,11 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
 
   if (use_decode)
     return run_decode(d, (int)T, (const uint16_t*)x, (const uint16_t*)D, (const uint16_t*)U,
-                      router, experts, shared, (uint16_t*)out, (char*)workspace, L, debug, o,
-                      (hipStream_t)stream);
+                      router, experts, shared, gu_bits, (uint16_t*)out, (char*)workspace, L,
+                      debug, o, (hipStream_t)stream);
   return run_grouped(d, (int)T, (const uint16_t*)x, (const uint16_t*)D, (const uint16_t*)U,
-                     router, experts, shared, (uint16_t*)out, (char*)workspace, L, debug, o,
-                     (hipStream_t)stream);
+                     router, experts, shared, gu_bits, (uint16_t*)out, (char*)workspace, L, debug,
+                     o, (hipStream_t)stream);
 }
 
 int moe_latent_forward(const moe_latent_dims* dims, int64_t T, const void* x, const void* D,

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert lib.moe_latent_version() == 2
+    assert lib.moe_latent_version() == 3
 
 
 def _dims(**kw):
@@ -64,11 +64,15 @@ A = 1 << 20
 
 
 def _call(lib, dims, T=4, x=A, D=2 * A, U=3 * A, router=True, experts=True, shared=True,
-          out=5 * A, ws=64 * A, ws_bytes=1 << 40, opts=None, bias=None, count=None):
+          out=5 * A, ws=64 * A, ws_bytes=1 << 40, opts=None, bias=None, count=None,
+          bits=(0, 0, 0), sh_bits=(0, 0, 0)):
     r = lsm.CRouter(7 * A, bias) if router else None
-    m = lsm.CFp4Matrix(8 * A, 9 * A, 10 * A)
-    ex = lsm.CFp4Experts(m, m, m, dims.n_experts if count is None else count) if experts else None
-    sh = lsm.CFp4Experts(m, m, m, dims.n_shared) if shared else None
+
+    def mats(b):
+        return [lsm.CFp4Matrix(8 * A, 9 * A, 10 * A, x) for x in b]
+    ex = (lsm.CFp4Experts(*mats(bits), dims.n_experts if count is None else count)
+          if experts else None)
+    sh = lsm.CFp4Experts(*mats(sh_bits), dims.n_shared) if shared else None
     rc = lib.moe_latent_forward_ex(ctypes.byref(dims), T, x, D, U,
                                    ctypes.byref(r) if r else None,
                                    ctypes.byref(ex) if ex else None,
@@ -186,8 +190,8 @@ def test_decode_packed_validation(lib):
 
 
 def _pack(lib, src=True, count=4, N=64, K=128, layout=1, dc=20 * A, ds=21 * A, codes=8 * A,
-          scales=9 * A):
-    m = lsm.CFp4Matrix(codes, scales, 10 * A)
+          scales=9 * A, bits=0):
+    m = lsm.CFp4Matrix(codes, scales, 10 * A, bits)
     rc = lib.moe_fp4_pack(ctypes.byref(m) if src else None, count, N, K, layout, dc, ds, None)
     return rc, lib.moe_latent_last_error().decode()
 
@@ -206,6 +210,31 @@ def test_pack_validation(lib):
     assert _pack(lib, ds=20 * A + 64)[0] == lsm.EINVAL             # scales inside packed codes
     assert _pack(lib, count=0) == (0, "")                          # nothing to do
     assert _pack(lib, count=0, layout=2) == (0, "")
+    assert _pack(lib, bits=5)[0] == lsm.EUNSUPPORTED               # unknown element format
+    assert _pack(lib, bits=3, K=96)[0] == lsm.EUNSUPPORTED         # E1M1, grouped: K % 64
+    # E1M1 codes are 3/8 of a byte per element: 4 x 64 x 128 x 3/8 = 12 KiB
+    assert _pack(lib, bits=3, dc=8 * A + 12288 - 16)[0] == lsm.EINVAL  # overlaps by 16 bytes
+    assert _pack(lib, bits=3, count=0) == (0, "")
+
+
+def test_format_validation(lib):
+    """Expert element formats: gate and up alike (e2m1 or E1M1), down e2m1,
+    one gate/up format per layer, E1M1 with latent a multiple of 64. Only
+    combinations that fail are called (a valid one would launch kernels on
+    these fake addresses)."""
+    d = _dims()
+    for bits in ((5, 5, 0), (3, 4, 0), (4, 3, 4), (0, 0, 3), (3, 3, 3), (3, 0, 0)):
+        rc, msg = _call(lib, d, bits=bits, sh_bits=bits)
+        assert rc == lsm.EUNSUPPORTED and "bits" in msg, (bits, msg)
+    rc, msg = _call(lib, d, bits=(3, 3, 4), sh_bits=(0, 0, 0))   # routed E1M1, shared e2m1
+    assert rc == lsm.EUNSUPPORTED and "shared" in msg
+    rc, msg = _call(lib, _dims(latent=1760), bits=(3, 3, 4), sh_bits=(3, 3, 4))
+    assert rc == lsm.EUNSUPPORTED and "64" in msg
+    # a packed copy in another format than the plain sets
+    o = _opts_with(_pw())                                         # e2m1 copies
+    rc, msg = _call(lib, d, bits=(3, 3, 0), sh_bits=(3, 3, 0), opts=o)
+    assert rc == lsm.EUNSUPPORTED and "grouped_packed" in msg
+    assert _call(lib, d, T=0, bits=(3, 3, 4), sh_bits=(3, 3, 4))[0] == 0
 
 
 def test_bf16_pack_validation(lib):
