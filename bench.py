@@ -11,6 +11,8 @@ Infinity Cache: one layer call touches ~97 MB.
 
 Secondary (``prefill`` object): the same layer on a 16K-token prefill with a
 Zipf(1.1) router bias, in tokens/s and matrix-core utilisation.
+``mixed_record``: the same layer with the mixed 3/4-bit expert record (3-bit
+E1M1 gate/up, 4-bit down), at decode T = 4 and per stage at the 16K prefill.
 
 ``value`` comes from K back-to-back steps with no events inside the timed
 region. A second pass over the same K steps records HIP events on the launch
@@ -43,17 +45,20 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix cores
 
-REC_BYTES_CODES = lambda L, I: 3 * L * I // 2 + 3 * L * I // 16   # one expert, codes + block scales
+def rec_bytes(L, I, gateup_bits=4):
+    """One expert's codes + E4M3 block scales (gate/up codes of gateup_bits,
+    4-bit down codes), without the three fp32 matrix scales."""
+    return 2 * L * I * gateup_bits // 8 + L * I // 2 + 3 * L * I // 16
 
 
 def kernel_bytes(d, T, n_routed, decode=True):
     """Algorithmic HBM bytes of each kernel of one layer call: every weight
-    byte it must read once (4-bit codes + E4M3 block scales + fp32 matrix
-    scales for experts, bf16 for D / R / U) plus its activation inputs and
-    outputs."""
+    byte it must read once (4-bit codes, or 3-bit E1M1 gate/up codes in the
+    mixed record, + E4M3 block scales + fp32 matrix scales for experts, bf16
+    for D / R / U) plus its activation inputs and outputs."""
     L, H, E, I, k = d.latent, d.hidden, d.n_experts, d.inter, d.top_k
-    fp4 = lambda n_, k_: n_ * k_ // 2 + n_ * k_ // 16
-    gu = 2 * fp4(I, L) + 8           # gate + up of one expert
+    fp4 = lambda n_, k_, b=4: n_ * k_ * b // 8 + n_ * k_ // 16
+    gu = 2 * fp4(I, L, d.gateup_bits) + 8   # gate + up of one expert
     dn = fp4(L, I) + 4               # down of one expert
     sh = d.n_shared
     x = out = T * H * 2
@@ -92,9 +97,11 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--only", choices=["decode", "prefill", "copy", "stack"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "copy", "stack", "mixed"], default=None,
                    help="run one workload and print its object (profiling; 'stack' is the "
                         "48-block residual stack at T = 8, reported only this way)")
+    p.add_argument("--no-mixed", action="store_true",
+                   help="skip the mixed 3/4-bit expert record")
     p.add_argument("--stack-steps", type=int, default=20)
     p.add_argument("--stack-warmup", type=int, default=3)
     p.add_argument("--summarize-pmc", metavar="CSV", default=None,
@@ -220,7 +227,7 @@ def clone_layer(lsm, dl):
         if dataclasses.is_dataclass(v) and not isinstance(v, type):
             return type(v)(**{f.name: (c(getattr(v, f.name)) if f.name != "dims" else getattr(v, f.name))
                               for f in dataclasses.fields(v)})
-        return v.clone()
+        return v.clone() if hasattr(v, "clone") else v   # tensors; ints (bits) as they are
     return c(dl)
 
 
@@ -270,7 +277,7 @@ def bench_decode(args, torch, lsm, synth, dev):
         lsm.forward(xs[i], layers[i], out=outs[i], workspace=ws, debug=dbg, path=path)
         torch.cuda.synchronize()
         n_touched.append(int((dbg.counts > 0).sum().item()))
-    rec = REC_BYTES_CODES(d.latent, d.inter)
+    rec = rec_bytes(d.latent, d.inter, d.gateup_bits)
     dense = 2 * d.latent * d.hidden * 2 + d.n_experts * d.latent * 2 + 2 * T * d.hidden * 2
     layer_bytes = [(n + d.n_shared) * (rec + 12) + dense for n in n_touched]
     use_decode = path == lsm.PATH_DECODE or (path == lsm.PATH_AUTO and T <= lsm.DECODE_MAX_T)
@@ -450,6 +457,89 @@ def bench_prefill(args, torch, lsm, synth, dev):
     }
 
 
+def bench_mixed(args, torch, lsm, synth, dev):
+    """The mixed 3/4-bit expert record (E1M1 gate/up, e2m1 down) on the
+    145B-shaped layer: decode T = 4 over rotating decode-packed copies, timed
+    as the headline pass, and the 16K prefill's per-stage times on
+    grouped-packed weights (3 untimed calls with stage events)."""
+    cfg = synth.CONFIGS["decode145"]
+    d, T = synth.replace(cfg.dims, gateup_bits=3), cfg.T
+    t0 = time.time()
+    host = synth.make_layer(d, cfg.seed, cfg.bias, cfg.zipf_s)
+    log(f"[mixed] generated layer in {time.time() - t0:.1f}s")
+    base = lsm.DeviceLayer.from_host(host, dev)
+    del host
+    dec = lsm.DeviceLayer(**{**base.__dict__}).pack(grouped=False).drop_plain()
+    layers = [dec] + [clone_layer(lsm, dec) for _ in range(args.copies - 1)]
+    xs = [torch.from_numpy(synth.make_x(T, d.hidden, cfg.seed + i).view("int16"))
+          .view(torch.bfloat16).to(dev) for i in range(args.copies)]
+    outs = [torch.empty_like(x) for x in xs]
+    ws = lsm.alloc_workspace(d, T, dev)
+    n_touched = []
+    for i in range(args.copies):
+        dbg = lsm.RouteDebug.alloc(d, T, dev)
+        lsm.forward(xs[i], layers[i], out=outs[i], workspace=ws, debug=dbg)
+        torch.cuda.synchronize()
+        n_touched.append(int((dbg.counts > 0).sum().item()))
+    rec = rec_bytes(d.latent, d.inter, 3)
+    dense = 2 * d.latent * d.hidden * 2 + d.n_experts * d.latent * 2 + 2 * T * d.hidden * 2
+    layer_bytes = sum((n + d.n_shared) * (rec + 12) + dense for n in n_touched) / len(n_touched)
+    gu_bytes = kernel_bytes(d, T, n_touched[0])["gateup"]
+
+    def step(i, ev=None):
+        c = i % args.copies
+        lsm.forward(xs[c], layers[c], out=outs[c], workspace=ws, stage_events=ev)
+    names = ["dproj", "router", "gateup", "down", "uproj"]
+    st = stage_times(lsm, torch, lambda ev: step(0, ev), names)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(args.steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    log(f"[mixed] decode T={T}: {us:.1f} us/step; stage us: "
+        + ", ".join(f"{s}={v * 1e3:.1f}" for s, v in st.items()))
+    res = {
+        "record": "E1M1 gate/up + e2m1 down, E4M3 per-16 block scales, fp32 per matrix",
+        "expert_record_bytes": rec + 12,
+        "decode": {
+            "T": T, "us_per_step": round(us, 2), "tok_s": round(T / (us * 1e-6), 1),
+            "layer_bytes_per_step": layer_bytes,
+            "layer_GBps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
+            "stage_us_untimed_pass": {s: round(v * 1e3, 2) for s, v in st.items()},
+            "gateup_GBps_untimed_pass": round(gu_bytes / (st["gateup"] * 1e-3) / 1e9, 1),
+            "experts_touched_per_copy": n_touched, "copies": args.copies,
+        },
+    }
+    del layers, dec, xs, outs, ws
+    if not args.no_prefill:
+        pcfg = synth.CONFIGS["prefill145"]
+        Tp = pcfg.T
+        pre = base.pack(decode=False)
+        # routing bias as in the prefill workload (the layer above has none)
+        pre.bias = torch.from_numpy(synth.zipf_bias(d.n_experts, pcfg.zipf_s)).to(dev)
+        x = torch.from_numpy(synth.make_x(Tp, d.hidden, pcfg.seed).view("int16")).view(
+            torch.bfloat16).to(dev)
+        out = torch.empty_like(x)
+        ws = lsm.alloc_workspace(d, Tp, dev)
+        pn = ["dproj", "router", "topk", "route", "gateup", "down", "combine", "uproj"]
+        pst = stage_times(lsm, torch, lambda ev: lsm.forward(
+            x, pre, out=out, workspace=ws, path=lsm.PATH_GROUPED, stage_events=ev), pn, n=3)
+        rows = Tp * d.top_k + Tp * d.n_shared
+        gu_fl = 2.0 * rows * d.latent * 2 * d.inter
+        res["prefill_untimed"] = {
+            "T": Tp, "ms_per_call": round(sum(pst.values()), 4),
+            "stage_ms": {s: round(v, 4) for s, v in pst.items()},
+            "gateup_tflops": round(gu_fl / (pst["gateup"] * 1e-3) / 1e12, 1),
+        }
+        log(f"[mixed] prefill T={Tp}: " + ", ".join(f"{s}={v:.3f}" for s, v in pst.items()))
+    return res
+
+
 def bench_stack(args, torch, lsm, synth, dev):
     """48 residual blocks (RMSNorm + latent MoE) of 145B shapes, all resident
     (~48 GB of decode-packed weights, far beyond the Infinity Cache), T = 8
@@ -478,7 +568,7 @@ def bench_stack(args, torch, lsm, synth, dev):
         torch.cuda.synchronize()
         n_touched.append(int((dbg.counts > 0).sum().item()))
         cur = out
-    rec = REC_BYTES_CODES(d.latent, d.inter)
+    rec = rec_bytes(d.latent, d.inter, d.gateup_bits)
     per_block_dense = (2 * d.latent * d.hidden * 2 + d.n_experts * d.latent * 2 + d.n_experts * 4
                        + d.hidden * 4 + 2 * T * d.hidden * 2)
     step_bytes = sum((n + d.n_shared) * (rec + 12) + per_block_dense for n in n_touched)
@@ -588,6 +678,9 @@ def main():
     if args.only == "stack":
         print(json.dumps(bench_stack(args, torch, lsm, synth, dev)), flush=True)
         return
+    if args.only == "mixed":
+        print(json.dumps(bench_mixed(args, torch, lsm, synth, dev)), flush=True)
+        return
     dec = bench_decode(args, torch, lsm, synth, dev)
     if args.only == "decode":
         dec.pop("host"), dec.pop("x0")
@@ -611,6 +704,10 @@ def main():
         del host
         line["prefill"] = bench_prefill(args, torch, lsm, synth, dev)
         host = None
+        torch.cuda.empty_cache()
+    if not args.no_mixed:
+        line["mixed_record"] = bench_mixed(args, torch, lsm, synth, dev)
+        torch.cuda.empty_cache()
     if not args.no_cpu:
         if host is None:
             import synth as _s

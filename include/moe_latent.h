@@ -62,10 +62,12 @@
  *   exponent 0 subnormal), 1 mantissa bit, so magnitudes 0, 0.5, 1, 1.5 (the
  *   e2m1 values whose top exponent bit is clear), with the same E4M3 block
  *   scales and fp32 matrix scale as e2m1:
- *     codes  uint8 [count][N][K/32][12]   one 12-byte chunk per 32 elements:
- *            a little-endian u64 whose bits 2i, 2i+1 are element i's
- *            mantissa and exponent bits (mantissa low), then a little-endian
- *            u32 whose bit i is element i's sign
+ *     codes  uint8 [count][N][K/32][12]   one 12-byte chunk per 32 elements,
+ *            three little-endian u32 words w0, w1, w2: for g < 3, nibble p
+ *            of w_g (bits 4p .. 4p+3) is element 8g + p as an e2m1 code
+ *            (sign bit 3, exponent bit 1, mantissa bit 0); the nibble's
+ *            bit 2, never set by an E1M1 value, holds element 24 + p: its
+ *            mantissa in w0, its exponent in w1, its sign in w2
  *     scales, gscale as above.
  *   Packed copies (moe_fp4_pack / moe_bf16_pack) hold the same bytes
  *   reordered so that each wave's weight loads are contiguous 1 KB runs; a

@@ -67,23 +67,31 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float s) {
   return r;
 }
 
-// Eight 3-bit E1M1 codes (sign, exponent bit, mantissa bit; magnitudes 0,
-// 0.5, 1, 1.5) -> the eight e2m1 codes of the same values, in dequant8's
-// nibble order. m16 holds the 2-bit magnitude indices (element i at bits 2i,
-// 2i+1), s8 the signs (element i at bit i). An E1M1 value is the e2m1 value
-// with the top exponent bit clear, so nibble i = sign_i << 3 | index_i. The
-// indices and signs are spread to 4-bit slots by three shift/or/mask steps
-// each.
-__device__ __forceinline__ uint32_t e1m1x8_to_e2m1(uint32_t m16, uint32_t s8) {
-  uint32_t x = m16 & 0xFFFFu;
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  uint32_t y = s8 & 0xFFu;
-  y = (y | (y << 12)) & 0x000F000Fu;
-  y = (y | (y << 6)) & 0x03030303u;
-  y = (y | (y << 3)) & 0x11111111u;
-  return x | (y << 3);
+// Elements 8G .. 8G+7 of a 32-element E1M1 chunk (3-bit codes: sign,
+// exponent bit, mantissa bit; magnitudes 0, 0.5, 1, 1.5) as the eight e2m1
+// codes of the same values, in dequant8's nibble order. The chunk's words
+// w0, w1, w2 hold elements 0..23 as e2m1 nibbles already (an E1M1 value is
+// the e2m1 value whose high exponent bit, nibble bit 2, is clear); that
+// free bit of nibble p carries element 24 + p: its mantissa in w0, its
+// exponent in w1, its sign in w2. So groups 0..2 cost one mask and group 3
+// three shifts and masks.
+template <int G>
+__device__ __forceinline__ uint32_t e1m1_group_to_e2m1(uint32_t w0, uint32_t w1, uint32_t w2) {
+  static_assert(G >= 0 && G < 4, "four groups of eight per chunk");
+  if constexpr (G == 0) return w0 & 0xBBBBBBBBu;
+  else if constexpr (G == 1) return w1 & 0xBBBBBBBBu;
+  else if constexpr (G == 2) return w2 & 0xBBBBBBBBu;
+  else
+    return ((w0 >> 2) & 0x11111111u) | ((w1 >> 1) & 0x22222222u) | ((w2 << 1) & 0x88888888u);
+}
+__device__ __forceinline__ uint32_t e1m1_group_to_e2m1(uint32_t w0, uint32_t w1, uint32_t w2,
+                                                       int g) {
+  switch (g) {  // g is a compile-time constant after unrolling
+    case 0: return e1m1_group_to_e2m1<0>(w0, w1, w2);
+    case 1: return e1m1_group_to_e2m1<1>(w0, w1, w2);
+    case 2: return e1m1_group_to_e2m1<2>(w0, w1, w2);
+    default: return e1m1_group_to_e2m1<3>(w0, w1, w2);
+  }
 }
 
 // Eight e2m1 codes -> their plain values as bf16 (exact; no block scale).

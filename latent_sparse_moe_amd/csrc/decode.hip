@@ -24,7 +24,7 @@
 //
 // Matrix-core tiles are v_mfma_f32_16x16x32_bf16 with weight rows as the M
 // operand (16 rows) and tokens as the N operand (16 columns, T used; the rest
-// are zero). Lane l serves weight row l%16; its lane group g = l/16 takes
+// repeat token T - 1 and are never stored, so no operand load is conditional). Lane l serves weight row l%16; its lane group g = l/16 takes
 // every fourth chunk of the wave's K range (chunk c*4 + g at step c), so one
 // load instruction reads 64 contiguous bytes of each of 16 rows. K order
 // inside a dot product is free; the token operand is read with the same
@@ -104,6 +104,13 @@ __device__ __forceinline__ const uint16_t* bf16_lane(const uint16_t* w, bool pac
 
 // ------------------------------------------------------------------ wave tiles
 
+// Keeps every load above issued before anything below: without it the
+// scheduler may sink late weight chunks and the matrix scales under the
+// first products, and each such load then adds its own memory round trip to
+// the end of the kernel. Only where no staged value is live across it: the
+// register allocator spills such values around the barrier.
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 // NCH chunks of 8 bf16 per lane group: the wave's K range is [kb, kb + 32*NCH).
 // Chunk c of the lane sits at base + c * step (elements); see bf16_lane.
 template <int NCH>
@@ -113,12 +120,11 @@ struct Bf16Rows {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) w[c] = *(const uint4*)(base + c * step);
   }
-  // acc += W . act over the range; act = token row (LDS) or null (zero column)
+  // acc += W . act over the range; act = this lane's token row in LDS
   __device__ __forceinline__ void mma(const uint16_t* act, int kb, int g, f32x4& acc) const {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      bf16x8 b = {};
-      if (act) b = *(const bf16x8*)(act + kb + (c * 4 + g) * 8);
+      const bf16x8 b = *(const bf16x8*)(act + kb + (c * 4 + g) * 8);
       acc = mfma16x16x32(__builtin_bit_cast(bf16x8, w[c]), b, acc);
     }
   }
@@ -127,11 +133,8 @@ struct Bf16Rows {
                                        f32x4& acc) const {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      bf16x8 bh = {}, bl = {};
-      if (hi) {
-        bh = *(const bf16x8*)(hi + kb + (c * 4 + g) * 8);
-        bl = *(const bf16x8*)(lo + kb + (c * 4 + g) * 8);
-      }
+      const bf16x8 bh = *(const bf16x8*)(hi + kb + (c * 4 + g) * 8);
+      const bf16x8 bl = *(const bf16x8*)(lo + kb + (c * 4 + g) * 8);
       const bf16x8 a = __builtin_bit_cast(bf16x8, w[c]);
       acc = mfma16x16x32(a, bh, acc);
       acc = mfma16x16x32(a, bl, acc);
@@ -145,8 +148,8 @@ struct Bf16Rows {
 // contiguous: every lane of the row loads those eight bytes (16 distinct
 // addresses per instruction instead of 64 two-byte ones; measured 12.7 ->
 // 11.3 us for the routed gate/up weight stream) and keeps its two.
-// BITS = 3: E1M1 codes, a lane's chunk of 32 weights being 12 bytes (a 2-bit
-// magnitude plane and a sign plane), widened to e2m1 nibbles in mma.
+// BITS = 3: E1M1 codes, a lane's chunk of 32 weights being 12 bytes (three
+// words of e2m1-shaped nibbles, see e1m1_group_to_e2m1), widened in mma.
 template <int NCH, int BITS = 4>
 struct Fp4Rows {
   static constexpr int kW = BITS == 4 ? 4 : 3;  // code words per chunk
@@ -160,9 +163,9 @@ struct Fp4Rows {
     if constexpr (BITS == 4)
       return c[i][q];
     else
-      return e1m1x8_to_e2m1(c[i][q >> 1] >> (16 * (q & 1)), c[i][2] >> (8 * q));
+      return e1m1_group_to_e2m1(c[i][0], c[i][1], c[i][2], q);
   }
-  // token operand from a row in LDS, or null (zero column)
+  // token operand: this lane's token row in LDS
   __device__ __forceinline__ void mma(const uint16_t* act, int kb, int g, f32x4& acc) const {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -170,8 +173,7 @@ struct Fp4Rows {
       const float s0 = e4m3_to_f32(sp & 0xFFu), s1 = e4m3_to_f32((sp >> 8) & 0xFFu);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        bf16x8 b = {};
-        if (act) b = *(const bf16x8*)(act + kb + (i * 4 + g) * 32 + q * 8);
+        const bf16x8 b = *(const bf16x8*)(act + kb + (i * 4 + g) * 32 + q * 8);
         acc = mfma16x16x32(dequant8(codes8(i, q), q < 2 ? s0 : s1), b, acc);
       }
     }
@@ -189,9 +191,8 @@ __device__ __forceinline__ void Fp4Rows<NCH, BITS>::load(const Fp4Lane& l) {
       const uint3 v = *(const uint3*)(l.c + i * l.cstep);
       c[i][0] = v.x; c[i][1] = v.y; c[i][2] = v.z;
     }
+    s[i] = *(const uint2*)(l.s + i * l.sstep);
   }
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) s[i] = *(const uint2*)(l.s + i * l.sstep);
 }
 
 // Sum the per-wave partial tiles through LDS in wave order; lane l of wave 0
@@ -214,21 +215,21 @@ __device__ __forceinline__ f32x4 reduce_waves(f32x4 acc, float* red /*[8][64][4]
 template <int NV>
 struct RowStage {
   uint4 v[NV];
-  // count is a multiple of 8 and >= 8; out-of-range slots re-read the last
-  // vector (never stored), which keeps the loads unconditional
+  // count is a multiple of 8 and >= 8. Out-of-range slots re-read the last
+  // vector and store it back to its own place (the same bytes the in-range
+  // slot writes there). Both halves stay unconditional: a store under a
+  // branch lets the compiler sink its load into the branch, which turns NV
+  // loads in flight into NV round trips one after another.
   __device__ __forceinline__ void load(const uint16_t* src, int count) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int i = min((int)(threadIdx.x + j * kDecThreads) * 8, count - 8);
-      v[j] = *(const uint4*)(src + i);
-    }
+    for (int j = 0; j < NV; ++j) v[j] = *(const uint4*)(src + slot(j, count));
   }
   __device__ __forceinline__ void store(uint16_t* dst, int count) const {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int i = (threadIdx.x + j * kDecThreads) * 8;
-      if (i < count) *(uint4*)(dst + i) = v[j];
-    }
+    for (int j = 0; j < NV; ++j) *(uint4*)(dst + slot(j, count)) = v[j];
+  }
+  static __device__ __forceinline__ int slot(int j, int count) {
+    return min((int)(threadIdx.x + j * kDecThreads) * 8, count - 8);
   }
 };
 
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_dproj(DecodeArgs a) {
   }
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  wr.mma(t < T ? xs + t * H : nullptr, kb, g, acc);
+  wr.mma(xs + min(t, T - 1) * H, kb, g, acc);  // token columns >= T are not stored
   const f32x4 tot = reduce_waves(acc, red);
   if (wave == 0 && t < T) {
 #pragma unroll
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) bias[r] = a.bias[min(e0 + g * 4 + r, E - 1)];
     }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    wr.mma2(t < T ? hi + t * L : nullptr, t < T ? lo + t * L : nullptr, kb, g, acc);
+    wr.mma2(hi + min(t, T - 1) * L, lo + min(t, T - 1) * L, kb, g, acc);
     const f32x4 tot = reduce_waves(acc, red);
     if (wave == 0 && t < T) {
 #pragma unroll
@@ -547,12 +548,11 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
   RowStage<(NCH_H + 1) / 2> st;  // T x latent, latent = 256 NCH_H
   st.load(a.hhi, T * L);
   GateUpTask<NCH_H, BITS> task;
-  if (busy) task.load(a.sh_gate, a.sh_up, a.packed, 0, I, L, n0, wave, lane);
   const float gsg = a.sh_gate.gscale[0], gsu = a.sh_up.gscale[0];
+  task.load(a.sh_gate, a.sh_up, a.packed, 0, I, L, n0, wave, lane);  // idle tiles: rows 0..15
   st.store(hi, T * L);
   __syncthreads();
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (busy) acc = task.mma(t < T ? hi + t * L : nullptr, L, wave, lane);
+  const f32x4 acc = task.mma(hi + min(t, T - 1) * L, L, wave, lane);
   finish_gateup(acc, red, busy, gsg, gsu, a.act, I, T, n0);
 }
 
@@ -586,10 +586,12 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   st.store(hi, T * L);
   __syncthreads();
   GateUpTask<NCH_H, BITS> task;
-  if (busy) task.load(a.gate, a.up, a.packed, e, I, L, n0, wave, lane);
+  // unconditional: an idle tile reads expert 0's rows 0..15 (in range) and
+  // stores nothing, which keeps the loads and their uses in one block
   const float gsg = a.gate.gscale[e], gsu = a.up.gscale[e];
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (busy) acc = task.mma(t < T ? hi + t * L : nullptr, L, wave, lane);
+  task.load(a.gate, a.up, a.packed, e, I, L, n0, wave, lane);
+  issue_fence();
+  const f32x4 acc = task.mma(hi + min(t, T - 1) * L, L, wave, lane);
   finish_gateup(acc, red, busy, gsg, gsu,
                 a.act + (size_t)(1 + (busy ? tile / tiles : 0)) * T * I, I, T, n0);
 }
@@ -618,12 +620,12 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_down(DecodeArgs a) {
   st.load(a.act + (size_t)s * T * I, T * I);
   const int row0 = rr * kDownRows + wave * 16;
   Fp4Rows<NCH_D> wd;
-  wd.load(fp4_lane(dm, a.packed, e, L, I, row0, 0));
   const float gs = gscale[e];
+  wd.load(fp4_lane(dm, a.packed, e, L, I, row0, 0));
   st.store(lds, T * I);
   __syncthreads();
   f32x4 y = {0.f, 0.f, 0.f, 0.f};
-  wd.mma(t < T ? lds + t * I : nullptr, 0, g, y);
+  wd.mma(lds + min(t, T - 1) * I, 0, g, y);
   if (t < T) {
     const float wt = w_guess * gs;
 #pragma unroll
@@ -684,7 +686,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
   st.store(zs, T * L);
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  wr.mma(t < T ? zs + t * L : nullptr, kb, g, acc);
+  wr.mma(zs + min(t, T - 1) * L, kb, g, acc);
   const f32x4 tot = reduce_waves(acc, red);
   if (wave == 0 && t < T) {
 #pragma unroll

@@ -123,8 +123,8 @@ struct ALoader {
 // scales per load instruction. The values loaded are the same.
 //
 // BITS = 3 reads 3-bit E1M1 codes (BK = 64): a lane's 32 weights of a step
-// are one 12-byte chunk (a 2-bit magnitude plane and a sign plane), widened
-// to e2m1 nibbles right before the dequantisation.
+// are one 12-byte chunk (three words of e2m1-shaped nibbles, see
+// e1m1_group_to_e2m1), widened right before the dequantisation.
 template <int BK, bool PK, int BITS = 4>
 struct Fp4B {
   static_assert(!PK || BK == 64, "the packed layout has 64-wide K steps");
@@ -166,11 +166,8 @@ struct Fp4B {
   // chunk ks (8 weights) of sub-tile j; scale block ks / 2 of the lane's half
   __device__ __forceinline__ bf16x8 frag(const Set& st, int j, int ks) const {
     const float sc = e4m3_to_f32((st.s[j] >> (8 * (ks >> 1))) & 0xFFu);
-    if (BITS == 3) {  // elements 8ks .. 8ks+7 of the chunk
-      const uint32_t m16 = st.c[j][ks >> 1] >> (16 * (ks & 1));
-      const uint32_t s8 = st.c[j][2] >> (8 * ks);
-      return dequant8(e1m1x8_to_e2m1(m16, s8), sc);
-    }
+    if (BITS == 3)  // elements 8ks .. 8ks+7 of the chunk
+      return dequant8(e1m1_group_to_e2m1(st.c[j][0], st.c[j][1], st.c[j][2], ks), sc);
     return dequant8(st.c[j][ks], sc);
   }
 };

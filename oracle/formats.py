@@ -2,7 +2,7 @@
 layouts (oracle; test infrastructure only).
 
 The pages name the expert format only as NVFP4, a 4-bit floating point
-format "trained natively at 4 bits" (yodev.dev article, section on what
+format the model was trained in natively (yodev.dev article, section on what
 Edge0-145B is; Hugging Face card header). They do not define it. The
 definitions below are the OCP ones:
 
@@ -14,7 +14,7 @@ definitions below are the OCP ones:
   field 0 is subnormal: magnitude = mantissa/8 * 2^-6.
 * bf16: the upper 16 bits of an IEEE binary32.
 
-The mixed 3/4-bit record: the card's Q3_K build is "only partly 3-bit" and
+The mixed 3/4-bit record: the card's Q3_K build is only partly 3-bit and
 its experts are fixed-size records (Hugging Face card "Edge0-145B . Q3_K",
 section "Architecture", the paragraph on the 1,630,720-byte expert record),
 but no page defines a 3-bit element format or its layout. The format below is
@@ -24,10 +24,14 @@ this repository's own design:
   exponent 0 is subnormal. Magnitudes 0, 0.5, 1, 1.5 (so each value is the
   e2m1 value of the same sign and the low two bits). Gate and up use it with
   the same E4M3 per-16 block scales and fp32 matrix scale; down stays e2m1.
-* Storage: per matrix row, one 12-byte chunk per 32 consecutive elements: a
-  little-endian 64-bit word whose bits 2i, 2i+1 are element i's exponent and
-  mantissa bits (the magnitude index), then a little-endian 32-bit word
-  whose bit i is element i's sign.
+* Storage: per matrix row, one 12-byte chunk per 32 consecutive elements,
+  read as three little-endian 32-bit words w0, w1, w2. Elements 0..23 of
+  the chunk are e2m1 codes of their value: element 8g + p (g < 3) is nibble
+  p of w_g (bits 4p .. 4p+3: sign at bit 3, exponent at bit 1, mantissa at
+  bit 0). The nibbles' bit 2, the e2m1 high exponent bit that E1M1 never
+  sets, holds element 24 + p: its mantissa at bit 4p+2 of w0, its exponent
+  there in w1, its sign there in w2. (A decoder turns any group of eight
+  into e2m1 nibbles with a few shifts and masks.)
 """
 from __future__ import annotations
 
@@ -86,20 +90,22 @@ def e1m1_value(code) -> np.ndarray:
 
 def unpack_e1m1(codes: np.ndarray) -> np.ndarray:
     """[..., n, 3k/8] chunked bytes -> [..., n, k] 3-bit codes (sign << 2 |
-    magnitude index), from the 12-byte chunks described above."""
+    exponent << 1 | mantissa), from the 12-byte chunks described above."""
     codes = np.asarray(codes, dtype=np.uint8)
     lead, nb = codes.shape[:-1], codes.shape[-1]
-    ch = codes.reshape(lead + (nb // 12, 12)).astype(np.uint64)
-    mag_word = np.zeros(lead + (nb // 12,), dtype=np.uint64)
-    sign_word = np.zeros(lead + (nb // 12,), dtype=np.uint64)
-    for b in range(8):
-        mag_word |= ch[..., b] << np.uint64(8 * b)
-    for b in range(4):
-        sign_word |= ch[..., 8 + b] << np.uint64(8 * b)
-    i = np.arange(32, dtype=np.uint64)
-    mag = (mag_word[..., None] >> (np.uint64(2) * i)) & np.uint64(3)
-    sgn = (sign_word[..., None] >> i) & np.uint64(1)
-    out = (sgn << np.uint64(2)) | mag
+    w = codes.reshape(lead + (nb // 12, 3, 4)).astype(np.uint32)
+    w = w[..., 0] | (w[..., 1] << 8) | (w[..., 2] << 16) | (w[..., 3] << 24)  # [..., c, 3]
+    p = np.arange(8, dtype=np.uint32)
+
+    def bit(word, b):  # bit b of nibble p of a word, for p = 0..7
+        return (word[..., None] >> (np.uint32(4) * p + np.uint32(b))) & np.uint32(1)
+
+    groups = []
+    for g in range(3):                     # elements 8g + p: e2m1 nibbles
+        wg = w[..., g]
+        groups.append((bit(wg, 3) << 2) | (bit(wg, 1) << 1) | bit(wg, 0))
+    groups.append((bit(w[..., 2], 2) << 2) | (bit(w[..., 1], 2) << 1) | bit(w[..., 0], 2))
+    out = np.stack(groups, axis=-2)        # [..., c, 4, 8]
     return out.reshape(lead + (nb // 12 * 32,)).astype(np.uint8)
 
 

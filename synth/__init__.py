@@ -17,9 +17,10 @@ Recipe (every stream is independent, so any tensor can be drawn alone):
 * With ``Dims.gateup_bits = 3`` (the mixed 3/4-bit record) gate and up use
   3-bit E1M1 codes instead (magnitudes 0, 0.5, 1, 1.5; 6 replaced by 1.5 in
   the recipe above); down stays e2m1. Codes are stored per row as K/32
-  chunks of 12 bytes: a 64-bit little-endian word of 2-bit magnitude indices
-  (element i at bits 2i, 2i+1), then a 32-bit word of signs (element i at
-  bit i).
+  chunks of 12 bytes, three little-endian 32-bit words w0, w1, w2: for
+  g < 3, nibble p of w_g is element 8g + p as an e2m1 code (sign bit 3,
+  exponent bit 1, mantissa bit 0) whose bit 2 carries one bit of element
+  24 + p (mantissa in w0, exponent in w1, sign in w2).
 * Router bias: zero, or the log of an unnormalised Zipf(s) prior,
   ``b_e = -s * ln(e + 1)`` ("hot experts").
 """

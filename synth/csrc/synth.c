@@ -198,9 +198,12 @@ static inline uint8_t e1m1_encode_rne(float v) {
 /* Quantise one [N][K] matrix to E1M1 codes with E4M3 per-16 block scales and
  * an fp32 matrix scale (the recipe of synth_quantize_fp4 with 1.5 as the
  * largest code magnitude). Codes: per row, K/32 chunks of 12 bytes, chunk c
- * holding elements 32c .. 32c+31: bytes 0..7 a little-endian 64-bit word with
- * element i's magnitude index at bits 2i, 2i+1; bytes 8..11 a 32-bit word
- * with element i's sign at bit i. */
+ * holding elements 32c .. 32c+31 as three little-endian 32-bit words w0, w1,
+ * w2. For g = 0, 1, 2, nibble p of w_g (bits 4p .. 4p+3) is element 8g + p as
+ * an e2m1 code: sign at bit 3, exponent at bit 1, mantissa at bit 0; its
+ * bit 2 (the e2m1 high exponent bit, always clear here) carries one bit of
+ * element 24 + p instead: the mantissa in w0, the exponent in w1, the sign
+ * in w2. */
 void synth_quantize_e1m1(const float *w, int64_t N, int64_t K, uint8_t *codes,
                          uint8_t *scales, float *gscale_out) {
   float amax = 0.0f;
@@ -214,8 +217,7 @@ void synth_quantize_e1m1(const float *w, int64_t N, int64_t K, uint8_t *codes,
   for (int64_t n = 0; n < N; ++n) {
     const float *row = w + n * K;
     for (int64_t c = 0; c < K / 32; ++c) {
-      uint64_t mag = 0;
-      uint32_t sgn = 0;
+      uint32_t word[3] = {0, 0, 0};
       for (int h = 0; h < 2; ++h) {
         const int64_t b = 2 * c + h;
         const float *blk = row + b * 16;
@@ -229,14 +231,20 @@ void synth_quantize_e1m1(const float *w, int64_t N, int64_t K, uint8_t *codes,
         float denom = e4m3_value(s) * gscale;
         for (int j = 0; j < 16; ++j) {
           uint8_t q = denom > 0.0f ? e1m1_encode_rne(blk[j] / denom) : 0;
-          const int i = 16 * h + j;
-          mag |= (uint64_t)(q & 3) << (2 * i);
-          sgn |= (uint32_t)((q >> 2) & 1) << i;
+          const int i = 16 * h + j, grp = i / 8, pos = i % 8;
+          const uint32_t m = q & 1, e = (q >> 1) & 1, sg = (q >> 2) & 1;
+          if (grp < 3) {  /* nibble pos of word grp, as an e2m1 code (bit 2 clear) */
+            word[grp] |= (m << (4 * pos)) | (e << (4 * pos + 1)) | (sg << (4 * pos + 3));
+          } else {        /* bit 2 of nibble pos: mantissa in word 0, exponent 1, sign 2 */
+            word[0] |= m << (4 * pos + 2);
+            word[1] |= e << (4 * pos + 2);
+            word[2] |= sg << (4 * pos + 2);
+          }
         }
       }
       uint8_t *dst = codes + n * (K / 32) * 12 + c * 12;
-      for (int i = 0; i < 8; ++i) dst[i] = (uint8_t)(mag >> (8 * i));
-      for (int i = 0; i < 4; ++i) dst[8 + i] = (uint8_t)(sgn >> (8 * i));
+      for (int w = 0; w < 3; ++w)
+        for (int b = 0; b < 4; ++b) dst[4 * w + b] = (uint8_t)(word[w] >> (8 * b));
     }
   }
 }

@@ -42,9 +42,10 @@ E1M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5]
 
 
 def e1m1_matrix(codes: np.ndarray, scales: np.ndarray, gscale: float) -> torch.Tensor:
-    """[n][3k/8] 12-byte chunks (64-bit magnitude word, 32-bit sign word, both
-    little-endian) -> float64 [n][k], decoded element by element with
-    Python integers."""
+    """[n][3k/8] 12-byte chunks (three little-endian 32-bit words; elements
+    0..23 as e2m1 nibbles with bit 2 clear, element 24 + p spread over bit
+    4p + 2 of the three words: mantissa, exponent, sign) -> float64 [n][k],
+    decoded element by element with Python integers."""
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     n, nb = c.shape
     k = nb // 12 * 32
@@ -52,11 +53,17 @@ def e1m1_matrix(codes: np.ndarray, scales: np.ndarray, gscale: float) -> torch.T
     for r in range(n):
         row = bytes(c[r])
         for ch in range(nb // 12):
-            mag = int.from_bytes(row[12 * ch:12 * ch + 8], "little")
-            sgn = int.from_bytes(row[12 * ch + 8:12 * ch + 12], "little")
+            w = [int.from_bytes(row[12 * ch + 4 * j:12 * ch + 4 * j + 4], "little") for j in range(3)]
             for i in range(32):
-                v = E1M1_MAGNITUDES[(mag >> (2 * i)) & 3]
-                vals[r, 32 * ch + i] = -v if (sgn >> i) & 1 else v
+                if i < 24:
+                    nib = (w[i // 8] >> (4 * (i % 8))) & 0xF   # bit 2: element 24 + i % 8
+                    neg, idx = nib >> 3, nib & 3
+                else:
+                    sh = 4 * (i - 24) + 2
+                    neg = (w[2] >> sh) & 1
+                    idx = (((w[1] >> sh) & 1) << 1) | ((w[0] >> sh) & 1)
+                v = E1M1_MAGNITUDES[idx]
+                vals[r, 32 * ch + i] = -v if neg else v
     sc = e4m3_to_f64(scales).repeat_interleave(16, dim=1)
     return vals * sc * float(gscale)
 

@@ -96,19 +96,28 @@ def check_e1m1_table():
 
 
 def check_e1m1_chunk_layout():
-    """A hand-built 12-byte chunk: element i carries code i % 8, so its
-    magnitude index i % 4 sits at bits 2i of the first word and its sign
-    (i % 8) // 4 at bit i of the second."""
-    mag = sum((i % 4) << (2 * i) for i in range(32))
-    sgn = sum(((i % 8) // 4) << i for i in range(32))
-    chunk = np.frombuffer(mag.to_bytes(8, "little") + sgn.to_bytes(4, "little"), dtype=np.uint8)
-    codes = oracle.unpack_e1m1(np.concatenate([chunk, chunk[::-1]])[None])[0]
-    assert codes[:32].tolist() == [i % 8 for i in range(32)], codes[:32]
-    rev = np.frombuffer(bytes(chunk[::-1]), dtype=np.uint8)
-    m2 = int.from_bytes(bytes(rev[:8]), "little")
-    s2 = int.from_bytes(bytes(rev[8:12]), "little")
-    want2 = [(((s2 >> i) & 1) << 2) | ((m2 >> (2 * i)) & 3) for i in range(32)]
-    assert codes[32:].tolist() == want2
+    """A chunk worked out by hand. Codes (sign, exponent, mantissa):
+    elements 0..7 are 001 (+0.5), 8..15 are 110 (-1), 16..23 are 0..7 in
+    order, 24..31 are 101 (-0.5). As e2m1 nibbles: w0 = 0x11111111, w1 =
+    0xAAAAAAAA, w2 = 0xBA983210; then element 24 + p adds its mantissa (1)
+    at bit 4p+2 of w0 and its sign (1) there in w2, its exponent (0) leaves
+    w1 alone: w0 = 0x55555555, w1 = 0xAAAAAAAA, w2 = 0xFEDC7654."""
+    words = [0x55555555, 0xAAAAAAAA, 0xFEDC7654]
+    chunk = np.frombuffer(b"".join(v.to_bytes(4, "little") for v in words), dtype=np.uint8)
+    codes = oracle.unpack_e1m1(chunk[None])[0]
+    want = [1] * 8 + [6] * 8 + list(range(8)) + [5] * 8
+    assert codes.tolist() == want, codes
+    vals = oracle.e1m1_value(codes)
+    assert vals[0] == 0.5 and vals[8] == -1.0 and vals[23] == -1.5 and vals[31] == -0.5
+    # a second chunk in the same row decodes independently (byte-swapped words)
+    two = oracle.unpack_e1m1(np.concatenate([chunk, chunk[::-1]])[None])[0]
+    assert two[:32].tolist() == want
+    rev = [int.from_bytes(bytes(chunk[::-1][4 * j:4 * j + 4]), "little") for j in range(3)]
+    assert rev == [0x5476DCFE, 0xAAAAAAAA, 0x55555555]
+    # element 0 of the second chunk: nibble 0 of w0 = 0xE -> sign 1, exp 1, mant 0
+    # (bit 2 set: that bit is element 24's mantissa); element 24: bit 2 of the
+    # three words' nibble 0 = (1, 0, 1) -> mantissa 1, exponent 0, sign 1
+    assert two[32] == 0b110 and two[56] == 0b101
 
 
 def check_e1m1_dequant_vs_brute(seed=4):

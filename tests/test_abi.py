@@ -277,3 +277,21 @@ def test_plain_weights_needed_without_packed_copies(lib):
     full = _pw(D=30 * A, U=31 * A, R=32 * A)
     o = lsm.COpts(lsm.PATH_AUTO, 0, None, 0.0, None, None, ctypes.pointer(full))
     assert _call(lib, d, T=64, D=0, opts=o)[0] == lsm.EINVAL
+
+
+def test_bench_helpers_on_host_layers():
+    """bench.py's layer copy and byte counts work on a layer held in host
+    memory (no kernel runs): the copy keeps every field, including each
+    matrix's element format, and the mixed record's expert is smaller."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    d = synth.replace(synth.TINY, gateup_bits=3)
+    dl = lsm.DeviceLayer.from_host(synth.make_layer(d, 1), "cpu")
+    cp = bench.clone_layer(lsm, dl)
+    assert cp.experts.gate.bits == 3 and cp.experts.down.bits == 4
+    assert cp.experts.gate.codes.data_ptr() != dl.experts.gate.codes.data_ptr()
+    assert torch.equal(cp.experts.gate.codes, dl.experts.gate.codes)
+    # 145B expert: 3 x 1792 x 640 weights; codes + one E4M3 byte per 16
+    assert bench.rec_bytes(1792, 640, 4) == 3 * 1792 * 640 * 4 // 8 + 3 * 1792 * 640 // 16
+    assert bench.rec_bytes(1792, 640, 3) == 1648640   # 2 x 3-bit + 1 x 4-bit matrices

@@ -188,7 +188,7 @@ def _tiny_mixed_vs_brute():
 
 def test_e1m1_planes_swapped_caught(monkeypatch):
     orig = F.unpack_e1m1
-    def bad(codes):   # reads the sign word from the first 4 bytes instead of the last
+    def bad(codes):   # reads the chunk's three words in the wrong order
         c = np.asarray(codes, dtype=np.uint8)
         lead, nb = c.shape[:-1], c.shape[-1]
         ch = c.reshape(lead + (nb // 12, 12))
