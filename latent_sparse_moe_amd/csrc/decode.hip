@@ -54,6 +54,7 @@ namespace moe {
 constexpr int kDecThreads = 512;  // 8 waves
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kDownRows = kDecodeDownRows;
+constexpr int kTailBatch = 32;  // partial rows loaded per round trip by the down kernel's tail
 static_assert(kDownRows == kDecWaves * 16, "one 16-row tile per wave");
 
 #define AGENT __HIP_MEMORY_SCOPE_AGENT
@@ -651,16 +652,18 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_down(DecodeArgs a) {
     if (n >= L) continue;
     const float* src = a.zpart + (size_t)tt * L + n;
     float v = 0.f;
-    int ss = s0;
-    for (; ss + 8 <= n_act + 1; ss += 8) {  // eight loads in flight, summed in order
-      float p[8];
+    // kTailBatch loads in flight per round trip, summed in slot order; slots
+    // past n_act re-read slot n_act (in range) and are not summed
+    for (int ss = s0; ss <= n_act; ss += kTailBatch) {
+      float p[kTailBatch];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        p[j] = __hip_atomic_load(src + (ss + j) * step, __ATOMIC_RELAXED, AGENT);
+      for (int j = 0; j < kTailBatch; ++j)
+        p[j] = __hip_atomic_load(src + min(ss + j, n_act) * step, __ATOMIC_RELAXED, AGENT);
+      issue_fence();  // else the first sums are placed between the loads, each a round trip
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v += p[j];
+      for (int j = 0; j < kTailBatch; ++j)
+        if (ss + j <= n_act) v += p[j];
     }
-    for (; ss <= n_act; ++ss) v += __hip_atomic_load(src + ss * step, __ATOMIC_RELAXED, AGENT);
     a.z[(size_t)tt * L + n] = f32_to_bf16_bits(v);
   }
 }
