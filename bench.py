@@ -102,6 +102,8 @@ def parse():
                         "48-block residual stack at T = 8, reported only this way)")
     p.add_argument("--no-mixed", action="store_true",
                    help="skip the mixed 3/4-bit expert record")
+    p.add_argument("--no-family", action="store_true",
+                   help="skip the decode shape family (T = 1, 2, 3, 5, 8), e.g. under a profiler")
     p.add_argument("--stack-steps", type=int, default=20)
     p.add_argument("--stack-warmup", type=int, default=3)
     p.add_argument("--summarize-pmc", metavar="CSV", default=None,
@@ -346,7 +348,8 @@ def bench_decode(args, torch, lsm, synth, dev):
             "path": "decode" if use_decode else "grouped",
             "copies": args.copies,
             "step_us_with_events": {k: round(v, 2) for k, v in percentiles(step_us).items()},
-            "shape_family": decode_family(args, torch, lsm, synth, d, layers, path, dev),
+            "shape_family": (None if args.no_family else
+                             decode_family(args, torch, lsm, synth, d, layers, path, dev)),
         },
         "host": host, "x0": xs_host[0],
     }
