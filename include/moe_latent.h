@@ -200,9 +200,10 @@ typedef struct moe_route_debug {
 #define MOE_LATENT_DECODE_MAX_T 8
 
 /* Stages of one call, for optional timing (moe_latent_opts.stage_events).
- * The decode path runs five kernels and reports them as DPROJ, ROUTER
- * (which also runs the shared expert's gate/up), GATEUP (which includes the
- * top-k), DOWN (which includes the combine) and UPROJ. */
+ * The decode path runs six kernels and reports them as DPROJ, ROUTER
+ * (which also takes the top-k and runs the shared expert's gate/up),
+ * GATEUP, DOWN (two kernels: the down products and the combine) and
+ * UPROJ. */
 #define MOE_LATENT_STAGE_NORM 0     /* RMSNorm of the residual block */
 #define MOE_LATENT_STAGE_DPROJ 1    /* h = x D^T */
 #define MOE_LATENT_STAGE_ROUTER 2   /* logits = h R^T + b */

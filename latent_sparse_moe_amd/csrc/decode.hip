@@ -2,7 +2,7 @@
 //
 // At a handful of tokens every weight byte feeds only T multiply-adds, so the
 // layer is bound by HBM bandwidth and by the fixed latency of each dependent
-// step. Five kernels; in each, every wave issues its loads before anything
+// step. Six kernels; in each, every wave issues its loads before anything
 // else (the router and routed gate/up kernels first stage their activations),
 // and a kernel boundary is the only grid-wide synchronisation (no workgroup
 // ever waits for another one to be scheduled):
@@ -18,13 +18,14 @@
 //   4. dec_down    one workgroup per (expert slot, 128 latent rows): the slot's
 //                  activations are staged once in LDS, each wave takes 16 rows;
 //                  partial rows, weighted by the gate weights, go to a per-slot
-//                  buffer. The last workgroup of a row range to finish sums the
-//                  slots in a fixed order and writes z (bf16).
-//   5. dec_uproj   out = z U^T (+ x)
+//                  buffer
+//   5. dec_combine z = the slots' partial rows summed in slot order (bf16)
+//   6. dec_uproj   out = z U^T (+ x)
 //
 // Matrix-core tiles are v_mfma_f32_16x16x32_bf16 with weight rows as the M
 // operand (16 rows) and tokens as the N operand (16 columns, T used; the rest
-// repeat token T - 1 and are never stored, so no operand load is conditional). Lane l serves weight row l%16; its lane group g = l/16 takes
+// repeat token T - 1 and are never stored, so no operand load is
+// conditional). Lane l serves weight row l%16; its lane group g = l/16 takes
 // every fourth chunk of the wave's K range (chunk c*4 + g at step c), so one
 // load instruction reads 64 contiguous bytes of each of 16 rows. K order
 // inside a dot product is free; the token operand is read with the same
@@ -35,10 +36,9 @@
 // microseconds if every gate/up workgroup repeated it.
 //
 // Cross-workgroup data inside one launch (router logits -> the last router
-// workgroup, per-slot partial rows -> the last down workgroup of a row range)
-// moves through agent-scope relaxed atomic accesses, which are coherent across
-// the chip's XCDs without flushing the L2 caches; everything else crosses
-// kernel boundaries.
+// workgroup) moves through agent-scope relaxed atomic accesses, which are
+// coherent across the chip's XCDs without flushing the L2 caches; everything
+// else crosses kernel boundaries.
 #include <limits.h>
 
 #include <mutex>
@@ -54,7 +54,7 @@ namespace moe {
 constexpr int kDecThreads = 512;  // 8 waves
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kDownRows = kDecodeDownRows;
-constexpr int kTailBatch = 32;  // partial rows loaded per round trip by the down kernel's tail
+constexpr int kTailBatch = 32;  // partial rows loaded per round trip by the combine
 static_assert(kDownRows == kDecWaves * 16, "one 16-row tile per wave");
 
 #define AGENT __HIP_MEMORY_SCOPE_AGENT
@@ -537,7 +537,6 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
     }
     __syncthreads();
     build_active_list(E, T * a.top_k, rl);
-    for (int i = tid; i < decode_row_ranges(L); i += kDecThreads) a.down_counter[i] = 0u;
     publish_routing(a, rl);
     return;
   }
@@ -602,10 +601,10 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
 template <int NCH_D>
 __global__ __launch_bounds__(kDecThreads) void k_dec_down(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [T][I] activations
-  __shared__ unsigned last_flag;
   const int L = a.latent, T = a.T, I = a.inter;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
+  (void)tid;
   const int nrr = decode_row_ranges(L);
   const int s = blockIdx.x / nrr, rr = blockIdx.x % nrr;
   // the routing table, read together (the guesses are clamped in range)
@@ -632,40 +631,37 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_down(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int n = row0 + g * 4 + r;
-      if (n < L)
-        __hip_atomic_store(a.zpart + ((size_t)s * T + t) * L + n, wt * y[r], __ATOMIC_RELAXED,
-                           AGENT);
+      if (n < L) a.zpart[((size_t)s * T + t) * L + n] = wt * y[r];
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // partial rows complete before the arrival count
-  __syncthreads();
+}
+
+// z[t][n] = bf16(sum over the active slots, in slot order, of the weighted
+// partial rows); one thread per output. Its own launch: the kernel boundary
+// makes every down workgroup's partial rows visible, which costs less than a
+// release, an arrival count and a last-arriver sum inside the down launch
+// (measured: 6.5 us of hand-off there against one extra launch here).
+__global__ __launch_bounds__(256) void k_dec_combine(DecodeArgs a) {
+  const int T = a.T, L = a.latent;
+  const int i = blockIdx.x * 256 + threadIdx.x;  // t * L + n
+  if (i >= T * L) return;
+  const int n_act = a.route_n_act[0];
   const int s0 = a.n_shared ? 0 : 1;
-  if (tid == 0)
-    last_flag = __hip_atomic_fetch_add(a.down_counter + rr, 1u, __ATOMIC_RELAXED, AGENT) ==
-                (unsigned)(n_act - s0);
-  __syncthreads();
-  if (!last_flag) return;
-  // last workgroup of the row range: z[t][rows] = sum over the slots in order
   const size_t step = (size_t)T * L;
-  for (int i = tid; i < T * kDownRows; i += kDecThreads) {
-    const int tt = i / kDownRows, n = rr * kDownRows + i % kDownRows;
-    if (n >= L) continue;
-    const float* src = a.zpart + (size_t)tt * L + n;
-    float v = 0.f;
-    // kTailBatch loads in flight per round trip, summed in slot order; slots
-    // past n_act re-read slot n_act (in range) and are not summed
-    for (int ss = s0; ss <= n_act; ss += kTailBatch) {
-      float p[kTailBatch];
+  const float* src = a.zpart + i;
+  float v = 0.f;
+  // kTailBatch loads in flight per round trip, summed in slot order; slots
+  // past n_act re-read slot n_act (in range) and are not summed
+  for (int ss = s0; ss <= n_act; ss += kTailBatch) {
+    float p[kTailBatch];
 #pragma unroll
-      for (int j = 0; j < kTailBatch; ++j)
-        p[j] = __hip_atomic_load(src + min(ss + j, n_act) * step, __ATOMIC_RELAXED, AGENT);
-      issue_fence();  // else the first sums are placed between the loads, each a round trip
+    for (int j = 0; j < kTailBatch; ++j) p[j] = src[min(ss + j, n_act) * step];
+    issue_fence();  // else the first sums are placed between the loads, each a round trip
 #pragma unroll
-      for (int j = 0; j < kTailBatch; ++j)
-        if (ss + j <= n_act) v += p[j];
-    }
-    a.z[(size_t)tt * L + n] = f32_to_bf16_bits(v);
+    for (int j = 0; j < kTailBatch; ++j)
+      if (ss + j <= n_act) v += p[j];
   }
+  a.z[i] = f32_to_bf16_bits(v);
 }
 
 // ------------------------------------------------------------------ 5. U
@@ -875,10 +871,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
     constexpr int n = decltype(N)::value;
     hipError_t e = ensure_lds((const void*)k_dec_down<n>, down_lds(kDecodeMaxT, I));
     if (e == hipSuccess)
-      e = mk.launch(kStageDown, k_dec_down<n>, dim3((1 + a.max_active) * decode_row_ranges(L)),
-                    block, down_lds(T, I), a);
+      e = mk.launch_first(kStageDown, k_dec_down<n>,
+                          dim3((1 + a.max_active) * decode_row_ranges(L)), block, down_lds(T, I), a);
     return e;
   });
+  if (err != hipSuccess) return err;
+  err = mk.launch_last(kStageDown, k_dec_combine, dim3((T * L + 255) / 256), dim3(256), 0, a);
   if (err != hipSuccess) return err;
   // 5. out = z U^T (+ x)
   return with_nch(L / 256, [&](auto N) {

@@ -116,6 +116,25 @@ struct StageMarks {
   hipError_t launch(int stage, K kernel, dim3 grid, dim3 block, size_t lds, Args... args) const {
     hipEvent_t e0 = ev ? (hipEvent_t)ev[2 * stage] : nullptr;
     hipEvent_t e1 = ev ? (hipEvent_t)ev[2 * stage + 1] : nullptr;
+    return launch_ev(e0, e1, kernel, grid, block, lds, args...);
+  }
+  // A stage of two launches: the first records the start event, the last
+  // the end event.
+  template <typename K, typename... Args>
+  hipError_t launch_first(int stage, K kernel, dim3 grid, dim3 block, size_t lds,
+                          Args... args) const {
+    return launch_ev(ev ? (hipEvent_t)ev[2 * stage] : nullptr, nullptr, kernel, grid, block, lds,
+                     args...);
+  }
+  template <typename K, typename... Args>
+  hipError_t launch_last(int stage, K kernel, dim3 grid, dim3 block, size_t lds,
+                         Args... args) const {
+    return launch_ev(nullptr, ev ? (hipEvent_t)ev[2 * stage + 1] : nullptr, kernel, grid, block,
+                     lds, args...);
+  }
+  template <typename K, typename... Args>
+  hipError_t launch_ev(hipEvent_t e0, hipEvent_t e1, K kernel, dim3 grid, dim3 block, size_t lds,
+                       Args... args) const {
     if (e0 || e1)
       hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0u, args...);
     else
@@ -145,7 +164,6 @@ struct DecodeArgs {
   uint16_t* act;       // [1 + max_active][T][inter]   slot 0: shared expert
   float* zpart;        // [1 + max_active][T][latent]  per-slot weighted down rows
   int max_active;      // min(n_experts, T * top_k): capacity of the routing table
-  unsigned* down_counter;  // [decode_row_ranges(latent)] finished down slots per row range
   uint16_t* z;         // [T][latent] combined expert output (bf16)
   unsigned* route_counter;  // router workgroups that finished (zeroed by dec_dproj)
   int* route_n_act;    // [1]
