@@ -94,6 +94,17 @@ __device__ __forceinline__ uint32_t e1m1_group_to_e2m1(uint32_t w0, uint32_t w1,
   }
 }
 
+// silu(g) = g / (1 + e^-g), with e^-g = 2^(-g log2 e) on the hardware base-2
+// exponential and the reciprocal on the hardware reciprocal (each within about
+// one fp32 ulp; the result is rounded to bf16 afterwards). Five instructions
+// instead of a correctly rounded exp and an IEEE division (about thirty).
+// Limits: g -> -inf gives e^-g = inf, a zero reciprocal and -0; g -> +inf
+// gives g.
+__device__ __forceinline__ float silu_fast(float g) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Eight e2m1 codes -> their plain values as bf16 (exact; no block scale).
 __device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t codes) {
   bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 0);

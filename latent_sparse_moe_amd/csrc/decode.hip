@@ -323,7 +323,7 @@ __device__ __forceinline__ void store_gateup(const f32x4& g4, const f32x4& u4, f
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float gg = gsg * g4[r], uu = gsu * u4[r];
-    v[r] = gg / (1.0f + expf(-gg)) * uu;
+    v[r] = silu_fast(gg) * uu;
   }
   *(uint2*)(act + (size_t)t * I + n0 + g * 4) =
       make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));

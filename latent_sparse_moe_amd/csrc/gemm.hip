@@ -602,7 +602,7 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, i
       for (int e = 0; e < 8; ++e) {
         const float g = gsg * acc[i][0][8 * q + e];
         const float u = gsu * acc[i][1][8 * q + e];
-        a[e] = g / (1.0f + expf(-g)) * u;
+        a[e] = silu_fast(g) * u;
       }
       *(uint4*)(act + (size_t)row * inter + nc) = pack_bf16x8(a);
     }
