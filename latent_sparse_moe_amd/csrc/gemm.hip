@@ -10,19 +10,24 @@
 // products. The operands take different routes, chosen from measured LDS
 // rates on gfx950 (16-byte reads ~200+ B/clk/CU, writes from registers ~64):
 //   - A (activation rows, shared by all four waves) is staged through LDS:
-//     loaded two K steps ahead into registers, written one step ahead into
-//     one of three LDS stages, read as fragments. Rows are BK elements with
-//     their 16-byte chunks XOR-swizzled by row pair (measured: a 16-byte read
-//     is served 16 lanes at a time over 256 bytes of banks, a 16-byte write 8
-//     lanes at a time), so that the fragment reads of 16 consecutive rows at
-//     one chunk and the row-order writes of the loader are conflict-free.
+//     loaded two K steps ahead straight from global memory into one of three
+//     LDS stages (global_load_lds_dwordx4, no registers in between), read as
+//     fragments. Rows are BK elements with their 16-byte chunks XOR-swizzled
+//     by row pair (measured: a 16-byte read is served 16 lanes at a time over
+//     256 bytes of banks), so that the fragment reads of 16 consecutive rows
+//     at one chunk are conflict-free; each lane loads the chunk that the
+//     swizzle puts in its slot. (Measured against loading A into registers
+//     and writing it to LDS one step later: 16K prefill 2.20 -> 2.14 ms.)
 //   - B (weights, used by exactly one wave) never touches LDS: each lane
 //     loads its own weight row's slice straight into registers, three K
 //     steps deep, and for the experts dequantises the 4-bit codes (exactly,
 //     to bf16) right before its matrix-core op. HBM and L2 traffic for expert
 //     weights is the 4.5-bit format.
-// The workgroup meets once per K step at an LDS-only barrier; nothing in the
-// steady-state loop is conditional, so the compiler's load waits are exact.
+// The workgroup meets once per K step at a barrier, after each wave has
+// waited for its own A loads of the next step (an explicit count: the
+// compiler does not track direct-to-LDS loads across waves); nothing in the
+// steady-state loop is conditional, so the compiler's other load waits are
+// exact.
 // The expert kernels are held to 256 registers per lane so that two
 // workgroups share a CU (two waves per SIMD): one wave's LDS, barrier and
 // load waits then overlap the other's matrix-core work (measured on the 16K
@@ -82,15 +87,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// 128 rows of bf16 A into a swizzled [128][BK] LDS tile. Thread t moves
-// 16-byte chunks t, t + 256, ... of the tile (consecutive threads read one
-// row's chunks in order) through register set `set`.
+// 128 rows of bf16 A into a swizzled [128][BK] LDS tile, straight from
+// global memory (global_load_lds_dwordx4: lane L of a wave writes its 16
+// bytes at the wave's LDS base + 16 L). Thread t fills the tile's 16-byte
+// slots t, t + 256, ...: it loads the logical chunk that the swizzle puts in
+// that slot (the XOR permutation is its own inverse). No registers hold A.
 template <int BK>
 struct ALoader {
-  static constexpr int V = kBM * Geo<BK>::kCpr / kThreads;
+  static constexpr int V = kBM * Geo<BK>::kCpr / kThreads;  // DMA loads per thread and step
   const uint16_t* src[V];
-  int dst[V];
-  uint4 reg[3][V];
+  int wbase;  // this wave's first slot (elements), wave-uniform
 
   // rowfn(r) = address of row r's K = 0 element
   template <class RowFn>
@@ -98,21 +104,35 @@ struct ALoader {
     using G = Geo<BK>;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const int chunk = v * kThreads + (int)threadIdx.x;
-      const int row = chunk / G::kCpr, c = chunk % G::kCpr;
+      const int slot = v * kThreads + (int)threadIdx.x;
+      const int row = slot / G::kCpr, pos = slot % G::kCpr;
+      const int c = pos ^ ((row / G::kRpl) % G::kCpr);
       src[v] = rowfn(row) + c * 8;
-      dst[v] = swz<BK>(row, c) * 8;
     }
+    wbase = __builtin_amdgcn_readfirstlane((int)(threadIdx.x & ~63)) * 8;
   }
-  __device__ __forceinline__ void issue(int kt, int set) {
+  __device__ __forceinline__ void issue(int kt, uint16_t* tile) const {
 #pragma unroll
-    for (int v = 0; v < V; ++v) reg[set][v] = *(const uint4*)(src[v] + kt * BK);
-  }
-  __device__ __forceinline__ void finish(uint16_t* tile, int set) const {
-#pragma unroll
-    for (int v = 0; v < V; ++v) *(uint4*)(tile + dst[v]) = reg[set][v];
+    for (int v = 0; v < V; ++v)
+      __builtin_amdgcn_global_load_lds((const void*)(src[v] + kt * BK),
+                                       (__attribute__((address_space(3))) void*)(tile + wbase + v * kThreads * 8),
+                                       16, 0, 0);
   }
 };
+
+// Workgroup barrier after this wave's own direct-to-LDS loads are waited
+// for (wait_vmcnt) and its LDS reads have been consumed: no memory fence, so
+// the compiler adds no wait for the loads still in flight.
+__device__ __forceinline__ void dma_barrier() { __builtin_amdgcn_s_barrier(); }
+
+// Waits until at most n vector-memory loads of this wave are outstanding
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left
+// at "no wait").
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
 
 // B operand in registers: expert weights in e2m1 codes + E4M3 block scales.
 // Lane (half h) of sub-tile j holds BK/2 codes and BK/32 scale bytes of its
@@ -130,6 +150,7 @@ struct Fp4B {
   static_assert(!PK || BK == 64, "the packed layout has 64-wide K steps");
   static_assert(BITS == 4 || (BITS == 3 && BK == 64), "3-bit codes need 64-wide K steps");
   static constexpr bool kInterleave = false;              // see gemm_step
+  static constexpr int kLoads = 4;  // load instructions per issue
   static constexpr int kWords = BITS == 4 ? BK / 16 : 3;  // code words per lane per step
   static constexpr int kCodeStep =                        // bytes between a lane's steps
       PK ? 64 * 4 * kWords : (BITS == 4 ? BK / 2 : 24);
@@ -182,6 +203,7 @@ template <int BK, bool PK>
 struct Bf16B {
   static_assert(!PK || BK == 64, "the packed layout has 64-wide K steps");
   static constexpr bool kInterleave = true;  // see gemm_step
+  static constexpr int kLoads = 2 * Geo<BK>::kSub;  // load instructions per issue
   static constexpr int kSub = Geo<BK>::kSub;
   struct Set {
     uint4 c[2][kSub];
@@ -211,11 +233,11 @@ struct Pipe {
   uint16_t* a[3];
 };
 
-// One K step on stage S = kt % 3: issue the loads of step kt + 2 (A into
-// register set (S+2)%3, B into B set (S+2)%3), run the matrix cores on A
-// stage S and B set S, and write A of step kt + 1 (loaded one step ago) into
-// stage (S+1)%3, which was read last in step kt - 2. Past the last step the
-// loads repeat step KT - 1 and the writes go to a stage nobody reads. Only
+// One K step on stage S = kt % 3: issue the loads of step kt + 2 (A into LDS
+// stage (S+2)%3, read last in step kt - 1, B into B set (S+2)%3), run the
+// matrix cores on A stage S and B set S, then wait for step kt + 1's loads
+// and meet at the barrier. Past the last step the loads repeat step KT - 1
+// into a stage nobody reads (and are waited for before the epilogue). Only
 // the first NI 32-row blocks of the tile are multiplied (the last tile of an
 // expert's rows may hold fewer than 128).
 template <int BK, int S, int NI, class BL>
@@ -226,7 +248,7 @@ __device__ __forceinline__ void gemm_step(int kt, int KT, ALoader<BK>& al, const
   using G = Geo<BK>;
   constexpr int N1 = (S + 1) % 3, N2 = (S + 2) % 3;
   const int kl = min(kt + 2, KT - 1);
-  al.issue(kl, N2);
+  al.issue(kl, p.a[N2]);  // stage N2 was read last in step kt - 1
   bl.issue(kl, bs[N2]);
   const uint16_t* ca = p.a[S];
 #pragma unroll
@@ -240,7 +262,6 @@ __device__ __forceinline__ void gemm_step(int kt, int KT, ALoader<BK>& al, const
     for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
-    if (ks == 0) al.finish(p.a[N1], N1);
   }
   if constexpr (BL::kInterleave) {
     // one matrix-core op, two vector ops and one LDS read at a time
@@ -254,7 +275,10 @@ __device__ __forceinline__ void gemm_step(int kt, int KT, ALoader<BK>& al, const
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
   }
-  lds_barrier();
+  // step kt + 1's A (loaded during step kt - 1) complete in every wave
+  // before the barrier: only this step's loads may still be in flight
+  wait_vmcnt<ALoader<BK>::V + BL::kLoads>();
+  dma_barrier();
 }
 
 template <int NI>
@@ -282,12 +306,12 @@ __device__ __forceinline__ void mainloop(ALoader<BK>& al, const BL& bl, int KT, 
 
   typename BL::Set bs[3];
   // prologue: step 0 in LDS and B set 0, step 1 in flight
-  al.issue(0, 0);
+  al.issue(0, p.a[0]);
   bl.issue(0, bs[0]);
-  al.issue(min(1, KT - 1), 1);
+  al.issue(min(1, KT - 1), p.a[1]);
   bl.issue(min(1, KT - 1), bs[1]);
-  al.finish(p.a[0], 0);
-  lds_barrier();
+  wait_vmcnt<ALoader<BK>::V + BL::kLoads>();
+  dma_barrier();
   int kt = 0;
   for (; kt + 3 <= KT; kt += 3) {
     gemm_step<BK, 0, NI>(kt, KT, al, bl, p, bs, frag, acc);
@@ -296,6 +320,9 @@ __device__ __forceinline__ void mainloop(ALoader<BK>& al, const BL& bl, int KT, 
   }
   if (kt < KT) gemm_step<BK, 0, NI>(kt, KT, al, bl, p, bs, frag, acc);
   if (kt + 1 < KT) gemm_step<BK, 1, NI>(kt + 1, KT, al, bl, p, bs, frag, acc);
+  // the repeated tail loads into LDS land before the workgroup can end (its
+  // LDS may then go to the next workgroup on this CU)
+  wait_vmcnt<0>();
 }
 
 // The products are computed transposed (weights as the first matrix-core
