@@ -150,6 +150,7 @@ struct Fp4B {
   static_assert(!PK || BK == 64, "the packed layout has 64-wide K steps");
   static_assert(BITS == 4 || (BITS == 3 && BK == 64), "3-bit codes need 64-wide K steps");
   static constexpr bool kInterleave = false;              // see gemm_step
+  static constexpr int kValuPerMfma = 0;
   static constexpr int kLoads = 4;  // load instructions per issue
   static constexpr int kWords = BITS == 4 ? BK / 16 : 3;  // code words per lane per step
   static constexpr int kCodeStep =                        // bytes between a lane's steps
@@ -203,6 +204,7 @@ template <int BK, bool PK>
 struct Bf16B {
   static_assert(!PK || BK == 64, "the packed layout has 64-wide K steps");
   static constexpr bool kInterleave = true;  // see gemm_step
+  static constexpr int kValuPerMfma = 2;
   static constexpr int kLoads = 2 * Geo<BK>::kSub;  // load instructions per issue
   static constexpr int kSub = Geo<BK>::kSub;
   struct Set {
@@ -271,7 +273,7 @@ __device__ __forceinline__ void gemm_step(int kt, int KT, ALoader<BK>& al, const
 #pragma unroll
     for (int m = 0; m < G::kSub * NI * 2; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, BL::kValuPerMfma, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
   }
