@@ -51,6 +51,10 @@ def rec_bytes(L, I, gateup_bits=4):
     return 2 * L * I * gateup_bits // 8 + L * I // 2 + 3 * L * I // 16
 
 
+# decode stages made of more than one kernel
+DECODE_STAGE_KERNELS = {"down": ("k_dec_down", "k_dec_combine")}
+
+
 def kernel_bytes(d, T, n_routed, decode=True):
     """Algorithmic HBM bytes of each kernel of one layer call: every weight
     byte it must read once (4-bit codes, or 3-bit E1M1 gate/up codes in the
@@ -127,10 +131,15 @@ def source_digest():
 
 
 def stored_traffic(kernel_prefix):
-    """HBM bytes per launch of a kernel from profiles/traffic.json (written
-    from two rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE, each divided by
-    the factor the same counter reads on the copy kernel), or None when that
-    file is absent or was taken on different kernel sources."""
+    """HBM bytes per launch of a kernel (or the sum over a tuple of kernels
+    that make up one stage) from profiles/traffic.json (written from two
+    rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE, each divided by the
+    factor the same counter reads on the copy kernel), or None when that
+    file is absent, lacks one of them, or was taken on different kernel
+    sources."""
+    if isinstance(kernel_prefix, tuple):
+        parts = [stored_traffic(k) for k in kernel_prefix]
+        return None if any(p is None for p in parts) else sum(parts)
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:
@@ -333,7 +342,8 @@ def bench_decode(args, torch, lsm, synth, dev):
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS if achieved else None,
-            "traffic": stored_traffic(("k_dec_" if use_decode else "k_") + dom),
+            "traffic": stored_traffic(DECODE_STAGE_KERNELS.get(dom, "k_dec_" + dom) if use_decode
+                                      else "k_" + dom),
             "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes,
             "kernel_us": dom_ms * 1e3,
         },
