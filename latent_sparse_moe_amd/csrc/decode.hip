@@ -9,12 +9,13 @@
 //
 //   1. dec_dproj   h = x D^T (RMSNorm fused for the residual block); K split
 //                  over the 8 waves; h leaves as bf16 hi + lo
-//   2. dec_router  logits = (hi + lo) R^T + b, 16 experts per workgroup; the
-//                  last router workgroup to finish takes the top-k of every
-//                  token and publishes the routing table. The shared expert's
-//                  gate/up (routing-independent) runs in the same launch.
-//   3. dec_gateup  one wave per (routed expert, 16 intermediate rows, matrix,
-//                  K half): silu(gate) * up
+//   2. dec_router  logits = (hi + lo) R^T + b, 16 experts per workgroup. The
+//                  shared expert's gate/up (routing-independent) runs in the
+//                  same launch.
+//   3. dec_gateup  every workgroup first takes the top-k of every token and
+//                  builds the active list (workgroup 0 also publishes the
+//                  routing table); then one wave per (routed expert, 16
+//                  intermediate rows, matrix, K half): silu(gate) * up
 //   4. dec_down    one workgroup per (expert slot, 128 latent rows): the slot's
 //                  activations are staged once in LDS, each wave takes 16 rows;
 //                  partial rows, weighted by the gate weights, go to a per-slot
@@ -31,14 +32,14 @@
 // inside a dot product is free; the token operand is read with the same
 // chunk mapping.
 //
-// The top-k runs once per call, in one workgroup: every wave of it executes
-// some hundreds of dependent instructions per token, which would cost several
-// microseconds if every gate/up workgroup repeated it.
+// Every gate/up workgroup repeats the top-k (some hundreds of dependent
+// instructions per token, on one wave per token) instead of one workgroup
+// of the router launch taking it after an in-launch hand-off (logits
+// stores, an arrival count, the last arriver's gather): measured, the
+// repeated top-k costs gate/up about what the hand-off and tail cost the
+// router at T = 4, and less at T = 1..3 (1.5 to 3.7 us per step).
 //
-// Cross-workgroup data inside one launch (router logits -> the last router
-// workgroup) moves through agent-scope relaxed atomic accesses, which are
-// coherent across the chip's XCDs without flushing the L2 caches; everything
-// else crosses kernel boundaries.
+// Data moves between workgroups only across kernel boundaries.
 #include <limits.h>
 
 #include <mutex>
@@ -234,6 +235,28 @@ struct RowStage {
   }
 };
 
+// count (a multiple of 8) bf16 elements from global src into LDS dst with
+// direct-to-LDS loads (global_load_lds_dwordx4: lane l of a wave writes 16
+// bytes at the wave's LDS base + 16 l). Thread t moves 16-byte slots t,
+// t + 512, ...; a wave whose first slot is past the end issues nothing, and
+// the lanes past the end of the last busy wave re-read the last slot and
+// write up to 63 slots past count (callers keep that much LDS behind the
+// rows). No registers hold the rows, so other loads can be in flight and
+// consumed meanwhile; the caller waits (vmcnt) before its barrier.
+template <int NV>
+__device__ __forceinline__ void stage_dma(const uint16_t* src, int count, uint16_t* dst) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nslots = count / 8;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int first = v * kDecThreads + wave * 64;  // wave-uniform
+    if (first < nslots)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)min(first + lane, nslots - 1) * 8),
+                                       (__attribute__((address_space(3))) void*)(dst + first * 8),
+                                       16, 0, 0);
+  }
+}
+
 // Dynamic LDS layouts (bytes), sized by the call's T.
 constexpr size_t kRedBytes = kDecWaves * 64 * 4 * sizeof(float);
 inline size_t dproj_lds(int T, int H) { return (size_t)T * H * 2 + kRedBytes + kDecodeMaxT * 4; }
@@ -255,7 +278,6 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_dproj(DecodeArgs a) {
   const int g = lane >> 4, t = lane & 15;
   const int row0 = blockIdx.x * 16;
   const int kb = wave * (H / kDecWaves);
-  if (blockIdx.x == 0 && tid == 0) *a.route_counter = 0u;  // for the router's last workgroup
   RowStage<(NCH + 1) / 2> xr;  // T x hidden, hidden = 256 NCH
   xr.load(a.x, T * H);
   Bf16Rows<NCH> wr;
@@ -366,21 +388,26 @@ __device__ __forceinline__ void finish_gateup(f32x4 acc, float* red, bool tile_b
 
 // ------------------------------------------------------------------ top-k
 
-// Top-k of one token's logits by this wave; lane j < k ends with choice j
-// (descending value, equal values to the lower expert). Renormalised
-// weights: exp(l_j - l_0) / sum over the k chosen. The logits were written
-// by other workgroups of this launch: agent-scope loads.
+// One token's logits as order-preserving keys, lane l holding experts
+// l, l + 64, ... (experts past E: key 0, below every logit's key). The loads
+// are unconditional (clamped index) so that they stay in flight together.
 template <int EPL>
-__device__ __forceinline__ void wave_topk(const float* row, int E, int k, int* out_e,
+__device__ __forceinline__ void wave_load_keys(const float* row, int E, float (&v)[EPL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
+}
+
+// Top-k of one token from its logits (wave_load_keys) by this wave; lane
+// j < k ends with choice j (descending value, equal values to the lower
+// expert). Renormalised weights: exp(l_j - l_0) / sum over the k chosen.
+template <int EPL>
+__device__ __forceinline__ void wave_topk(const float (&v)[EPL], int E, int k, int* out_e,
                                           float* out_w) {
   const int lane = threadIdx.x & 63;
   uint32_t key[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? order_key(__hip_atomic_load(row + min(e, E - 1), __ATOMIC_RELAXED, AGENT))
-                   : 0u;
-  }
+  for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < E ? order_key(v[i]) : 0u;
   uint32_t my_key;
   int my_e;
   wave_select_topk<EPL>(key, E, k, my_key, my_e);
@@ -476,8 +503,6 @@ __device__ __forceinline__ void publish_routing(const DecodeArgs& a, const Route
 template <int NCH_R, int NCH_H, int BITS>
 __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  __shared__ RouteLds rl;
-  __shared__ unsigned last_flag;
   const int L = a.latent, T = a.T, E = a.n_experts, I = a.inter;
   uint16_t* hi = lds;           // [T][L]
   uint16_t* lo = lds + T * L;   // [T][L]
@@ -513,31 +538,9 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ee = e0 + g * 4 + r;
-        if (ee < E)
-          __hip_atomic_store(a.logits + (size_t)t * E + ee, tot[r] + bias[r], __ATOMIC_RELAXED,
-                             AGENT);
+        if (ee < E) a.logits[(size_t)t * E + ee] = tot[r] + bias[r];
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // the logits stores complete before the arrival count
-    __syncthreads();
-    if (tid == 0)
-      last_flag = __hip_atomic_fetch_add(a.route_counter, 1u, __ATOMIC_RELAXED, AGENT) ==
-                  (unsigned)(nrb - 1);
-    __syncthreads();
-    if (!last_flag) return;
-    // the last router workgroup: top-k of every token, then the routing table
-    for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
-    if (wave < T) {
-      if (E <= 512)
-        wave_topk<8>(a.logits + (size_t)wave * E, E, a.top_k, rl.idx + wave * a.top_k,
-                     rl.w + wave * a.top_k);
-      else
-        wave_topk<16>(a.logits + (size_t)wave * E, E, a.top_k, rl.idx + wave * a.top_k,
-                      rl.w + wave * a.top_k);
-    }
-    __syncthreads();
-    build_active_list(E, T * a.top_k, rl);
-    publish_routing(a, rl);
     return;
   }
   // shared expert gate/up: two 16-row tiles per workgroup (see GateUpTask)
@@ -561,30 +564,48 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
 template <int NCH_H, int BITS>
 __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  const int L = a.latent, T = a.T, I = a.inter;
+  __shared__ RouteLds rl;
+  const int L = a.latent, T = a.T, I = a.inter, E = a.n_experts;
   uint16_t* hi = lds;  // [T][L]
   float* red = (float*)(lds + T * L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = lane & 15;
   const int tiles = I / 16;
   const int tile = blockIdx.x * 2 + (wave >> 2);  // (slot - 1) * tiles + row tile
-  // the routing table: entry count and this tile's expert, read together
-  const int n_act = a.route_n_act[0];
-  const int e_guess = a.route_list[min(tile / tiles, a.max_active - 1)];
-  if ((int)blockIdx.x * 2 >= n_act * tiles) return;  // both tiles idle (uniform)
-  const bool busy = tile < n_act * tiles;
-  const int e = busy ? e_guess : 0;
-  const int n0 = busy ? (tile % tiles) * 16 : 0;
   // The activations are staged, and waited for, before any weight load is
   // issued. Four workgroups share a CU and all of them stream weights at
   // once, so activations loaded behind the weights arrive only when most of
   // the CU's weights have; every workgroup's compute would then start after
   // the data window instead of riding on it (measured: 60.3 -> 58.2 us per
-  // decode step at T = 4).
-  RowStage<(NCH_H + 1) / 2> st;  // T x latent, latent = 256 NCH_H
-  st.load(a.hhi, T * L);
-  st.store(hi, T * L);
+  // decode step at T = 4). Their loads are in flight while the routing is
+  // worked out: every workgroup takes the top-k of every token from the
+  // router's logits and builds the active list (the same result in each);
+  // workgroup 0 publishes the routing table for the down and combine kernels.
+  // the logits and the staged rows (straight into LDS) are loaded together,
+  // one round trip; the top-k works on the logits while the rows land
+  for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
+  const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;
+  constexpr int NV = (NCH_H + 1) / 2;  // T x latent, latent = 256 NCH_H: up to 8 rows
+  if (E <= 512) {
+    float v[8];
+    wave_load_keys<8>(lrow, E, v);
+    stage_dma<NV>(a.hhi, T * L, hi);
+    if (wave < T) wave_topk<8>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
+  } else {
+    float v[16];
+    wave_load_keys<16>(lrow, E, v);
+    stage_dma<NV>(a.hhi, T * L, hi);
+    if (wave < T) wave_topk<16>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
   __syncthreads();
+  build_active_list(E, T * a.top_k, rl);
+  if (blockIdx.x == 0) publish_routing(a, rl);
+  const int n_act = rl.n_act;
+  if ((int)blockIdx.x * 2 >= n_act * tiles) return;  // both tiles idle (uniform)
+  const bool busy = tile < n_act * tiles;
+  const int e = busy ? rl.list[tile / tiles] : 0;
+  const int n0 = busy ? (tile % tiles) * 16 : 0;
   GateUpTask<NCH_H, BITS> task;
   // unconditional: an idle tile reads expert 0's rows 0..15 (in range) and
   // stores nothing, which keeps the loads and their uses in one block

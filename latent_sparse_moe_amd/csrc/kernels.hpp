@@ -165,7 +165,6 @@ struct DecodeArgs {
   float* zpart;        // [1 + max_active][T][latent]  per-slot weighted down rows
   int max_active;      // min(n_experts, T * top_k): capacity of the routing table
   uint16_t* z;         // [T][latent] combined expert output (bf16)
-  unsigned* route_counter;  // router workgroups that finished (zeroed by dec_dproj)
   int* route_n_act;    // [1]
   int* route_list;     // [max_active]
   float* route_wtab;   // [1 + max_active][T]
