@@ -42,6 +42,7 @@
 // Data moves between workgroups only across kernel boundaries.
 #include <limits.h>
 
+#include <map>
 #include <mutex>
 #include <set>
 #include <type_traits>
@@ -278,6 +279,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_dproj(DecodeArgs a) {
   const int g = lane >> 4, t = lane & 15;
   const int row0 = blockIdx.x * 16;
   const int kb = wave * (H / kDecWaves);
+  if (a.topk_in_router && blockIdx.x == 0 && tid == 0) *a.route_counter = 0u;
   RowStage<(NCH + 1) / 2> xr;  // T x hidden, hidden = 256 NCH
   xr.load(a.x, T * H);
   Bf16Rows<NCH> wr;
@@ -391,11 +393,16 @@ __device__ __forceinline__ void finish_gateup(f32x4 acc, float* red, bool tile_b
 // One token's logits as order-preserving keys, lane l holding experts
 // l, l + 64, ... (experts past E: key 0, below every logit's key). The loads
 // are unconditional (clamped index) so that they stay in flight together.
+// in_launch: the logits were written by other workgroups of this launch
+// (agent-scope loads); else by an earlier launch.
 template <int EPL>
-__device__ __forceinline__ void wave_load_keys(const float* row, int E, float (&v)[EPL]) {
+__device__ __forceinline__ void wave_load_keys(const float* row, int E, float (&v)[EPL],
+                                               bool in_launch = false) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
+  for (int i = 0; i < EPL; ++i)
+    v[i] = in_launch ? __hip_atomic_load(row + min(lane + 64 * i, E - 1), __ATOMIC_RELAXED, AGENT)
+                     : row[min(lane + 64 * i, E - 1)];
 }
 
 // Top-k of one token from its logits (wave_load_keys) by this wave; lane
@@ -503,6 +510,8 @@ __device__ __forceinline__ void publish_routing(const DecodeArgs& a, const Route
 template <int NCH_R, int NCH_H, int BITS>
 __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  __shared__ RouteLds rl;
+  __shared__ unsigned last_flag;
   const int L = a.latent, T = a.T, E = a.n_experts, I = a.inter;
   uint16_t* hi = lds;           // [T][L]
   uint16_t* lo = lds + T * L;   // [T][L]
@@ -538,9 +547,34 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ee = e0 + g * 4 + r;
-        if (ee < E) a.logits[(size_t)t * E + ee] = tot[r] + bias[r];
+        if (ee < E)
+          __hip_atomic_store(a.logits + (size_t)t * E + ee, tot[r] + bias[r], __ATOMIC_RELAXED,
+                             AGENT);
       }
     }
+    if (!a.topk_in_router) return;  // the gate/up workgroups take the top-k
+    __builtin_amdgcn_s_waitcnt(0);  // the logits stores complete before the arrival count
+    __syncthreads();
+    if (tid == 0)
+      last_flag = __hip_atomic_fetch_add(a.route_counter, 1u, __ATOMIC_RELAXED, AGENT) ==
+                  (unsigned)(nrb - 1);
+    __syncthreads();
+    if (!last_flag) return;
+    // the last router workgroup: top-k of every token, then the routing table
+    for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
+    const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;
+    if (E <= 512) {
+      float v[8];
+      wave_load_keys<8>(lrow, E, v, true);
+      if (wave < T) wave_topk<8>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
+    } else {
+      float v[16];
+      wave_load_keys<16>(lrow, E, v, true);
+      if (wave < T) wave_topk<16>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
+    }
+    __syncthreads();
+    build_active_list(E, T * a.top_k, rl);
+    publish_routing(a, rl);
     return;
   }
   // shared expert gate/up: two 16-row tiles per workgroup (see GateUpTask)
@@ -561,7 +595,26 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
 
 // ------------------------------------------------------------------ 3. routed gate/up
 
+// The wave's tile of a routed gate/up workgroup: expert e (active slot
+// `slot`), rows n0 .. n0+15, with the token rows staged in `hi`. An idle tile
+// (busy false) reads expert 0's rows 0..15 (in range) and stores nothing,
+// which keeps the loads and their uses in one block.
 template <int NCH_H, int BITS>
+__device__ __forceinline__ void gateup_tiles(const DecodeArgs& a, const uint16_t* hi, float* red,
+                                             bool busy, int e, int slot, int n0) {
+  const int L = a.latent, T = a.T, I = a.inter;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = lane & 15;
+  GateUpTask<NCH_H, BITS> task;
+  const float gsg = a.gate.gscale[e], gsu = a.up.gscale[e];
+  task.load(a.gate, a.up, a.packed, e, I, L, n0, wave, lane);
+  issue_fence();
+  const f32x4 acc = task.mma(hi + min(t, T - 1) * L, L, wave, lane);
+  finish_gateup(acc, red, busy, gsg, gsu, a.act + (size_t)(1 + slot) * T * I, I, T, n0);
+}
+
+// TOPK: this workgroup takes the top-k itself (a.topk_in_router is false);
+// else it reads the routing table the router published.
+template <int NCH_H, int BITS, bool TOPK>
 __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ RouteLds rl;
@@ -577,44 +630,47 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   // once, so activations loaded behind the weights arrive only when most of
   // the CU's weights have; every workgroup's compute would then start after
   // the data window instead of riding on it (measured: 60.3 -> 58.2 us per
-  // decode step at T = 4). Their loads are in flight while the routing is
-  // worked out: every workgroup takes the top-k of every token from the
-  // router's logits and builds the active list (the same result in each);
-  // workgroup 0 publishes the routing table for the down and combine kernels.
-  // the logits and the staged rows (straight into LDS) are loaded together,
-  // one round trip; the top-k works on the logits while the rows land
-  for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
-  const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;
+  // decode step at T = 4). They go straight into LDS, so no registers hold
+  // them while the routing is worked out.
   constexpr int NV = (NCH_H + 1) / 2;  // T x latent, latent = 256 NCH_H: up to 8 rows
-  if (E <= 512) {
-    float v[8];
-    wave_load_keys<8>(lrow, E, v);
+  if constexpr (!TOPK) {  // the routing table is published: read it
+    const int n_act = a.route_n_act[0];
+    const int e_guess = a.route_list[min(tile / tiles, a.max_active - 1)];
+    if ((int)blockIdx.x * 2 >= n_act * tiles) return;  // both tiles idle (uniform)
     stage_dma<NV>(a.hhi, T * L, hi);
-    if (wave < T) wave_topk<8>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
+    __syncthreads();
+    const bool busy = tile < n_act * tiles;
+    gateup_tiles<NCH_H, BITS>(a, hi, red, busy, busy ? e_guess : 0, busy ? tile / tiles : 0,
+                              busy ? (tile % tiles) * 16 : 0);
   } else {
-    float v[16];
-    wave_load_keys<16>(lrow, E, v);
-    stage_dma<NV>(a.hhi, T * L, hi);
-    if (wave < T) wave_topk<16>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
+    // every workgroup takes the top-k of every token from the router's
+    // logits, loaded together with the staged rows (one round trip), and
+    // builds the active list (the same result in each); workgroup 0
+    // publishes the routing table for the down and combine kernels
+    for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
+    const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;
+    if (E <= 512) {
+      float v[8];
+      wave_load_keys<8>(lrow, E, v);
+      stage_dma<NV>(a.hhi, T * L, hi);
+      if (wave < T) wave_topk<8>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
+    } else {
+      float v[16];
+      wave_load_keys<16>(lrow, E, v);
+      stage_dma<NV>(a.hhi, T * L, hi);
+      if (wave < T) wave_topk<16>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
+    __syncthreads();
+    build_active_list(E, T * a.top_k, rl);
+    if (blockIdx.x == 0) publish_routing(a, rl);
+    const int n_act = rl.n_act;
+    if ((int)blockIdx.x * 2 >= n_act * tiles) return;  // both tiles idle (uniform)
+    const bool busy = tile < n_act * tiles;
+    gateup_tiles<NCH_H, BITS>(a, hi, red, busy, busy ? rl.list[tile / tiles] : 0,
+                              busy ? tile / tiles : 0, busy ? (tile % tiles) * 16 : 0);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
-  __syncthreads();
-  build_active_list(E, T * a.top_k, rl);
-  if (blockIdx.x == 0) publish_routing(a, rl);
-  const int n_act = rl.n_act;
-  if ((int)blockIdx.x * 2 >= n_act * tiles) return;  // both tiles idle (uniform)
-  const bool busy = tile < n_act * tiles;
-  const int e = busy ? rl.list[tile / tiles] : 0;
-  const int n0 = busy ? (tile % tiles) * 16 : 0;
-  GateUpTask<NCH_H, BITS> task;
-  // unconditional: an idle tile reads expert 0's rows 0..15 (in range) and
-  // stores nothing, which keeps the loads and their uses in one block
-  const float gsg = a.gate.gscale[e], gsu = a.up.gscale[e];
-  task.load(a.gate, a.up, a.packed, e, I, L, n0, wave, lane);
-  issue_fence();
-  const f32x4 acc = task.mma(hi + min(t, T - 1) * L, L, wave, lane);
-  finish_gateup(acc, red, busy, gsg, gsu,
-                a.act + (size_t)(1 + (busy ? tile / tiles : 0)) * T * I, I, T, n0);
 }
 
 // ------------------------------------------------------------------ 4. down + combine
@@ -844,10 +900,45 @@ hipError_t launch_pack_bf16_decode(const uint16_t* w, int N, int K, uint16_t* pw
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& mk) {
+// Workgroups of a gate/up instantiation resident on the device at once (its
+// occupancy at the largest LDS size times the CU count), once per device.
+static int gateup_resident(const void* fn, size_t lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find({fn, dev});
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kDecThreads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cache[{fn, dev}] = per_cu * cus;
+}
+
+hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMarks& mk) {
+  DecodeArgs a = args;
   const int H = a.hidden, L = a.latent, I = a.inter, E = a.n_experts, T = a.T;
   const dim3 block(kDecThreads);
   hipError_t err;
+  // Top-k placement: in every gate/up workgroup when the gate/up grid is
+  // resident in one round (then it overlaps the staging and costs each
+  // workgroup once), else in the router's last workgroup (a second round
+  // of gate/up workgroups would pay it again).
+  {
+    int resident = 0;
+    err = with_nch(L / 256, [&](auto N) {
+      constexpr int n = decltype(N)::value;
+      const void* fn = a.gateup_bits == 3 ? (const void*)k_dec_gateup<n, 3, true>
+                                          : (const void*)k_dec_gateup<n, 4, true>;
+      hipError_t e = ensure_lds(fn, gateup_lds(kDecodeMaxT, L));
+      if (e == hipSuccess) resident = gateup_resident(fn, gateup_lds(kDecodeMaxT, L));
+      return e;
+    });
+    if (err != hipSuccess) return err;
+    a.topk_in_router = (a.max_active * (I / 16) + 1) / 2 > resident;
+  }
   // 1. h = x D^T
   err = with_nch(H / 256, [&](auto N) {
     constexpr int n = decltype(N)::value;
@@ -877,7 +968,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& 
   const auto gateup = [&](auto N, auto B) {
     constexpr int n = decltype(N)::value, bits = decltype(B)::value;
     const int nblk = (a.max_active * (I / 16) + 1) / 2;
-    const auto fn = k_dec_gateup<n, bits>;
+    const auto fn = a.topk_in_router ? k_dec_gateup<n, bits, false> : k_dec_gateup<n, bits, true>;
     hipError_t e = ensure_lds((const void*)fn, gateup_lds(kDecodeMaxT, L));
     if (e == hipSuccess) e = mk.launch(kStageGateup, fn, dim3(nblk), block, gateup_lds(T, L), a);
     return e;

@@ -157,6 +157,11 @@ struct DecodeArgs {
   int hidden, latent, inter, n_experts, top_k, n_shared, T;
   bool packed;  // D, U, R and the expert sets above are in the decode-packed layouts
   int gateup_bits;  // 4: e2m1 gate/up codes (routed and shared); 3: E1M1
+  // where the top-k runs: in the last router workgroup to finish (true) or
+  // in every gate/up workgroup (false; chosen when the gate/up grid is
+  // resident in one round)
+  bool topk_in_router;
+  unsigned* route_counter;  // router workgroups that finished (zeroed by dec_dproj)
   // scratch (workspace)
   uint16_t* hhi;       // [T][latent]
   uint16_t* hlo;       // [T][latent]

@@ -46,7 +46,7 @@ struct Layout {
   size_t d_logits;       // fp32 [T][E]
   size_t d_act;          // bf16 [1 + max_active][T][inter]
   size_t d_zpart;        // fp32 [1 + max_active][T][latent]
-  size_t d_n_act, d_list, d_wtab, d_z;
+  size_t d_n_act, d_list, d_wtab, d_counter, d_z;
   size_t total;
 };
 
@@ -85,10 +85,11 @@ Layout layout_of(const moe_latent_dims& d, int64_t T) {
     L.d_n_act = take(4);
     L.d_list = take(max_act * 4);
     L.d_wtab = take((1 + max_act) * T * 4);
+    L.d_counter = take(4);
     L.d_z = take(T * d.latent * 2);
   } else {
     L.d_hhi = L.d_hlo = L.d_logits = L.d_act = L.d_zpart = L.d_n_act = L.d_list = L.d_wtab = 0;
-    L.d_z = 0;
+    L.d_counter = L.d_z = 0;
   }
   L.total = at;
   return L;
@@ -320,6 +321,7 @@ int run_decode(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_
   a.route_n_act = (int*)(ws + L.d_n_act);
   a.route_list = (int*)(ws + L.d_list);
   a.route_wtab = (float*)(ws + L.d_wtab);
+  a.route_counter = (unsigned*)(ws + L.d_counter);
   a.max_active = d.n_experts < T * d.top_k ? d.n_experts : T * d.top_k;
   a.z = (uint16_t*)(ws + L.d_z);
   a.out = out;
