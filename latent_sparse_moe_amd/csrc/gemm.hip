@@ -717,7 +717,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   TileWork tw;
   if (!tile_work(rv, tile / nt, &tw)) return;
   const int n0 = (tile % nt) * kBN;
-  down_tile<BK, PK, 4>(act, rv, ex, y, inter, latent, tw, n0, pipe);
+  const int nb = row_blocks(tw);
+  if (nb == 1) down_tile<BK, PK, 1>(act, rv, ex, y, inter, latent, tw, n0, pipe);
+  else if (nb == 2) down_tile<BK, PK, 2>(act, rv, ex, y, inter, latent, tw, n0, pipe);
+  else down_tile<BK, PK, 4>(act, rv, ex, y, inter, latent, tw, n0, pipe);
 }
 
 // ------------------------------------------------------------------ launchers
