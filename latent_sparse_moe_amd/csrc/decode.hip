@@ -56,7 +56,6 @@ namespace moe {
 constexpr int kDecThreads = 512;  // 8 waves
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kDownRows = kDecodeDownRows;
-constexpr int kTailBatch = 32;  // partial rows loaded per round trip by the combine
 static_assert(kDownRows == kDecWaves * 16, "one 16-row tile per wave");
 
 #define AGENT __HIP_MEMORY_SCOPE_AGENT
@@ -718,24 +717,30 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_down(DecodeArgs a) {
 // makes every down workgroup's partial rows visible, which costs less than a
 // release, an arrival count and a last-arriver sum inside the down launch
 // (measured: 6.5 us of hand-off there against one extra launch here).
+// The loads cover every slot of the table's capacity (1 + max_active rows,
+// all in range), NB at a time, so none of them waits for the active count,
+// which decides only what is summed. Up to 60 rows (T <= 5 at top-10) the
+// batch stays below the 64 loads a wave can count in flight; past that one
+// batch of 96, which the compiler splits with waits, still measured faster
+// than two batches (T = 8: 63.5 -> 63.0 us per step).
+template <int NB>
 __global__ __launch_bounds__(256) void k_dec_combine(DecodeArgs a) {
   const int T = a.T, L = a.latent;
   const int i = blockIdx.x * 256 + threadIdx.x;  // t * L + n
   if (i >= T * L) return;
   const int n_act = a.route_n_act[0];
   const int s0 = a.n_shared ? 0 : 1;
+  const int last = a.max_active;  // highest slot of the table
   const size_t step = (size_t)T * L;
   const float* src = a.zpart + i;
   float v = 0.f;
-  // kTailBatch loads in flight per round trip, summed in slot order; slots
-  // past n_act re-read slot n_act (in range) and are not summed
-  for (int ss = s0; ss <= n_act; ss += kTailBatch) {
-    float p[kTailBatch];
+  for (int ss = s0; ss <= last; ss += NB) {
+    float p[NB];
 #pragma unroll
-    for (int j = 0; j < kTailBatch; ++j) p[j] = src[min(ss + j, n_act) * step];
+    for (int j = 0; j < NB; ++j) p[j] = src[min(ss + j, last) * step];
     issue_fence();  // else the first sums are placed between the loads, each a round trip
 #pragma unroll
-    for (int j = 0; j < kTailBatch; ++j)
+    for (int j = 0; j < NB; ++j)
       if (ss + j <= n_act) v += p[j];
   }
   a.z[i] = f32_to_bf16_bits(v);
@@ -988,7 +993,15 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMark
     return e;
   });
   if (err != hipSuccess) return err;
-  err = mk.launch_last(kStageDown, k_dec_combine, dim3((T * L + 255) / 256), dim3(256), 0, a);
+  {
+    const int n_rows = a.max_active + (a.n_shared ? 1 : 0);  // slots the combine reads
+    const dim3 cg((T * L + 255) / 256), cb(256);
+    err = n_rows <= 16   ? mk.launch_last(kStageDown, k_dec_combine<16>, cg, cb, 0, a)
+          : n_rows <= 32 ? mk.launch_last(kStageDown, k_dec_combine<32>, cg, cb, 0, a)
+          : n_rows <= 48 ? mk.launch_last(kStageDown, k_dec_combine<48>, cg, cb, 0, a)
+          : n_rows <= 60 ? mk.launch_last(kStageDown, k_dec_combine<60>, cg, cb, 0, a)
+                         : mk.launch_last(kStageDown, k_dec_combine<96>, cg, cb, 0, a);
+  }
   if (err != hipSuccess) return err;
   // 5. out = z U^T (+ x)
   return with_nch(L / 256, [&](auto N) {
