@@ -225,6 +225,27 @@ def test_decode_path_deterministic():
         assert np.array_equal(a[f], b[f]), f
 
 
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_decode_path_uninitialised_workspace(T):
+    """The workspace needs no initialisation: a decode call on a workspace
+    filled with 0xFF bytes (NaN floats) equals the same call on a zeroed one
+    bit for bit. This covers the combine's loads of table slots past the
+    call's active count, which hold stale values and must not be summed."""
+    cfg, host, dl = layer_for("decode145")
+    dev = device()
+    x = torch.from_numpy(synth.make_x(T, cfg.dims.hidden, 60 + T).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    outs = []
+    for fill in (0, 255):
+        say(f"[case] decode T={T}, workspace bytes set to {fill:#04x}")
+        ws = lsm.alloc_workspace(cfg.dims, T, dev)
+        ws.fill_(fill)
+        out = lsm.forward(x, dl, workspace=ws, path=lsm.PATH_DECODE)
+        torch.cuda.synchronize()
+        outs.append(out.view(torch.int16).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
 def test_auto_path_picks_decode_and_rejects_unsupported():
     cfg, host, dl = layer_for("tiny")
     x = torch.zeros((4, cfg.dims.hidden), dtype=torch.bfloat16, device=device())
