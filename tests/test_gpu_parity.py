@@ -225,22 +225,25 @@ def test_decode_path_deterministic():
         assert np.array_equal(a[f], b[f]), f
 
 
-@pytest.mark.parametrize("T", [1, 4, 8])
-def test_decode_path_uninitialised_workspace(T):
-    """The workspace needs no initialisation: a decode call on a workspace
-    filled with 0xFF bytes (NaN floats) equals the same call on a zeroed one
-    bit for bit. This covers the combine's loads of table slots past the
-    call's active count, which hold stale values and must not be summed."""
+@pytest.mark.parametrize("path,T", [(lsm.PATH_DECODE, 1), (lsm.PATH_DECODE, 4),
+                                    (lsm.PATH_DECODE, 8), (lsm.PATH_GROUPED, 300)])
+def test_uninitialised_workspace(path, T):
+    """The workspace needs no initialisation: a call on a workspace filled
+    with 0xFF bytes (NaN floats, index -1) equals the same call on a zeroed
+    one bit for bit. On the decode path this covers the combine's loads of
+    table slots past the call's active count, which hold stale values and
+    must not be summed; on the grouped path, the padded rows of partial
+    tiles, which are multiplied but never stored."""
     cfg, host, dl = layer_for("decode145")
     dev = device()
     x = torch.from_numpy(synth.make_x(T, cfg.dims.hidden, 60 + T).view(np.int16)).view(
         torch.bfloat16).to(dev)
     outs = []
     for fill in (0, 255):
-        say(f"[case] decode T={T}, workspace bytes set to {fill:#04x}")
+        say(f"[case] path={path} T={T}, workspace bytes set to {fill:#04x}")
         ws = lsm.alloc_workspace(cfg.dims, T, dev)
         ws.fill_(fill)
-        out = lsm.forward(x, dl, workspace=ws, path=lsm.PATH_DECODE)
+        out = lsm.forward(x, dl, workspace=ws, path=path)
         torch.cuda.synchronize()
         outs.append(out.view(torch.int16).cpu().numpy())
     assert np.array_equal(outs[0], outs[1])
