@@ -74,7 +74,7 @@ hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int coun
 hipError_t launch_pack_bf16(const uint16_t* w, int N, int K, uint16_t* pw, hipStream_t stream);
 
 // Routing bookkeeping (route.hip).
-constexpr int kRouteChunk = 4096;  // pairs per histogram / permute chunk
+constexpr int kRouteChunk = 2048;  // pairs per histogram / permute chunk
 constexpr int kMaxExperts = 1024;
 
 hipError_t launch_rmsnorm(const uint16_t* x, const float* w, float eps, uint16_t* u, int T,

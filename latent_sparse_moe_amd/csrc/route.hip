@@ -157,7 +157,7 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
 //   off[E+1] = pairs + n_shared*T for the shared expert's rows);
 //   tile_off likewise over ceil(count/128) (the grouped GEMM m-tiles);
 //   chunk_hist[c][e] becomes the pairs of e in chunks before c (the permute
-//   adds off[e]). A thread's chunk counts are loaded 16 at a time before
+//   adds off[e]). A thread's chunk counts are loaded 32 at a time before
 //   any is used, so the walk over the chunks is not one load round trip per
 //   chunk.
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_hist,
@@ -169,13 +169,13 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
-    for (int c0 = 0; c0 < n_chunks; c0 += 16) {
-      int v[16];
+    for (int c0 = 0; c0 < n_chunks; c0 += 32) {
+      int v[32];
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < 32; ++j)
         v[j] = c0 + j < n_chunks ? chunk_hist[(size_t)(c0 + j) * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < 32; ++j) {
         if (c0 + j < n_chunks) chunk_hist[(size_t)(c0 + j) * E + e] = cnt;
         cnt += v[j];
       }
