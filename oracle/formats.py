@@ -112,8 +112,9 @@ def unpack_e1m1(codes: np.ndarray) -> np.ndarray:
 def dequant_e1m1(codes: np.ndarray, scales: np.ndarray, gscale) -> np.ndarray:
     """One E1M1 matrix [n][k] -> float64 weights:
     W[n, k] = e1m1(code[n, k]) * e4m3(scale[n, k // 16]) * gscale."""
-    q = e1m1_value(unpack_e1m1(codes))
-    s = np.repeat(e4m3fn_value(scales), 16, axis=-1)
+    # the values of all 8 codes and 256 scale bytes, looked up per element
+    q = e1m1_value(np.arange(8))[unpack_e1m1(codes)]
+    s = np.repeat(e4m3fn_value(np.arange(256))[np.asarray(scales, dtype=np.uint8)], 16, axis=-1)
     return q * s * np.float64(np.float32(gscale))
 
 
@@ -124,7 +125,8 @@ def dequant_fp4(codes: np.ndarray, scales: np.ndarray, gscale) -> np.ndarray:
     (two-level NVFP4-style scaling: a block scale per 16 consecutive k of one
     row, and one fp32 scale for the whole matrix).
     """
-    q = e2m1_value(unpack_codes(codes))
-    s = e4m3fn_value(scales)
+    # the values of all 16 codes and 256 scale bytes, looked up per element
+    q = e2m1_value(np.arange(16))[unpack_codes(codes)]
+    s = e4m3fn_value(np.arange(256))[np.asarray(scales, dtype=np.uint8)]
     s_full = np.repeat(s, 16, axis=-1)
     return q * s_full * np.float64(np.float32(gscale))
