@@ -247,10 +247,11 @@ def pack_fp4(m: DeviceFp4, N: int, K: int, layout: int = PACK_GROUPED,
              stream: Optional[torch.cuda.Stream] = None) -> DeviceFp4:
     """A packed copy of one fp4 matrix set [count][N][K] (moe_fp4_pack)."""
     lib = load_library()
-    codes = torch.empty_like(m.codes)
-    scales = torch.empty_like(m.scales)
     if stream is None:
         stream = torch.cuda.current_stream(m.codes.device)
+    with torch.cuda.stream(stream):  # allocated on the stream the copy runs on
+        codes = torch.empty_like(m.codes)
+        scales = torch.empty_like(m.scales)
     src = m.c()
     rc = lib.moe_fp4_pack(ctypes.byref(src), m.codes.shape[0], N, K, layout, codes.data_ptr(),
                           scales.data_ptr(), stream.cuda_stream)
@@ -263,9 +264,10 @@ def pack_bf16(w: torch.Tensor, layout: int = PACK_GROUPED,
               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """A packed copy of a bf16 matrix [N][K] (moe_bf16_pack)."""
     lib = load_library()
-    out = torch.empty_like(w)
     if stream is None:
         stream = torch.cuda.current_stream(w.device)
+    with torch.cuda.stream(stream):  # allocated on the stream the copy runs on
+        out = torch.empty_like(w)
     rc = lib.moe_bf16_pack(w.data_ptr(), w.shape[0], w.shape[1], layout, out.data_ptr(),
                            stream.cuda_stream)
     if rc != 0:
@@ -311,25 +313,52 @@ class RouteDebug:
         return CRouteDebug(*[getattr(self, f).data_ptr() for f, _ in CRouteDebug._fields_])
 
 
-def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None, debug: Optional[RouteDebug] = None,
-            path: int = PATH_AUTO, residual: bool = False, norm_eps: float = 1e-6,
-            stream: Optional[torch.cuda.Stream] = None, stage_events=None) -> torch.Tensor:
-    """out = MoE(x) (or x + MoE(rmsnorm(x) * norm_w) with residual=True),
-    enqueued on ``stream`` (default: torch's current stream).
+def _check_rows(name: str, t, hidden: int) -> None:
+    """t must be a contiguous 2-D bf16 CUDA tensor [T][hidden] (the layout the
+    library reads and writes as row-major bf16)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor (got {type(t).__name__})")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16 (got {t.dtype})")
+    if t.dim() != 2 or t.shape[1] != hidden:
+        raise ValueError(f"{name} must have shape [T][{hidden}] (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
 
-    ``stage_events``: optional dict {stage name: (start, end)} of
-    torch.cuda.Event(enable_timing=True), recorded around that stage's
-    kernels on ``stream``."""
-    lib = load_library()
+
+def _check_layer_device(layer: "DeviceLayer", dev: torch.device) -> None:
+    for name in ("D", "U", "R", "bias", "norm_w"):
+        t = getattr(layer, name)
+        if t is not None and t.device != dev:
+            raise ValueError(f"layer.{name} is on {t.device}, x on {dev}")
+    for bank_name in ("experts", "shared"):
+        b = getattr(layer, bank_name)
+        if b is not None and b.gate.codes.device != dev:
+            raise ValueError(f"layer.{bank_name} is on {b.gate.codes.device}, x on {dev}")
+
+
+def _check_call(x, layer, out, workspace):
     d = layer.dims
-    T = x.shape[0]
-    if out is None:
-        out = torch.empty_like(x)
-    if workspace is None and T > 0:
-        workspace = alloc_workspace(d, T, x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device)
+    _check_rows("x", x, d.hidden)
+    if out is not None:
+        _check_rows("out", out, d.hidden)
+        if out.shape != x.shape or out.device != x.device:
+            raise ValueError(f"out must match x: shape {tuple(x.shape)} on {x.device} "
+                             f"(got {tuple(out.shape)} on {out.device})")
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous() \
+                or workspace.device != x.device:
+            raise ValueError("workspace must be a contiguous uint8 tensor on x's device")
+    # devices last, so the layout checks above also run on host tensors
+    if x.device.type != "cuda":
+        raise ValueError(f"x must be on a CUDA (HIP) device (got {x.device})")
+    _check_layer_device(layer, x.device)
+
+
+def _call_args(x, layer, out, debug, path, residual, norm_eps, stage_events):
+    """ctypes arguments shared by the forward entry points (up to and
+    excluding out / workspace), plus the objects they point into."""
+    d = layer.dims
     router = CRouter(_ptr(layer.R), _ptr(layer.bias))
     ex = layer.experts.c() if layer.experts is not None else None
     sh = layer.shared.c() if layer.shared is not None else None
@@ -346,13 +375,46 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
                  ev_arr, ctypes.pointer(gp[0]) if gp is not None else None,
                  ctypes.pointer(dp[0]) if dp is not None else None)
     dbg = debug.c() if debug is not None else None
+    head = (ctypes.byref(_dims(d)), x.shape[0], x.data_ptr(), _ptr(layer.D), _ptr(layer.U),
+            ctypes.byref(router), ctypes.byref(ex) if ex is not None else None,
+            ctypes.byref(sh) if sh is not None else None)
+    keep = (router, ex, sh, ev_arr, gp, dp, opts, dbg)
+    return head, (ctypes.byref(dbg) if dbg is not None else None), ctypes.byref(opts), keep
+
+
+def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, debug: Optional[RouteDebug] = None,
+            path: int = PATH_AUTO, residual: bool = False, norm_eps: float = 1e-6,
+            stream: Optional[torch.cuda.Stream] = None, stage_events=None) -> torch.Tensor:
+    """out = MoE(x) (or x + MoE(rmsnorm(x) * norm_w) with residual=True),
+    enqueued on ``stream`` (default: torch's current stream)
+    (moe_latent_forward_ex).
+
+    x (and ``out`` when given) must be contiguous bf16 [T][hidden] tensors on
+    one CUDA device; ``workspace`` a contiguous uint8 tensor on that device.
+    Buffers this call allocates (``out``, the workspace) come from torch's
+    allocator on ``stream``, so the allocator does not hand them to other
+    work before the kernels enqueued on ``stream`` are done with them.
+
+    ``stage_events``: optional dict {stage name: (start, end)} of
+    torch.cuda.Event(enable_timing=True), recorded around that stage's
+    kernels on ``stream``."""
+    lib = load_library()
+    _check_call(x, layer, out, workspace)
+    T = x.shape[0]
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.stream(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        if workspace is None and T > 0:
+            workspace = alloc_workspace(layer.dims, T, x.device)
+    head, dbg, opts, keep = _call_args(x, layer, out, debug, path, residual, norm_eps,
+                                       stage_events)
     rc = lib.moe_latent_forward_ex(
-        ctypes.byref(_dims(d)), T, x.data_ptr(), _ptr(layer.D), _ptr(layer.U),
-        ctypes.byref(router), ctypes.byref(ex) if ex is not None else None,
-        ctypes.byref(sh) if sh is not None else None,
-        out.data_ptr(), workspace.data_ptr() if workspace is not None else None,
-        workspace.numel() if workspace is not None else 0,
-        ctypes.byref(dbg) if dbg is not None else None, ctypes.byref(opts), stream.cuda_stream)
+        *head, out.data_ptr(), workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, dbg, opts, stream.cuda_stream)
+    del keep
     if rc != 0:
         raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
     return out

@@ -552,13 +552,18 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
       }
     }
     if (!a.topk_in_router) return;  // the gate/up workgroups take the top-k
-    __builtin_amdgcn_s_waitcnt(0);  // the logits stores complete before the arrival count
+    // Hand-off: every thread's logits stores are released at agent scope
+    // before the workgroup's arrival is counted (release fence, barrier,
+    // acquire-release increment); the last arriver acquires at agent scope
+    // before it reads any workgroup's logits.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (tid == 0)
-      last_flag = __hip_atomic_fetch_add(a.route_counter, 1u, __ATOMIC_RELAXED, AGENT) ==
+      last_flag = __hip_atomic_fetch_add(a.route_counter, 1u, __ATOMIC_ACQ_REL, AGENT) ==
                   (unsigned)(nrb - 1);
     __syncthreads();
     if (!last_flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     // the last router workgroup: top-k of every token, then the routing table
     for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
     const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;

@@ -295,3 +295,50 @@ def test_bench_helpers_on_host_layers():
     # 145B expert: 3 x 1792 x 640 weights; codes + one E4M3 byte per 16
     assert bench.rec_bytes(1792, 640, 4) == 3 * 1792 * 640 * 4 // 8 + 3 * 1792 * 640 // 16
     assert bench.rec_bytes(1792, 640, 3) == 1648640   # 2 x 3-bit + 1 x 4-bit matrices
+
+
+# ------------------------------------------------------------------ Python binding argument checks
+# The binding checks tensor dtypes, shapes, contiguity and devices before it
+# hands raw pointers to the library; host tensors are enough to exercise each
+# rejection (nothing reaches the library or a device).
+
+def _host_layer():
+    return lsm.DeviceLayer(dims=synth.TINY, D=None, U=None, R=None, bias=None, experts=None,
+                           shared=None)
+
+
+@pytest.mark.parametrize("case", ["dtype", "rank", "width", "strided", "device"])
+def test_binding_rejects_bad_x(case):
+    H = synth.TINY.hidden
+    x = torch.zeros((4, H), dtype=torch.bfloat16)
+    if case == "dtype":
+        x = x.float()
+    elif case == "rank":
+        x = x.reshape(-1)
+    elif case == "width":
+        x = torch.zeros((4, H + 32), dtype=torch.bfloat16)
+    elif case == "strided":
+        x = torch.zeros((H, 4), dtype=torch.bfloat16).t()   # [4][H] view, column-major
+    with pytest.raises((ValueError, TypeError)):
+        lsm.forward(x, _host_layer())
+
+
+@pytest.mark.parametrize("case", ["dtype", "shape", "strided"])
+def test_binding_rejects_bad_out(case):
+    H = synth.TINY.hidden
+    x = torch.zeros((4, H), dtype=torch.bfloat16)
+    out = torch.zeros((4, H), dtype=torch.bfloat16)
+    if case == "dtype":
+        out = out.float()
+    elif case == "shape":
+        out = torch.zeros((3, H), dtype=torch.bfloat16)
+    elif case == "strided":
+        out = torch.zeros((H, 4), dtype=torch.bfloat16).t()
+    with pytest.raises(ValueError, match="out"):
+        lsm.forward(x, _host_layer(), out=out)
+
+
+def test_binding_rejects_bad_workspace():
+    x = torch.zeros((4, synth.TINY.hidden), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="workspace"):
+        lsm.forward(x, _host_layer(), workspace=torch.zeros(1024, dtype=torch.int32))

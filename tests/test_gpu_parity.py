@@ -99,24 +99,31 @@ def test_decode145_more_tokens():
         run_case(f"decode145 T={T}", host, dl, x, lsm.PATH_GROUPED)
 
 
-def _sample(T, n=48, seed=0):
-    rng = np.random.default_rng(seed)
-    s = set(rng.choice(T, size=min(n, T), replace=False).tolist())
-    s.update([0, T - 1])
-    return np.array(sorted(s))
+# Full-size workloads: every output row against the oracle (the oracle takes
+# tens of seconds here, hence the longer time limit).
 
-
-def test_prefill120_sampled():
+@pytest.mark.timeout(900)
+def test_prefill120_full():
     cfg, host, dl = layer_for("prefill120")
     x = synth.make_x(cfg.T, cfg.dims.hidden, cfg.seed)
-    run_case("prefill120", host, dl, x, lsm.PATH_GROUPED, tokens=_sample(cfg.T))
+    run_case("prefill120 (every row)", host, dl, x, lsm.PATH_GROUPED)
 
 
-def test_prefill145_zipf_sampled():
+@pytest.mark.timeout(900)
+def test_prefill145_zipf_full():
     cfg, host, dl = layer_for("prefill145")
     x = synth.make_x(cfg.T, cfg.dims.hidden, cfg.seed)
-    ref, gpu = run_case("prefill145", host, dl, x, lsm.PATH_GROUPED, tokens=_sample(cfg.T))
+    ref, gpu = run_case("prefill145 (every row)", host, dl, x, lsm.PATH_GROUPED)
     say(f"  active experts {int((gpu['counts'] > 0).sum())}, hottest {int(gpu['counts'].max())}")
+
+
+@pytest.mark.timeout(900)
+def test_prefill145_zipf_full_packed():
+    """The bench's launch configuration: grouped-packed weights."""
+    cfg, host, dl = layer_for("prefill145")
+    pk = lsm.DeviceLayer(**{**dl.__dict__}).pack(decode=False)
+    x = synth.make_x(cfg.T, cfg.dims.hidden, cfg.seed)
+    run_case("prefill145 packed (every row)", host, pk, x, lsm.PATH_GROUPED)
 
 
 def test_deterministic():
@@ -153,7 +160,7 @@ def test_residual_block():
 DEC_SMALL = synth.Dims(hidden=512, latent=256, n_experts=64, inter=128, top_k=4, n_shared=1)
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_decode_path_145b(T):
     cfg, host, dl = layer_for("decode145")
     x = synth.make_x(T, cfg.dims.hidden, cfg.seed if T == 4 else 300 + T)
@@ -541,3 +548,42 @@ def test_pack_bf16_decode_layout(N, K):
             c0 = 32 * c + 8 * (l // 16)
             ref[:, c, l, :] = w[rows + l % 16, c0:c0 + 8]
     assert np.array_equal(got, ref.reshape(-1))
+
+
+# ------------------------------------------------------------------ the plain entry point
+
+@pytest.mark.parametrize("name", ["tiny", "decode145"])
+def test_plain_entry_point(name):
+    """moe_latent_forward (the call without options) through ctypes: routing
+    and output at the oracle bar, and bit for bit the result of the options
+    entry point at its defaults."""
+    import ctypes
+    cfg, host, dl = layer_for(name)
+    d, T = cfg.dims, cfg.T
+    dev = device()
+    x_bits = synth.make_x(T, d.hidden, cfg.seed)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty_like(x)
+    ws = lsm.alloc_workspace(d, T, dev)
+    dbg = lsm.RouteDebug.alloc(d, T, dev)
+    lib = lsm.load_library()
+    router = lsm.CRouter(dl.R.data_ptr(), dl.bias.data_ptr() if dl.bias is not None else None)
+    ex, sh = dl.experts.c(), dl.shared.c()
+    cdims = lsm.CDims(d.hidden, d.latent, d.n_experts, d.inter, d.top_k, d.n_shared)
+    cdbg = dbg.c()
+    say(f"[case] moe_latent_forward {name} T={T}")
+    rc = lib.moe_latent_forward(ctypes.byref(cdims), T, x.data_ptr(), dl.D.data_ptr(),
+                                dl.U.data_ptr(), ctypes.byref(router), ctypes.byref(ex),
+                                ctypes.byref(sh), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                ctypes.byref(cdbg), torch.cuda.current_stream(dev).cuda_stream)
+    assert rc == 0, lib.moe_latent_last_error().decode()
+    torch.cuda.synchronize()
+    gpu = {"out": out.float().cpu().numpy()}
+    for f in ("topk_idx", "topk_w", "counts", "offsets", "perm", "logits"):
+        gpu[f] = getattr(dbg, f).cpu().numpy()
+    ref = oracle.forward(host, x_bits)
+    check_routing(ref, gpu, d.top_k, d.n_experts)
+    err, _ = check_output(ref, gpu["out"])
+    other = run_gpu(dl, x_bits)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy(), other["out_bits"])
+    say(f"[ok] moe_latent_forward {name}: rel_l2={err:.3e}")
