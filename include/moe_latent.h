@@ -271,6 +271,35 @@ int moe_latent_forward_ex(const moe_latent_dims *dims, int64_t T, const void *x,
                           void *out, void *workspace, size_t workspace_bytes,
                           moe_route_debug *debug, const moe_latent_opts *opts, void *stream);
 
+/* Largest scratch (bytes) the allocation-free entry point serves: every
+ * call whose moe_latent_workspace_bytes() is at most this (any decode-path
+ * call at the 145B and 120B shapes, T <= 8; grouped-path calls up to a few
+ * hundred tokens at those shapes). */
+#define MOE_LATENT_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): as
+ * moe_latent_forward_ex, without the workspace arguments. The scratch is a
+ * static device array of MOE_LATENT_NOALLOC_MAX_BYTES inside the library,
+ * one per device, held from the library's first use on that device until
+ * the process ends; the call itself allocates and frees nothing. The array
+ * used is the one of the calling thread's current device, which must be
+ * the device `stream` belongs to (as for any launch). Every call on one
+ * device shares that device's array and leaves its contents behind (the
+ * kernels need no initialised scratch). Calls enqueued one after another on
+ * one stream are ordered by it; calls that can overlap on one GPU (several
+ * streams, or several host threads with their own streams) race on the
+ * array unless the caller serialises them. Returns MOE_LATENT_EWORKSPACE
+ * (before any HIP call) when moe_latent_workspace_bytes(dims, T) exceeds
+ * MOE_LATENT_NOALLOC_MAX_BYTES, MOE_LATENT_EHIP if the array's address
+ * cannot be obtained; all other arguments and errors as
+ * moe_latent_forward_ex. */
+int moe_latent_forward_noalloc(const moe_latent_dims *dims, int64_t T, const void *x,
+                               const void *D, const void *U, const moe_router *router,
+                               const moe_fp4_experts *experts, const moe_fp4_experts *shared,
+                               void *out, moe_route_debug *debug, const moe_latent_opts *opts,
+                               void *stream);
+
 /* Human-readable description of the last non-zero return on this thread
  * ("" if none). The pointer stays valid until the next call on the thread. */
 const char *moe_latent_last_error(void);

@@ -68,8 +68,9 @@ STAGES = ("norm", "dproj", "router", "topk", "route", "gateup", "down", "combine
 N_STAGES = len(STAGES)
 
 
-EXPORTS = ("moe_latent_forward", "moe_latent_forward_ex", "moe_latent_workspace_bytes",
-           "moe_latent_last_error", "moe_latent_version", "moe_fp4_pack", "moe_bf16_pack")
+EXPORTS = ("moe_latent_forward", "moe_latent_forward_ex", "moe_latent_forward_noalloc",
+           "moe_latent_workspace_bytes", "moe_latent_last_error", "moe_latent_version",
+           "moe_fp4_pack", "moe_bf16_pack")
 
 _lib = None
 
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_latent_forward.restype = ctypes.c_int
     lib.moe_latent_forward_ex.argtypes = fwd_args + [P(COpts), c_vp]
     lib.moe_latent_forward_ex.restype = ctypes.c_int
+    lib.moe_latent_forward_noalloc.argtypes = fwd_args[:9] + [P(CRouteDebug), P(COpts), c_vp]
+    lib.moe_latent_forward_noalloc.restype = ctypes.c_int
     lib.moe_latent_workspace_bytes.argtypes = [P(CDims), c_i64]
     lib.moe_latent_workspace_bytes.restype = c_size
     lib.moe_latent_last_error.argtypes = []
@@ -420,7 +423,31 @@ def forward(x: torch.Tensor, layer: DeviceLayer, *, out: Optional[torch.Tensor] 
     return out
 
 
+def forward_noalloc(x: torch.Tensor, layer: DeviceLayer, out: torch.Tensor, *,
+                    debug: Optional[RouteDebug] = None, path: int = PATH_AUTO,
+                    residual: bool = False, norm_eps: float = 1e-6,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """As forward(), through moe_latent_forward_noalloc: no workspace, the
+    library's per-device scratch array instead, and ``out`` supplied by the
+    caller (nothing is allocated). Raises MoeLatentError (EWORKSPACE) when
+    the call needs more than NOALLOC_MAX_BYTES of scratch."""
+    lib = load_library()
+    _check_call(x, layer, out, None)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    head, dbg, opts, keep = _call_args(x, layer, out, debug, path, residual, norm_eps, None)
+    rc = lib.moe_latent_forward_noalloc(*head, out.data_ptr(), dbg, opts, stream.cuda_stream)
+    del keep
+    if rc != 0:
+        raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
+    return out
+
+
+NOALLOC_MAX_BYTES = 32 << 20   # MOE_LATENT_NOALLOC_MAX_BYTES
+
+
 __all__ = ["load_library", "DeviceLayer", "DeviceExperts", "DeviceFp4", "RouteDebug", "forward",
+           "forward_noalloc", "NOALLOC_MAX_BYTES",
            "pack_fp4", "pack_experts", "pack_bf16", "PackedWeights", "PACK_GROUPED", "PACK_DECODE",
            "workspace_bytes", "alloc_workspace", "MoeLatentError", "EXPORTS",
            "PATH_AUTO", "PATH_GROUPED", "PATH_DECODE", "DECODE_MAX_T", "STAGES"]

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "kernels.hpp"
@@ -409,11 +411,50 @@ size_t moe_latent_workspace_bytes(const moe_latent_dims* dims, int64_t T) {
   return layout_of(*dims, T).total;
 }
 
-int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x, const void* D,
-                          const void* U, const moe_router* router,
-                          const moe_fp4_experts* experts, const moe_fp4_experts* shared,
-                          void* out, void* workspace, size_t workspace_bytes,
-                          moe_route_debug* debug, const moe_latent_opts* opts, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch of the allocation-free entry point: one array per device (each
+// device that loads the library's code object holds its own copy until the
+// process ends). Host code never names it as an address: its device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = MOE_LATENT_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The scratch array's device address on the calling thread's current device
+// (looked up on the first call on that device), or nullptr with the error
+// set.
+void* scratch_address() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(MOE_LATENT_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  static std::mutex mu;
+  static std::map<int, void*> by_device;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = by_device.find(dev);
+  if (it != by_device.end()) return it->second;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    fail(MOE_LATENT_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+         hipGetErrorString(e));
+    return nullptr;
+  }
+  by_device[dev] = ptr;
+  return ptr;
+}
+
+// Validation and dispatch shared by the entry points. noalloc: the
+// workspace arguments are ignored and the device's scratch array is used.
+int forward_impl(const moe_latent_dims* dims, int64_t T, const void* x, const void* D,
+                 const void* U, const moe_router* router, const moe_fp4_experts* experts,
+                 const moe_fp4_experts* shared, void* out, void* workspace,
+                 size_t workspace_bytes, moe_route_debug* debug, const moe_latent_opts* opts,
+                 void* stream, bool noalloc) {
   g_err.clear();
   int rc = check_dims(dims);
   if (rc) return rc;
@@ -529,6 +570,17 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
   const size_t xbytes = (size_t)T * d.hidden * 2;
   if (overlaps(x, xbytes, out, xbytes)) return fail(MOE_LATENT_EINVAL, "out overlaps x");
   const Layout L = layout_of(d, T);
+  if (noalloc) {
+    if (L.total > kScratchBytes)
+      return fail(MOE_LATENT_EWORKSPACE,
+                  "this call needs %zu bytes of scratch; the allocation-free entry point "
+                  "holds %zu (use moe_latent_forward_ex with a workspace)",
+                  L.total, kScratchBytes);
+    // every argument is valid: the first HIP call of this entry point
+    workspace = scratch_address();
+    if (!workspace) return MOE_LATENT_EHIP;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace) return fail(MOE_LATENT_EINVAL, "workspace is NULL");
   if (!aligned(workspace, 256)) return fail(MOE_LATENT_EINVAL, "workspace must be 256-byte aligned");
   if (workspace_bytes < L.total)
@@ -543,6 +595,28 @@ int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x,
   return run_grouped(d, (int)T, (const uint16_t*)x, (const uint16_t*)D, (const uint16_t*)U,
                      router, experts, shared, gu_bits, (uint16_t*)out, (char*)workspace, L, debug,
                      o, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_latent_forward_ex(const moe_latent_dims* dims, int64_t T, const void* x, const void* D,
+                          const void* U, const moe_router* router,
+                          const moe_fp4_experts* experts, const moe_fp4_experts* shared,
+                          void* out, void* workspace, size_t workspace_bytes,
+                          moe_route_debug* debug, const moe_latent_opts* opts, void* stream) {
+  return forward_impl(dims, T, x, D, U, router, experts, shared, out, workspace, workspace_bytes,
+                      debug, opts, stream, false);
+}
+
+int moe_latent_forward_noalloc(const moe_latent_dims* dims, int64_t T, const void* x,
+                               const void* D, const void* U, const moe_router* router,
+                               const moe_fp4_experts* experts, const moe_fp4_experts* shared,
+                               void* out, moe_route_debug* debug, const moe_latent_opts* opts,
+                               void* stream) {
+  return forward_impl(dims, T, x, D, U, router, experts, shared, out, nullptr, 0, debug, opts,
+                      stream, true);
 }
 
 int moe_latent_forward(const moe_latent_dims* dims, int64_t T, const void* x, const void* D,

@@ -342,3 +342,29 @@ def test_binding_rejects_bad_workspace():
     x = torch.zeros((4, synth.TINY.hidden), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="workspace"):
         lsm.forward(x, _host_layer(), workspace=torch.zeros(1024, dtype=torch.int32))
+
+
+def _call_noalloc(lib, dims, T=4, x=A, out=1 << 36):
+    r = lsm.CRouter(7 * A, None)
+    mats = [lsm.CFp4Matrix(8 * A, 9 * A, 10 * A, 0) for _ in range(3)]
+    ex = lsm.CFp4Experts(*mats, dims.n_experts)
+    sh = lsm.CFp4Experts(*mats, dims.n_shared)
+    rc = lib.moe_latent_forward_noalloc(ctypes.byref(dims), T, x, 2 * A, 3 * A, ctypes.byref(r),
+                                        ctypes.byref(ex), ctypes.byref(sh), out, None, None,
+                                        None)
+    return rc, lib.moe_latent_last_error().decode()
+
+
+def test_noalloc_rejects_oversized_calls_before_any_hip_call(lib):
+    d = _dims()
+    need = lib.moe_latent_workspace_bytes(ctypes.byref(d), 4096)
+    assert need > lsm.NOALLOC_MAX_BYTES
+    rc, msg = _call_noalloc(lib, d, T=4096)
+    assert rc == lsm.EWORKSPACE and "allocation-free" in msg
+    # invalid arguments are still reported as such, and T = 0 is a no-op
+    assert _call_noalloc(lib, d, x=0)[0] == lsm.EINVAL
+    assert _call_noalloc(lib, d, T=0, x=0, out=0)[0] == 0
+    # every decode-path call of the 145B and 120B layers fits the scratch array
+    for lat in (1792, 1280):
+        assert lib.moe_latent_workspace_bytes(ctypes.byref(_dims(latent=lat)), 8) \
+            <= lsm.NOALLOC_MAX_BYTES
