@@ -9,10 +9,14 @@ rotate over ``--copies`` copies at distinct HBM addresses (and each copy has
 its own input tokens) so successive steps cannot be served by the 256 MB
 Infinity Cache: one layer call touches ~97 MB.
 
-Secondary (``prefill`` object): the same layer on a 16K-token prefill with a
-Zipf(1.1) router bias, in tokens/s and matrix-core utilisation.
-``mixed_record``: the same layer with the mixed 3/4-bit expert record (3-bit
-E1M1 gate/up, 4-bit down), at decode T = 4 and per stage at the 16K prefill.
+Secondary objects:
+``prefill``: the same layer on a 16K-token prefill with a Zipf(1.1) router
+bias, in tokens/s and matrix-core utilisation; ``prefill120``: the
+120B-shaped layer (latent 1280) on a 4096-token prefill; ``mixed_record``:
+the same layer with the mixed 3/4-bit expert record (3-bit E1M1 gate/up,
+4-bit down), at decode T = 4 and per stage at the 16K prefill; ``stack``:
+48 residual blocks of 145B shapes, all resident, one decode step at T = 8
+(bytes, GB/s and fraction of the HBM peak).
 
 ``value`` comes from K back-to-back steps with no events inside the timed
 region. A second pass over the same K steps records HIP events on the launch
@@ -21,8 +25,9 @@ stream around the dominant kernel (``roofline``) and at every step boundary
 they stay out of the headline pass. ``roofline.traffic`` is read from the
 committed rocprofv3 counter summary of that kernel when the kernel source is
 unchanged since the counters were taken, else null. ``cpu_baseline`` is the
-float64 oracle on the host cores, on a bounded sample of the same decode
-workload.
+float64 oracle on the host cores (median whole-layer call time of the same
+decode workload, all cores and one thread, each in a child process with its
+BLAS thread count set).
 
 Profiling helpers: ``--only copy`` runs a plain 1 GiB device copy (the
 calibration kernel for the HBM byte counters), ``--only decode`` /
@@ -100,14 +105,16 @@ def parse():
     p.add_argument("--prefill-warmup", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
-    p.add_argument("--only", choices=["decode", "prefill", "copy", "stack", "mixed"], default=None,
-                   help="run one workload and print its object (profiling; 'stack' is the "
-                        "48-block residual stack at T = 8, reported only this way)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="oracle time per CPU measurement (all cores; half of it at one thread)")
+    p.add_argument("--only", choices=["decode", "prefill", "prefill120", "copy", "stack", "mixed"],
+                   default=None, help="run one workload and print its object (profiling)")
     p.add_argument("--no-mixed", action="store_true",
                    help="skip the mixed 3/4-bit expert record")
     p.add_argument("--no-family", action="store_true",
                    help="skip the decode shape family (T = 1, 2, 3, 5, 8), e.g. under a profiler")
+    p.add_argument("--no-stack", action="store_true",
+                   help="skip the 48-block stack (its 48 layers take about 2 minutes to generate)")
     p.add_argument("--stack-steps", type=int, default=20)
     p.add_argument("--stack-warmup", type=int, default=3)
     p.add_argument("--summarize-pmc", metavar="CSV", default=None,
@@ -361,7 +368,6 @@ def bench_decode(args, torch, lsm, synth, dev):
             "shape_family": (None if args.no_family else
                              decode_family(args, torch, lsm, synth, d, layers, path, dev)),
         },
-        "host": host, "x0": xs_host[0],
     }
     return res
 
@@ -396,12 +402,15 @@ def decode_family(args, torch, lsm, synth, d, layers, path, dev, Ts=(1, 2, 3, 5,
     return out
 
 
-def bench_prefill(args, torch, lsm, synth, dev):
-    cfg = synth.CONFIGS["prefill145"]
+def bench_prefill(args, torch, lsm, synth, dev, name="prefill145"):
+    """A prefill workload on the grouped path: ``prefill145`` (16K tokens,
+    145B shapes, Zipf(1.1) router bias) or ``prefill120`` (4096 tokens,
+    latent 1280, no bias)."""
+    cfg = synth.CONFIGS[name]
     d, T = cfg.dims, cfg.T
     t0 = time.time()
     host = synth.make_layer(d, cfg.seed, cfg.bias, cfg.zipf_s)
-    log(f"[prefill] generated layer in {time.time() - t0:.1f}s")
+    log(f"[{name}] generated layer in {time.time() - t0:.1f}s")
     # experts also in the packed layout the grouped kernels load from (a
     # one-time reorder at load time, outside the timed region)
     dl = lsm.DeviceLayer.from_host(host, dev).pack(decode=False)
@@ -429,7 +438,7 @@ def bench_prefill(args, torch, lsm, synth, dev):
     torch.cuda.synchronize()
     st = stage_times(lsm, torch, step, names, n=3)
     dom = max(st, key=st.get)
-    log(f"[prefill] stage ms: " + ", ".join(f"{s}={v:.3f}" for s, v in st.items()))
+    log(f"[{name}] stage ms: " + ", ".join(f"{s}={v:.3f}" for s, v in st.items()))
     for _ in range(args.prefill_warmup):
         step()
     torch.cuda.synchronize()
@@ -452,8 +461,10 @@ def bench_prefill(args, torch, lsm, synth, dev):
     step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.prefill_steps)]
     dom_tf = fl[dom] / (dom_ms * 1e-3) / 1e12 if dom in fl else None
     layer_tf = total_flop / (ms * 1e-3) / 1e12
+    what = ("16K prefill tokens/s (145B-shaped layer, Zipf router bias)" if name == "prefill145"
+            else f"{T}-token prefill tokens/s (120B-shaped layer, latent {d.latent})")
     return {
-        "metric": "16K prefill tokens/s (145B-shaped layer, Zipf router bias)",
+        "metric": what,
         "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
         "steps": args.prefill_steps, "warmup": args.prefill_warmup,
         "layer_tflops": layer_tf, "layer_frac_of_bf16_peak": layer_tf / BF16_PEAK_TFLOPS,
@@ -466,9 +477,10 @@ def bench_prefill(args, torch, lsm, synth, dev):
                      "kernel_ms": dom_ms},
         "step_ms_with_events": {k: round(v, 4) for k, v in percentiles(step_ms).items()},
         "stage_ms_untimed_pass": {s: round(v, 4) for s, v in st.items()},
-        "config": {"workload": "prefill145", "T": T, "hidden": d.hidden, "latent": d.latent,
+        "config": {"workload": name, "T": T, "hidden": d.hidden, "latent": d.latent,
                    "experts": d.n_experts, "inter": d.inter, "top_k": d.top_k,
-                   "shared": d.n_shared, "router_bias": "zipf(1.1)"},
+                   "shared": d.n_shared,
+                   "router_bias": "zipf(1.1)" if cfg.bias == "zipf" else "none"},
     }
 
 
@@ -571,6 +583,8 @@ def bench_stack(args, torch, lsm, synth, dev):
         # decode-packed copies only: the plain weights are freed once packed
         dls.append(lsm.DeviceLayer.from_host(h, dev).pack(grouped=False).drop_plain())
         del h
+        if (l + 1) % 8 == 0:
+            log(f"[stack] {l + 1}/{nl} blocks resident ({time.time() - t0:.0f}s)")
     log(f"[stack] generated and uploaded {nl} blocks in {time.time() - t0:.1f}s")
     x = torch.from_numpy(synth.make_x(T, d.hidden, cfg.seed).view("int16")).view(torch.bfloat16).to(dev)
     bufs = [torch.empty_like(x), torch.empty_like(x)]
@@ -647,28 +661,79 @@ def _tensors(v):
         yield v
 
 
-def cpu_baseline(args, host, x0):
+def cpu_child(threads, seconds, min_calls):
+    """Runs in a child process started with OMP_NUM_THREADS and
+    OPENBLAS_NUM_THREADS = threads (set before numpy loads its BLAS): the
+    float64 oracle on the decode workload (145B layer, T = 4, seed 0), whole
+    layer calls back to back for about ``seconds`` (at least ``min_calls``);
+    prints one JSON object."""
     import numpy as np
     import oracle
+    import synth
+    cfg = synth.CONFIGS["decode145"]
+    host = synth.make_layer(cfg.dims, cfg.seed, cfg.bias, cfg.zipf_s)
+    x0 = synth.make_x(cfg.T, cfg.dims.hidden, cfg.seed)
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        threads = 1
-    n, t0 = 0, time.perf_counter()
-    while True:
+        blas = None
+    ts, t0 = [], time.perf_counter()
+    while len(ts) < min_calls or time.perf_counter() - t0 < seconds:
+        a = time.perf_counter()
         oracle.forward(host, x0)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or n >= 200:
+        ts.append(time.perf_counter() - a)
+        if len(ts) >= 20:
             break
-    T = x0.shape[0]
-    return {"value": T * n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} full decode-layer calls (T={T}) of the float64 oracle, {el:.1f}s; "
-                      f"host os.cpu_count()={os.cpu_count()}"}
+    print(json.dumps({"threads": threads, "blas_threads": blas, "calls": len(ts),
+                      "median_s": statistics.median(ts), "T": int(x0.shape[0])}), flush=True)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(args):
+    """The float64 oracle, untuned, on the host cores: median time of whole
+    decode-layer calls (T = 4) with every host core, and with one, each in
+    a child process whose OMP_NUM_THREADS / OPENBLAS_NUM_THREADS are set."""
+    import subprocess
+    n = min(os.cpu_count() or 1, 64)
+    runs = {}
+    for threads, secs, mn in ((n, args.cpu_seconds, 5), (1, args.cpu_seconds / 2, 3)):
+        env = dict(os.environ, OMP_NUM_THREADS=str(threads), OPENBLAS_NUM_THREADS=str(threads),
+                   MKL_NUM_THREADS=str(threads))
+        res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-child",
+                              str(threads), str(secs), str(mn)], env=env, capture_output=True,
+                             text=True, timeout=600)
+        if res.returncode != 0:
+            raise RuntimeError(f"cpu baseline child failed: {res.stderr[-2000:]}")
+        runs[threads] = json.loads(res.stdout.strip().splitlines()[-1])
+        log(f"[cpu] {threads} threads: median {runs[threads]['median_s']:.2f} s per call over "
+            f"{runs[threads]['calls']} calls")
+    full, one = runs[n], runs[1]
+    T = full["T"]
+    return {"value": T / full["median_s"], "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "impl": "float64 oracle (numpy)",
+            "sample": f"median of {full['calls']} whole decode-layer calls (145B shapes, T={T}) "
+                      f"with OMP_NUM_THREADS=OPENBLAS_NUM_THREADS={n}",
+            "median_s_per_call": full["median_s"], "blas_threads": full["blas_threads"],
+            "one_thread": {"value": T / one["median_s"], "unit": "tokens/s",
+                           "median_s_per_call": one["median_s"], "calls": one["calls"]},
+            "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def main():
+    if len(sys.argv) == 5 and sys.argv[1] == "--cpu-child":
+        cpu_child(int(sys.argv[2]), float(sys.argv[3]), int(sys.argv[4]))
+        return
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -689,8 +754,9 @@ def main():
     if args.only == "copy":
         print(json.dumps(copy_probe(torch, dev)), flush=True)
         return
-    if args.only == "prefill":
-        print(json.dumps(bench_prefill(args, torch, lsm, synth, dev)), flush=True)
+    if args.only in ("prefill", "prefill120"):
+        print(json.dumps(bench_prefill(args, torch, lsm, synth, dev, args.only.replace(
+            "prefill", "prefill145") if args.only == "prefill" else args.only)), flush=True)
         return
     if args.only == "stack":
         print(json.dumps(bench_stack(args, torch, lsm, synth, dev)), flush=True)
@@ -700,10 +766,8 @@ def main():
         return
     dec = bench_decode(args, torch, lsm, synth, dev)
     if args.only == "decode":
-        dec.pop("host"), dec.pop("x0")
         print(json.dumps(dec), flush=True)
         return
-    host, x0 = dec.pop("host"), dec.pop("x0")
     torch.cuda.empty_cache()
     line = {
         "metric": "latent-MoE layer tokens/sec: decode T=4 (HBM GB/s) and 16K prefill (MFMA %)",
@@ -718,19 +782,18 @@ def main():
         "decode_detail": dec["detail"],
     }
     if not args.no_prefill:
-        del host
         line["prefill"] = bench_prefill(args, torch, lsm, synth, dev)
-        host = None
+        torch.cuda.empty_cache()
+        line["prefill120"] = bench_prefill(args, torch, lsm, synth, dev, "prefill120")
         torch.cuda.empty_cache()
     if not args.no_mixed:
         line["mixed_record"] = bench_mixed(args, torch, lsm, synth, dev)
         torch.cuda.empty_cache()
+    if not args.no_stack:
+        line["stack"] = bench_stack(args, torch, lsm, synth, dev)
+        torch.cuda.empty_cache()
     if not args.no_cpu:
-        if host is None:
-            import synth as _s
-            cfg = _s.CONFIGS["decode145"]
-            host = _s.make_layer(cfg.dims, cfg.seed, cfg.bias, cfg.zipf_s)
-        line["cpu_baseline"] = cpu_baseline(args, host, x0)
+        line["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(line), flush=True)
 
 

@@ -1,0 +1,76 @@
+"""All 48 blocks of the residual stack workload (145B shapes, T = 8, Zipf
+router bias, block l drawn with seed l) on the decode path, the
+configuration the stack benchmark times (needs an MI355X).
+
+Blocks are generated, checked and freed one at a time, so device and host
+memory hold one block. For every block l:
+
+* the GPU's MoE on the oracle chain's MoE input u_l = bf16(rmsnorm(x_l) g):
+  routing exact (near ties excluded) and every output row at the layer bar;
+* the GPU's own chain (its RMSNorm, MoE and residual add): block l applied
+  to the GPU chain's x_l, against the oracle's block on that same x_l:
+  routing and every row of the block's MoE part (x_{l+1} - x_l) at the
+  layer bar, near ties excluded.
+
+The two chains themselves are not compared at the bar: they drift apart
+(bf16 roundings of the residual stream differ in the last bit, and a
+routing choice near a tie then goes one way on one side and the other way
+on the other in some later block), so after 48 blocks they are different
+trajectories; the drift is printed."""
+import numpy as np
+import pytest
+import torch
+
+import latent_sparse_moe_amd as lsm
+import oracle
+import synth
+from gpu_helpers import check_output, check_routing, rel_l2, row_rel_l2, run_gpu, say, device
+from oracle.latent_moe import _to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.timeout(900)
+def test_stack145_all_48_blocks_decode_path():
+    cfg = synth.CONFIGS["stack145"]
+    d, nl = cfg.dims, cfg.n_layers
+    x0 = synth.make_x(cfg.T, d.hidden, cfg.seed)
+    cur = x0            # GPU chain state (bf16 bits)
+    xo = x0             # oracle chain state
+    worst_moe = worst_chain = 0.0
+    excluded = 0
+    for l in range(nl):
+        host = synth.make_layer(d, cfg.seed + l, cfg.bias, cfg.zipf_s)
+        dl = lsm.DeviceLayer.from_host(host, device())
+        # the MoE on the oracle chain's own input
+        y, res = oracle.block_forward(host, xo, 1e-6)
+        u = _to_bf16_bits(oracle.rmsnorm(oracle.bf16_value(xo), host.norm_w, 1e-6))
+        say(f"[case] stack145 block {l}: MoE on the oracle chain's input, decode path")
+        gpu = run_gpu(dl, u, path=lsm.PATH_DECODE)
+        check_routing(res, gpu, d.top_k, d.n_experts)
+        err, _ = check_output(res, gpu["out"])
+        worst_moe = max(worst_moe, err)
+        # the GPU chain's block l against the oracle's block on the same x_l
+        say(f"[case] stack145 block {l}: GPU chain block, decode path, residual")
+        g = run_gpu(dl, cur, path=lsm.PATH_DECODE, residual=True)
+        yc, rc = oracle.block_forward(host, cur, 1e-6)
+        check_routing(rc, g, d.top_k, d.n_experts)
+        ok = rc.gap >= 1e-4
+        excluded += int((~ok).sum())
+        # the block's output is a bf16 tensor (the residual stream between
+        # blocks) on both sides: the oracle's block output is rounded as its
+        # own chain rounds it
+        xc = oracle.bf16_value(cur)
+        yb = oracle.bf16_value(_to_bf16_bits(yc))
+        rows = row_rel_l2(g["out"][ok] - xc[ok], yb[ok] - xc[ok])
+        assert rows.size == 0 or rows.max() <= 2e-2, (l, rows.max())
+        worst_chain = max([worst_chain] + rows.tolist())
+        cur = g["out_bits"].view(np.uint16)
+        xo = _to_bf16_bits(y)
+        del dl
+        torch.cuda.empty_cache()
+    xv0 = oracle.bf16_value(x0)
+    drift = rel_l2(oracle.bf16_value(cur) - xv0, oracle.bf16_value(xo) - xv0)
+    say(f"[ok] 48 blocks: worst MoE rel_l2 on the oracle's inputs {worst_moe:.3e}; worst row of "
+        f"the GPU chain's blocks {worst_chain:.3e} ({excluded} near-tie token-blocks left out); "
+        f"drift of the two chains after 48 blocks {drift:.3e}")
