@@ -123,7 +123,7 @@
 extern "C" {
 #endif
 
-#define MOE_LATENT_ABI_VERSION 3
+#define MOE_LATENT_ABI_VERSION 4
 
 #define MOE_LATENT_OK 0
 #define MOE_LATENT_EINVAL (-1)       /* null pointer, bad size, misaligned pointer, aliasing */
@@ -167,6 +167,10 @@ typedef struct moe_packed_weights {
   const void *D;                  /* bf16 [latent][hidden] */
   const void *U;                  /* bf16 [hidden][latent] */
   const void *R;                  /* bf16 router.w [n_experts][latent] */
+  /* decode path only, optional: the router folded onto the residual width
+   * (moe_router_fold). Given, the decode path computes the logits from x in
+   * the same launch as h = x D^T and does not read R. */
+  const void *RD;
 } moe_packed_weights;
 
 /* Packing layouts (moe_fp4_pack, moe_bf16_pack). */
@@ -232,9 +236,9 @@ typedef struct moe_latent_opts {
    * D, n_experts % 32 == 0 for R (else MOE_LATENT_EUNSUPPORTED). */
   const moe_packed_weights *grouped_packed;
   /* NULL, or decode-packed copies: all of experts, shared (n_shared = 1),
-   * D, U and R, read by the decode path instead of the plain arguments.
-   * Needs n_experts % 16 == 0 (the decode path's dims rules give the rest).
-   * Neither path reads the other's copies. */
+   * D, U and R or RD (or both), read by the decode path instead of the
+   * plain arguments. Needs n_experts % 16 == 0 (the decode path's dims
+   * rules give the rest). Neither path reads the other's copies. */
   const moe_packed_weights *decode_packed;
 } moe_latent_opts;
 
@@ -325,6 +329,22 @@ int moe_fp4_pack(const moe_fp4_matrix *src, int32_t count, int32_t N, int32_t K,
  * K % 64; decode: N % 16, K % 32); EINVAL for an unknown layout, NULL,
  * misaligned or overlapping buffers. */
 int moe_bf16_pack(const void *src, int32_t N, int32_t K, int32_t layout, void *dst, void *stream);
+
+/* The router folded onto the residual width, for the decode path: since
+ * l = h R^T + b with h = x D^T (the layer recipe above), l = x W^T + b with
+ * W = R D, [n_experts][hidden]. W is accumulated in fp64 and stored as two
+ * bf16 matrices, hi = bf16(W) and lo = bf16(W - hi) (together about 16
+ * significant bits, as the latent vector's hi + lo halves the unfolded
+ * router reads), each in the decode-packed bf16 layout, hi first: dst holds
+ * 2 * n_experts * hidden bf16 (device memory, 16-byte aligned, overlapping
+ * neither D nor R). D and R are the plain layouts (bf16 [latent][hidden],
+ * [n_experts][latent]). A one-time step when weights are loaded, enqueued
+ * on `stream`. The decode path reads dst through moe_packed_weights.RD; its
+ * logits then agree with the unfolded router's to rounding (not bit for
+ * bit). MOE_LATENT_EUNSUPPORTED unless n_experts % 16 == 0 and
+ * hidden % 32 == 0; EINVAL for NULL, misaligned or overlapping buffers. */
+int moe_router_fold(const moe_latent_dims *dims, const void *D, const void *R, void *dst,
+                    void *stream);
 
 #ifdef __cplusplus
 }

@@ -51,7 +51,7 @@ class CRouteDebug(ctypes.Structure):
 
 class CPackedWeights(ctypes.Structure):
     _fields_ = [("experts", ctypes.POINTER(CFp4Experts)), ("shared", ctypes.POINTER(CFp4Experts)),
-                ("D", c_vp), ("U", c_vp), ("R", c_vp)]
+                ("D", c_vp), ("U", c_vp), ("R", c_vp), ("RD", c_vp)]
 
 
 class COpts(ctypes.Structure):
@@ -70,7 +70,7 @@ N_STAGES = len(STAGES)
 
 EXPORTS = ("moe_latent_forward", "moe_latent_forward_ex", "moe_latent_forward_noalloc",
            "moe_latent_workspace_bytes", "moe_latent_last_error", "moe_latent_version",
-           "moe_fp4_pack", "moe_bf16_pack")
+           "moe_fp4_pack", "moe_bf16_pack", "moe_router_fold")
 
 _lib = None
 
@@ -103,6 +103,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_fp4_pack.restype = ctypes.c_int
     lib.moe_bf16_pack.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]
     lib.moe_bf16_pack.restype = ctypes.c_int
+    lib.moe_router_fold.argtypes = [P(CDims), c_vp, c_vp, c_vp, c_vp]
+    lib.moe_router_fold.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -164,12 +166,16 @@ class DeviceLayer:
     decode_packed: Optional["PackedWeights"] = None
 
     def pack(self, grouped: bool = True, decode: bool = True,
-             stream: Optional[torch.cuda.Stream] = None) -> "DeviceLayer":
+             stream: Optional[torch.cuda.Stream] = None,
+             fold_router: bool = True) -> "DeviceLayer":
         """Adds packed copies of the weights (same bytes, reordered so each
         wave's loads are contiguous). Grouped: each matrix whose dims allow
         it (experts: latent and inter % 64; D: hidden % 64; U: latent % 64;
         router rows: also n_experts % 32). Decode: every matrix, when the
-        decode kernels take these dims and n_experts % 16 == 0."""
+        decode kernels take these dims and n_experts % 16 == 0, and (with
+        fold_router) the router folded onto the residual width
+        (moe_router_fold), which lets the decode path compute the logits
+        from x beside h = x D^T."""
         d = self.dims
         if grouped:
             g = PackedWeights()
@@ -190,7 +196,8 @@ class DeviceLayer:
                 pack_experts(self.experts, d, PACK_DECODE, stream),
                 pack_experts(self.shared, d, PACK_DECODE, stream) if self.shared is not None else None,
                 pack_bf16(self.D, PACK_DECODE, stream), pack_bf16(self.U, PACK_DECODE, stream),
-                pack_bf16(self.R, PACK_DECODE, stream))
+                pack_bf16(self.R, PACK_DECODE, stream),
+                fold_router_weights(d, self.D, self.R, stream) if fold_router else None)
         return self
 
     def drop_plain(self) -> "DeviceLayer":
@@ -235,6 +242,7 @@ class PackedWeights:
     D: Optional[torch.Tensor] = None
     U: Optional[torch.Tensor] = None
     R: Optional[torch.Tensor] = None
+    RD: Optional[torch.Tensor] = None   # decode only: folded router (moe_router_fold)
 
     def c(self):
         """(CPackedWeights, objects to keep alive while it is used)."""
@@ -242,7 +250,7 @@ class PackedWeights:
         sh = self.shared.c() if self.shared is not None else None
         cp = CPackedWeights(ctypes.pointer(ex) if ex is not None else None,
                             ctypes.pointer(sh) if sh is not None else None,
-                            _ptr(self.D), _ptr(self.U), _ptr(self.R))
+                            _ptr(self.D), _ptr(self.U), _ptr(self.R), _ptr(self.RD))
         return cp, (ex, sh)
 
 
@@ -273,6 +281,23 @@ def pack_bf16(w: torch.Tensor, layout: int = PACK_GROUPED,
         out = torch.empty_like(w)
     rc = lib.moe_bf16_pack(w.data_ptr(), w.shape[0], w.shape[1], layout, out.data_ptr(),
                            stream.cuda_stream)
+    if rc != 0:
+        raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
+    return out
+
+
+def fold_router_weights(dims, D: torch.Tensor, R: torch.Tensor,
+                        stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The router folded onto the residual width, W = R D, as bf16 hi and lo
+    matrices in the decode-packed layout (moe_router_fold): bf16
+    [2][n_experts][hidden]."""
+    lib = load_library()
+    if stream is None:
+        stream = torch.cuda.current_stream(D.device)
+    with torch.cuda.stream(stream):
+        out = torch.empty((2, dims.n_experts, dims.hidden), dtype=torch.bfloat16, device=D.device)
+    rc = lib.moe_router_fold(ctypes.byref(_dims(dims)), D.data_ptr(), R.data_ptr(), out.data_ptr(),
+                             stream.cuda_stream)
     if rc != 0:
         raise MoeLatentError(rc, lib.moe_latent_last_error().decode())
     return out
@@ -449,5 +474,6 @@ NOALLOC_MAX_BYTES = 32 << 20   # MOE_LATENT_NOALLOC_MAX_BYTES
 __all__ = ["load_library", "DeviceLayer", "DeviceExperts", "DeviceFp4", "RouteDebug", "forward",
            "forward_noalloc", "NOALLOC_MAX_BYTES",
            "pack_fp4", "pack_experts", "pack_bf16", "PackedWeights", "PACK_GROUPED", "PACK_DECODE",
+           "fold_router_weights",
            "workspace_bytes", "alloc_workspace", "MoeLatentError", "EXPORTS",
            "PATH_AUTO", "PATH_GROUPED", "PATH_DECODE", "DECODE_MAX_T", "STAGES"]

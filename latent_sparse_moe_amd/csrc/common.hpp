@@ -117,6 +117,24 @@ __device__ __forceinline__ bf16x8 e2m1x8_to_bf16(uint32_t codes) {
   return r;
 }
 
+// Waits until at most n vector-memory loads of this wave are outstanding
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left
+// at "no wait"). Loads complete in issue order, so this waits for all but
+// the n most recent.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads still in
+// flight are not waited for (a full __syncthreads() would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <class T>
 __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);

@@ -2,44 +2,39 @@
 //
 // At a handful of tokens every weight byte feeds only T multiply-adds, so the
 // layer is bound by HBM bandwidth and by the fixed latency of each dependent
-// step. Six kernels; in each, every wave issues its loads before anything
-// else (the router and routed gate/up kernels first stage their activations),
-// and a kernel boundary is the only grid-wide synchronisation (no workgroup
-// ever waits for another one to be scheduled):
+// step (a kernel boundary costs a launch plus at least one memory round
+// trip). Four kernels, each a grid-wide dependency of the next:
 //
-//   1. dec_dproj   h = x D^T (RMSNorm fused for the residual block); K split
-//                  over the 8 waves; h leaves as bf16 hi + lo
-//   2. dec_router  logits = (hi + lo) R^T + b, 16 experts per workgroup. The
-//                  shared expert's gate/up (routing-independent) runs in the
-//                  same launch.
-//   3. dec_gateup  every workgroup first takes the top-k of every token and
-//                  builds the active list (workgroup 0 also publishes the
-//                  routing table); then one wave per (routed expert, 16
-//                  intermediate rows, matrix, K half): silu(gate) * up
-//   4. dec_down    one workgroup per (expert slot, 128 latent rows): the slot's
-//                  activations are staged once in LDS, each wave takes 16 rows;
-//                  partial rows, weighted by the gate weights, go to a per-slot
-//                  buffer
-//   5. dec_combine z = the slots' partial rows summed in slot order (bf16)
-//   6. dec_uproj   out = z U^T (+ x)
+//   1. dec_front   h = x D^T (RMSNorm fused for the residual block) and, in
+//                  the same launch, the router logits straight from x: the
+//                  router folded onto the residual width, W = R D (computed
+//                  once when the weights are packed, stored as bf16 hi + lo),
+//                  gives l = x W^T = (x D^T) R^T. Without a folded router the
+//                  logits come from h in a second launch (dec_dproj writes h
+//                  as bf16 hi + lo, dec_router reads both halves).
+//   2. dec_gateup  one workgroup per CU; each takes the top-k of every token
+//                  from the logits and builds the active-expert list
+//                  (workgroup 0 publishes the routing table); then the
+//                  (expert slot, 16 intermediate rows) tasks are split
+//                  evenly over the grid, one per wave at a time: the gate
+//                  and the up tile over the whole latent width, SiLU * up
+//                  in registers. Slot 0 is the shared expert.
+//   3. dec_down    one workgroup per (16 latent rows, group of 8 slots), one
+//                  slot per wave; the weighted products are summed in slot
+//                  order and added into z in 64-bit fixed point with
+//                  integer atomics (exact, so the arrival order does not
+//                  matter)
+//   4. dec_uproj   out = bf16(z) U^T (+ x)
 //
 // Matrix-core tiles are v_mfma_f32_16x16x32_bf16 with weight rows as the M
 // operand (16 rows) and tokens as the N operand (16 columns, T used; the rest
 // repeat token T - 1 and are never stored, so no operand load is
 // conditional). Lane l serves weight row l%16; its lane group g = l/16 takes
 // every fourth chunk of the wave's K range (chunk c*4 + g at step c), so one
-// load instruction reads 64 contiguous bytes of each of 16 rows. K order
-// inside a dot product is free; the token operand is read with the same
-// chunk mapping.
-//
-// Every gate/up workgroup repeats the top-k (some hundreds of dependent
-// instructions per token, on one wave per token) instead of one workgroup
-// of the router launch taking it after an in-launch hand-off (logits
-// stores, an arrival count, the last arriver's gather): measured, the
-// repeated top-k costs gate/up about what the hand-off and tail cost the
-// router at T = 4, and less at T = 1..3 (1.5 to 3.7 us per step).
-//
-// Data moves between workgroups only across kernel boundaries.
+// load instruction reads 64 contiguous bytes of each of 16 rows (1 KB of
+// contiguous memory on the decode-packed copies). K order inside a dot
+// product is free; the token operand is read with the same chunk mapping.
+// Every wave issues all its weight loads before its first product.
 #include <limits.h>
 
 #include <map>
@@ -55,8 +50,8 @@ namespace moe {
 
 constexpr int kDecThreads = 512;  // 8 waves
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kDownRows = kDecodeDownRows;
-static_assert(kDownRows == kDecWaves * 16, "one 16-row tile per wave");
+constexpr int kDownGroup = kDecodeDownGroup;
+static_assert(kDownGroup == kDecWaves, "one expert slot per down wave");
 
 #define AGENT __HIP_MEMORY_SCOPE_AGENT
 
@@ -257,37 +252,55 @@ __device__ __forceinline__ void stage_dma(const uint16_t* src, int count, uint16
   }
 }
 
-// Dynamic LDS layouts (bytes), sized by the call's T.
+
+// As stage_dma, by one wave into its own region (no workgroup barrier
+// needed before the wave reads it): lane l moves 16-byte slots l, l + 64,
+// ...; at most 63 slots past count are written (regions are padded to a
+// whole number of 1 KB).
+template <int NV>
+__device__ __forceinline__ void stage_dma_wave(const uint16_t* src, int count, uint16_t* dst) {
+  const int lane = threadIdx.x & 63;
+  const int nslots = count / 8;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int first = v * 64;
+    if (first < nslots)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)min(first + lane, nslots - 1) * 8),
+                                       (__attribute__((address_space(3))) void*)(dst + first * 8),
+                                       16, 0, 0);
+  }
+}
+
+// Dynamic LDS layouts (bytes), sized by the call's T. Regions that
+// stage_dma fills keep 1 KB behind them (its overrun).
 constexpr size_t kRedBytes = kDecWaves * 64 * 4 * sizeof(float);
-inline size_t dproj_lds(int T, int H) { return (size_t)T * H * 2 + kRedBytes + kDecodeMaxT * 4; }
+constexpr size_t kDmaPad = 1024;
+inline size_t front_lds(int T, int H) { return (size_t)T * H * 2 + kRedBytes + kDecodeMaxT * 4; }
 inline size_t router_lds(int T, int L) { return (size_t)2 * T * L * 2 + kRedBytes; }
-inline size_t gateup_lds(int T, int L) { return (size_t)T * L * 2 + kRedBytes; }
-inline size_t down_lds(int T, int I) { return (size_t)T * I * 2; }
+inline size_t gateup_lds(int T, int L) { return (size_t)T * L * 2 + kDmaPad; }
+// a down wave's activation region (elements): T x inter rounded up to 1 KB
+__host__ __device__ inline int down_region(int T, int I) { return (T * I + 511) / 512 * 512; }
+inline size_t down_lds(int T, int I) {
+  return (size_t)kDownGroup * down_region(T, I) * 2 + kRedBytes;
+}
 inline size_t uproj_lds(int T, int L) { return (size_t)T * L * 2 + kRedBytes; }
 
-// ------------------------------------------------------------------ 1. D
+// ------------------------------------------------------------------ 1. D (+ folded router)
 
-template <int NCH>
-__global__ __launch_bounds__(kDecThreads) void k_dec_dproj(DecodeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  const int H = a.hidden, L = a.latent, T = a.T;
-  uint16_t* xs = lds;                       // [T][H] bf16
-  float* red = (float*)(lds + T * H);       // [8][64][4]
-  float* rstd = red + kDecWaves * 64 * 4;   // [T]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, t = lane & 15;
-  const int row0 = blockIdx.x * 16;
-  const int kb = wave * (H / kDecWaves);
-  if (a.topk_in_router && blockIdx.x == 0 && tid == 0) *a.route_counter = 0u;
-  RowStage<(NCH + 1) / 2> xr;  // T x hidden, hidden = 256 NCH
-  xr.load(a.x, T * H);
-  Bf16Rows<NCH> wr;
-  int step;
-  const uint16_t* wb = bf16_lane(a.D, a.packed, L, H, row0, kb, &step);
-  wr.load(wb, step);
-  xr.store(xs, T * H);
-  __syncthreads();
-  if (a.norm_weight) {  // residual block: RMSNorm per token in fp32, then bf16, in place
+// Stages x (T x hidden) into LDS: the loads are issued by load(), the
+// caller issues its weight loads, then finish() stores the rows and (for the
+// residual block) applies RMSNorm in place: per token, in fp32, rounded to
+// bf16 (the layer's input is a bf16 tensor).
+template <int NV>
+struct XStage {
+  RowStage<NV> r;
+  __device__ __forceinline__ void load(const DecodeArgs& a) { r.load(a.x, a.T * a.hidden); }
+  __device__ __forceinline__ void finish(const DecodeArgs& a, uint16_t* xs, float* rstd) {
+    const int H = a.hidden, T = a.T;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    r.store(xs, T * H);
+    __syncthreads();
+    if (!a.norm_weight) return;
     if (wave < T) {
       const uint16_t* xrow = xs + wave * H;
       float ss = 0.f;
@@ -316,92 +329,144 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_dproj(DecodeArgs a) {
                            bf16_bits_to_f32(d[q] >> 16) * rstd[tt] * a.norm_weight[k + 2 * q + 1]);
       *(uint4*)(xs + i) = make_uint4(o[0], o[1], o[2], o[3]);
     }
+    __syncthreads();
   }
-  __syncthreads();
+};
+
+// Workgroups [0, latent/16) compute h for 16 latent rows each (K split over
+// the 8 waves) and write bf16(h), plus the low half h - bf16(h) when hlo is
+// set (the unfolded router reads both). With a folded router (a.RD), the
+// next n_parts * E/16 workgroups compute logits for 16 experts over one of
+// n_parts K parts: l_part = x_part . (W_hi + W_lo)_part (the bias with part
+// 0). NCH = hidden / 256, NCHR = NCH / n_parts. The workgroups also zero
+// the fixed-point sum the down kernel adds into.
+template <int NCH, int NCHR>
+__global__ __launch_bounds__(kDecThreads) void k_dec_front(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int H = a.hidden, L = a.latent, T = a.T, E = a.n_experts;
+  uint16_t* xs = lds;                       // [T][H] bf16
+  float* red = (float*)(lds + T * H);       // [8][64][4]
+  float* rstd = red + kDecWaves * 64 * 4;   // [T]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, t = lane & 15;
+  for (int i = blockIdx.x * kDecThreads + tid; i < T * L; i += gridDim.x * kDecThreads)
+    a.zfix[i] = 0ull;  // the down kernel adds into it
+  const int nd = L / 16;
+  XStage<(NCH + 1) / 2> xr;  // T x hidden, hidden = 256 NCH
+  if ((int)blockIdx.x < nd) {
+    const int row0 = blockIdx.x * 16;
+    const int kb = wave * (H / kDecWaves);
+    xr.load(a);
+    Bf16Rows<NCH> wr;
+    int step;
+    wr.load(bf16_lane(a.D, a.packed, L, H, row0, kb, &step), step);
+    xr.finish(a, xs, rstd);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    wr.mma(xs + min(t, T - 1) * H, kb, g, acc);  // token columns >= T are not stored
+    const f32x4 tot = reduce_waves(acc, red);
+    if (wave == 0 && t < T) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = row0 + g * 4 + r;
+        const uint16_t hi = f32_to_bf16_bits(tot[r]);
+        a.hhi[(size_t)t * L + n] = hi;
+        if (a.hlo) a.hlo[(size_t)t * L + n] = f32_to_bf16_bits(tot[r] - bf16_bits_to_f32(hi));
+      }
+    }
+    return;
+  }
+  // folded router: 16 experts, K part `part`
+  const int rb = blockIdx.x - nd;
+  const int e0 = (rb / a.n_parts) * 16, part = rb % a.n_parts;
+  const int kb = part * (H / a.n_parts) + wave * (H / a.n_parts / kDecWaves);
+  xr.load(a);
+  Bf16Rows<NCHR> wh, wl;
+  int step;
+  wh.load(bf16_lane(a.RD, true, E, H, e0, kb, &step), step);
+  wl.load(bf16_lane(a.RD + (size_t)E * H, true, E, H, e0, kb, &step), step);
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.bias && part == 0 && wave == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias[r] = a.bias[e0 + g * 4 + r];
+  }
+  xr.finish(a, xs, rstd);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  wr.mma(xs + min(t, T - 1) * H, kb, g, acc);  // token columns >= T are not stored
+  const uint16_t* xrow = xs + min(t, T - 1) * H;
+  wh.mma(xrow, kb, g, acc);
+  wl.mma(xrow, kb, g, acc);
+  const f32x4 tot = reduce_waves(acc, red);
+  if (wave == 0 && t < T) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      a.logits[((size_t)part * T + t) * E + e0 + g * 4 + r] = tot[r] + bias[r];
+  }
+}
+
+// ------------------------------------------------------------------ 1b. router from h
+
+// logits = (hi + lo) R^T + b for 16 experts per workgroup (the unfolded
+// router; K split over the 8 waves). latent = 256 NCH.
+template <int NCH>
+__global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int L = a.latent, T = a.T, E = a.n_experts;
+  uint16_t* hi = lds;           // [T][L]
+  uint16_t* lo = lds + T * L;   // [T][L]
+  float* red = (float*)(lo + T * L);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, t = lane & 15;
+  const int e0 = blockIdx.x * 16;
+  const int kb = wave * (L / kDecWaves);
+  RowStage<(NCH + 1) / 2> sh_hi, sh_lo;  // T x latent, latent = 256 NCH
+  // latent rows staged (and waited for) before the router rows are loaded
+  // (measured: 0.6 us less per decode step)
+  sh_hi.load(a.hhi, T * L);
+  sh_lo.load(a.hlo, T * L);
+  sh_hi.store(hi, T * L);
+  sh_lo.store(lo, T * L);
+  __syncthreads();
+  (void)tid;
+  Bf16Rows<NCH> wr;
+  int step;
+  wr.load(bf16_lane(a.R, a.packed, E, L, e0, kb, &step), step);
+  float bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.bias && wave == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias[r] = a.bias[min(e0 + g * 4 + r, E - 1)];
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  wr.mma2(hi + min(t, T - 1) * L, lo + min(t, T - 1) * L, kb, g, acc);
   const f32x4 tot = reduce_waves(acc, red);
   if (wave == 0 && t < T) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int n = row0 + g * 4 + r;
-      if (n < L) {
-        const uint16_t hi = f32_to_bf16_bits(tot[r]);
-        a.hhi[(size_t)t * L + n] = hi;
-        a.hlo[(size_t)t * L + n] = f32_to_bf16_bits(tot[r] - bf16_bits_to_f32(hi));
-      }
+      const int ee = e0 + g * 4 + r;
+      if (ee < E) a.logits[(size_t)t * E + ee] = tot[r] + bias[r];
     }
-  }
-}
-
-// ------------------------------------------------------------------ 2. router + shared gate/up
-
-// SiLU(gate) * up of a 16-row tile, to act[t][n0 + rows] (bf16, t < T).
-__device__ __forceinline__ void store_gateup(const f32x4& g4, const f32x4& u4, float gsg,
-                                             float gsu, uint16_t* act, int I, int T, int n0,
-                                             int lane) {
-  const int t = lane & 15, g = lane >> 4;
-  if (t >= T) return;
-  float v[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float gg = gsg * g4[r], uu = gsu * u4[r];
-    v[r] = silu_fast(gg) * uu;
-  }
-  *(uint2*)(act + (size_t)t * I + n0 + g * 4) =
-      make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-}
-
-// Gate/up of one expert for two 16-row tiles per workgroup: wave w handles
-// tile w/4, matrix (w/2)%2 (gate, up), K half w%2. The halves and matrices
-// meet in LDS; waves 0 and 4 apply SiLU*mul and store.
-template <int NCH_H, int BITS>
-struct GateUpTask {
-  Fp4Rows<NCH_H, BITS> wr;
-  __device__ __forceinline__ void load(const Fp4Mat& gate, const Fp4Mat& up, bool packed, int e,
-                                       int I, int L, int n0, int wave, int lane) {
-    const int mat = (wave >> 1) & 1, half = wave & 1;
-    (void)lane;
-    wr.load(fp4_lane(mat ? up : gate, packed, e, I, L, n0, half * (L / 2), BITS));
-  }
-  __device__ __forceinline__ f32x4 mma(const uint16_t* act, int L, int wave, int lane) const {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    wr.mma(act, (wave & 1) * (L / 2), lane >> 4, acc);
-    return acc;
-  }
-};
-
-// Writes this wave's tile, then (waves 0 and 4) combines the four partial
-// tiles of its row tile: gate = half0 + half1, up = half0 + half1.
-__device__ __forceinline__ void finish_gateup(f32x4 acc, float* red, bool tile_busy, float gsg,
-                                              float gsu, uint16_t* act, int I, int T, int n0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  *(f32x4*)(red + (wave * 64 + lane) * 4) = acc;
-  __syncthreads();
-  if ((wave & 3) == 0 && tile_busy) {
-    const f32x4 g0 = *(const f32x4*)(red + ((wave + 0) * 64 + lane) * 4);
-    const f32x4 g1 = *(const f32x4*)(red + ((wave + 1) * 64 + lane) * 4);
-    const f32x4 u0 = *(const f32x4*)(red + ((wave + 2) * 64 + lane) * 4);
-    const f32x4 u1 = *(const f32x4*)(red + ((wave + 3) * 64 + lane) * 4);
-    store_gateup(g0 + g1, u0 + u1, gsg, gsu, act, I, T, n0, lane);
   }
 }
 
 // ------------------------------------------------------------------ top-k
 
 // One token's logits as order-preserving keys, lane l holding experts
-// l, l + 64, ... (experts past E: key 0, below every logit's key). The loads
-// are unconditional (clamped index) so that they stay in flight together.
-// in_launch: the logits were written by other workgroups of this launch
-// (agent-scope loads); else by an earlier launch.
+// l, l + 64, ... (experts past E: key 0, below every logit's key). A logit
+// is the sum of its n_parts parts, in part order. The loads are
+// unconditional (clamped index) so that they stay in flight together.
 template <int EPL>
-__device__ __forceinline__ void wave_load_keys(const float* row, int E, float (&v)[EPL],
-                                               bool in_launch = false) {
+__device__ __forceinline__ void wave_load_keys(const float* row, int E, int part_stride,
+                                               int n_parts, float (&v)[EPL]) {
   const int lane = threadIdx.x & 63;
+  float p1[EPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i)
-    v[i] = in_launch ? __hip_atomic_load(row + min(lane + 64 * i, E - 1), __ATOMIC_RELAXED, AGENT)
-                     : row[min(lane + 64 * i, E - 1)];
+  for (int i = 0; i < EPL; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    v[i] = row[e];
+    p1[i] = row[(n_parts > 1 ? part_stride : 0) + e];
+  }
+  if (n_parts > 1) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] += p1[i];
+  }
 }
 
 // Top-k of one token from its logits (wave_load_keys) by this wave; lane
@@ -482,7 +547,7 @@ __device__ __forceinline__ void publish_routing(const DecodeArgs& a, const Route
     for (int i = tid; i < P; i += kDecThreads) a.dbg_w[i] = rl.w[i];
   if (a.dbg_logits)
     for (int i = tid; i < T * E; i += kDecThreads)
-      a.dbg_logits[i] = __hip_atomic_load(a.logits + i, __ATOMIC_RELAXED, AGENT);
+      a.dbg_logits[i] = a.n_parts > 1 ? a.logits[i] + a.logits[T * E + i] : a.logits[i];
   // counts, offsets and the stable permutation of the P pairs (pair p of
   // expert e goes after the pairs of smaller experts and the earlier pairs of e)
   if (a.dbg_counts)
@@ -506,252 +571,225 @@ __device__ __forceinline__ void publish_routing(const DecodeArgs& a, const Route
     }
 }
 
-template <int NCH_R, int NCH_H, int BITS>
-__global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  __shared__ RouteLds rl;
-  __shared__ unsigned last_flag;
-  const int L = a.latent, T = a.T, E = a.n_experts, I = a.inter;
-  uint16_t* hi = lds;           // [T][L]
-  uint16_t* lo = lds + T * L;   // [T][L]
-  float* red = (float*)(lo + T * L);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, t = lane & 15;
-  const int nrb = (E + 15) / 16;
-
-  if ((int)blockIdx.x < nrb) {
-    const int e0 = blockIdx.x * 16;
-    const int kb = wave * (L / kDecWaves);
-    RowStage<(NCH_R + 1) / 2> sh_hi, sh_lo;  // T x latent, latent = 256 NCH_R
-    // latent rows staged (and waited for) before the router rows are loaded,
-    // as in the routed gate/up kernel (measured: 0.6 us less per decode step)
-    sh_hi.load(a.hhi, T * L);
-    sh_lo.load(a.hlo, T * L);
-    sh_hi.store(hi, T * L);
-    sh_lo.store(lo, T * L);
-    __syncthreads();
-    Bf16Rows<NCH_R> wr;
-    int step;
-    const uint16_t* wb = bf16_lane(a.R, a.packed, E, L, e0, kb, &step);
-    wr.load(wb, step);
-    float bias[4] = {0.f, 0.f, 0.f, 0.f};
-    if (a.bias && wave == 0) {
+// SiLU(gate) * up of a 16-row tile, to act[t][n0 + rows] (bf16, t < T).
+__device__ __forceinline__ void store_gateup(const f32x4& g4, const f32x4& u4, float gsg,
+                                             float gsu, uint16_t* act, int I, int T, int n0,
+                                             int lane) {
+  const int t = lane & 15, g = lane >> 4;
+  if (t >= T) return;
+  float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bias[r] = a.bias[min(e0 + g * 4 + r, E - 1)];
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    wr.mma2(hi + min(t, T - 1) * L, lo + min(t, T - 1) * L, kb, g, acc);
-    const f32x4 tot = reduce_waves(acc, red);
-    if (wave == 0 && t < T) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ee = e0 + g * 4 + r;
-        if (ee < E)
-          __hip_atomic_store(a.logits + (size_t)t * E + ee, tot[r] + bias[r], __ATOMIC_RELAXED,
-                             AGENT);
-      }
-    }
-    if (!a.topk_in_router) return;  // the gate/up workgroups take the top-k
-    // Hand-off: every thread's logits stores are released at agent scope
-    // before the workgroup's arrival is counted (release fence, barrier,
-    // acquire-release increment); the last arriver acquires at agent scope
-    // before it reads any workgroup's logits.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
-    if (tid == 0)
-      last_flag = __hip_atomic_fetch_add(a.route_counter, 1u, __ATOMIC_ACQ_REL, AGENT) ==
-                  (unsigned)(nrb - 1);
-    __syncthreads();
-    if (!last_flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // the last router workgroup: top-k of every token, then the routing table
-    for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
-    const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;
-    if (E <= 512) {
-      float v[8];
-      wave_load_keys<8>(lrow, E, v, true);
-      if (wave < T) wave_topk<8>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
-    } else {
-      float v[16];
-      wave_load_keys<16>(lrow, E, v, true);
-      if (wave < T) wave_topk<16>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
-    }
-    __syncthreads();
-    build_active_list(E, T * a.top_k, rl);
-    publish_routing(a, rl);
-    return;
+  for (int r = 0; r < 4; ++r) {
+    const float gg = gsg * g4[r], uu = gsu * u4[r];
+    v[r] = silu_fast(gg) * uu;
   }
-  // shared expert gate/up: two 16-row tiles per workgroup (see GateUpTask)
-  if (!a.n_shared) return;
-  const int tile = (blockIdx.x - nrb) * 2 + (wave >> 2);
-  const bool busy = tile * 16 < I;
-  const int n0 = busy ? tile * 16 : 0;
-  RowStage<(NCH_H + 1) / 2> st;  // T x latent, latent = 256 NCH_H
-  st.load(a.hhi, T * L);
-  GateUpTask<NCH_H, BITS> task;
-  const float gsg = a.sh_gate.gscale[0], gsu = a.sh_up.gscale[0];
-  task.load(a.sh_gate, a.sh_up, a.packed, 0, I, L, n0, wave, lane);  // idle tiles: rows 0..15
-  st.store(hi, T * L);
-  __syncthreads();
-  const f32x4 acc = task.mma(hi + min(t, T - 1) * L, L, wave, lane);
-  finish_gateup(acc, red, busy, gsg, gsu, a.act, I, T, n0);
+  *(uint2*)(act + (size_t)t * I + n0 + g * 4) =
+      make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
-// ------------------------------------------------------------------ 3. routed gate/up
 
-// The wave's tile of a routed gate/up workgroup: expert e (active slot
-// `slot`), rows n0 .. n0+15, with the token rows staged in `hi`. An idle tile
-// (busy false) reads expert 0's rows 0..15 (in range) and stores nothing,
-// which keeps the loads and their uses in one block.
-template <int NCH_H, int BITS>
-__device__ __forceinline__ void gateup_tiles(const DecodeArgs& a, const uint16_t* hi, float* red,
-                                             bool busy, int e, int slot, int n0) {
+// ------------------------------------------------------------------ 2. top-k + gate/up
+
+// One wave's task: the gate and up tiles of one expert slot, 16 rows
+// (n0 .. n0+15) over the whole latent width, SiLU(gate) * up to
+// act[slot][t][n0 + rows]. hs = the token rows in LDS. latent = 128 NCH.
+// The chunks are software-pipelined: W chunk pairs (gate and up) stay in
+// flight and each pair is dequantised and multiplied as soon as it lands,
+// so the vector work of the exact dequantisation overlaps the weight
+// stream instead of piling up after it (measured at the 145B decode shapes
+// with T = 4: 20.1 us with every chunk issued up front, 17.5 us with
+// W = 2, 18.6 us with 4 and 20.3 us with 8).
+template <int NCH, int BITS>
+__device__ __forceinline__ void gateup_task(const DecodeArgs& a, const uint16_t* hs, int slot,
+                                            int e, int n0) {
+  constexpr int W = 2;  // chunk pairs in flight per wave (measured best of 2, 4, 8)
   const int L = a.latent, T = a.T, I = a.inter;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = lane & 15;
-  GateUpTask<NCH_H, BITS> task;
-  const float gsg = a.gate.gscale[e], gsu = a.up.gscale[e];
-  task.load(a.gate, a.up, a.packed, e, I, L, n0, wave, lane);
-  issue_fence();
-  const f32x4 acc = task.mma(hi + min(t, T - 1) * L, L, wave, lane);
-  finish_gateup(acc, red, busy, gsg, gsu, a.act + (size_t)(1 + slot) * T * I, I, T, n0);
+  const int lane = threadIdx.x & 63, t = lane & 15, g = lane >> 4;
+  const bool sh = slot == 0;
+  const Fp4Mat gm = sh ? a.sh_gate : a.gate;
+  const Fp4Mat um = sh ? a.sh_up : a.up;
+  const float gsg = gm.gscale[e], gsu = um.gscale[e];
+  const Fp4Lane lg = fp4_lane(gm, a.packed, e, I, L, n0, 0, BITS);
+  const Fp4Lane lu = fp4_lane(um, a.packed, e, I, L, n0, 0, BITS);
+  Fp4Rows<NCH, BITS> wg, wu;
+  auto ld = [&](int i) {
+    if constexpr (BITS == 4) {
+      const uint4 v = *(const uint4*)(lg.c + i * lg.cstep);
+      wg.c[i][0] = v.x; wg.c[i][1] = v.y; wg.c[i][2] = v.z; wg.c[i][3] = v.w;
+      const uint4 u = *(const uint4*)(lu.c + i * lu.cstep);
+      wu.c[i][0] = u.x; wu.c[i][1] = u.y; wu.c[i][2] = u.z; wu.c[i][3] = u.w;
+    } else {
+      const uint3 v = *(const uint3*)(lg.c + i * lg.cstep);
+      wg.c[i][0] = v.x; wg.c[i][1] = v.y; wg.c[i][2] = v.z;
+      const uint3 u = *(const uint3*)(lu.c + i * lu.cstep);
+      wu.c[i][0] = u.x; wu.c[i][1] = u.y; wu.c[i][2] = u.z;
+    }
+    wg.s[i] = *(const uint2*)(lg.s + i * lg.sstep);
+    wu.s[i] = *(const uint2*)(lu.s + i * lu.sstep);
+  };
+  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* row = hs + min(t, T - 1) * L;
+#pragma unroll
+  for (int i = 0; i < W && i < NCH; ++i) ld(i);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + W < NCH) ld(i + W);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t spg = ((g & 2) ? wg.s[i].y : wg.s[i].x) >> (16 * (g & 1));
+    const uint32_t spu = ((g & 2) ? wu.s[i].y : wu.s[i].x) >> (16 * (g & 1));
+    const float g0 = e4m3_to_f32(spg & 0xFFu), g1 = e4m3_to_f32((spg >> 8) & 0xFFu);
+    const float u0 = e4m3_to_f32(spu & 0xFFu), u1 = e4m3_to_f32((spu >> 8) & 0xFFu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8 b = *(const bf16x8*)(row + (i * 4 + g) * 32 + q * 8);
+      ag = mfma16x16x32(dequant8(wg.codes8(i, q), q < 2 ? g0 : g1), b, ag);
+      au = mfma16x16x32(dequant8(wu.codes8(i, q), q < 2 ? u0 : u1), b, au);
+    }
+  }
+  store_gateup(ag, au, gsg, gsu, a.act + (size_t)slot * T * I, I, T, n0, lane);
 }
 
-// TOPK: this workgroup takes the top-k itself (a.topk_in_router is false);
-// else it reads the routing table the router published.
-template <int NCH_H, int BITS, bool TOPK>
+// Each workgroup takes the top-k of every token (one wave per token) from
+// the logits, loaded together with its staged token rows (one round trip),
+// and builds the active list (the same in every workgroup); workgroup 0
+// publishes the routing table for the down kernel. The (slot, 16-row tile)
+// tasks of the live slots (slot 0: the shared expert when there is one;
+// slot s >= 1: the s-th active expert) are then split evenly over the grid
+// (one workgroup per CU, so the top-k is paid once per CU and every CU
+// shares the dequantisation work): workgroup b takes tasks
+// [b P / G, (b + 1) P / G) of the P, wave w every eighth of them from w.
+// latent = 128 NCH.
+template <int NCH, int BITS>
 __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ RouteLds rl;
   const int L = a.latent, T = a.T, I = a.inter, E = a.n_experts;
-  uint16_t* hi = lds;  // [T][L]
-  float* red = (float*)(lds + T * L);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = lane & 15;
+  uint16_t* hs = lds;  // [T][L] (+ the DMA pad)
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int tiles = I / 16;
-  const int tile = blockIdx.x * 2 + (wave >> 2);  // (slot - 1) * tiles + row tile
-  // The activations are staged, and waited for, before any weight load is
-  // issued. Four workgroups share a CU and all of them stream weights at
-  // once, so activations loaded behind the weights arrive only when most of
-  // the CU's weights have; every workgroup's compute would then start after
-  // the data window instead of riding on it (measured: 60.3 -> 58.2 us per
-  // decode step at T = 4). They go straight into LDS, so no registers hold
-  // them while the routing is worked out.
-  constexpr int NV = (NCH_H + 1) / 2;  // T x latent, latent = 256 NCH_H: up to 8 rows
-  if constexpr (!TOPK) {  // the routing table is published: read it
-    const int n_act = a.route_n_act[0];
-    const int e_guess = a.route_list[min(tile / tiles, a.max_active - 1)];
-    if ((int)blockIdx.x * 2 >= n_act * tiles) return;  // both tiles idle (uniform)
-    stage_dma<NV>(a.hhi, T * L, hi);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
-    __syncthreads();
-    const bool busy = tile < n_act * tiles;
-    gateup_tiles<NCH_H, BITS>(a, hi, red, busy, busy ? e_guess : 0, busy ? tile / tiles : 0,
-                              busy ? (tile % tiles) * 16 : 0);
+  constexpr int NV = (NCH + 3) / 4;  // 16-byte slots per thread: T x latent, T <= 8
+  for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
+  const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;
+  if (E <= 512) {
+    float v[8];
+    wave_load_keys<8>(lrow, E, T * E, a.n_parts, v);
+    stage_dma<NV>(a.hhi, T * L, hs);
+    if (wave < T) wave_topk<8>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
   } else {
-    // every workgroup takes the top-k of every token from the router's
-    // logits, loaded together with the staged rows (one round trip), and
-    // builds the active list (the same result in each); workgroup 0
-    // publishes the routing table for the down and combine kernels
-    for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
-    const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;
-    if (E <= 512) {
-      float v[8];
-      wave_load_keys<8>(lrow, E, v);
-      stage_dma<NV>(a.hhi, T * L, hi);
-      if (wave < T) wave_topk<8>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
-    } else {
-      float v[16];
-      wave_load_keys<16>(lrow, E, v);
-      stage_dma<NV>(a.hhi, T * L, hi);
-      if (wave < T) wave_topk<16>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
-    __syncthreads();
-    build_active_list(E, T * a.top_k, rl);
-    if (blockIdx.x == 0) publish_routing(a, rl);
-    const int n_act = rl.n_act;
-    if ((int)blockIdx.x * 2 >= n_act * tiles) return;  // both tiles idle (uniform)
-    const bool busy = tile < n_act * tiles;
-    gateup_tiles<NCH_H, BITS>(a, hi, red, busy, busy ? rl.list[tile / tiles] : 0,
-                              busy ? tile / tiles : 0, busy ? (tile % tiles) * 16 : 0);
+    float v[16];
+    wave_load_keys<16>(lrow, E, T * E, a.n_parts, v);
+    stage_dma<NV>(a.hhi, T * L, hs);
+    if (wave < T) wave_topk<16>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
+  __syncthreads();
+  build_active_list(E, T * a.top_k, rl);
+  if (blockIdx.x == 0) publish_routing(a, rl);
+  const int s0 = a.n_shared ? 0 : 1;  // first live slot
+  const int P = (rl.n_act + 1 - s0) * tiles;
+  const int G = gridDim.x;
+  const int p1 = (int)((int64_t)(blockIdx.x + 1) * P / G);
+  for (int p = (int)((int64_t)blockIdx.x * P / G) + wave; p < p1; p += kDecWaves) {
+    const int slot = s0 + p / tiles;
+    gateup_task<NCH, BITS>(a, hs, slot, slot == 0 ? 0 : rl.list[slot - 1], (p % tiles) * 16);
   }
 }
 
-// ------------------------------------------------------------------ 4. down + combine
+// ------------------------------------------------------------------ 3. down + combine
 
-template <int NCH_D>
-__global__ __launch_bounds__(kDecThreads) void k_dec_down(DecodeArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [T][I] activations
+// Workgroup (16 latent rows r0 .. r0+15, slot group q): wave w takes slot
+// s = 8q + w (slot 0 the shared expert, s >= 1 the s-th active expert;
+// slots past the active ones, and slot 0 without a shared expert, have
+// nothing to do). The wave stages its slot's activations (the matrix-core
+// token operand) into its own LDS region, streams the 16 rows of its
+// slot's down matrix chunk by chunk with the next chunk in flight, and
+// scales the product by the gate weight and the matrix scale. (Reading the
+// token operand straight from L2 instead took four 16-byte loads per lane
+// and chunk, three quarters of them repeats at T = 4: 12.4 us for the
+// 145B layer at T = 4.) The eight
+// slots' products are added in slot order through LDS, and the group sum is
+// added into zfix in 64-bit fixed point (units of 2^-32) with integer
+// atomics: integer addition is exact, so the result does not depend on the
+// order in which the groups arrive. inter = 128 NCH.
+// Held to at most 85 registers (six waves per SIMD) so that three
+// workgroups share a CU and the grid of (latent/16) x groups workgroups
+// runs in one round at T = 4 (672 workgroups, 768 resident); at 94
+// registers it took two.
+template <int NCH>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_dec_down(
+    DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // 8 activation regions, red
   const int L = a.latent, T = a.T, I = a.inter;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
+  const int ntile = L / 16;
+  const int r0 = (blockIdx.x % ntile) * 16, q = blockIdx.x / ntile;
+  const int region = down_region(T, I);
+  float* red = (float*)(lds + kDownGroup * region);
   (void)tid;
-  const int nrr = decode_row_ranges(L);
-  const int s = blockIdx.x / nrr, rr = blockIdx.x % nrr;
-  // the routing table, read together (the guesses are clamped in range)
+  // the routing table, read together (clamped indices; used only when live)
   const int n_act = a.route_n_act[0];
-  const int e_guess = a.route_list[min(max(s - 1, 0), a.max_active - 1)];
-  const float w_guess = a.route_wtab[min(s, a.max_active) * T + min(t, T - 1)];
-  const bool sh = s == 0;
-  if (sh ? a.n_shared == 0 : s > n_act) return;  // uniform over the workgroup
-  const int e = sh ? 0 : e_guess;
-  const Fp4Mat& dm = sh ? a.sh_down : a.down;
-  const float* gscale = dm.gscale;
-  RowStage<(NCH_D + 3) / 4> st;  // T x inter, inter = 128 NCH_D
-  st.load(a.act + (size_t)s * T * I, T * I);
-  const int row0 = rr * kDownRows + wave * 16;
-  Fp4Rows<NCH_D> wd;
-  const float gs = gscale[e];
-  wd.load(fp4_lane(dm, a.packed, e, L, I, row0, 0));
-  st.store(lds, T * I);
-  __syncthreads();
+  const int s = kDownGroup * q + wave;
+  const int sc = min(s, a.max_active);
+  const int e_guess = a.route_list[max(sc - 1, 0)];
+  const float w_guess = a.route_wtab[sc * T + min(t, T - 1)];
+  if (q >= (n_act + kDownGroup) / kDownGroup) return;  // uniform over the workgroup
   f32x4 y = {0.f, 0.f, 0.f, 0.f};
-  wd.mma(lds + min(t, T - 1) * I, 0, g, y);
-  if (t < T) {
-    const float wt = w_guess * gs;
+  if ((s > 0 || a.n_shared) && s <= n_act) {  // uniform over the wave
+    const bool sh = s == 0;
+    const Fp4Mat dm = sh ? a.sh_down : a.down;
+    const int e = sh ? 0 : e_guess;
+    const float gs = dm.gscale[e];
+    // this slot's activations into the wave's own LDS region, before any
+    // weight load: the wave waits for them with a count of its later loads
+    uint16_t* act = lds + wave * region;
+    stage_dma_wave<2 * NCH>(a.act + (size_t)s * T * I, T * I, act);
+    issue_fence();
+    const Fp4Lane l = fp4_lane(dm, a.packed, e, L, I, r0, 0);
+    Fp4Rows<NCH> wd;
+    // software-pipelined as in the gate/up kernel: the next chunk is in
+    // flight while one is multiplied
+    auto ld = [&](int i) {
+      const uint4 v = *(const uint4*)(l.c + i * l.cstep);
+      wd.c[i][0] = v.x; wd.c[i][1] = v.y; wd.c[i][2] = v.z; wd.c[i][3] = v.w;
+      wd.s[i] = *(const uint2*)(l.s + i * l.sstep);
+    };
+    ld(0);
+    issue_fence();
+    wait_vmcnt<2>();  // everything but chunk 0's two loads: the staged rows have landed
+    const uint16_t* arow = act + min(t, T - 1) * I;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < NCH) ld(i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t sp = ((g & 2) ? wd.s[i].y : wd.s[i].x) >> (16 * (g & 1));
+      const float s0 = e4m3_to_f32(sp & 0xFFu), s1 = e4m3_to_f32((sp >> 8) & 0xFFu);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        y = mfma16x16x32(dequant8(wd.codes8(i, k), k < 2 ? s0 : s1),
+                         *(const bf16x8*)(arow + (i * 4 + g) * 32 + k * 8), y);
+    }
+    const float sw = w_guess * gs;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] *= sw;
+  }
+  *(f32x4*)(red + (wave * 64 + lane) * 4) = y;
+  __syncthreads();
+  if (wave == 0 && t < T) {
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < kDecWaves; ++w) tot += *(const f32x4*)(red + (w * 64 + lane) * 4);
+    unsigned long long* zp = a.zfix + (size_t)t * L + r0 + g * 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int n = row0 + g * 4 + r;
-      if (n < L) a.zpart[((size_t)s * T + t) * L + n] = wt * y[r];
+      const long long fx = (long long)__builtin_rintf(tot[r] * 4294967296.0f);
+      __hip_atomic_fetch_add(zp + r, (unsigned long long)fx, __ATOMIC_RELAXED, AGENT);
     }
   }
 }
 
-// z[t][n] = bf16(sum over the active slots, in slot order, of the weighted
-// partial rows); one thread per output. Its own launch: the kernel boundary
-// makes every down workgroup's partial rows visible, which costs less than a
-// release, an arrival count and a last-arriver sum inside the down launch
-// (measured: 6.5 us of hand-off there against one extra launch here).
-// The loads cover every slot of the table's capacity (1 + max_active rows,
-// all in range), NB at a time, so none of them waits for the active count,
-// which decides only what is summed. Up to 60 rows (T <= 5 at top-10) the
-// batch stays below the 64 loads a wave can count in flight; past that one
-// batch of 96, which the compiler splits with waits, still measured faster
-// than two batches (T = 8: 63.5 -> 63.0 us per step).
-template <int NB>
-__global__ __launch_bounds__(256) void k_dec_combine(DecodeArgs a) {
-  const int T = a.T, L = a.latent;
-  const int i = blockIdx.x * 256 + threadIdx.x;  // t * L + n
-  if (i >= T * L) return;
-  const int n_act = a.route_n_act[0];
-  const int s0 = a.n_shared ? 0 : 1;
-  const int last = a.max_active;  // highest slot of the table
-  const size_t step = (size_t)T * L;
-  const float* src = a.zpart + i;
-  float v = 0.f;
-  for (int ss = s0; ss <= last; ss += NB) {
-    float p[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) p[j] = src[min(ss + j, last) * step];
-    issue_fence();  // else the first sums are placed between the loads, each a round trip
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      if (ss + j <= n_act) v += p[j];
-  }
-  a.z[i] = f32_to_bf16_bits(v);
-}
-
-// ------------------------------------------------------------------ 5. U
+// ------------------------------------------------------------------ 4. U
 
 template <int NCH>
 __global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
@@ -763,13 +801,25 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
   const int g = lane >> 4, t = lane & 15;
   const int m0 = blockIdx.x * 16;
   const int kb = wave * (L / kDecWaves);
-  RowStage<(NCH + 1) / 2> st;  // T x latent, latent = 256 NCH
-  st.load(a.z, T * L);
+  (void)tid;
+  // z = bf16(zfix * 2^-32): thread i converts pairs 2 (i + 512 j) of the
+  // T x latent sums (loads issued before the weight loads)
+  constexpr int NZ = (kDecodeMaxT * 256 * NCH / 2 + kDecThreads - 1) / kDecThreads;
+  ulonglong2 zv[NZ];
+#pragma unroll
+  for (int j = 0; j < NZ; ++j)
+    zv[j] = *(const ulonglong2*)(a.zfix + 2 * min(tid + j * kDecThreads, T * L / 2 - 1));
   Bf16Rows<NCH> wr;
   int step;
   const uint16_t* wb = bf16_lane(a.U, a.packed, H, L, m0, kb, &step);
   wr.load(wb, step);
-  st.store(zs, T * L);
+#pragma unroll
+  for (int j = 0; j < NZ; ++j) {
+    const int i = min(tid + j * kDecThreads, T * L / 2 - 1);  // the last pair repeats (same value)
+    *(uint32_t*)(zs + 2 * i) =
+        pack_bf16x2((float)(long long)zv[j].x * 2.3283064365386963e-10f,
+                    (float)(long long)zv[j].y * 2.3283064365386963e-10f);
+  }
   __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   wr.mma(zs + min(t, T - 1) * L, kb, g, acc);
@@ -828,17 +878,107 @@ static bool nch_ok(int n) {
 bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int T) {
   if (T < 1 || T > kDecodeMaxT || n_experts > kMaxExperts || top_k > 16) return false;
   // D, U and the router split K over 8 waves x 4 lane groups x 8 bf16;
-  // expert rows are consumed in 32-weight chunks by 4 lane groups.
+  // expert rows are consumed in 128-weight chunks by 4 lane groups.
   if (hidden % 256 || latent % 256 || inter % 128) return false;
   if (!nch_ok(hidden / 256) || !nch_ok(latent / 256) || !nch_ok(inter / 128)) return false;
-  if (latent / 128 > 14) return false;  // register budget of the gate/up waves
-  // (activation staging is sized per kernel from the same chunk counts:
-  // RowStage<ceil(width / 512)> holds 8 rows of `width`)
+  // register budgets: a gate/up wave holds 2 x latent/128 chunks of
+  // weights, a down wave inter/128 chunks and their token operands
+  if (latent / 128 > 14 || inter / 128 > 7) return false;
   const size_t lim = 96 * 1024;
-  return dproj_lds(kDecodeMaxT, hidden) <= lim && router_lds(kDecodeMaxT, latent) <= lim &&
-         router_lds(kDecodeMaxT, latent) + sizeof(RouteLds) <= lim &&
-         gateup_lds(kDecodeMaxT, latent) <= lim &&
+  return front_lds(kDecodeMaxT, hidden) <= lim && router_lds(kDecodeMaxT, latent) <= lim &&
+         gateup_lds(kDecodeMaxT, latent) + sizeof(RouteLds) <= lim &&
          down_lds(kDecodeMaxT, inter) <= lim && uproj_lds(kDecodeMaxT, latent) <= lim;
+}
+
+int decode_front_parts(int hidden) { return (hidden / 256) % 2 == 0 ? 2 : 1; }
+
+// Compute units of the current device (once per device).
+static int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return cache[dev] = n;
+}
+
+hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMarks& mk) {
+  DecodeArgs a = args;
+  const int H = a.hidden, L = a.latent, I = a.inter, E = a.n_experts, T = a.T;
+  const dim3 block(kDecThreads);
+  hipError_t err;
+  // 1. h = x D^T (+ the router logits from x with a folded router)
+  const int nparts = a.RD ? decode_front_parts(H) : 1;
+  a.n_parts = nparts;
+  err = with_nch(H / 256, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    constexpr int nr = n % 2 == 0 ? n / 2 : n;
+    const auto fn = k_dec_front<n, nr>;
+    hipError_t e = ensure_lds((const void*)fn, front_lds(kDecodeMaxT, H));
+    const int grid = L / 16 + (a.RD ? nparts * (E / 16) : 0);
+    if (e == hipSuccess) e = mk.launch(kStageDproj, fn, dim3(grid), block, front_lds(T, H), a);
+    return e;
+  });
+  if (err != hipSuccess) return err;
+  // 1b. without a folded router: logits = (hi + lo) R^T + b
+  if (!a.RD) {
+    err = with_nch(L / 256, [&](auto N) {
+      constexpr int n = decltype(N)::value;
+      hipError_t e = ensure_lds((const void*)k_dec_router<n>, router_lds(kDecodeMaxT, L));
+      if (e == hipSuccess)
+        e = mk.launch(kStageRouter, k_dec_router<n>, dim3((E + 15) / 16), block, router_lds(T, L),
+                      a);
+      return e;
+    });
+    if (err != hipSuccess) return err;
+  }
+  // 2. top-k + gate/up (slot 0: the shared expert)
+  const auto gateup = [&](auto N, auto B) {
+    constexpr int n = decltype(N)::value, bits = decltype(B)::value;
+    if constexpr (2 * n > 14) {
+      return hipErrorInvalidValue;  // excluded by decode_supported
+    } else {
+      const int tasks = (1 + a.max_active) * (I / 16);
+      const int grid = std::min(cu_count(), (tasks + kDecWaves - 1) / kDecWaves);
+      const auto fn = k_dec_gateup<2 * n, bits>;
+      hipError_t e = ensure_lds((const void*)fn, gateup_lds(kDecodeMaxT, L));
+      if (e == hipSuccess)
+        e = mk.launch(kStageGateup, fn, dim3(std::max(grid, 1)), block, gateup_lds(T, L), a);
+      return e;
+    }
+  };
+  err = with_nch(L / 256, [&](auto N) {
+    return a.gateup_bits == 3 ? gateup(N, std::integral_constant<int, 3>{})
+                              : gateup(N, std::integral_constant<int, 4>{});
+  });
+  if (err != hipSuccess) return err;
+  // 3. down + combine
+  err = with_nch(I / 128, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    if constexpr (n > 7) {
+      return hipErrorInvalidValue;  // excluded by decode_supported
+    } else {
+      const int grid = (L / 16) * decode_down_groups(a.max_active);
+      hipError_t e = ensure_lds((const void*)k_dec_down<n>, down_lds(kDecodeMaxT, I));
+      if (e == hipSuccess)
+        e = mk.launch(kStageDown, k_dec_down<n>, dim3(grid), block, down_lds(T, I), a);
+      return e;
+    }
+  });
+  if (err != hipSuccess) return err;
+  // 4. out = z U^T (+ x)
+  return with_nch(L / 256, [&](auto N) {
+    constexpr int n = decltype(N)::value;
+    hipError_t e = ensure_lds((const void*)k_dec_uproj<n>, uproj_lds(kDecodeMaxT, L));
+    if (e == hipSuccess)
+      e = mk.launch(kStageUproj, k_dec_uproj<n>, dim3((H + 15) / 16), block, uproj_lds(T, L), a);
+    return e;
+  });
 }
 
 // ------------------------------------------------------------------ decode-packed layouts
@@ -910,112 +1050,40 @@ hipError_t launch_pack_bf16_decode(const uint16_t* w, int N, int K, uint16_t* pw
   return hipGetLastError();
 }
 
-// Workgroups of a gate/up instantiation resident on the device at once (its
-// occupancy at the largest LDS size times the CU count), once per device.
-static int gateup_resident(const void* fn, size_t lds) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  static std::mutex mu;
-  static std::map<std::pair<const void*, int>, int> cache;
-  std::lock_guard<std::mutex> lock(mu);
-  const auto it = cache.find({fn, dev});
-  if (it != cache.end()) return it->second;
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kDecThreads, lds) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  return cache[{fn, dev}] = per_cu * cus;
+// The router folded onto the residual width: W[e][i] = sum_j R[e][j] D[j][i]
+// (so x W^T = (x D^T) R^T), accumulated in fp64 in j order, then stored as
+// hi = bf16(W) and lo = bf16(W - hi) (together about 16 significant bits)
+// at their places in the decode-packed bf16 layout of an [E][hidden]
+// matrix: hi in dst[0 .. E*hidden), lo after it. One thread per element;
+// the workgroup's 256 threads share e (the R row is read as a broadcast).
+__global__ __launch_bounds__(256) void k_router_fold(const uint16_t* __restrict__ R,
+                                                     const uint16_t* __restrict__ D, int E,
+                                                     int latent, int hidden,
+                                                     uint16_t* __restrict__ dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // column (hidden)
+  const int e = blockIdx.y;                      // row (expert)
+  if (i >= hidden) return;
+  const uint16_t* rrow = R + (size_t)e * latent;
+  double acc = 0.0;
+  for (int j = 0; j < latent; ++j)
+    acc = fma((double)bf16_bits_to_f32(rrow[j]), (double)bf16_bits_to_f32(D[(size_t)j * hidden + i]),
+              acc);
+  const float w = (float)acc;
+  const uint16_t hi = f32_to_bf16_bits(w);
+  const uint16_t lo = f32_to_bf16_bits(w - bf16_bits_to_f32(hi));
+  // decode-packed position: block (e / 16, i / 32), lane (e % 16) + 16 ((i % 32) / 8), element i % 8
+  const size_t pos = ((size_t)(e / 16) * (hidden / 32) + i / 32) * 512 +
+                     ((e % 16) + 16 * ((i % 32) / 8)) * 8 + i % 8;
+  dst[pos] = hi;
+  dst[(size_t)E * hidden + pos] = lo;
 }
 
-hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMarks& mk) {
-  DecodeArgs a = args;
-  const int H = a.hidden, L = a.latent, I = a.inter, E = a.n_experts, T = a.T;
-  const dim3 block(kDecThreads);
-  hipError_t err;
-  // Top-k placement: in every gate/up workgroup when the gate/up grid is
-  // resident in one round (then it overlaps the staging and costs each
-  // workgroup once), else in the router's last workgroup (a second round
-  // of gate/up workgroups would pay it again).
-  {
-    int resident = 0;
-    err = with_nch(L / 256, [&](auto N) {
-      constexpr int n = decltype(N)::value;
-      const void* fn = a.gateup_bits == 3 ? (const void*)k_dec_gateup<n, 3, true>
-                                          : (const void*)k_dec_gateup<n, 4, true>;
-      hipError_t e = ensure_lds(fn, gateup_lds(kDecodeMaxT, L));
-      if (e == hipSuccess) resident = gateup_resident(fn, gateup_lds(kDecodeMaxT, L));
-      return e;
-    });
-    if (err != hipSuccess) return err;
-    a.topk_in_router = (a.max_active * (I / 16) + 1) / 2 > resident;
-  }
-  // 1. h = x D^T
-  err = with_nch(H / 256, [&](auto N) {
-    constexpr int n = decltype(N)::value;
-    hipError_t e = ensure_lds((const void*)k_dec_dproj<n>, dproj_lds(kDecodeMaxT, H));
-    if (e == hipSuccess)
-      e = mk.launch(kStageDproj, k_dec_dproj<n>, dim3((L + 15) / 16), block, dproj_lds(T, H), a);
-    return e;
-  });
-  if (err != hipSuccess) return err;
-  // 2. router logits + top-k + routing table, shared expert gate/up
-  const auto router = [&](auto N, auto B) {
-    constexpr int n = decltype(N)::value, bits = decltype(B)::value;
-    const int nrb = (E + 15) / 16;
-    const int nsh = a.n_shared ? (I / 16 + 1) / 2 : 0;
-    const auto fn = k_dec_router<n, n, bits>;
-    hipError_t e = ensure_lds((const void*)fn, router_lds(kDecodeMaxT, L));
-    if (e == hipSuccess)
-      e = mk.launch(kStageRouter, fn, dim3(nrb + nsh), block, router_lds(T, L), a);
-    return e;
-  };
-  err = with_nch(L / 256, [&](auto N) {
-    return a.gateup_bits == 3 ? router(N, std::integral_constant<int, 3>{})
-                              : router(N, std::integral_constant<int, 4>{});
-  });
-  if (err != hipSuccess) return err;
-  // 3. routed gate/up
-  const auto gateup = [&](auto N, auto B) {
-    constexpr int n = decltype(N)::value, bits = decltype(B)::value;
-    const int nblk = (a.max_active * (I / 16) + 1) / 2;
-    const auto fn = a.topk_in_router ? k_dec_gateup<n, bits, false> : k_dec_gateup<n, bits, true>;
-    hipError_t e = ensure_lds((const void*)fn, gateup_lds(kDecodeMaxT, L));
-    if (e == hipSuccess) e = mk.launch(kStageGateup, fn, dim3(nblk), block, gateup_lds(T, L), a);
-    return e;
-  };
-  err = with_nch(L / 256, [&](auto N) {
-    return a.gateup_bits == 3 ? gateup(N, std::integral_constant<int, 3>{})
-                              : gateup(N, std::integral_constant<int, 4>{});
-  });
-  if (err != hipSuccess) return err;
-  // 4. down + combine
-  err = with_nch(I / 128, [&](auto N) {
-    constexpr int n = decltype(N)::value;
-    hipError_t e = ensure_lds((const void*)k_dec_down<n>, down_lds(kDecodeMaxT, I));
-    if (e == hipSuccess)
-      e = mk.launch_first(kStageDown, k_dec_down<n>,
-                          dim3((1 + a.max_active) * decode_row_ranges(L)), block, down_lds(T, I), a);
-    return e;
-  });
-  if (err != hipSuccess) return err;
-  {
-    const int n_rows = a.max_active + (a.n_shared ? 1 : 0);  // slots the combine reads
-    const dim3 cg((T * L + 255) / 256), cb(256);
-    err = n_rows <= 16   ? mk.launch_last(kStageDown, k_dec_combine<16>, cg, cb, 0, a)
-          : n_rows <= 32 ? mk.launch_last(kStageDown, k_dec_combine<32>, cg, cb, 0, a)
-          : n_rows <= 48 ? mk.launch_last(kStageDown, k_dec_combine<48>, cg, cb, 0, a)
-          : n_rows <= 60 ? mk.launch_last(kStageDown, k_dec_combine<60>, cg, cb, 0, a)
-                         : mk.launch_last(kStageDown, k_dec_combine<96>, cg, cb, 0, a);
-  }
-  if (err != hipSuccess) return err;
-  // 5. out = z U^T (+ x)
-  return with_nch(L / 256, [&](auto N) {
-    constexpr int n = decltype(N)::value;
-    hipError_t e = ensure_lds((const void*)k_dec_uproj<n>, uproj_lds(kDecodeMaxT, L));
-    if (e == hipSuccess)
-      e = mk.launch(kStageUproj, k_dec_uproj<n>, dim3((H + 15) / 16), block, uproj_lds(T, L), a);
-    return e;
-  });
+hipError_t launch_router_fold(const uint16_t* R, const uint16_t* D, int E, int latent, int hidden,
+                              uint16_t* dst, hipStream_t stream) {
+  if (E <= 0 || hidden <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_router_fold, dim3((hidden + 255) / 256, E), dim3(256), 0, stream, R, D, E,
+                     latent, hidden, dst);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -79,14 +79,6 @@ __device__ __forceinline__ int swz(int row, int c) {
 // an fp32 accumulation differs from plain K order; the set of products
 // does not.
 
-// Workgroup barrier that orders LDS accesses only: global loads still in
-// flight (the next steps' operands) are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // 128 rows of bf16 A into a swizzled [128][BK] LDS tile, straight from
 // global memory (global_load_lds_dwordx4: lane L of a wave writes its 16
 // bytes at the wave's LDS base + 16 L). Thread t fills the tile's 16-byte
@@ -124,15 +116,6 @@ struct ALoader {
 // for (wait_vmcnt) and its LDS reads have been consumed: no memory fence, so
 // the compiler adds no wait for the loads still in flight.
 __device__ __forceinline__ void dma_barrier() { __builtin_amdgcn_s_barrier(); }
-
-// Waits until at most n vector-memory loads of this wave are outstanding
-// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left
-// at "no wait").
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
 
 // B operand in registers: expert weights in e2m1 codes + E4M3 block scales.
 // Lane (half h) of sub-tile j holds BK/2 codes and BK/32 scale bytes of its

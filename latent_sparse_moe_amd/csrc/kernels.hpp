@@ -148,6 +148,7 @@ struct DecodeArgs {
   const uint16_t* x;
   const uint16_t* D;
   const uint16_t* R;
+  const uint16_t* RD;        // folded router [2][E][hidden] (hi, lo; decode-packed), or null
   const uint16_t* U;
   const float* bias;         // or null
   const float* norm_weight;  // residual block when non-null
@@ -157,19 +158,17 @@ struct DecodeArgs {
   int hidden, latent, inter, n_experts, top_k, n_shared, T;
   bool packed;  // D, U, R and the expert sets above are in the decode-packed layouts
   int gateup_bits;  // 4: e2m1 gate/up codes (routed and shared); 3: E1M1
-  // where the top-k runs: in the last router workgroup to finish (true) or
-  // in every gate/up workgroup (false; chosen when the gate/up grid is
-  // resident in one round)
-  bool topk_in_router;
-  unsigned* route_counter;  // router workgroups that finished (zeroed by dec_dproj)
+  int n_parts;      // the logits are the sum of n_parts [T][E] parts (set by launch_decode)
   // scratch (workspace)
-  uint16_t* hhi;       // [T][latent]
-  uint16_t* hlo;       // [T][latent]
-  float* logits;       // [T][E]
+  uint16_t* hhi;       // [T][latent] bf16(h)
+  uint16_t* hlo;       // [T][latent] h - bf16(h) (unfolded router only; else null)
+  float* logits;       // [n_parts][T][E]
   uint16_t* act;       // [1 + max_active][T][inter]   slot 0: shared expert
-  float* zpart;        // [1 + max_active][T][latent]  per-slot weighted down rows
+  // [T][latent] combined expert output in 64-bit fixed point (units of
+  // 2^-32), zeroed by the first kernel, summed by the down kernel
+  unsigned long long* zfix;
   int max_active;      // min(n_experts, T * top_k): capacity of the routing table
-  uint16_t* z;         // [T][latent] combined expert output (bf16)
+  int gu_grid;         // gate/up workgroups (set by launch_decode)
   int* route_n_act;    // [1]
   int* route_list;     // [max_active]
   float* route_wtab;   // [1 + max_active][T]
@@ -185,10 +184,17 @@ struct DecodeArgs {
 };
 
 bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int T);
-constexpr int kDecodeDownRows = 128;  // latent rows per down workgroup (8 waves x 16)
-__host__ __device__ inline int decode_row_ranges(int latent) {
-  return (latent + kDecodeDownRows - 1) / kDecodeDownRows;
+constexpr int kDecodeDownGroup = 8;  // expert slots per down workgroup (one per wave)
+// Slot groups of the down kernel for a routing table of max_active experts
+// (slots 0 .. max_active, slot 0 the shared expert).
+__host__ __device__ inline int decode_down_groups(int max_active) {
+  return (max_active + kDecodeDownGroup) / kDecodeDownGroup;
 }
+// The router folded onto the residual width (moe_router_fold): W = R D in
+// fp64, stored as bf16 hi = bf16(W) and lo = bf16(W - hi) in the
+// decode-packed bf16 layout ([2][E][hidden]); E % 16 == 0, hidden % 32 == 0.
+hipError_t launch_router_fold(const uint16_t* R, const uint16_t* D, int E, int latent, int hidden,
+                              uint16_t* dst, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& mk);
 // Decode-packed layouts (decode.hip): fp4 set [count][N][K] with N % 16 == 0,
 // K % 128 == 0; bf16 [N][K] with N % 16 == 0, K % 32 == 0.

@@ -45,10 +45,10 @@ struct Layout {
   size_t z;         // bf16 [T][latent]
   // decode path (T <= kDecodeMaxT)
   size_t d_hhi, d_hlo;   // bf16 [T][latent]
-  size_t d_logits;       // fp32 [T][E]
+  size_t d_logits;       // fp32 [2][T][E]
   size_t d_act;          // bf16 [1 + max_active][T][inter]
-  size_t d_zpart;        // fp32 [1 + max_active][T][latent]
-  size_t d_n_act, d_list, d_wtab, d_counter, d_z;
+  size_t d_zfix;         // int64 [T][latent] (fixed point)
+  size_t d_n_act, d_list, d_wtab;
   size_t total;
 };
 
@@ -81,17 +81,14 @@ Layout layout_of(const moe_latent_dims& d, int64_t T) {
     const int64_t max_act = d.n_experts < T * d.top_k ? d.n_experts : T * d.top_k;
     L.d_hhi = take(T * d.latent * 2);
     L.d_hlo = take(T * d.latent * 2);
-    L.d_logits = take(T * d.n_experts * 4);
+    L.d_logits = take(2 * T * d.n_experts * 4);
     L.d_act = take((1 + max_act) * T * d.inter * 2);
-    L.d_zpart = take((1 + max_act) * T * d.latent * 4);
+    L.d_zfix = take(T * d.latent * 8);
     L.d_n_act = take(4);
     L.d_list = take(max_act * 4);
     L.d_wtab = take((1 + max_act) * T * 4);
-    L.d_counter = take(4);
-    L.d_z = take(T * d.latent * 2);
   } else {
-    L.d_hhi = L.d_hlo = L.d_logits = L.d_act = L.d_zpart = L.d_n_act = L.d_list = L.d_wtab = 0;
-    L.d_counter = L.d_z = 0;
+    L.d_hhi = L.d_hlo = L.d_logits = L.d_act = L.d_zfix = L.d_n_act = L.d_list = L.d_wtab = 0;
   }
   L.total = at;
   return L;
@@ -294,6 +291,7 @@ int run_decode(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_
   a.x = x;
   a.D = D;
   a.R = dp ? (const uint16_t*)dp->R : router->w;
+  a.RD = dp ? (const uint16_t*)dp->RD : nullptr;
   a.U = U;
   a.bias = router->bias;
   a.norm_weight = o.residual ? o.norm_weight : nullptr;
@@ -316,16 +314,14 @@ int run_decode(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_
   a.n_shared = d.n_shared;
   a.T = T;
   a.hhi = (uint16_t*)(ws + L.d_hhi);
-  a.hlo = (uint16_t*)(ws + L.d_hlo);
+  a.hlo = a.RD ? nullptr : (uint16_t*)(ws + L.d_hlo);
   a.logits = (float*)(ws + L.d_logits);
   a.act = (uint16_t*)(ws + L.d_act);
-  a.zpart = (float*)(ws + L.d_zpart);
+  a.zfix = (unsigned long long*)(ws + L.d_zfix);
   a.route_n_act = (int*)(ws + L.d_n_act);
   a.route_list = (int*)(ws + L.d_list);
   a.route_wtab = (float*)(ws + L.d_wtab);
-  a.route_counter = (unsigned*)(ws + L.d_counter);
   a.max_active = d.n_experts < T * d.top_k ? d.n_experts : T * d.top_k;
-  a.z = (uint16_t*)(ws + L.d_z);
   a.out = out;
   if (dbg) {
     a.dbg_idx = dbg->topk_idx;
@@ -400,6 +396,27 @@ int moe_fp4_pack(const moe_fp4_matrix* src, int32_t count, int32_t N, int32_t K,
   else
     HIP_TRY(moe::launch_pack_fp4_decode(src->codes, src->scales, count, N, K, bits, dst_codes,
                                         dst_scales, (hipStream_t)stream));
+  return 0;
+}
+
+int moe_router_fold(const moe_latent_dims* dims, const void* D, const void* R, void* dst,
+                    void* stream) {
+  g_err.clear();
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  const moe_latent_dims& d = *dims;
+  if (!D || !R || !dst) return fail(MOE_LATENT_EINVAL, "D, R and dst must be non-NULL");
+  if (d.n_experts % 16 || d.hidden % 32)
+    return fail(MOE_LATENT_EUNSUPPORTED, "the folded router needs n_experts a multiple of 16 and "
+                                         "hidden of 32 (%d, %d)", d.n_experts, d.hidden);
+  if (!aligned(D, 16) || !aligned(R, 16) || !aligned(dst, 16))
+    return fail(MOE_LATENT_EINVAL, "D, R and dst must be 16-byte aligned");
+  const size_t nd = (size_t)2 * d.n_experts * d.hidden * 2;
+  if (overlaps(dst, nd, D, (size_t)d.latent * d.hidden * 2) ||
+      overlaps(dst, nd, R, (size_t)d.n_experts * d.latent * 2))
+    return fail(MOE_LATENT_EINVAL, "dst overlaps D or R");
+  HIP_TRY(moe::launch_router_fold((const uint16_t*)R, (const uint16_t*)D, d.n_experts, d.latent,
+                                  d.hidden, (uint16_t*)dst, (hipStream_t)stream));
   return 0;
 }
 
@@ -524,14 +541,15 @@ int forward_impl(const moe_latent_dims* dims, int64_t T, const void* x, const vo
                   d.n_experts);
   }
   if (const moe_packed_weights* dp = o.decode_packed) {
-    if (!dp->experts || (d.n_shared && !dp->shared) || !dp->D || !dp->U || !dp->R)
+    if (!dp->experts || (d.n_shared && !dp->shared) || !dp->D || !dp->U || (!dp->R && !dp->RD))
       return fail(MOE_LATENT_EINVAL, "decode_packed needs experts, shared (n_shared = 1), D, U "
-                                     "and R");
+                                     "and R or RD");
     if (d.n_experts % 16)
       return fail(MOE_LATENT_EUNSUPPORTED, "decode-packed weights need n_experts a multiple of 16 "
                                            "(%d)", d.n_experts);
-    if (!aligned(dp->D, 16) || !aligned(dp->U, 16) || !aligned(dp->R, 16))
-      return fail(MOE_LATENT_EINVAL, "decode-packed D, U and R must be 16-byte aligned");
+    if (!aligned(dp->D, 16) || !aligned(dp->U, 16) || (dp->R && !aligned(dp->R, 16)) ||
+        (dp->RD && !aligned(dp->RD, 16)))
+      return fail(MOE_LATENT_EINVAL, "decode-packed D, U, R and RD must be 16-byte aligned");
     if ((rc = check_set(dp->experts, "decode_packed->experts", d.n_experts))) return rc;
     if (d.n_shared && (rc = check_set(dp->shared, "decode_packed->shared", d.n_shared))) return rc;
   }

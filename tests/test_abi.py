@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version(lib):
-    assert lib.moe_latent_version() == 3
+    assert lib.moe_latent_version() == 4
 
 
 def _dims(**kw):

@@ -84,7 +84,7 @@ def test_mixed_packed_bit_exact(name, T):
     say(f"[case] mixed packed vs plain {name} T={T}")
     plain = run_gpu(dl, x, path=lsm.PATH_GROUPED)
     pk = lsm.DeviceLayer(**{**dl.__dict__})
-    pk.pack()
+    pk.pack(fold_router=False)   # the same logits as the plain path: bit for bit
     assert pk.grouped_packed.experts.gate.bits == 3 and pk.decode_packed.experts.up.bits == 3
     got = run_gpu(pk, x, path=lsm.PATH_GROUPED)
     assert np.array_equal(got["out_bits"], plain["out_bits"])
@@ -158,3 +158,14 @@ def test_pack_e1m1_decode_layout(count, N, K):
             ps[:, :, c, i, :] = scales[:, rows + i, 8 * c:8 * c + 8]
     assert np.array_equal(p.codes.cpu().numpy().reshape(count, -1), pc.reshape(count, -1))
     assert np.array_equal(p.scales.cpu().numpy().reshape(count, -1), ps.reshape(count, -1))
+
+
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_mixed_decode145_folded_router(T):
+    """The mixed record on the decode path with decode-packed weights and the
+    folded router (the bench's configuration) against the oracle."""
+    host, dl = mixed_layer("decode145")
+    pk = lsm.DeviceLayer(**{**dl.__dict__}).pack(grouped=False)
+    assert pk.decode_packed.RD is not None
+    run_case(f"decode145 folded T={T}", host, pk, synth.make_x(T, host.dims.hidden, 97 + T),
+             lsm.PATH_DECODE)

@@ -167,6 +167,50 @@ def test_decode_path_145b(T):
     run_case(f"decode145 decode-path T={T}", host, dl, x, lsm.PATH_DECODE)
 
 
+_folded = {}
+
+
+def folded_layer(name):
+    """A layer's decode-packed copies with the folded router (the bench's
+    decode configuration), plain weights dropped."""
+    if name not in _folded:
+        cfg, host, dl = layer_for(name)
+        _folded[name] = lsm.DeviceLayer(**{**dl.__dict__}).pack(grouped=False).drop_plain()
+    return _folded[name]
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_decode_path_145b_folded_router(T):
+    cfg, host, dl = layer_for("decode145")
+    x = synth.make_x(T, cfg.dims.hidden, cfg.seed if T == 4 else 300 + T)
+    run_case(f"decode145 decode-path folded router T={T}", host, folded_layer("decode145"), x,
+             lsm.PATH_DECODE)
+
+
+def test_decode_path_120b_folded_router():
+    cfg, host, dl = layer_for("prefill120")
+    x = synth.make_x(4, cfg.dims.hidden, 41)
+    run_case("120b decode-path folded router T=4", host, folded_layer("prefill120"), x,
+             lsm.PATH_DECODE)
+
+
+def test_folded_router_logits_agree_with_unfolded():
+    """The folded router's logits (from x) and the unfolded ones (from h's
+    hi + lo halves) agree to about 1e-5 on the 145B layer; both are within
+    1e-4 of the float64 oracle."""
+    cfg, host, dl = layer_for("decode145")
+    x = synth.make_x(8, cfg.dims.hidden, 77)
+    say("[case] folded vs unfolded router logits, decode145 T=8")
+    a = run_gpu(dl, x, path=lsm.PATH_DECODE)
+    b = run_gpu(folded_layer("decode145"), x, path=lsm.PATH_DECODE)
+    ref = oracle.forward(host, x)
+    da = np.abs(a["logits"] - ref.logits).max()
+    db = np.abs(b["logits"] - ref.logits).max()
+    dab = np.abs(a["logits"] - b["logits"]).max()
+    say(f"[ok] max |logit error|: unfolded {da:.2e}, folded {db:.2e}, between {dab:.2e}")
+    assert da < 1e-4 and db < 1e-4 and dab < 1e-4
+
+
 def test_decode_path_120b():
     cfg, host, dl = layer_for("prefill120")
     x = synth.make_x(4, cfg.dims.hidden, 41)
@@ -366,12 +410,16 @@ def _tied_layer():
     return host
 
 
-@pytest.mark.parametrize("path,T", [(lsm.PATH_GROUPED, 300), (lsm.PATH_DECODE, 8)])
-def test_exact_ties_go_to_lower_expert(path, T):
+@pytest.mark.parametrize("path,T,folded", [(lsm.PATH_GROUPED, 300, False),
+                                           (lsm.PATH_DECODE, 8, False),
+                                           (lsm.PATH_DECODE, 8, True)])
+def test_exact_ties_go_to_lower_expert(path, T, folded):
     host = _tied_layer()
     dl = lsm.DeviceLayer.from_host(host, device())
+    if folded:   # repeated router rows give repeated folded rows, so ties stay exact
+        dl = dl.pack(grouped=False).drop_plain()
     x = synth.make_x(T, TIE_DIMS.hidden, 29)
-    say(f"[case] exact ties path={path} T={T}")
+    say(f"[case] exact ties path={path} T={T} folded={folded}")
     gpu = run_gpu(dl, x, path=path)
     ref = oracle.forward(host, x)
     lg = gpu["logits"]
@@ -472,7 +520,7 @@ def test_packed_weights_bit_exact(name, T):
     say(f"[case] packed vs plain {name} T={T}")
     plain = run_gpu(dl, x, path=lsm.PATH_GROUPED)
     packed_layer = lsm.DeviceLayer(**{**dl.__dict__})
-    packed_layer.pack()
+    packed_layer.pack(fold_router=False)   # same logits as the plain path: bit for bit
     gp = packed_layer.grouped_packed
     assert gp.experts is not None and gp.D is not None and gp.U is not None
     assert (gp.R is None) == (name == "e24")

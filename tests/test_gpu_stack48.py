@@ -41,7 +41,8 @@ def test_stack145_all_48_blocks_decode_path():
     excluded = 0
     for l in range(nl):
         host = synth.make_layer(d, cfg.seed + l, cfg.bias, cfg.zipf_s)
-        dl = lsm.DeviceLayer.from_host(host, device())
+        # decode-packed copies with the folded router, plain weights dropped
+        dl = lsm.DeviceLayer.from_host(host, device()).pack(grouped=False).drop_plain()
         # the MoE on the oracle chain's own input
         y, res = oracle.block_forward(host, xo, 1e-6)
         u = _to_bf16_bits(oracle.rmsnorm(oracle.bf16_value(xo), host.norm_w, 1e-6))
