@@ -14,6 +14,20 @@ architecture"):
 SwiGLU_e(v) = W_down (silu(W_gate v) * (W_up v)), each W dequantised from its
 e2m1 codes, E4M3 block scales and fp32 matrix scale; silu(v) = v/(1+e^-v).
 
+Routing groups (agentspulse tutorial, section "latent MoE architecture": a
+layer holds eight D/U pairs, and a label on each expert names the pair it
+uses; card, "Architecture" paragraph: the down projection is done per routing
+group). With G groups, expert e belongs to group g(e) = e // (E/G) (any
+labelling is this one after renumbering the experts), and
+
+    h_g  = x D_g^T                                  for every group g
+    l_e  = h_{g(e)} R_e^T + b_e
+    z_g  = sum over the token's choices j in group g of w_j SwiGLU_{S_j}(h_g)
+           (+ SwiGLU_shared(h_0) for g = 0: the shared expert belongs to group 0)
+    out  = sum_g z_g U_g^T
+
+G = 1 is the layer above.
+
 Everything is float64. ``x``, ``D``, ``U`` and ``R`` are bf16 inputs,
 widened exactly.
 """
@@ -51,6 +65,30 @@ def swiglu_expert(v: np.ndarray, bank, e: int) -> np.ndarray:
     wd = _bank_matrix(bank, "down", e)   # [latent][inter]
     a = silu(v @ wg.T) * (v @ wu.T)
     return a @ wd.T
+
+
+# The shared expert's routing group (reading: the pages give the shared
+# expert no group label; it runs on group 0's latent and adds into it).
+SHARED_GROUP = 0
+
+
+def group_latent(h: np.ndarray, g: int, latent: int) -> np.ndarray:
+    """Group g's latent vectors: columns g*latent .. (g+1)*latent of h."""
+    return h[..., g * latent:(g + 1) * latent]
+
+
+def router_logits(h: np.ndarray, R: np.ndarray, b: np.ndarray, n_groups: int,
+                  latent: int) -> np.ndarray:
+    """l_e = h_{g(e)} R_e^T + b_e: each expert scored from its own group's
+    latent, expert e in group e // (E / n_groups) (card, "Architecture": the
+    router scores the experts from the latent; one group is the plain layer)."""
+    E = R.shape[0]
+    epg = E // n_groups
+    logits = np.empty((h.shape[0], E))
+    for g in range(n_groups):
+        ex = slice(g * epg, (g + 1) * epg)
+        logits[:, ex] = group_latent(h, g, latent) @ R[ex].T + b[ex]
+    return logits
 
 
 def gate_topk(logits32: np.ndarray, k: int):
@@ -113,7 +151,7 @@ def route_bookkeeping(idx: np.ndarray, n_experts: int):
 
 @dataclass
 class OracleResult:
-    h: np.ndarray            # float64 [T][latent]
+    h: np.ndarray            # float64 [T][G*latent] (G routing groups; G = 1: [T][latent])
     logits: np.ndarray       # float64 [T][E]
     logits32: np.ndarray     # float32 [T][E] (the values the choice is made on)
     idx: np.ndarray          # int32 [T][k]
@@ -123,7 +161,7 @@ class OracleResult:
     offsets: np.ndarray      # int32 [E+1]
     perm: np.ndarray         # int32 [T*k]
     tokens: np.ndarray       # int64 [Ts]: tokens whose outputs were computed
-    z: np.ndarray            # float64 [Ts][latent]: combined expert output
+    z: np.ndarray            # float64 [Ts][G*latent]: combined expert output
     out: np.ndarray          # float64 [Ts][hidden]
 
 
@@ -141,33 +179,44 @@ def forward(layer, x_bits: Optional[np.ndarray] = None, tokens: Optional[Sequenc
     else:
         x = np.asarray(x_values, dtype=np.float64)
     T = x.shape[0]
-    D = bf16_value(layer.D)
-    U = bf16_value(layer.U)
+    L = d.latent
+    G = getattr(d, "n_groups", 1)
+    epg = d.n_experts // G           # experts per routing group
+    D = bf16_value(layer.D)          # [G*latent][hidden]: D_g = rows g*latent ..
+    U = bf16_value(layer.U)          # [hidden][G*latent]: U_g = columns g*latent ..
     R = bf16_value(layer.R)
     b = (np.zeros(d.n_experts) if layer.bias is None
          else np.asarray(layer.bias, dtype=np.float32).astype(np.float64))
 
-    # D projects each token down to the latent width (card, "Architecture").
+    # D projects each token down to the latent width (card, "Architecture");
+    # with routing groups, through every group's D_g (the card's per-group
+    # down projection), group g's latent in columns g*latent .. of h.
     h = x @ D.T
-    # The router scores every expert from the latent vector.
-    logits = h @ R.T + b
+    # The router scores every expert from the latent vector (of the expert's
+    # group: expert e belongs to group e // (n_experts / G)).
+    logits = router_logits(h, R, b, G, L)
     logits32 = logits.astype(np.float32)
     idx, w, gap = gate_topk(logits32, d.top_k)
     counts, offsets, perm = route_bookkeeping(idx, d.n_experts)
 
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     hs = h[tok]
-    # Combined expert output: weighted routed experts plus the shared expert
-    # with weight 1 (card: "a shared expert runs alongside").
-    z = np.zeros((tok.size, d.latent))
+    # Combined expert output: weighted routed experts plus the shared expert,
+    # which the card places beside the routed ones, with weight 1. Each expert
+    # reads and adds into its own group's latent; the shared expert belongs
+    # to group 0.
+    z = np.zeros((tok.size, G * L))
     sel_idx = idx[tok]
     for e in np.unique(sel_idx):
         rows, js = np.nonzero(sel_idx == e)
-        ye = swiglu_expert(hs[rows], layer.experts, int(e))
-        z[rows] += w[tok[rows], js][:, None] * ye
+        g = int(e) // epg
+        ye = swiglu_expert(group_latent(hs[rows], g, L), layer.experts, int(e))
+        group_latent(z, g, L)[rows] += w[tok[rows], js][:, None] * ye
     if d.n_shared:
-        z += swiglu_expert(hs, layer.shared, 0)
-    # U projects the combined result back to the hidden width.
+        group_latent(z, SHARED_GROUP, L)[:] += swiglu_expert(group_latent(hs, SHARED_GROUP, L),
+                                                             layer.shared, 0)
+    # U projects the combined result back to the hidden width (summed over
+    # the groups' U_g).
     out = z @ U.T
     return OracleResult(h=h, logits=logits, logits32=logits32, idx=idx, w=w, gap=gap,
                         counts=counts, offsets=offsets, perm=perm, tokens=tok, z=z, out=out)

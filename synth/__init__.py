@@ -23,6 +23,8 @@ Recipe (every stream is independent, so any tensor can be drawn alone):
   24 + p (mantissa in w0, exponent in w1, sign in w2).
 * Router bias: zero, or the log of an unnormalised Zipf(s) prior,
   ``b_e = -s * ln(e + 1)`` ("hot experts").
+* Routing groups (``Dims.n_groups`` = G): D [G*latent][hidden] and U
+  [hidden][G*latent] drawn as one matrix each from the same streams.
 """
 from __future__ import annotations
 
@@ -165,6 +167,7 @@ class Dims:
     top_k: int
     n_shared: int = 1
     gateup_bits: int = 4   # 4: e2m1 gate/up; 3: E1M1 gate/up (down is e2m1 either way)
+    n_groups: int = 1      # routing groups: one (D_g, U_g) pair per n_experts / n_groups experts
 
 
 @dataclass
@@ -174,6 +177,8 @@ class Layer:
     D uint16 [latent][hidden] bf16 bits, U uint16 [hidden][latent],
     R uint16 [n_experts][latent], bias fp32 [n_experts] or None,
     norm_w fp32 [hidden] (pre-norm weight, used by the residual block).
+    With n_groups = G > 1: D is [G*latent][hidden] (group g's D_g = rows
+    g*latent ..) and U is [hidden][G*latent] (U_g = columns g*latent ..).
     """
     dims: Dims
     D: np.ndarray
@@ -264,9 +269,10 @@ def zipf_bias(n_experts: int, s: float) -> np.ndarray:
 
 def make_layer(dims: Dims, seed: int = 0, bias: str = "none", zipf_s: float = 1.1) -> Layer:
     H, L, E, I = dims.hidden, dims.latent, dims.n_experts, dims.inter
-    assert H % 32 == 0 and L % 32 == 0 and I % 32 == 0
-    D = normal_bf16(seed, TAG_D, 0, (L, H), H ** -0.5)
-    U = normal_bf16(seed, TAG_U, 0, (H, L), L ** -0.5)
+    G = dims.n_groups
+    assert H % 32 == 0 and L % 32 == 0 and I % 32 == 0 and E % G == 0
+    D = normal_bf16(seed, TAG_D, 0, (G * L, H), H ** -0.5)
+    U = normal_bf16(seed, TAG_U, 0, (H, G * L), L ** -0.5)
     R = normal_bf16(seed, TAG_R, 0, (E, L), L ** -0.5)
     b = zipf_bias(E, zipf_s) if bias == "zipf" else None
     gb = dims.gateup_bits
@@ -298,6 +304,11 @@ CONFIGS = {
                          description="120B-shaped layer (l=1280), T=4096 prefill"),
     "stack145": Config("stack145", E145, T=8, seed=0, bias="zipf", n_layers=48,
                        description="48 residual blocks (RMSNorm + latent MoE), T=8, Zipf bias"),
+    "grouped145": Config("grouped145", replace(E145, n_groups=8), T=4, seed=0,
+                         description="145B-shaped layer with 8 routing groups of 64 experts, "
+                                     "each with its own (D_g, U_g), decode T=4"),
+    "grouped_tiny": Config("grouped_tiny", replace(TINY, n_groups=4), T=8, seed=0,
+                           description="tiny layer with 4 routing groups of 4 experts"),
 }
 
 

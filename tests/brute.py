@@ -3,7 +3,10 @@ oracle. It shares no code with ``oracle/``: the number formats are decoded a
 different way (e2m1 by lookup in the OCP table of magnitudes, E4M3 through
 torch's float8_e4m3fn dtype, bf16 through torch's bfloat16 dtype) and the
 layer runs token by token, expert by expert, with Python loops over rows and
-torch float64 dot products. Only for small shapes."""
+torch float64 dot products. With routing groups, each expert's logit and
+output use its own group's latent (label e * G // E), the shared expert
+group 0's, and the output is the sum of the per-group up projections. Only
+for small shapes."""
 from __future__ import annotations
 
 import math
@@ -116,10 +119,16 @@ def brute_forward(layer, x_bits: np.ndarray = None, x_values=None):
          else torch.from_numpy(np.asarray(layer.bias, dtype=np.float32)).to(torch.float64))
     bl = BruteLayer(layer)
     T = x.shape[0]
+    L = d.latent
+    G = getattr(d, "n_groups", 1)
+    group = [e * G // d.n_experts for e in range(d.n_experts)]   # the expert's label
+    Dg = [D[g * L:(g + 1) * L] for g in range(G)]                 # D_g [latent][hidden]
+    Ug = [U[:, g * L:(g + 1) * L] for g in range(G)]              # U_g [hidden][latent]
     outs, idxs, ws, logits_all = [], [], [], []
     for t in range(T):
-        h = torch.mv(D, x[t])
-        logits = torch.mv(R, h) + b
+        hg = [torch.mv(Dg[g], x[t]) for g in range(G)]
+        logits = torch.tensor([float(torch.dot(R[e], hg[group[e]])) for e in range(d.n_experts)],
+                              dtype=torch.float64) + b
         l32 = logits.to(torch.float32).to(torch.float64).tolist()
         logits_all.append(l32)
         order = sorted(range(d.n_experts), key=lambda e: (-l32[e], e))
@@ -130,12 +139,15 @@ def brute_forward(layer, x_bits: np.ndarray = None, x_values=None):
         p = [v / tot for v in ex]
         ps = sum(p[e] for e in sel)
         w = [p[e] / ps for e in sel]
-        z = torch.zeros(d.latent, dtype=torch.float64)
+        zg = [torch.zeros(L, dtype=torch.float64) for _ in range(G)]
         for j, e in enumerate(sel):
-            z += w[j] * run_expert(bl, "experts", e, h)
+            zg[group[e]] += w[j] * run_expert(bl, "experts", e, hg[group[e]])
         if d.n_shared:
-            z += run_expert(bl, "shared", 0, h)
-        outs.append(torch.mv(U, z))
+            zg[0] += run_expert(bl, "shared", 0, hg[0])
+        out_t = torch.zeros(U.shape[0], dtype=torch.float64)
+        for g in range(G):
+            out_t += torch.mv(Ug[g], zg[g])
+        outs.append(out_t)
         idxs.append(sel)
         ws.append(w)
     return (torch.stack(outs).numpy(), np.array(idxs, dtype=np.int32), np.array(ws),

@@ -482,3 +482,61 @@ def check_stack_vs_torch_chain(seed=17):
         cur = _torch_block_bits(layer, cur, 64)
         assert np.array_equal(xs[l + 1], cur), l
     assert np.array_equal(xs[2], xs[1])
+
+
+# --------------------------------------------------------------- routing groups
+
+def _grouped_tiny(seed=21, bias="zipf", zs=0.7):
+    d = synth.replace(synth.TINY, n_groups=4)
+    return synth.make_layer(d, seed, bias, zs)
+
+
+def check_grouped_vs_brute(seed=21):
+    """The grouped layer (4 groups of 4 experts, each with its own D_g and
+    U_g) against the independent per-token evaluation."""
+    layer = _grouped_tiny(seed)
+    x = synth.make_x(6, layer.dims.hidden, seed)
+    check_vs_brute(layer, x)
+
+
+def check_grouped_repeated_pairs_equal_one_pair(seed=22):
+    """With every (D_g, U_g) equal to (D_0, U_0), the grouped layer equals the
+    layer with one pair: every group's latent is the same h, the router sees
+    the same logits, and sum_g z_g U_0^T = (sum_g z_g) U_0^T."""
+    layer = _grouped_tiny(seed)
+    d = layer.dims
+    L, G = d.latent, d.n_groups
+    one = synth.make_layer(synth.replace(d, n_groups=1), seed, "zipf", 0.7)
+    layer.D = np.tile(one.D, (G, 1))
+    layer.U = np.tile(one.U, (1, G))
+    x = synth.make_x(9, d.hidden, seed)
+    a = oracle.forward(layer, x)
+    b = oracle.forward(one, x)
+    assert np.array_equal(a.idx, b.idx)
+    assert np.allclose(a.out, b.out, rtol=1e-12, atol=1e-12), np.abs(a.out - b.out).max()
+    assert np.allclose(a.h[:, :L], b.h, rtol=0, atol=0)
+
+
+def check_grouped_up_projection_per_group(seed=23):
+    """Only group g's U_g nonzero: the output is z_g U_g^T, i.e. exactly the
+    contribution of the token's choices in group g (and of the shared
+    expert for g = 0); the other groups' terms vanish."""
+    layer = _grouped_tiny(seed)
+    d = layer.dims
+    L, G, epg = d.latent, d.n_groups, d.n_experts // d.n_groups
+    x = synth.make_x(7, d.hidden, seed)
+    full = oracle.forward(layer, x)
+    total = np.zeros_like(full.out)
+    for g in range(G):
+        lg = synth.make_layer(d, seed, "zipf", 0.7)
+        U = lg.U.copy()
+        keep = np.zeros_like(U)
+        keep[:, g * L:(g + 1) * L] = U[:, g * L:(g + 1) * L]
+        lg.U = keep
+        r = oracle.forward(lg, x)
+        # tokens with no choice in group g (and g != 0) get exactly zero
+        for t in range(x.shape[0]):
+            if g != 0 and not any(int(e) // epg == g for e in full.idx[t]):
+                assert np.all(r.out[t] == 0.0), (g, t)
+        total += r.out
+    assert np.allclose(total, full.out, rtol=1e-12, atol=1e-12)

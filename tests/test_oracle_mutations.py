@@ -219,3 +219,47 @@ def test_mixed_record_gateup_read_as_fp4_caught(monkeypatch):
         return F.dequant_fp4(m.codes[e][..., : m.scales.shape[-1] * 8], m.scales[e], m.gscale[e])
     monkeypatch.setattr(M, "_bank_matrix", bad_bank_matrix)
     assert _fails(_tiny_mixed_vs_brute)
+
+
+# ---- routing groups: each planted mistake must fail a grouped pin
+
+def _grouped_fails():
+    return _fails(pins.check_grouped_vs_brute, pins.check_grouped_repeated_pairs_equal_one_pair,
+                  pins.check_grouped_up_projection_per_group)
+
+
+def test_router_reads_group0_latent_caught(monkeypatch):
+    """Every expert's logit read from group 0's latent."""
+    def bad(h, R, b, n_groups, latent):
+        return h[:, :latent] @ R.T + b
+    monkeypatch.setattr(M, "router_logits", bad)
+    assert _grouped_fails()
+
+
+def test_experts_read_group0_latent_caught(monkeypatch):
+    """Every expert run on group 0's latent (and added into group 0)."""
+    monkeypatch.setattr(M, "group_latent", lambda h, g, latent: h[..., :latent])
+    assert _grouped_fails()
+
+
+def test_shared_expert_in_group1_caught(monkeypatch):
+    """The shared expert run on, and added into, group 1."""
+    monkeypatch.setattr(M, "SHARED_GROUP", 1)
+    assert _grouped_fails()
+
+
+def test_groups_up_projections_swapped_caught(monkeypatch):
+    """z_0 projected with U_1 and z_1 with U_0."""
+    src = M.forward
+
+    def fwd(layer, x_bits=None, tokens=None, x_values=None):
+        r = src(layer, x_bits, tokens, x_values)
+        if getattr(layer.dims, "n_groups", 1) > 1:
+            L = layer.dims.latent
+            U = oracle.bf16_value(layer.U).copy()
+            U[:, :L], U[:, L:2 * L] = U[:, L:2 * L].copy(), U[:, :L].copy()
+            r.out = r.z @ U.T
+        return r
+    monkeypatch.setattr(M, "forward", fwd)
+    monkeypatch.setattr(oracle, "forward", fwd)
+    assert _grouped_fails()

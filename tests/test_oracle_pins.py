@@ -152,3 +152,15 @@ def test_vs_brute_tiny_mixed_record():
     layer = synth.make_layer(d, 21)
     x = synth.make_x(6, d.hidden, 21)
     pins.check_vs_brute(layer, x)
+
+
+def test_grouped_vs_brute():
+    pins.check_grouped_vs_brute()
+
+
+def test_grouped_repeated_pairs_equal_one_pair():
+    pins.check_grouped_repeated_pairs_equal_one_pair()
+
+
+def test_grouped_up_projection_per_group():
+    pins.check_grouped_up_projection_per_group()
