@@ -42,10 +42,10 @@
  * kernels; `out` is bf16, rounded to nearest even.
  *
  * Layouts (all row-major, innermost index contiguous; "bf16" is the upper
- * half of an IEEE binary32, passed as uint16_t):
+ * half of an IEEE binary32, passed as uint16_t; G = dims.n_groups):
  *   x, out         bf16 [T][hidden]
- *   D              bf16 [latent][hidden]
- *   U              bf16 [hidden][latent]
+ *   D              bf16 [G * latent][hidden]   (D_g = rows g*latent ..)
+ *   U              bf16 [hidden][G * latent]   (U_g = columns g*latent ..)
  *   router.w       bf16 [n_experts][latent];  router.bias fp32 [n_experts] or NULL
  *   fp4 matrix set of `count` matrices of shape [N][K]:
  *     codes  uint8 [count][N][K/2]   element 2j in the low nibble of byte j,
@@ -133,7 +133,8 @@ extern "C" {
 
 /* Supported dims: hidden, latent, inter positive multiples of 32;
  * 1 <= n_experts <= 1024; 1 <= top_k <= min(16, n_experts);
- * n_shared in {0, 1}; T * top_k < 2^31. */
+ * n_shared in {0, 1}; n_groups 0 or 1 (one D/U pair) or G > 1 dividing
+ * n_experts; T * top_k < 2^31. */
 typedef struct moe_latent_dims {
   int32_t hidden;    /* residual width (2560) */
   int32_t latent;    /* latent width (1792 for 145B, 1280 for 120B) */
@@ -141,6 +142,17 @@ typedef struct moe_latent_dims {
   int32_t inter;     /* SwiGLU width of every expert (640) */
   int32_t top_k;     /* routed experts per token (10) */
   int32_t n_shared;  /* shared experts (0 or 1) */
+  /* Routing groups G (0 means 1): one (D_g, U_g) pair per group of
+   * n_experts / G experts (agentspulse tutorial, section "latent MoE
+   * architecture": a layer holds eight such pairs, a label on each expert
+   * names its pair; Hugging Face card, "Architecture": the down projection
+   * is done per routing group). Reading: expert e belongs to group
+   * e / (n_experts / G) (any labelling is this one after renumbering the
+   * experts); every token is projected by every D_g; expert e's logit and
+   * output use its group's latent h_g = x D_g^T; the shared expert belongs
+   * to group 0; out = sum_g z_g U_g^T, z_g the weighted outputs of the
+   * token's experts in group g. */
+  int32_t n_groups;
 } moe_latent_dims;
 
 typedef struct moe_fp4_matrix {
@@ -195,7 +207,8 @@ typedef struct moe_route_debug {
 
 /* Execution path: the grouped-GEMM pipeline (any T) or the weight-streaming
  * decode kernels (T <= MOE_LATENT_DECODE_MAX_T; hidden and latent multiples
- * of 256 with latent <= 1792, inter a multiple of 128). AUTO picks the decode
+ * of 256 with latent <= 1792, inter a multiple of 128 up to 640, and with
+ * routing groups n_experts / G a multiple of 16). AUTO picks the decode
  * kernels whenever T and the dims allow it; DECODE with other sizes returns
  * MOE_LATENT_EUNSUPPORTED. */
 #define MOE_LATENT_PATH_AUTO 0
@@ -332,7 +345,8 @@ int moe_bf16_pack(const void *src, int32_t N, int32_t K, int32_t layout, void *d
 
 /* The router folded onto the residual width, for the decode path: since
  * l = h R^T + b with h = x D^T (the layer recipe above), l = x W^T + b with
- * W = R D, [n_experts][hidden]. W is accumulated in fp64 and stored as two
+ * W = R D, [n_experts][hidden] (with routing groups, row e of W is
+ * R_e D_{g(e)}). W is accumulated in fp64 and stored as two
  * bf16 matrices, hi = bf16(W) and lo = bf16(W - hi) (together about 16
  * significant bits, as the latent vector's hi + lo halves the unfolded
  * router reads), each in the decode-packed bf16 layout, hi first: dst holds

@@ -29,7 +29,7 @@ c_i32, c_i64, c_size, c_vp, c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_siz
 
 class CDims(ctypes.Structure):
     _fields_ = [("hidden", c_i32), ("latent", c_i32), ("n_experts", c_i32), ("inter", c_i32),
-                ("top_k", c_i32), ("n_shared", c_i32)]
+                ("top_k", c_i32), ("n_shared", c_i32), ("n_groups", c_i32)]
 
 
 class CFp4Matrix(ctypes.Structure):
@@ -116,7 +116,8 @@ class MoeLatentError(RuntimeError):
 
 
 def _dims(d) -> CDims:
-    return CDims(d.hidden, d.latent, d.n_experts, d.inter, d.top_k, d.n_shared)
+    return CDims(d.hidden, d.latent, d.n_experts, d.inter, d.top_k, d.n_shared,
+                 getattr(d, "n_groups", 1))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -153,8 +154,8 @@ class DeviceExperts:
 class DeviceLayer:
     """One layer's weights in device memory, laid out as moe_latent.h describes."""
     dims: object
-    D: torch.Tensor                 # bf16 [latent][hidden]
-    U: torch.Tensor                 # bf16 [hidden][latent]
+    D: torch.Tensor                 # bf16 [G*latent][hidden] (G routing groups, default 1)
+    U: torch.Tensor                 # bf16 [hidden][G*latent]
     R: torch.Tensor                 # bf16 [n_experts][latent]
     bias: Optional[torch.Tensor]    # float32 [n_experts]
     experts: DeviceExperts
@@ -187,7 +188,7 @@ class DeviceLayer:
                 g.D = pack_bf16(self.D, PACK_GROUPED, stream)
             if d.latent % 64 == 0:
                 g.U = pack_bf16(self.U, PACK_GROUPED, stream)
-                if d.n_experts % 32 == 0:
+                if (d.n_experts // getattr(d, "n_groups", 1)) % 32 == 0:
                     g.R = pack_bf16(self.R, PACK_GROUPED, stream)
             self.grouped_packed = g
         if decode and d.hidden % 256 == 0 and d.latent % 256 == 0 and d.inter % 128 == 0 \

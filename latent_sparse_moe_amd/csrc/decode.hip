@@ -221,6 +221,15 @@ struct RowStage {
 #pragma unroll
     for (int j = 0; j < NV; ++j) v[j] = *(const uint4*)(src + slot(j, count));
   }
+  // rows of `width` elements (a multiple of 8) taken `stride` apart in src;
+  // stored contiguously by store(dst, rows * width)
+  __device__ __forceinline__ void load_rows(const uint16_t* src, int rows, int width, int stride) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = slot(j, rows * width);
+      v[j] = *(const uint4*)(src + (size_t)(i / width) * stride + i % width);
+    }
+  }
   __device__ __forceinline__ void store(uint16_t* dst, int count) const {
 #pragma unroll
     for (int j = 0; j < NV; ++j) *(uint4*)(dst + slot(j, count)) = v[j];
@@ -253,6 +262,25 @@ __device__ __forceinline__ void stage_dma(const uint16_t* src, int count, uint16
 }
 
 
+// As stage_dma for `rows` rows of `width` elements (a multiple of 8) taken
+// `stride` apart in src, stored contiguously at dst.
+template <int NV>
+__device__ __forceinline__ void stage_dma_rows(const uint16_t* src, int rows, int width, int stride,
+                                               uint16_t* dst) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nslots = rows * width / 8;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int first = v * kDecThreads + wave * 64;  // wave-uniform
+    if (first < nslots) {
+      const int i = min(first + lane, nslots - 1) * 8;
+      __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)(i / width) * stride + i % width),
+                                       (__attribute__((address_space(3))) void*)(dst + first * 8),
+                                       16, 0, 0);
+    }
+  }
+}
+
 // As stage_dma, by one wave into its own region (no workgroup barrier
 // needed before the wave reads it): lane l moves 16-byte slots l, l + 64,
 // ...; at most 63 slots past count are written (regions are padded to a
@@ -277,7 +305,10 @@ constexpr size_t kRedBytes = kDecWaves * 64 * 4 * sizeof(float);
 constexpr size_t kDmaPad = 1024;
 inline size_t front_lds(int T, int H) { return (size_t)T * H * 2 + kRedBytes + kDecodeMaxT * 4; }
 inline size_t router_lds(int T, int L) { return (size_t)2 * T * L * 2 + kRedBytes; }
-inline size_t gateup_lds(int T, int L) { return (size_t)T * L * 2 + kDmaPad; }
+// two regions of token rows: with routing groups a workgroup's tasks read
+// the latents of at most two groups
+__host__ __device__ inline size_t gateup_region(int T, int L) { return (size_t)T * L + kDmaPad / 2; }
+inline size_t gateup_lds(int T, int L) { return 2 * gateup_region(T, L) * 2; }
 // a down wave's activation region (elements): T x inter rounded up to 1 KB
 __host__ __device__ inline int down_region(int T, int I) { return (T * I + 511) / 512 * 512; }
 inline size_t down_lds(int T, int I) {
@@ -333,9 +364,10 @@ struct XStage {
   }
 };
 
-// Workgroups [0, latent/16) compute h for 16 latent rows each (K split over
-// the 8 waves) and write bf16(h), plus the low half h - bf16(h) when hlo is
-// set (the unfolded router reads both). With a folded router (a.RD), the
+// Workgroups [0, G*latent/16) compute h for 16 latent rows each (K split
+// over the 8 waves; with routing groups the rows of every group's D_g) and
+// write bf16(h), plus the low half h - bf16(h) when hlo is set (the
+// unfolded router reads both). With a folded router (a.RD), the
 // next n_parts * E/16 workgroups compute logits for 16 experts over one of
 // n_parts K parts: l_part = x_part . (W_hi + W_lo)_part (the bias with part
 // 0). NCH = hidden / 256, NCHR = NCH / n_parts. The workgroups also zero
@@ -344,14 +376,15 @@ template <int NCH, int NCHR>
 __global__ __launch_bounds__(kDecThreads) void k_dec_front(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int H = a.hidden, L = a.latent, T = a.T, E = a.n_experts;
+  const int GL = a.n_groups * L;            // latent rows of all groups' D_g
   uint16_t* xs = lds;                       // [T][H] bf16
   float* red = (float*)(lds + T * H);       // [8][64][4]
   float* rstd = red + kDecWaves * 64 * 4;   // [T]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
-  for (int i = blockIdx.x * kDecThreads + tid; i < T * L; i += gridDim.x * kDecThreads)
+  for (int i = blockIdx.x * kDecThreads + tid; i < T * GL; i += gridDim.x * kDecThreads)
     a.zfix[i] = 0ull;  // the down kernel adds into it
-  const int nd = L / 16;
+  const int nd = GL / 16;
   XStage<(NCH + 1) / 2> xr;  // T x hidden, hidden = 256 NCH
   if ((int)blockIdx.x < nd) {
     const int row0 = blockIdx.x * 16;
@@ -359,7 +392,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_front(DecodeArgs a) {
     xr.load(a);
     Bf16Rows<NCH> wr;
     int step;
-    wr.load(bf16_lane(a.D, a.packed, L, H, row0, kb, &step), step);
+    wr.load(bf16_lane(a.D, a.packed, GL, H, row0, kb, &step), step);
     xr.finish(a, xs, rstd);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     wr.mma(xs + min(t, T - 1) * H, kb, g, acc);  // token columns >= T are not stored
@@ -369,8 +402,8 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_front(DecodeArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int n = row0 + g * 4 + r;
         const uint16_t hi = f32_to_bf16_bits(tot[r]);
-        a.hhi[(size_t)t * L + n] = hi;
-        if (a.hlo) a.hlo[(size_t)t * L + n] = f32_to_bf16_bits(tot[r] - bf16_bits_to_f32(hi));
+        a.hhi[(size_t)t * GL + n] = hi;
+        if (a.hlo) a.hlo[(size_t)t * GL + n] = f32_to_bf16_bits(tot[r] - bf16_bits_to_f32(hi));
       }
     }
     return;
@@ -410,18 +443,20 @@ template <int NCH>
 __global__ __launch_bounds__(kDecThreads) void k_dec_router(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int L = a.latent, T = a.T, E = a.n_experts;
+  const int GL = a.n_groups * L;
   uint16_t* hi = lds;           // [T][L]
   uint16_t* lo = lds + T * L;   // [T][L]
   float* red = (float*)(lo + T * L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
   const int e0 = blockIdx.x * 16;
+  const int grp = e0 / (E / a.n_groups);  // the 16 experts' routing group
   const int kb = wave * (L / kDecWaves);
   RowStage<(NCH + 1) / 2> sh_hi, sh_lo;  // T x latent, latent = 256 NCH
   // latent rows staged (and waited for) before the router rows are loaded
   // (measured: 0.6 us less per decode step)
-  sh_hi.load(a.hhi, T * L);
-  sh_lo.load(a.hlo, T * L);
+  sh_hi.load_rows(a.hhi + (size_t)grp * L, T, L, GL);
+  sh_lo.load_rows(a.hlo + (size_t)grp * L, T, L, GL);
   sh_hi.store(hi, T * L);
   sh_lo.store(lo, T * L);
   __syncthreads();
@@ -665,21 +700,24 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ RouteLds rl;
   const int L = a.latent, T = a.T, I = a.inter, E = a.n_experts;
-  uint16_t* hs = lds;  // [T][L] (+ the DMA pad)
+  const int GL = a.n_groups * L, epg = E / a.n_groups;
+  uint16_t* hs = lds;  // two regions of [T][L] (+ the DMA pad)
+  const int region = (int)gateup_region(T, L);
   const int tid = threadIdx.x, wave = tid >> 6;
   const int tiles = I / 16;
   constexpr int NV = (NCH + 3) / 4;  // 16-byte slots per thread: T x latent, T <= 8
   for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
   const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;
+  const bool one_group = a.n_groups == 1;  // the rows are known before the routing
   if (E <= 512) {
     float v[8];
     wave_load_keys<8>(lrow, E, T * E, a.n_parts, v);
-    stage_dma<NV>(a.hhi, T * L, hs);
+    if (one_group) stage_dma<NV>(a.hhi, T * L, hs);
     if (wave < T) wave_topk<8>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
   } else {
     float v[16];
     wave_load_keys<16>(lrow, E, T * E, a.n_parts, v);
-    stage_dma<NV>(a.hhi, T * L, hs);
+    if (one_group) stage_dma<NV>(a.hhi, T * L, hs);
     if (wave < T) wave_topk<16>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
@@ -689,10 +727,24 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   const int s0 = a.n_shared ? 0 : 1;  // first live slot
   const int P = (rl.n_act + 1 - s0) * tiles;
   const int G = gridDim.x;
+  const int p0 = (int)((int64_t)blockIdx.x * P / G);
   const int p1 = (int)((int64_t)(blockIdx.x + 1) * P / G);
-  for (int p = (int)((int64_t)blockIdx.x * P / G) + wave; p < p1; p += kDecWaves) {
+  // routing groups: this workgroup's tasks span at most two slots, so at
+  // most two groups' latents (region 0: the first task's group)
+  auto group_of = [&](int slot) { return slot == 0 ? 0 : rl.list[slot - 1] / epg; };
+  int ga = 0;
+  if (!one_group && p0 < p1) {
+    ga = group_of(s0 + p0 / tiles);
+    const int gb = group_of(s0 + (p1 - 1) / tiles);
+    stage_dma_rows<NV>(a.hhi + (size_t)ga * L, T, L, GL, hs);
+    if (gb != ga) stage_dma_rows<NV>(a.hhi + (size_t)gb * L, T, L, GL, hs + region);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  if (!one_group) __syncthreads();
+  for (int p = p0 + wave; p < p1; p += kDecWaves) {
     const int slot = s0 + p / tiles;
-    gateup_task<NCH, BITS>(a, hs, slot, slot == 0 ? 0 : rl.list[slot - 1], (p % tiles) * 16);
+    const uint16_t* rows = hs + (group_of(slot) == ga ? 0 : region);
+    gateup_task<NCH, BITS>(a, rows, slot, slot == 0 ? 0 : rl.list[slot - 1], (p % tiles) * 16);
   }
 }
 
@@ -720,14 +772,15 @@ template <int NCH>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_dec_down(
     DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // 8 activation regions, red
+  __shared__ int wgrp[kDecWaves];  // each wave's routing group (-1: no slot)
   const int L = a.latent, T = a.T, I = a.inter;
+  const int GL = a.n_groups * L, epg = a.n_experts / a.n_groups;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
   const int ntile = L / 16;
   const int r0 = (blockIdx.x % ntile) * 16, q = blockIdx.x / ntile;
   const int region = down_region(T, I);
   float* red = (float*)(lds + kDownGroup * region);
-  (void)tid;
   // the routing table, read together (clamped indices; used only when live)
   const int n_act = a.route_n_act[0];
   const int s = kDownGroup * q + wave;
@@ -736,7 +789,9 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(6, 
   const float w_guess = a.route_wtab[sc * T + min(t, T - 1)];
   if (q >= (n_act + kDownGroup) / kDownGroup) return;  // uniform over the workgroup
   f32x4 y = {0.f, 0.f, 0.f, 0.f};
-  if ((s > 0 || a.n_shared) && s <= n_act) {  // uniform over the wave
+  const bool live = (s > 0 || a.n_shared) && s <= n_act;
+  if (lane == 0) wgrp[wave] = live ? (s == 0 ? 0 : e_guess / epg) : -1;
+  if (live) {  // uniform over the wave
     const bool sh = s == 0;
     const Fp4Mat dm = sh ? a.sh_down : a.down;
     const int e = sh ? 0 : e_guess;
@@ -778,14 +833,30 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(6, 
   *(f32x4*)(red + (wave * 64 + lane) * 4) = y;
   __syncthreads();
   if (wave == 0 && t < T) {
-    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-    for (int w = 0; w < kDecWaves; ++w) tot += *(const f32x4*)(red + (w * 64 + lane) * 4);
-    unsigned long long* zp = a.zfix + (size_t)t * L + r0 + g * 4;
+    // the slots' products in slot order, one sum per run of slots of one
+    // routing group (slots are in ascending expert order, so a group's
+    // slots are adjacent), each added into that group's z
+    auto flush = [&](const f32x4& tot, int grp) {
+      unsigned long long* zp = a.zfix + (size_t)t * GL + (size_t)grp * L + r0 + g * 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const long long fx = (long long)__builtin_rintf(tot[r] * 4294967296.0f);
-      __hip_atomic_fetch_add(zp + r, (unsigned long long)fx, __ATOMIC_RELAXED, AGENT);
+      for (int r = 0; r < 4; ++r) {
+        const long long fx = (long long)__builtin_rintf(tot[r] * 4294967296.0f);
+        __hip_atomic_fetch_add(zp + r, (unsigned long long)fx, __ATOMIC_RELAXED, AGENT);
+      }
+    };
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    int cur = -1;
+    for (int w = 0; w < kDecWaves; ++w) {
+      const int gw = wgrp[w];
+      if (gw < 0) continue;
+      if (gw != cur) {
+        if (cur >= 0) flush(tot, cur);
+        tot = f32x4{0.f, 0.f, 0.f, 0.f};
+        cur = gw;
+      }
+      tot += *(const f32x4*)(red + (w * 64 + lane) * 4);
     }
+    if (cur >= 0) flush(tot, cur);
   }
 }
 
@@ -795,34 +866,40 @@ template <int NCH>
 __global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int L = a.latent, H = a.hidden, T = a.T;
+  const int GL = a.n_groups * L;
   uint16_t* zs = lds;  // [T][L] bf16
   float* red = (float*)(lds + T * L);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
   const int m0 = blockIdx.x * 16;
-  const int kb = wave * (L / kDecWaves);
-  (void)tid;
-  // z = bf16(zfix * 2^-32): thread i converts pairs 2 (i + 512 j) of the
-  // T x latent sums (loads issued before the weight loads)
-  constexpr int NZ = (kDecodeMaxT * 256 * NCH / 2 + kDecThreads - 1) / kDecThreads;
-  ulonglong2 zv[NZ];
-#pragma unroll
-  for (int j = 0; j < NZ; ++j)
-    zv[j] = *(const ulonglong2*)(a.zfix + 2 * min(tid + j * kDecThreads, T * L / 2 - 1));
-  Bf16Rows<NCH> wr;
-  int step;
-  const uint16_t* wb = bf16_lane(a.U, a.packed, H, L, m0, kb, &step);
-  wr.load(wb, step);
-#pragma unroll
-  for (int j = 0; j < NZ; ++j) {
-    const int i = min(tid + j * kDecThreads, T * L / 2 - 1);  // the last pair repeats (same value)
-    *(uint32_t*)(zs + 2 * i) =
-        pack_bf16x2((float)(long long)zv[j].x * 2.3283064365386963e-10f,
-                    (float)(long long)zv[j].y * 2.3283064365386963e-10f);
-  }
-  __syncthreads();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  wr.mma(zs + min(t, T - 1) * L, kb, g, acc);
+  // one pass per routing group g: z_g U_g^T (one pass without groups)
+  for (int grp = 0; grp < a.n_groups; ++grp) {
+    const int kb = grp * L + wave * (L / kDecWaves);
+    // z_g = bf16(zfix * 2^-32): thread i converts pairs 2 (i + 512 j) of the
+    // T x latent sums (loads issued before the weight loads)
+    constexpr int NZ = (kDecodeMaxT * 256 * NCH / 2 + kDecThreads - 1) / kDecThreads;
+    ulonglong2 zv[NZ];
+#pragma unroll
+    for (int j = 0; j < NZ; ++j) {
+      const int i = 2 * min(tid + j * kDecThreads, T * L / 2 - 1);
+      zv[j] = *(const ulonglong2*)(a.zfix + (size_t)(i / L) * GL + grp * L + i % L);
+    }
+    Bf16Rows<NCH> wr;
+    int step;
+    const uint16_t* wb = bf16_lane(a.U, a.packed, H, GL, m0, kb, &step);
+    wr.load(wb, step);
+    if (grp > 0) __syncthreads();  // the previous group's rows have been read
+#pragma unroll
+    for (int j = 0; j < NZ; ++j) {
+      const int i = min(tid + j * kDecThreads, T * L / 2 - 1);  // the last pair repeats (same value)
+      *(uint32_t*)(zs + 2 * i) =
+          pack_bf16x2((float)(long long)zv[j].x * 2.3283064365386963e-10f,
+                      (float)(long long)zv[j].y * 2.3283064365386963e-10f);
+    }
+    __syncthreads();
+    wr.mma(zs + min(t, T - 1) * L - grp * L, kb, g, acc);
+  }
   const f32x4 tot = reduce_waves(acc, red);
   if (wave == 0 && t < T) {
 #pragma unroll
@@ -875,8 +952,11 @@ static bool nch_ok(int n) {
   return n == 1 || n == 2 || n == 4 || n == 5 || n == 7 || n == 8 || n == 10;
 }
 
-bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int T) {
+bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int n_groups,
+                      int T) {
   if (T < 1 || T > kDecodeMaxT || n_experts > kMaxExperts || top_k > 16) return false;
+  // routing groups: a router workgroup's 16 experts share a group
+  if (n_groups > 1 && (n_experts / n_groups) % 16) return false;
   // D, U and the router split K over 8 waves x 4 lane groups x 8 bf16;
   // expert rows are consumed in 128-weight chunks by 4 lane groups.
   if (hidden % 256 || latent % 256 || inter % 128) return false;
@@ -920,7 +1000,7 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMark
     constexpr int nr = n % 2 == 0 ? n / 2 : n;
     const auto fn = k_dec_front<n, nr>;
     hipError_t e = ensure_lds((const void*)fn, front_lds(kDecodeMaxT, H));
-    const int grid = L / 16 + (a.RD ? nparts * (E / 16) : 0);
+    const int grid = a.n_groups * L / 16 + (a.RD ? nparts * (E / 16) : 0);
     if (e == hipSuccess) e = mk.launch(kStageDproj, fn, dim3(grid), block, front_lds(T, H), a);
     return e;
   });
@@ -944,7 +1024,11 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMark
       return hipErrorInvalidValue;  // excluded by decode_supported
     } else {
       const int tasks = (1 + a.max_active) * (I / 16);
-      const int grid = std::min(cu_count(), (tasks + kDecWaves - 1) / kDecWaves);
+      // one workgroup per CU, at most 8 tasks each when fewer suffice, and
+      // at most inter/16 tasks each (so a workgroup's tasks span at most
+      // two slots: the two latent regions of the routing-group staging)
+      const int grid = std::max(std::min(cu_count(), (tasks + kDecWaves - 1) / kDecWaves),
+                                (tasks + I / 16 - 1) / (I / 16));
       const auto fn = k_dec_gateup<2 * n, bits>;
       hipError_t e = ensure_lds((const void*)fn, gateup_lds(kDecodeMaxT, L));
       if (e == hipSuccess)
@@ -1051,19 +1135,20 @@ hipError_t launch_pack_bf16_decode(const uint16_t* w, int N, int K, uint16_t* pw
 }
 
 // The router folded onto the residual width: W[e][i] = sum_j R[e][j] D[j][i]
-// (so x W^T = (x D^T) R^T), accumulated in fp64 in j order, then stored as
+// (so x W^T = (x D^T) R^T; with routing groups, D is the expert's D_g), accumulated in fp64 in j order, then stored as
 // hi = bf16(W) and lo = bf16(W - hi) (together about 16 significant bits)
 // at their places in the decode-packed bf16 layout of an [E][hidden]
 // matrix: hi in dst[0 .. E*hidden), lo after it. One thread per element;
 // the workgroup's 256 threads share e (the R row is read as a broadcast).
 __global__ __launch_bounds__(256) void k_router_fold(const uint16_t* __restrict__ R,
                                                      const uint16_t* __restrict__ D, int E,
-                                                     int latent, int hidden,
+                                                     int latent, int hidden, int n_groups,
                                                      uint16_t* __restrict__ dst) {
   const int i = blockIdx.x * 256 + threadIdx.x;  // column (hidden)
   const int e = blockIdx.y;                      // row (expert)
   if (i >= hidden) return;
   const uint16_t* rrow = R + (size_t)e * latent;
+  D += (size_t)(e / (E / n_groups)) * latent * hidden;  // the expert's group's D_g
   double acc = 0.0;
   for (int j = 0; j < latent; ++j)
     acc = fma((double)bf16_bits_to_f32(rrow[j]), (double)bf16_bits_to_f32(D[(size_t)j * hidden + i]),
@@ -1079,10 +1164,10 @@ __global__ __launch_bounds__(256) void k_router_fold(const uint16_t* __restrict_
 }
 
 hipError_t launch_router_fold(const uint16_t* R, const uint16_t* D, int E, int latent, int hidden,
-                              uint16_t* dst, hipStream_t stream) {
+                              int n_groups, uint16_t* dst, hipStream_t stream) {
   if (E <= 0 || hidden <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_router_fold, dim3((hidden + 255) / 256, E), dim3(256), 0, stream, R, D, E,
-                     latent, hidden, dst);
+                     latent, hidden, n_groups < 1 ? 1 : n_groups, dst);
   return hipGetLastError();
 }
 

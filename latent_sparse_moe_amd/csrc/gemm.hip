@@ -393,8 +393,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
         const int nv = min(8, N - n);
         if (EPI == kEpiSplit) {
           // latent vector as bf16 hi + bf16 lo: hi feeds the experts, hi + lo
-          // (about 16 significant bits) feeds the router
-          uint16_t* o = (uint16_t*)ep.out + (size_t)m * ep.ldo + n;
+          // (about 16 significant bits) feeds the router; group g's columns
+          // (of group_w, a multiple of 8) go to its own hi | lo block
+          uint16_t* o = (uint16_t*)ep.out + (size_t)m * ep.ldo + n + (n / ep.group_w) * ep.group_w;
           float lo[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) lo[e] = v[e] - bf16_bits_to_f32(f32_to_bf16_bits(v[e]));
@@ -597,10 +598,13 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, i
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   const int P = rv.pairs;
   ALoader<BK> al;
+  // the expert's routing group's latent (the shared expert: group 0)
+  const uint16_t* hgrp = hcat + (size_t)(tw.group < rv.n_experts ? tw.group / rv.experts_per_group
+                                                                  : 0) * rv.group_stride;
   al.init([&](int r) {
     const int row = min(tw.rbeg + r, tw.rend - 1);
     const int tok = row < P ? rv.perm[row] / rv.top_k : row - P;
-    return hcat + (size_t)tok * ldh;
+    return hgrp + (size_t)tok * ldh;
   });
   Fp4B<BK, PK, BITS> bl;
 #pragma unroll

@@ -39,6 +39,11 @@ struct RouteView {
   int n_shared;
   int pairs;  // T * top_k
   int top_k;
+  // routing groups of D/U: expert e reads the latent of group
+  // e / experts_per_group, at column (that group) * group_stride of its
+  // token's row (the shared expert: group 0)
+  int experts_per_group;
+  int group_stride;
 };
 
 enum { kEpiSplit = 0, kEpiLogits = 1, kEpiOut = 2 };
@@ -46,7 +51,11 @@ enum { kEpiSplit = 0, kEpiLogits = 1, kEpiOut = 2 };
 struct DenseEpilogue {
   void* out;
   int ldo;
-  int lo_off;              // kEpiSplit: column offset of the lo half
+  // kEpiSplit: output column n (of group g = n / group_w) goes to column
+  // n + g * group_w (hi) and that plus lo_off (lo): per group, group_w hi
+  // columns then group_w lo columns when lo_off = group_w
+  int lo_off;
+  int group_w;
   const float* bias;       // kEpiLogits: [N] or null
   const uint16_t* resid;   // kEpiOut: bf16 [M][ldr] added before rounding, or null
   int ldr;
@@ -89,8 +98,11 @@ hipError_t launch_route_scan(int32_t* chunk_hist, int n_chunks, int E, int pairs
 hipError_t launch_route_permute(const int32_t* idx, int pairs, int E,
                                 const int32_t* chunk_base, const int32_t* off, int32_t* perm,
                                 int32_t* slot, hipStream_t stream);
-hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w, int T, int k,
-                          int pairs, int latent, int n_shared, uint16_t* z, hipStream_t stream);
+// z [T][G * latent]: group g's columns hold the token's experts of group g
+// (expert e in group e / experts_per_group; the shared expert in group 0).
+hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w,
+                          const int32_t* idx, int T, int k, int pairs, int latent, int n_shared,
+                          int n_groups, int experts_per_group, uint16_t* z, hipStream_t stream);
 
 // ------------------------------------------------------------------ decode path
 
@@ -156,15 +168,16 @@ struct DecodeArgs {
   Fp4Mat gate, up, down;           // routed experts
   Fp4Mat sh_gate, sh_up, sh_down;  // shared expert (count 1)
   int hidden, latent, inter, n_experts, top_k, n_shared, T;
+  int n_groups;  // routing groups: D [G*latent][hidden], U [hidden][G*latent]; h, z [T][G*latent]
   bool packed;  // D, U, R and the expert sets above are in the decode-packed layouts
   int gateup_bits;  // 4: e2m1 gate/up codes (routed and shared); 3: E1M1
   int n_parts;      // the logits are the sum of n_parts [T][E] parts (set by launch_decode)
   // scratch (workspace)
-  uint16_t* hhi;       // [T][latent] bf16(h)
-  uint16_t* hlo;       // [T][latent] h - bf16(h) (unfolded router only; else null)
+  uint16_t* hhi;       // [T][G*latent] bf16(h)
+  uint16_t* hlo;       // [T][G*latent] h - bf16(h) (unfolded router only; else null)
   float* logits;       // [n_parts][T][E]
   uint16_t* act;       // [1 + max_active][T][inter]   slot 0: shared expert
-  // [T][latent] combined expert output in 64-bit fixed point (units of
+  // [T][G*latent] combined expert output in 64-bit fixed point (units of
   // 2^-32), zeroed by the first kernel, summed by the down kernel
   unsigned long long* zfix;
   int max_active;      // min(n_experts, T * top_k): capacity of the routing table
@@ -183,7 +196,8 @@ struct DecodeArgs {
   float* dbg_logits;
 };
 
-bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int T);
+bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_k, int n_groups,
+                      int T);
 constexpr int kDecodeDownGroup = 8;  // expert slots per down workgroup (one per wave)
 // Slot groups of the down kernel for a routing table of max_active experts
 // (slots 0 .. max_active, slot 0 the shared expert).
@@ -194,7 +208,7 @@ __host__ __device__ inline int decode_down_groups(int max_active) {
 // fp64, stored as bf16 hi = bf16(W) and lo = bf16(W - hi) in the
 // decode-packed bf16 layout ([2][E][hidden]); E % 16 == 0, hidden % 32 == 0.
 hipError_t launch_router_fold(const uint16_t* R, const uint16_t* D, int E, int latent, int hidden,
-                              uint16_t* dst, hipStream_t stream);
+                              int n_groups, uint16_t* dst, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st, const StageMarks& mk);
 // Decode-packed layouts (decode.hip): fp4 set [count][N][K] with N % 16 == 0,
 // K % 128 == 0; bf16 [N][K] with N % 16 == 0, K % 32 == 0.

@@ -27,10 +27,13 @@ int fail(int code, const char* fmt, ...) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Routing groups of D/U (dims.n_groups, 0 meaning 1).
+int groups_of(const moe_latent_dims& d) { return d.n_groups > 1 ? d.n_groups : 1; }
+
 // Byte offsets of the scratch buffers inside the workspace.
 struct Layout {
   size_t u;         // bf16 [T][hidden]       RMSNorm output (residual block)
-  size_t hcat;      // bf16 [T][2*latent]     latent vector: hi | lo halves
+  size_t hcat;      // bf16 [T][G][2*latent]  latent vector per group: hi | lo halves
   size_t logits;    // fp32 [T][E]
   size_t idx;       // int32 [T][k]
   size_t w;         // fp32 [T][k]
@@ -42,12 +45,12 @@ struct Layout {
   size_t slot;      // int32 [P]
   size_t act;       // bf16 [P + T*n_shared][inter]
   size_t y;         // bf16 [P + T*n_shared][latent]
-  size_t z;         // bf16 [T][latent]
+  size_t z;         // bf16 [T][G*latent]
   // decode path (T <= kDecodeMaxT)
-  size_t d_hhi, d_hlo;   // bf16 [T][latent]
+  size_t d_hhi, d_hlo;   // bf16 [T][G*latent]
   size_t d_logits;       // fp32 [2][T][E]
   size_t d_act;          // bf16 [1 + max_active][T][inter]
-  size_t d_zfix;         // int64 [T][latent] (fixed point)
+  size_t d_zfix;         // int64 [T][G*latent] (fixed point)
   size_t d_n_act, d_list, d_wtab;
   size_t total;
 };
@@ -56,6 +59,7 @@ Layout layout_of(const moe_latent_dims& d, int64_t T) {
   const int64_t P = T * d.top_k;
   const int64_t nch = (P + moe::kRouteChunk - 1) / moe::kRouteChunk;
   const int64_t rows = P + T * d.n_shared;
+  const int64_t GL = (int64_t)groups_of(d) * d.latent;  // latent columns over all groups
   Layout L;
   size_t at = 0;
   auto take = [&](int64_t bytes) {
@@ -64,7 +68,7 @@ Layout layout_of(const moe_latent_dims& d, int64_t T) {
     return o;
   };
   L.u = take(T * d.hidden * 2);
-  L.hcat = take(T * 2 * d.latent * 2);
+  L.hcat = take(T * 2 * GL * 2);
   L.logits = take(T * d.n_experts * 4);
   L.idx = take(P * 4);
   L.w = take(P * 4);
@@ -76,14 +80,14 @@ Layout layout_of(const moe_latent_dims& d, int64_t T) {
   L.slot = take(P * 4);
   L.act = take(rows * d.inter * 2);
   L.y = take(rows * d.latent * 2);
-  L.z = take(T * d.latent * 2);
+  L.z = take(T * GL * 2);
   if (T <= moe::kDecodeMaxT) {
     const int64_t max_act = d.n_experts < T * d.top_k ? d.n_experts : T * d.top_k;
-    L.d_hhi = take(T * d.latent * 2);
-    L.d_hlo = take(T * d.latent * 2);
+    L.d_hhi = take(T * GL * 2);
+    L.d_hlo = take(T * GL * 2);
     L.d_logits = take(2 * T * d.n_experts * 4);
     L.d_act = take((1 + max_act) * T * d.inter * 2);
-    L.d_zfix = take(T * d.latent * 8);
+    L.d_zfix = take(T * GL * 8);
     L.d_n_act = take(4);
     L.d_list = take(max_act * 4);
     L.d_wtab = take((1 + max_act) * T * 4);
@@ -109,6 +113,10 @@ int check_dims(const moe_latent_dims* d) {
                 d->n_experts);
   if (d->n_shared != 0 && d->n_shared != 1)
     return fail(MOE_LATENT_EUNSUPPORTED, "n_shared must be 0 or 1 (got %d)", d->n_shared);
+  if (d->n_groups < 0) return fail(MOE_LATENT_EINVAL, "n_groups must be >= 0 (got %d)", d->n_groups);
+  if (d->n_groups > 1 && d->n_experts % d->n_groups)
+    return fail(MOE_LATENT_EUNSUPPORTED, "n_groups %d must divide n_experts %d", d->n_groups,
+                d->n_experts);
   return 0;
 }
 
@@ -191,6 +199,7 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   uint16_t* y = (uint16_t*)(ws + L.y);
   uint16_t* z = (uint16_t*)(ws + L.z);
 
+  const int G = groups_of(d), epg = E / G;
   const moe::StageMarks sm{o.stage_events, st};
   // S0 (residual block only): pre-norm.
   const uint16_t* a_in = x;
@@ -200,27 +209,33 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
     HIP_TRY(sm.mark(moe::kStageNorm, 1));
     a_in = u;
   }
-  // S1: h = x D^T, stored as bf16 hi | lo.
+  // S1: h = x D^T (every group's D_g), stored per group as bf16 hi | lo.
   moe::DenseEpilogue ep{};
   ep.out = hcat;
-  ep.ldo = 2 * Lat;
+  ep.ldo = 2 * G * Lat;
   ep.lo_off = Lat;
+  ep.group_w = Lat;
   HIP_TRY(sm.mark(moe::kStageDproj, 0));
   const moe_packed_weights* gp = o.grouped_packed;
   const uint16_t* pD = gp ? (const uint16_t*)gp->D : nullptr;
   const uint16_t* pU = gp ? (const uint16_t*)gp->U : nullptr;
   const uint16_t* pR = gp ? (const uint16_t*)gp->R : nullptr;
-  HIP_TRY(moe::launch_gemm_dense(moe::kEpiSplit, a_in, H, pD ? pD : D, H, H, T, Lat, H, ep, st,
-                                 pD != nullptr));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiSplit, a_in, H, pD ? pD : D, H, H, T, G * Lat, H, ep,
+                                 st, pD != nullptr));
   HIP_TRY(sm.mark(moe::kStageDproj, 1));
-  // S2: logits = (hi + lo) R^T + b, as a GEMM over K = 2*latent with R read twice.
-  ep = moe::DenseEpilogue{};
-  ep.out = logits;
-  ep.ldo = E;
-  ep.bias = router->bias;
+  // S2: logits = (hi + lo) R^T + b, as a GEMM over K = 2*latent with R read
+  // twice; one per routing group (its experts read its latent).
   HIP_TRY(sm.mark(moe::kStageRouter, 0));
-  HIP_TRY(moe::launch_gemm_dense(moe::kEpiLogits, hcat, 2 * Lat, pR ? pR : router->w, Lat, Lat, T,
-                                 E, 2 * Lat, ep, st, pR != nullptr));
+  const uint16_t* Rw = pR ? pR : router->w;
+  for (int g = 0; g < G; ++g) {
+    ep = moe::DenseEpilogue{};
+    ep.out = logits + (size_t)g * epg;
+    ep.ldo = E;
+    ep.bias = router->bias ? router->bias + (size_t)g * epg : nullptr;
+    HIP_TRY(moe::launch_gemm_dense(moe::kEpiLogits, hcat + (size_t)g * 2 * Lat, 2 * G * Lat,
+                                   Rw + (size_t)g * epg * Lat, Lat, Lat, T, epg, 2 * Lat, ep, st,
+                                   pR != nullptr));
+  }
   HIP_TRY(sm.mark(moe::kStageRouter, 1));
   // S3: top-k + renormalised softmax weights.
   HIP_TRY(sm.mark(moe::kStageTopk, 0));
@@ -233,7 +248,7 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   HIP_TRY(moe::launch_route_permute(idx, P, E, chunk, off, perm, slot, st));
   HIP_TRY(sm.mark(moe::kStageRoute, 1));
   // S7-S9: grouped expert GEMMs (routed groups, then the shared expert).
-  moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k};
+  moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k, epg, 2 * Lat};
   moe::ExpertsView ex{};
   ex.packed = gp && gp->experts;
   ex.gateup_bits = gu_bits;
@@ -241,14 +256,14 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   if (d.n_shared) ex.shared = to_set(ex.packed ? gp->shared : shared);
   const int max_mtiles = (P + 127) / 128 + (E < P ? E : P) + d.n_shared * ((T + 127) / 128);
   HIP_TRY(sm.mark(moe::kStageGateup, 0));
-  HIP_TRY(moe::launch_expert_gateup(hcat, 2 * Lat, rv, ex, act, I, Lat, max_mtiles, st));
+  HIP_TRY(moe::launch_expert_gateup(hcat, 2 * G * Lat, rv, ex, act, I, Lat, max_mtiles, st));
   HIP_TRY(sm.mark(moe::kStageGateup, 1));
   HIP_TRY(sm.mark(moe::kStageDown, 0));
   HIP_TRY(moe::launch_expert_down(act, rv, ex, y, I, Lat, max_mtiles, st));
   HIP_TRY(sm.mark(moe::kStageDown, 1));
   // S10: weighted combine in fixed order.
   HIP_TRY(sm.mark(moe::kStageCombine, 0));
-  HIP_TRY(moe::launch_combine(y, slot, w, T, k, P, Lat, d.n_shared, z, st));
+  HIP_TRY(moe::launch_combine(y, slot, w, idx, T, k, P, Lat, d.n_shared, G, epg, z, st));
   HIP_TRY(sm.mark(moe::kStageCombine, 1));
   // S11: out = z U^T (+ x for the residual block).
   ep = moe::DenseEpilogue{};
@@ -259,8 +274,8 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
     ep.ldr = H;
   }
   HIP_TRY(sm.mark(moe::kStageUproj, 0));
-  HIP_TRY(moe::launch_gemm_dense(moe::kEpiOut, z, Lat, pU ? pU : U, Lat, Lat, T, H, Lat, ep, st,
-                                 pU != nullptr));
+  HIP_TRY(moe::launch_gemm_dense(moe::kEpiOut, z, G * Lat, pU ? pU : U, G * Lat, G * Lat, T, H,
+                                 G * Lat, ep, st, pU != nullptr));
   HIP_TRY(sm.mark(moe::kStageUproj, 1));
 
   if (dbg) {
@@ -312,6 +327,7 @@ int run_decode(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_
   a.n_experts = d.n_experts;
   a.top_k = d.top_k;
   a.n_shared = d.n_shared;
+  a.n_groups = groups_of(d);
   a.T = T;
   a.hhi = (uint16_t*)(ws + L.d_hhi);
   a.hlo = a.RD ? nullptr : (uint16_t*)(ws + L.d_hlo);
@@ -412,11 +428,11 @@ int moe_router_fold(const moe_latent_dims* dims, const void* D, const void* R, v
   if (!aligned(D, 16) || !aligned(R, 16) || !aligned(dst, 16))
     return fail(MOE_LATENT_EINVAL, "D, R and dst must be 16-byte aligned");
   const size_t nd = (size_t)2 * d.n_experts * d.hidden * 2;
-  if (overlaps(dst, nd, D, (size_t)d.latent * d.hidden * 2) ||
+  if (overlaps(dst, nd, D, (size_t)groups_of(d) * d.latent * d.hidden * 2) ||
       overlaps(dst, nd, R, (size_t)d.n_experts * d.latent * 2))
     return fail(MOE_LATENT_EINVAL, "dst overlaps D or R");
   HIP_TRY(moe::launch_router_fold((const uint16_t*)R, (const uint16_t*)D, d.n_experts, d.latent,
-                                  d.hidden, (uint16_t*)dst, (hipStream_t)stream));
+                                  d.hidden, groups_of(d), (uint16_t*)dst, (hipStream_t)stream));
   return 0;
 }
 
@@ -488,7 +504,7 @@ int forward_impl(const moe_latent_dims* dims, int64_t T, const void* x, const vo
                 MOE_LATENT_DECODE_MAX_T, (long long)T);
   if (T == 0) return 0;  // nothing to do; buffers may be empty (NULL)
   const bool dec_ok = moe::decode_supported(d.hidden, d.latent, d.inter, d.n_experts, d.top_k,
-                                            (int)T);
+                                            groups_of(d), (int)T);
   if (o.path == MOE_LATENT_PATH_DECODE && !dec_ok)
     return fail(MOE_LATENT_EUNSUPPORTED, "the decode path does not take these dims / T");
   const bool use_decode =
@@ -536,9 +552,9 @@ int forward_impl(const moe_latent_dims* dims, int64_t T, const void* x, const vo
     if ((gp->U || gp->R) && d.latent % 64)
       return fail(MOE_LATENT_EUNSUPPORTED, "grouped-packed U and R need latent a multiple of 64 "
                                            "(%d)", d.latent);
-    if (gp->R && d.n_experts % 32)
-      return fail(MOE_LATENT_EUNSUPPORTED, "grouped-packed R needs n_experts a multiple of 32 (%d)",
-                  d.n_experts);
+    if (gp->R && (d.n_experts / groups_of(d)) % 32)
+      return fail(MOE_LATENT_EUNSUPPORTED, "grouped-packed R needs n_experts / n_groups a "
+                                           "multiple of 32 (%d)", d.n_experts / groups_of(d));
   }
   if (const moe_packed_weights* dp = o.decode_packed) {
     if (!dp->experts || (d.n_shared && !dp->shared) || !dp->D || !dp->U || (!dp->R && !dp->RD))

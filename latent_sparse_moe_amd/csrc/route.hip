@@ -285,71 +285,84 @@ hipError_t launch_route_permute(const int32_t* idx, int pairs, int E, const int3
 
 // z[t] = sum_j w[t][j] * y[slot(t, j)] (+ y[pairs + t], the shared expert),
 // summed in the fixed order j = 0..k-1 then shared, fp32, one bf16 rounding.
+// With G routing groups, z[t] has G blocks of latent columns and choice j
+// adds into the block of its expert's group idx[t][j] / experts_per_group
+// (the shared expert into block 0); each block is summed in the same order.
 // A thread owns 8 columns of one token. It reads the token's K slots and
 // weights first, then issues all K + 1 row loads before summing, so that
 // each thread has K + 1 loads in flight rather than one at a time.
 template <int K>
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ y,
                                                  const int32_t* __restrict__ slot,
-                                                 const float* __restrict__ w, int T, int pairs,
-                                                 int latent, int n_shared,
+                                                 const float* __restrict__ w,
+                                                 const int32_t* __restrict__ idx, int T, int pairs,
+                                                 int latent, int n_shared, int G, int epg,
                                                  uint16_t* __restrict__ z) {
   const int cpt = latent / 8;
   const int gid = blockIdx.x * 256 + threadIdx.x;
   const int t = gid / cpt, c8 = gid % cpt;
   if (t >= T) return;
-  int r[K];
+  int r[K], grp[K];
   float wt[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     r[j] = slot[(size_t)t * K + j];
     wt[j] = w[(size_t)t * K + j];
+    grp[j] = G > 1 ? idx[(size_t)t * K + j] / epg : 0;
   }
   uint4 v[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) v[j] = *(const uint4*)(y + (size_t)r[j] * latent + c8 * 8);
   uint4 vs = make_uint4(0u, 0u, 0u, 0u);
   if (n_shared) vs = *(const uint4*)(y + (size_t)(pairs + t) * latent + c8 * 8);
-  float acc[8];
+  for (int g = 0; g < G; ++g) {
+    float acc[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
 #pragma unroll
-  for (int j = 0; j < K; ++j) {
-    const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    for (int j = 0; j < K; ++j) {
+      if (grp[j] != g) continue;
+      const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] = fmaf(wt[j], bf16_bits_to_f32(d[q] & 0xFFFFu), acc[2 * q]);
-      acc[2 * q + 1] = fmaf(wt[j], bf16_bits_to_f32(d[q] >> 16), acc[2 * q + 1]);
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(wt[j], bf16_bits_to_f32(d[q] & 0xFFFFu), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(wt[j], bf16_bits_to_f32(d[q] >> 16), acc[2 * q + 1]);
+      }
     }
-  }
-  if (n_shared) {
-    const uint32_t d[4] = {vs.x, vs.y, vs.z, vs.w};
+    if (n_shared && g == 0) {
+      const uint32_t d[4] = {vs.x, vs.y, vs.z, vs.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += bf16_bits_to_f32(d[q] & 0xFFFFu);
-      acc[2 * q + 1] += bf16_bits_to_f32(d[q] >> 16);
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_bits_to_f32(d[q] & 0xFFFFu);
+        acc[2 * q + 1] += bf16_bits_to_f32(d[q] >> 16);
+      }
     }
+    *(uint4*)(z + ((size_t)t * G + g) * latent + c8 * 8) =
+        make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
   }
-  *(uint4*)(z + (size_t)t * latent + c8 * 8) =
-      make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
 }
 
 template <int K>
 static void launch_combine_k(dim3 grid, hipStream_t stream, const uint16_t* y, const int32_t* slot,
-                             const float* w, int T, int pairs, int latent, int n_shared,
-                             uint16_t* z) {
-  hipLaunchKernelGGL(k_combine<K>, grid, dim3(256), 0, stream, y, slot, w, T, pairs, latent,
-                     n_shared, z);
+                             const float* w, const int32_t* idx, int T, int pairs, int latent,
+                             int n_shared, int G, int epg, uint16_t* z) {
+  hipLaunchKernelGGL(k_combine<K>, grid, dim3(256), 0, stream, y, slot, w, idx, T, pairs, latent,
+                     n_shared, G, epg, z);
 }
 
-hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w, int T, int k,
-                          int pairs, int latent, int n_shared, uint16_t* z, hipStream_t stream) {
+hipError_t launch_combine(const uint16_t* y, const int32_t* slot, const float* w,
+                          const int32_t* idx, int T, int k, int pairs, int latent, int n_shared,
+                          int n_groups, int experts_per_group, uint16_t* z, hipStream_t stream) {
   const long total = (long)T * (latent / 8);
   const dim3 grid((unsigned)((total + 255) / 256));
+  const int G = n_groups < 1 ? 1 : n_groups;
   switch (k) {
-#define MOE_COMBINE_CASE(KV) \
-    case KV: launch_combine_k<KV>(grid, stream, y, slot, w, T, pairs, latent, n_shared, z); break;
+#define MOE_COMBINE_CASE(KV)                                                                  \
+    case KV:                                                                                  \
+      launch_combine_k<KV>(grid, stream, y, slot, w, idx, T, pairs, latent, n_shared, G,     \
+                           experts_per_group, z);                                             \
+      break;
     MOE_COMBINE_CASE(1) MOE_COMBINE_CASE(2) MOE_COMBINE_CASE(3) MOE_COMBINE_CASE(4)
     MOE_COMBINE_CASE(5) MOE_COMBINE_CASE(6) MOE_COMBINE_CASE(7) MOE_COMBINE_CASE(8)
     MOE_COMBINE_CASE(9) MOE_COMBINE_CASE(10) MOE_COMBINE_CASE(11) MOE_COMBINE_CASE(12)

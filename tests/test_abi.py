@@ -89,6 +89,8 @@ def _call(lib, dims, T=4, x=A, D=2 * A, U=3 * A, router=True, experts=True, shar
     (dict(top_k=11, n_experts=10), lsm.EUNSUPPORTED),
     (dict(n_experts=2048), lsm.EUNSUPPORTED),
     (dict(n_shared=2), lsm.EUNSUPPORTED),
+    (dict(n_groups=-1), lsm.EINVAL),
+    (dict(n_groups=3), lsm.EUNSUPPORTED),      # does not divide 512 experts
 ])
 def test_bad_dims(lib, kw, code):
     rc, msg = _call(lib, _dims(**kw))
@@ -368,3 +370,12 @@ def test_noalloc_rejects_oversized_calls_before_any_hip_call(lib):
     for lat in (1792, 1280):
         assert lib.moe_latent_workspace_bytes(ctypes.byref(_dims(latent=lat)), 8) \
             <= lsm.NOALLOC_MAX_BYTES
+
+
+def test_grouped_workspace_grows_with_groups(lib):
+    """Routing groups: the latent vector and the combined output hold every
+    group's columns (G * latent)."""
+    one = lib.moe_latent_workspace_bytes(ctypes.byref(_dims()), 300)
+    eight = lib.moe_latent_workspace_bytes(ctypes.byref(_dims(n_groups=8)), 300)
+    assert eight >= one + 300 * 7 * 1792 * (4 + 2)
+    assert lib.moe_latent_workspace_bytes(ctypes.byref(_dims(n_groups=1)), 300) == one

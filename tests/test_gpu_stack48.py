@@ -9,8 +9,13 @@ memory hold one block. For every block l:
   routing exact (near ties excluded) and every output row at the layer bar;
 * the GPU's own chain (its RMSNorm, MoE and residual add): block l applied
   to the GPU chain's x_l, against the oracle's block on that same x_l:
-  routing and every row of the block's MoE part (x_{l+1} - x_l) at the
-  layer bar, near ties excluded.
+  every row of the block's MoE part (x_{l+1} - x_l) at the layer bar, and
+  the expert sets. Here the two sides normalise x_l themselves (the GPU in
+  fp32, the oracle in float64) before rounding u_l to bf16, so a few
+  elements of u_l can differ by one bf16 ulp, which moves logits by about
+  1e-4: tokens whose k-th and (k+1)-th logits are within 1e-3 are left out
+  of this half, and the gate weights are compared exactly only in the
+  first half (identical inputs).
 
 The two chains themselves are not compared at the bar: they drift apart
 (bf16 roundings of the residual stream differ in the last bit, and a
@@ -55,8 +60,9 @@ def test_stack145_all_48_blocks_decode_path():
         say(f"[case] stack145 block {l}: GPU chain block, decode path, residual")
         g = run_gpu(dl, cur, path=lsm.PATH_DECODE, residual=True)
         yc, rc = oracle.block_forward(host, cur, 1e-6)
-        check_routing(rc, g, d.top_k, d.n_experts)
-        ok = rc.gap >= 1e-4
+        ok = rc.gap >= 1e-3
+        for tt in np.nonzero(ok)[0]:
+            assert set(g["topk_idx"][tt].tolist()) == set(rc.idx[tt].tolist()), (l, tt)
         excluded += int((~ok).sum())
         # the block's output is a bf16 tensor (the residual stream between
         # blocks) on both sides: the oracle's block output is rounded as its
@@ -73,5 +79,5 @@ def test_stack145_all_48_blocks_decode_path():
     xv0 = oracle.bf16_value(x0)
     drift = rel_l2(oracle.bf16_value(cur) - xv0, oracle.bf16_value(xo) - xv0)
     say(f"[ok] 48 blocks: worst MoE rel_l2 on the oracle's inputs {worst_moe:.3e}; worst row of "
-        f"the GPU chain's blocks {worst_chain:.3e} ({excluded} near-tie token-blocks left out); "
+        f"the GPU chain's blocks {worst_chain:.3e} ({excluded} token-blocks within 1e-3 left out); "
         f"drift of the two chains after 48 blocks {drift:.3e}")
