@@ -14,7 +14,9 @@ Secondary objects:
 bias, in tokens/s and matrix-core utilisation; ``prefill120``: the
 120B-shaped layer (latent 1280) on a 4096-token prefill; ``mixed_record``:
 the same layer with the mixed 3/4-bit expert record (3-bit E1M1 gate/up,
-4-bit down), at decode T = 4 and per stage at the 16K prefill; ``stack``:
+4-bit down), at decode T = 4 and per stage at the 16K prefill; ``grouped``:
+the layer with 8 routing groups, each with its own (D_g, U_g), at decode
+T = 4 and a 4096-token prefill; ``stack``:
 48 residual blocks of 145B shapes, all resident, one decode step at T = 8
 (bytes, GB/s and fraction of the HBM peak).
 
@@ -107,12 +109,15 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="oracle time per CPU measurement (all cores; half of it at one thread)")
-    p.add_argument("--only", choices=["decode", "prefill", "prefill120", "copy", "stack", "mixed"],
+    p.add_argument("--only", choices=["decode", "prefill", "prefill120", "copy", "stack", "mixed",
+                                      "grouped"],
                    default=None, help="run one workload and print its object (profiling)")
     p.add_argument("--no-mixed", action="store_true",
                    help="skip the mixed 3/4-bit expert record")
     p.add_argument("--no-family", action="store_true",
                    help="skip the decode shape family (T = 1, 2, 3, 5, 8), e.g. under a profiler")
+    p.add_argument("--no-grouped", action="store_true",
+                   help="skip the routing-groups layer (8 D/U pairs)")
     p.add_argument("--no-stack", action="store_true",
                    help="skip the 48-block stack (its 48 layers take about 2 minutes to generate)")
     p.add_argument("--stack-steps", type=int, default=20)
@@ -569,6 +574,92 @@ def bench_mixed(args, torch, lsm, synth, dev):
     return res
 
 
+def bench_grouped(args, torch, lsm, synth, dev):
+    """Routing groups of D/U: the 145B-shaped layer with 8 groups of 64
+    experts, each group with its own (D_g, U_g). Decode T = 4 over rotating
+    decode-packed copies (folded router), timed as the headline pass; and a
+    4096-token prefill on the grouped path with grouped-packed weights."""
+    cfg = synth.CONFIGS["grouped145"]
+    d, T, G = cfg.dims, cfg.T, cfg.dims.n_groups
+    t0 = time.time()
+    host = synth.make_layer(d, cfg.seed, cfg.bias, cfg.zipf_s)
+    log(f"[grouped] generated layer in {time.time() - t0:.1f}s")
+    plain = lsm.DeviceLayer.from_host(host, dev)
+    del host
+    dec = lsm.DeviceLayer(**{**plain.__dict__}).pack(grouped=False).drop_plain()
+    copies = max(2, args.copies // 2)   # each copy is ~1.3 GB: 4 copies pass the Infinity Cache
+    layers = [dec] + [clone_layer(lsm, dec) for _ in range(copies - 1)]
+    xs = [torch.from_numpy(synth.make_x(T, d.hidden, cfg.seed + i).view("int16"))
+          .view(torch.bfloat16).to(dev) for i in range(copies)]
+    outs = [torch.empty_like(x) for x in xs]
+    ws = lsm.alloc_workspace(d, T, dev)
+    n_touched = []
+    for i in range(copies):
+        dbg = lsm.RouteDebug.alloc(d, T, dev)
+        lsm.forward(xs[i], layers[i], out=outs[i], workspace=ws, debug=dbg)
+        torch.cuda.synchronize()
+        n_touched.append(int((dbg.counts > 0).sum().item()))
+    rec = rec_bytes(d.latent, d.inter, d.gateup_bits)
+    dense = (2 * G * d.latent * d.hidden * 2 + 2 * d.n_experts * d.hidden * 2
+             + 2 * T * d.hidden * 2)   # D_g and U_g of every group, the folded router (hi + lo)
+    layer_bytes = sum((n + d.n_shared) * (rec + 12) + dense for n in n_touched) / copies
+
+    def step(i):
+        c = i % copies
+        lsm.forward(xs[c], layers[c], out=outs[c], workspace=ws)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(args.steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    log(f"[grouped] decode T={T}: {us:.1f} us/step, {layer_bytes / 1e6:.1f} MB/step")
+    res = {"config": {"workload": "grouped145", "groups": G, "experts_per_group": d.n_experts // G,
+                      "hidden": d.hidden, "latent": d.latent, "experts": d.n_experts,
+                      "inter": d.inter, "top_k": d.top_k, "shared": d.n_shared},
+           "decode": {"T": T, "us_per_step": round(us, 2), "tok_s": round(T / (us * 1e-6), 1),
+                      "layer_bytes_per_step": layer_bytes,
+                      "layer_GBps": round(layer_bytes / (us * 1e-6) / 1e9, 1),
+                      "frac_of_hbm_peak": round(layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "experts_touched_per_copy": n_touched, "copies": copies}}
+    del layers, dec, xs, outs, ws
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        Tp = 4096
+        pre = plain.pack(decode=False)
+        x = torch.from_numpy(synth.make_x(Tp, d.hidden, cfg.seed).view("int16")).view(
+            torch.bfloat16).to(dev)
+        out = torch.empty_like(x)
+        ws = lsm.alloc_workspace(d, Tp, dev)
+        rows = Tp * d.top_k + Tp * d.n_shared
+        flop = (2.0 * Tp * d.hidden * G * d.latent + 2.0 * Tp * d.latent * d.n_experts
+                + 2.0 * rows * d.latent * 3 * d.inter + 2.0 * Tp * G * d.latent * d.hidden)
+
+        def pstep():
+            lsm.forward(x, pre, out=out, workspace=ws, path=lsm.PATH_GROUPED)
+        pstep()
+        torch.cuda.synchronize()
+        for _ in range(args.prefill_warmup):
+            pstep()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.prefill_steps):
+            pstep()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.prefill_steps
+        log(f"[grouped] prefill T={Tp}: {ms:.3f} ms/call")
+        res["prefill"] = {"T": Tp, "ms_per_step": round(ms, 4), "tok_s": round(Tp / (ms * 1e-3), 1),
+                          "algorithmic_tflop_per_step": flop / 1e12,
+                          "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                          "frac_of_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    return res
+
+
 def bench_stack(args, torch, lsm, synth, dev):
     """48 residual blocks (RMSNorm + latent MoE) of 145B shapes, all resident
     (~48 GB of decode-packed weights, far beyond the Infinity Cache), T = 8
@@ -764,6 +855,9 @@ def main():
     if args.only == "mixed":
         print(json.dumps(bench_mixed(args, torch, lsm, synth, dev)), flush=True)
         return
+    if args.only == "grouped":
+        print(json.dumps(bench_grouped(args, torch, lsm, synth, dev)), flush=True)
+        return
     dec = bench_decode(args, torch, lsm, synth, dev)
     if args.only == "decode":
         print(json.dumps(dec), flush=True)
@@ -788,6 +882,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_mixed:
         line["mixed_record"] = bench_mixed(args, torch, lsm, synth, dev)
+        torch.cuda.empty_cache()
+    if not args.no_grouped:
+        line["grouped"] = bench_grouped(args, torch, lsm, synth, dev)
         torch.cuda.empty_cache()
     if not args.no_stack:
         line["stack"] = bench_stack(args, torch, lsm, synth, dev)
