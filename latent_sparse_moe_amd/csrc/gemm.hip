@@ -577,8 +577,9 @@ hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int coun
 // expert's rows is usually partial; gate/up runs it with 1, 2 or 4 blocks
 // of matrix-core work (at the 16K-token routing this cuts the padded rows
 // from 15% to 4%). Each count has its own copy of the tile body, so nothing
-// stays live across the dispatch. Down keeps one copy: with more, the
-// register allocator spills inside its K loop, which costs more than the
+// stays live across the dispatch. Down keeps one copy (four blocks): its
+// tile body already spills a few registers per lane in the packed layout,
+// and more copies made the K loop spill more, which cost more than the
 // padding.
 __device__ __forceinline__ int row_blocks(const TileWork& tw) {
   return min(4, (tw.rend - tw.rbeg + 31) / 32);
@@ -598,13 +599,10 @@ __device__ __forceinline__ void gateup_tile(const uint16_t* __restrict__ hcat, i
   const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
   const int P = rv.pairs;
   ALoader<BK> al;
-  // the expert's routing group's latent (the shared expert: group 0)
-  const uint16_t* hgrp = hcat + (size_t)(tw.group < rv.n_experts ? tw.group / rv.experts_per_group
-                                                                  : 0) * rv.group_stride;
   al.init([&](int r) {
     const int row = min(tw.rbeg + r, tw.rend - 1);
     const int tok = row < P ? rv.perm[row] / rv.top_k : row - P;
-    return hgrp + (size_t)tok * ldh;
+    return hcat + (size_t)tok * ldh;
   });
   Fp4B<BK, PK, BITS> bl;
 #pragma unroll
@@ -650,6 +648,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (!tile_work(rv, tile / nt, &tw)) return;
   const int n0 = (tile % nt) * (kBN / 2);
   const int nb = row_blocks(tw);
+  // the latent of the expert's routing group (the shared expert: group 0);
+  // added here, ahead of the row-block dispatch, it leaves the tile bodies'
+  // register allocation as it is without groups (computed inside them it
+  // made the K loop spill)
+  hcat += (size_t)(tw.group < rv.n_experts ? tw.group / rv.experts_per_group : 0) * rv.group_stride;
   if (nb == 1) gateup_tile<BK, PK, BITS, 1>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
   else if (nb == 2) gateup_tile<BK, PK, BITS, 2>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
   else gateup_tile<BK, PK, BITS, 4>(hcat, ldh, rv, ex, act, inter, latent, tw, n0, pipe);
