@@ -127,6 +127,32 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
+// Direct-to-LDS DMA of 16 or 4 bytes per lane (lane L's bytes land at
+// lds_base + L * size; lds_base wave-uniform). In asm, so the compiler does
+// not see the LDS write: where it cannot tell LDS stages apart it would
+// otherwise wait for every DMA in flight before each LDS read. Callers
+// order these loads themselves, with vmcnt waits and barriers. M0 is
+// restored afterwards.
+__device__ __forceinline__ void dma_lds16(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+__device__ __forceinline__ void dma_lds4(const void* g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads still in
 // flight are not waited for (a full __syncthreads() would wait for them).
 __device__ __forceinline__ void lds_barrier() {

@@ -110,6 +110,13 @@ struct ALoader {
                                        (__attribute__((address_space(3))) void*)(tile + wbase + v * kThreads * 8),
                                        16, 0, 0);
   }
+  // the same loads, unseen by the compiler (see dma_lds16)
+  __device__ __forceinline__ void issue_asm(int kt, uint16_t* tile) const {
+    const uint32_t base = lds_addr(tile) + (uint32_t)wbase * 2;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      dma_lds16(src[v] + kt * BK, __builtin_amdgcn_readfirstlane(base + v * kThreads * 16));
+  }
 };
 
 // Workgroup barrier after this wave's own direct-to-LDS loads are waited
@@ -443,31 +450,22 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
 
 // ------------------------------------------------------------------ grouped
 
-// Index of the group whose tile range holds global m-tile `mt`:
-// the largest g with tile_off[g] <= mt (tile_off has ngroups + 1 entries).
-__device__ __forceinline__ int find_group(const int* tile_off, int ngroups, int mt) {
-  int lo = 0, hi = ngroups;  // invariant: tile_off[lo] <= mt < tile_off[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_off[mid] <= mt) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 struct TileWork {
   int group;   // expert index; n_experts = the shared expert
   int rbeg;    // first permuted row of this tile
   int rend;    // end of the group's rows
 };
 
+// m-tile mt of the routing's tile list, which has tile_off[groups] entries.
+// The entry is loaded alongside the count (one round trip): grids never
+// exceed the list's capacity, and entries past the count are not used.
 __device__ __forceinline__ bool tile_work(const RouteView& rv, int mt, TileWork* w) {
-  const int ngroups = rv.n_experts + rv.n_shared;
-  const int total = rv.tile_off[ngroups];
+  const int4 t = rv.ttab[mt];
+  const int total = rv.tile_off[rv.n_experts + rv.n_shared];
   if (mt >= total) return false;
-  const int g = find_group(rv.tile_off, ngroups, mt);
-  w->group = g;
-  w->rbeg = rv.off[g] + (mt - rv.tile_off[g]) * kBM;
-  w->rend = rv.off[g + 1];
+  w->group = t.x;
+  w->rbeg = t.y;
+  w->rend = t.z;
   return true;
 }
 
@@ -713,6 +711,406 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   else down_tile<BK, PK, 4>(act, rv, ex, y, inter, latent, tw, n0, pipe);
 }
 
+// ------------------------------------------------------------------ grouped, persistent
+
+// The expert GEMMs for K of at least two steps run persistent: two
+// workgroups per CU, each walking its share of the tile list (the list is
+// cut into eight runs of about equal cost, one per XCD, computed with the
+// routing; a workgroup takes every 64th tile of its XCD's run, so the
+// n-tiles of an m-tile and the m-tiles of an expert run side by side on one
+// XCD and share its L2). Measured on the 128-row kernels with every load and
+// the dequantisation taken out, a tile's set-up and epilogue cost as much as
+// a third of the time (down, ten K steps per tile, ran at 40 % of the
+// matrix cores' rate even so). Here the loads run on across tiles: the last
+// two K steps of a tile load the first two of the workgroup's next tile,
+// and that tile's rows and weight pointers are set up before the epilogue.
+// For that the stages are indexed at run time, so both operands go through
+// LDS: three stages, each the A tile (as in the kernels above) and each
+// wave's weight codes and scales of the step (direct-to-LDS DMA from the
+// lane's own addresses; per sub-tile 64 lanes x 16 bytes of e2m1 codes, or
+// three planes of 64 dwords of the 3-bit chunks, and the dword holding each
+// lane's two scale bytes). A wave reads its step's codes and scales from
+// LDS at the start of the step and dequantises from registers as before.
+// Every step issues the same loads (after the last tile the last step is
+// loaded again into a stage nobody reads), so the waits are exact counts.
+
+constexpr int kPStages = 3;
+
+template <bool PK, int BITS>
+struct PWeights {
+  using FB = Fp4B<64, PK, BITS>;
+  using Set = typename FB::Set;
+  static constexpr int kCodeBytes = BITS == 4 ? 1024 : 768;  // per sub-tile and step
+  static constexpr int kSubBytes = kCodeBytes + 256;
+  static constexpr int kWaveBytes = 2 * kSubBytes;
+  static constexpr int kLoads = BITS == 4 ? 4 : 8;  // DMA instructions per step
+  const uint8_t* cp[2];  // this lane's codes of sub-tile j at step 0
+  const uint8_t* sp[2];  // the aligned dword holding its scale bytes at step 0
+  int shift[2];          // where in that dword they start (bits)
+
+  __device__ __forceinline__ void set(int j, const uint8_t* c, const uint8_t* s) {
+    cp[j] = c;
+    sp[j] = (const uint8_t*)((uintptr_t)s & ~(uintptr_t)3);
+    shift[j] = (int)((uintptr_t)s & 3) * 8;
+  }
+  // step k's codes and scales into this wave's region of a stage
+  __device__ __forceinline__ void issue(int k, uint8_t* wreg) const {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(wreg));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t d = base + j * kSubBytes;
+      if (BITS == 4) {
+        dma_lds16(cp[j] + (size_t)k * FB::kCodeStep, d);
+      } else {
+#pragma unroll
+        for (int w = 0; w < 3; ++w) dma_lds4(cp[j] + (size_t)k * FB::kCodeStep + 4 * w, d + 256 * w);
+      }
+      dma_lds4(sp[j] + (size_t)k * FB::kScaleStep, d + kCodeBytes);
+    }
+  }
+  __device__ static __forceinline__ bf16x8 frag(const Set& st, int j, int ks) {
+    const FB f{};
+    return f.frag(st, j, ks);
+  }
+  // this lane's codes and scale bytes of the step, from the wave's region
+  // (shift: that of the tile the step belongs to)
+  __device__ static __forceinline__ void read(const uint8_t* wreg, const int (&shift)[2], Set& st) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* d = wreg + j * kSubBytes;
+      if (BITS == 4) {
+        const uint4 v = *(const uint4*)(d + lane * 16);
+        st.c[j][0] = v.x; st.c[j][1] = v.y; st.c[j][2] = v.z; st.c[j][3] = v.w;
+      } else {
+#pragma unroll
+        for (int w = 0; w < 3; ++w) st.c[j][w] = *(const uint32_t*)(d + 256 * w + lane * 4);
+      }
+      st.s[j] = *(const uint32_t*)(d + kCodeBytes + lane * 4) >> shift[j];
+    }
+  }
+};
+
+// Where the loads for two steps ahead come from: the tile being run, then
+// (from its second-last step on) the workgroup's next tile.
+template <class W>
+struct PIssue {
+  ALoader<64> a;
+  W b;
+  int k;  // next step to load
+};
+
+template <bool PK, int BITS>
+struct PGateUp {
+  using W = PWeights<PK, BITS>;
+  static constexpr int kTileN = kBN / 2;  // SwiGLU columns per tile
+  static constexpr int kSplit = 0;
+  const uint16_t* hcat;
+  int ldh;
+  RouteView rv;
+  ExpertsView ex;
+  uint16_t* act;
+  int inter, latent;
+
+  __device__ __forceinline__ int n_tiles() const { return (inter + kTileN - 1) / kTileN; }
+  __device__ __forceinline__ int k_steps() const { return latent / 64; }
+  __device__ __forceinline__ void setup(const TileWork& tw, int n0, ALoader<64>& al, W& bl) const {
+    const int wave = threadIdx.x >> 6, P = rv.pairs;
+    // the latent of the expert's routing group (the shared expert: group 0)
+    const uint16_t* h =
+        hcat + (size_t)(tw.group < rv.n_experts ? tw.group / rv.experts_per_group : 0) * rv.group_stride;
+    al.init([&](int r) {
+      const int row = min(tw.rbeg + r, tw.rend - 1);
+      const int tok = row < P ? rv.perm[row] / rv.top_k : row - P;
+      return h + (size_t)tok * ldh;
+    });
+    int le;
+    const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t *c, *s;
+      fp4_lane_ptrs<64, PK, BITS>(j ? set.up : set.gate, le, n0 + wave * 32, inter, latent, &c, &s);
+      bl.set(j, c, s);
+    }
+  }
+  template <int NI>
+  __device__ __forceinline__ void epilogue(const TileWork& tw, int n0, const f32x16 (&acc)[NI][2]) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int le;
+    const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
+    const float gsg = set.gate.gscale[le], gsu = set.up.gscale[le];
+    const int nbase = n0 + wave * 32;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = tw.rbeg + i * 32 + (lane & 31);
+      if (row >= tw.rend) continue;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int nc = nbase + acc_col(q, lane);
+        if (nc >= inter) continue;  // inter is a multiple of 32: all eight or none
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          a[e] = silu_fast(gsg * acc[i][0][8 * q + e]) * (gsu * acc[i][1][8 * q + e]);
+        *(uint4*)(act + (size_t)row * inter + nc) = pack_bf16x8(a);
+      }
+    }
+  }
+};
+
+template <bool PK>
+struct PDown {
+  using W = PWeights<PK, 4>;
+  static constexpr int kTileN = kBN;
+  static constexpr int kSplit = 1;
+  const uint16_t* act;
+  RouteView rv;
+  ExpertsView ex;
+  uint16_t* y;
+  int inter, latent;
+
+  __device__ __forceinline__ int n_tiles() const { return (latent + kTileN - 1) / kTileN; }
+  __device__ __forceinline__ int k_steps() const { return inter / 64; }
+  __device__ __forceinline__ void setup(const TileWork& tw, int n0, ALoader<64>& al, W& bl) const {
+    const int wave = threadIdx.x >> 6;
+    al.init([&](int r) { return act + (size_t)min(tw.rbeg + r, tw.rend - 1) * inter; });
+    int le;
+    const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t *c, *s;
+      fp4_lane_ptrs<64, PK>(set.down, le, n0 + wave * 64 + j * 32, latent, inter, &c, &s);
+      bl.set(j, c, s);
+    }
+  }
+  template <int NI>
+  __device__ __forceinline__ void epilogue(const TileWork& tw, int n0, const f32x16 (&acc)[NI][2]) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int le;
+    const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
+    const float gsd = set.down.gscale[le];
+    const int nbase = n0 + wave * 64;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = tw.rbeg + i * 32 + (lane & 31);
+      if (row >= tw.rend) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int nc = nbase + j * 32 + acc_col(q, lane);
+          if (nc >= latent) continue;  // latent is a multiple of 32: all eight or none
+          *(uint4*)(y + (size_t)row * latent + nc) = pack_bf16x8(acc[i][j], q, gsd);
+        }
+    }
+  }
+};
+
+// Advances the load stream by one step: past the tile's last step it
+// continues with the next tile, or (after the last tile) repeats the last
+// step into a stage nobody reads. Written without branches: a join in the
+// control flow makes the compiler forget which LDS stages the DMA in
+// flight writes, and it then waits for all of it before the next LDS read.
+template <class W>
+__device__ __forceinline__ void padvance(PIssue<W>& is, int KT, bool has_next, const ALoader<64>& aln,
+                                         const W& bln) {
+  const bool wrap = ++is.k == KT;
+  const bool sw = wrap && has_next;
+  is.k = wrap ? (has_next ? 0 : KT - 1) : is.k;
+#pragma unroll
+  for (int v = 0; v < ALoader<64>::V; ++v) is.a.src[v] = sw ? aln.src[v] : is.a.src[v];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    is.b.cp[j] = sw ? bln.cp[j] : is.b.cp[j];
+    is.b.sp[j] = sw ? bln.sp[j] : is.b.sp[j];
+  }
+}
+
+// Pointers to the three stages, each its own LDS array: with a stage
+// index known at compile time the compiler sees that the fragment reads of
+// one stage do not touch the stages the DMA is filling, and adds no wait
+// for those loads (with one array indexed at run time it waits for all of
+// them before every LDS read).
+struct PStages {
+  uint16_t* a[kPStages];  // A tiles
+  uint8_t* b[kPStages];   // each wave's weights
+};
+
+// One K step of a tile on stage S (see pkernel).
+template <int S, int NI, class W>
+__device__ __forceinline__ void pstep(int KT, bool has_next, PIssue<W>& is, const ALoader<64>& aln,
+                                      const W& bln, const PStages& ps, const int (&shift)[2],
+                                      const int (&frag)[4], f32x16 (&acc)[NI][2]) {
+  constexpr int S2 = (S + 2) % kPStages;
+  const int wave = threadIdx.x >> 6;
+  // the loads two steps ahead, into the stage every wave finished with at
+  // the last barrier
+  is.a.issue_asm(is.k, ps.a[S2]);
+  is.b.issue(is.k, ps.b[S2] + wave * W::kWaveBytes);
+  padvance(is, KT, has_next, aln, bln);
+  typename W::Set bs;
+  W::read(ps.b[S] + wave * W::kWaveBytes, shift, bs);
+  const uint16_t* ca = ps.a[S];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8 a[NI], b[2];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) a[i] = *(const bf16x8*)(ca + i * 32 * 64 + frag[ks]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = W::frag(bs, j, ks);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
+  }
+  // the next step's loads complete in this wave (those two ahead may be in
+  // flight), then in every wave
+  wait_vmcnt<ALoader<64>::V + W::kLoads>();
+  dma_barrier();
+}
+
+// A tile's KT steps with its first step on stage P.
+template <int P, int NI, class W>
+__device__ __forceinline__ void psteps(int KT, bool has_next, PIssue<W>& is, const ALoader<64>& aln,
+                                       const W& bln, const PStages& ps, const int (&shift)[2],
+                                       const int (&frag)[4], f32x16 (&acc)[NI][2]) {
+  constexpr int P1 = (P + 1) % kPStages, P2 = (P + 2) % kPStages;
+  int kt = 0;
+  for (; kt + 3 <= KT; kt += 3) {
+    pstep<P, NI>(KT, has_next, is, aln, bln, ps, shift, frag, acc);
+    pstep<P1, NI>(KT, has_next, is, aln, bln, ps, shift, frag, acc);
+    pstep<P2, NI>(KT, has_next, is, aln, bln, ps, shift, frag, acc);
+  }
+  if (kt < KT) pstep<P, NI>(KT, has_next, is, aln, bln, ps, shift, frag, acc);
+  if (kt + 1 < KT) pstep<P1, NI>(KT, has_next, is, aln, bln, ps, shift, frag, acc);
+}
+
+// One tile's K steps, starting on stage s (updated to the stage after its
+// last step), then between(), then the epilogue. The loads of its first
+// two steps are in flight or done, the first complete in every wave; shift:
+// where the tile's scale bytes sit in their dwords.
+template <int NI, class Op, class F>
+__device__ __forceinline__ void ptile_run(const Op& op, const TileWork& tw, int n0, const int (&shift)[2],
+                                          bool has_next, PIssue<typename Op::W>& is,
+                                          const ALoader<64>& aln, const typename Op::W& bln,
+                                          const PStages& ps, int& s, const int (&frag)[4], F between) {
+  const int KT = op.k_steps();
+  f32x16 acc[NI][2];
+  zero_acc<NI>(acc);
+  if (s == 0) psteps<0, NI>(KT, has_next, is, aln, bln, ps, shift, frag, acc);
+  else if (s == 1) psteps<1, NI>(KT, has_next, is, aln, bln, ps, shift, frag, acc);
+  else psteps<2, NI>(KT, has_next, is, aln, bln, ps, shift, frag, acc);
+  s = (s + KT) % kPStages;
+  between();
+  op.template epilogue<NI>(tw, n0, acc);
+}
+
+template <class Op>
+__device__ __forceinline__ void pkernel(const Op& op) {
+  using W = typename Op::W;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a0[kBM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a1[kBM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_a2[kBM * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b0[4 * W::kWaveBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b1[4 * W::kWaveBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b2[4 * W::kWaveBytes];
+  const PStages ps{{lds_a0, lds_a1, lds_a2}, {lds_b0, lds_b1, lds_b2}};
+  const int nt = op.n_tiles(), KT = op.k_steps();
+  const int x = blockIdx.x % kXcds, nq = gridDim.x / kXcds;
+  const int* split = op.rv.split + 9 * Op::kSplit;
+  const int hi = split[x + 1];
+  int t = split[x] + blockIdx.x / kXcds;
+  if (t >= hi) return;
+  auto info = [&](int i, TileWork* tw, int* n0) {
+    const int mt = i / nt;
+    const int4 w = op.rv.ttab[mt];
+    *tw = TileWork{w.x, w.y, w.z};
+    *n0 = (i - mt * nt) * Op::kTileN;
+  };
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int frag[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) frag[ks] = swz<64>(lane & 31, (lane >> 5) * 4 + ks) * 8;
+  // this tile and the next one set up, the first two steps' loads issued
+  TileWork cur, nxt;
+  int n0, n1;
+  info(t, &cur, &n0);
+  PIssue<W> is;
+  op.setup(cur, n0, is.a, is.b);
+  int shift[2] = {is.b.shift[0], is.b.shift[1]};
+  bool has_next = t + nq < hi;
+  nxt = cur;
+  n1 = n0;
+  ALoader<64> aln = is.a;
+  W bln = is.b;
+  if (has_next) {
+    info(t + nq, &nxt, &n1);
+    op.setup(nxt, n1, aln, bln);
+  }
+  is.k = 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    is.a.issue_asm(is.k, ps.a[k]);
+    is.b.issue(is.k, ps.b[k] + wave * W::kWaveBytes);
+    padvance(is, KT, has_next, aln, bln);
+  }
+  wait_vmcnt<ALoader<64>::V + W::kLoads>();
+  dma_barrier();
+  int s = 0;
+  for (;;) {
+    // the tile after the next one, set up between this tile's steps and its
+    // epilogue (its row loads then wait for nothing but the next tile's
+    // second step)
+    const bool has2 = has_next && t + 2 * nq < hi;
+    TileWork nxt2;
+    int n2;
+    ALoader<64> an2;  // not live during the tile's steps
+    W bn2;
+    auto between = [&]() {
+      if (has2) {
+        info(t + 2 * nq, &nxt2, &n2);
+        op.setup(nxt2, n2, an2, bn2);
+      } else {
+        nxt2 = nxt;
+        n2 = n1;
+        an2 = aln;
+        bn2 = bln;
+      }
+    };
+    const int nb = row_blocks(cur);
+    if (nb == 1) ptile_run<1>(op, cur, n0, shift, has_next, is, aln, bln, ps, s, frag, between);
+    else if (nb == 2) ptile_run<2>(op, cur, n0, shift, has_next, is, aln, bln, ps, s, frag, between);
+    else ptile_run<4>(op, cur, n0, shift, has_next, is, aln, bln, ps, s, frag, between);
+    if (!has_next) break;
+    t += nq;
+    cur = nxt;
+    n0 = n1;
+    shift[0] = bln.shift[0];
+    shift[1] = bln.shift[1];
+    nxt = nxt2;
+    n1 = n2;
+    aln = an2;
+    bln = bn2;
+    has_next = has2;
+  }
+  // the DMA into LDS has landed before the workgroup ends
+  wait_vmcnt<0>();
+}
+
+template <bool PK, int BITS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_gateup_p(
+    const uint16_t* __restrict__ hcat, int ldh, RouteView rv, ExpertsView ex,
+    uint16_t* __restrict__ act, int inter, int latent) {
+  pkernel(PGateUp<PK, BITS>{hcat, ldh, rv, ex, act, inter, latent});
+}
+
+template <bool PK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_expert_down_p(
+    const uint16_t* __restrict__ act, RouteView rv, ExpertsView ex, uint16_t* __restrict__ y,
+    int inter, int latent) {
+  pkernel(PDown<PK>{act, rv, ex, y, inter, latent});
+}
+
 // ------------------------------------------------------------------ launchers
 
 static inline int pick_bk(int K, int kwrap) { return (K % 64 == 0 && kwrap % 64 == 0) ? 64 : 32; }
@@ -743,11 +1141,42 @@ hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t
   return hipGetLastError();
 }
 
+// Two persistent workgroups per CU, a multiple of 8 in all (every XCD the
+// same number).
+static int persistent_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+      n = 256;
+    cached[dev] = 2 * (n / kXcds) * kXcds;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& rv,
                                 const ExpertsView& ex, uint16_t* act, int inter, int latent,
                                 int max_mtiles, hipStream_t stream) {
-  dim3 grid(max_mtiles * ((inter + kBN / 2 - 1) / (kBN / 2))), block(kThreads);
   if ((ex.packed || ex.gateup_bits == 3) && latent % 64 != 0) return hipErrorInvalidValue;
+  if (latent % 64 == 0 && latent >= 128) {  // persistent: K steps of 64, at least two
+    const dim3 grid(persistent_grid()), block(kThreads);
+#define MOE_LAUNCH_GUP(PKV, BITSV)                                                                 \
+  hipLaunchKernelGGL((k_expert_gateup_p<PKV, BITSV>), grid, block, 0, stream, hcat, ldh, rv, ex,   \
+                     act, inter, latent)
+    if (ex.gateup_bits == 3) {
+      if (ex.packed) MOE_LAUNCH_GUP(true, 3);
+      else MOE_LAUNCH_GUP(false, 3);
+    } else if (ex.packed) {
+      MOE_LAUNCH_GUP(true, 4);
+    } else {
+      MOE_LAUNCH_GUP(false, 4);
+    }
+#undef MOE_LAUNCH_GUP
+    return hipGetLastError();
+  }
+  dim3 grid(max_mtiles * ((inter + kBN / 2 - 1) / (kBN / 2))), block(kThreads);
 #define MOE_LAUNCH_GU(BKV, PKV, BITSV)                                                           \
   hipLaunchKernelGGL((k_expert_gateup<BKV, PKV, BITSV>), grid, block, 0, stream, hcat, ldh, rv, ex, \
                      act, inter, latent)
@@ -768,8 +1197,16 @@ hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& 
 hipError_t launch_expert_down(const uint16_t* act, const RouteView& rv, const ExpertsView& ex,
                               uint16_t* y, int inter, int latent, int max_mtiles,
                               hipStream_t stream) {
-  dim3 grid(max_mtiles * ((latent + kBN - 1) / kBN)), block(kThreads);
   if (ex.packed && inter % 64 != 0) return hipErrorInvalidValue;
+  if (inter % 64 == 0 && inter >= 128) {  // persistent: K steps of 64, at least two
+    const dim3 grid(persistent_grid()), block(kThreads);
+    if (ex.packed)
+      hipLaunchKernelGGL((k_expert_down_p<true>), grid, block, 0, stream, act, rv, ex, y, inter, latent);
+    else
+      hipLaunchKernelGGL((k_expert_down_p<false>), grid, block, 0, stream, act, rv, ex, y, inter, latent);
+    return hipGetLastError();
+  }
+  dim3 grid(max_mtiles * ((latent + kBN - 1) / kBN)), block(kThreads);
   if (ex.packed)
     hipLaunchKernelGGL((k_expert_down<64, true>), grid, block, 0, stream, act, rv, ex, y, inter,
                        latent);

@@ -44,6 +44,11 @@ struct RouteView {
   // token's row (the shared expert: group 0)
   int experts_per_group;
   int group_stride;
+  // the m-tiles listed ({group, first row, end of the group's rows, 0}),
+  // tile_off[n_groups] of them, and each XCD's run of the tile list
+  // (m-tile x n-tile, n fastest): gate/up split[0..8], down split[9..17]
+  const int4* ttab;
+  const int* split;
 };
 
 enum { kEpiSplit = 0, kEpiLogits = 1, kEpiOut = 2 };
@@ -94,7 +99,7 @@ hipError_t launch_route_hist(const int32_t* idx, int pairs, int E, int32_t* chun
                              hipStream_t stream);
 hipError_t launch_route_scan(int32_t* chunk_hist, int n_chunks, int E, int pairs, int T,
                              int n_shared, int32_t* counts, int32_t* off, int32_t* tile_off,
-                             hipStream_t stream);
+                             int4* ttab, int nt_gu, int nt_dn, int32_t* split, hipStream_t stream);
 hipError_t launch_route_permute(const int32_t* idx, int pairs, int E,
                                 const int32_t* chunk_base, const int32_t* off, int32_t* perm,
                                 int32_t* slot, hipStream_t stream);

@@ -30,6 +30,13 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // Routing groups of D/U (dims.n_groups, 0 meaning 1).
 int groups_of(const moe_latent_dims& d) { return d.n_groups > 1 ? d.n_groups : 1; }
 
+// Upper bound on the grouped path's 128-row m-tiles: full tiles of all
+// pairs, one partial tile per expert that has pairs, the shared expert's.
+int64_t max_mtiles(const moe_latent_dims& d, int64_t T) {
+  const int64_t P = T * d.top_k;
+  return (P + 127) / 128 + (d.n_experts < P ? d.n_experts : P) + d.n_shared * ((T + 127) / 128);
+}
+
 // Byte offsets of the scratch buffers inside the workspace.
 struct Layout {
   size_t u;         // bf16 [T][hidden]       RMSNorm output (residual block)
@@ -41,6 +48,8 @@ struct Layout {
   size_t counts;    // int32 [E]
   size_t off;       // int32 [E + 2]
   size_t tile_off;  // int32 [E + 2]
+  size_t ttab;      // int4 [max m-tiles]     the m-tiles listed
+  size_t split;     // int32 [2][9]           each XCD's run of the tile list
   size_t perm;      // int32 [P]
   size_t slot;      // int32 [P]
   size_t act;       // bf16 [P + T*n_shared][inter]
@@ -76,6 +85,8 @@ Layout layout_of(const moe_latent_dims& d, int64_t T) {
   L.counts = take(d.n_experts * 4);
   L.off = take((d.n_experts + 2) * 4);
   L.tile_off = take((d.n_experts + 2) * 4);
+  L.ttab = take(max_mtiles(d, T) * 16);
+  L.split = take(2 * 9 * 4);
   L.perm = take(P * 4);
   L.slot = take(P * 4);
   L.act = take(rows * d.inter * 2);
@@ -193,6 +204,8 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   int32_t* counts = (int32_t*)(ws + L.counts);
   int32_t* off = (int32_t*)(ws + L.off);
   int32_t* tile_off = (int32_t*)(ws + L.tile_off);
+  int4* ttab = (int4*)(ws + L.ttab);
+  int32_t* split = (int32_t*)(ws + L.split);
   int32_t* perm = (int32_t*)(ws + L.perm);
   int32_t* slot = (int32_t*)(ws + L.slot);
   uint16_t* act = (uint16_t*)(ws + L.act);
@@ -244,22 +257,23 @@ int run_grouped(const moe_latent_dims& d, int T, const uint16_t* x, const uint16
   // S4-S6: histogram, prefix sums, stable permutation.
   HIP_TRY(sm.mark(moe::kStageRoute, 0));
   HIP_TRY(moe::launch_route_hist(idx, P, E, chunk, st));
-  HIP_TRY(moe::launch_route_scan(chunk, nch, E, P, T, d.n_shared, counts, off, tile_off, st));
+  HIP_TRY(moe::launch_route_scan(chunk, nch, E, P, T, d.n_shared, counts, off, tile_off, ttab,
+                                 (I + 127) / 128, (Lat + 255) / 256, split, st));
   HIP_TRY(moe::launch_route_permute(idx, P, E, chunk, off, perm, slot, st));
   HIP_TRY(sm.mark(moe::kStageRoute, 1));
   // S7-S9: grouped expert GEMMs (routed groups, then the shared expert).
-  moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k, epg, 2 * Lat};
+  moe::RouteView rv{tile_off, off, perm, E, d.n_shared, P, k, epg, 2 * Lat, ttab, split};
   moe::ExpertsView ex{};
   ex.packed = gp && gp->experts;
   ex.gateup_bits = gu_bits;
   ex.routed = to_set(ex.packed ? gp->experts : experts);
   if (d.n_shared) ex.shared = to_set(ex.packed ? gp->shared : shared);
-  const int max_mtiles = (P + 127) / 128 + (E < P ? E : P) + d.n_shared * ((T + 127) / 128);
+  const int n_mtiles = (int)max_mtiles(d, T);
   HIP_TRY(sm.mark(moe::kStageGateup, 0));
-  HIP_TRY(moe::launch_expert_gateup(hcat, 2 * G * Lat, rv, ex, act, I, Lat, max_mtiles, st));
+  HIP_TRY(moe::launch_expert_gateup(hcat, 2 * G * Lat, rv, ex, act, I, Lat, n_mtiles, st));
   HIP_TRY(sm.mark(moe::kStageGateup, 1));
   HIP_TRY(sm.mark(moe::kStageDown, 0));
-  HIP_TRY(moe::launch_expert_down(act, rv, ex, y, I, Lat, max_mtiles, st));
+  HIP_TRY(moe::launch_expert_down(act, rv, ex, y, I, Lat, n_mtiles, st));
   HIP_TRY(sm.mark(moe::kStageDown, 1));
   // S10: weighted combine in fixed order.
   HIP_TRY(sm.mark(moe::kStageCombine, 0));

@@ -160,12 +160,33 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
 //   adds off[e]). A thread's chunk counts are loaded 32 at a time before
 //   any is used, so the walk over the chunks is not one load round trip per
 //   chunk.
+//   ttab: the m-tiles listed, m-tile i = {group, first row, end of the
+//   group's rows, 0} (experts in order, then the shared expert's).
+//   split[9k .. 9k+8] (k = 0 for gate/up with nt[0] n-tiles per m-tile,
+//   k = 1 for down with nt[1]): the tile list (m-tiles times n-tiles, n
+//   fastest) cut into eight runs of about equal cost, one per XCD (run x =
+//   tiles [split[9k+x], split[9k+x+1])). An m-tile's cost is tile_cost of
+//   its row count, the same for each of its n-tiles.
+__device__ __forceinline__ int tile_cost(int rows) {
+  const int nb = (rows + 31) / 32;  // blocks of 32 rows the tile runs with: 1, 2 or 4
+  return nb <= 1 ? 6 : nb <= 2 ? 7 : 10;
+}
+
+// Cost of the m-tiles of a group of cnt > 0 rows: 10 per full tile, the
+// last one by its rows.
+__device__ __forceinline__ int group_cost(int cnt) {
+  const int n = (cnt + 127) / 128;
+  return 10 * (n - 1) + tile_cost(cnt - 128 * (n - 1));
+}
+
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk_hist,
                                                      int n_chunks, int E, int pairs, int T,
                                                      int n_shared, int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ off,
-                                                     int32_t* __restrict__ tile_off) {
-  __shared__ int totals[2];
+                                                     int32_t* __restrict__ tile_off,
+                                                     int4* __restrict__ ttab, int nt_gu, int nt_dn,
+                                                     int32_t* __restrict__ split) {
+  __shared__ int totals[3];
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
@@ -184,24 +205,87 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ chunk
   const int tiles = (cnt + 127) / 128;
   const int ex_cnt = block_exclusive_scan_1024(cnt, &totals[0]);
   const int ex_tiles = block_exclusive_scan_1024(tiles, &totals[1]);
+  const int ex_cost = block_exclusive_scan_1024(cnt > 0 ? group_cost(cnt) : 0, &totals[2]);
+  // per group (the shared expert last): first row, first m-tile, cost before it
+  __shared__ int g_off[kMaxExperts + 2], g_tile[kMaxExperts + 2], g_cost[kMaxExperts + 2];
+  const int shared_tiles = n_shared * ((T + 127) / 128);
+  const int G = E + n_shared;  // groups
   if (e < E) {
     counts[e] = cnt;
     off[e] = ex_cnt;
     tile_off[e] = ex_tiles;
+    g_off[e] = ex_cnt;
+    g_tile[e] = ex_tiles;
+    g_cost[e] = ex_cost;
   }
   if (e == 0) {
     off[E] = pairs;
     off[E + 1] = pairs + n_shared * T;
     tile_off[E] = totals[1];
-    tile_off[E + 1] = totals[1] + n_shared * ((T + 127) / 128);
+    tile_off[E + 1] = totals[1] + shared_tiles;
+    g_off[E] = pairs;
+    g_off[E + 1] = pairs + n_shared * T;
+    g_tile[E] = totals[1];
+    g_tile[E + 1] = totals[1] + shared_tiles;
+    g_cost[E] = totals[2];
+    g_cost[E + 1] = totals[2] + (n_shared && T > 0 ? group_cost(T) : 0);
+  }
+  __syncthreads();
+  // the group of m-tile i: the largest g with g_tile[g] <= i (LDS search)
+  auto group_of_tile = [&](int i) {
+    int lo = 0, hi = G;  // g_tile[lo] <= i < g_tile[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (g_tile[mid] <= i) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  const int n_mt = g_tile[G];
+  for (int i = threadIdx.x; i < n_mt; i += 1024) {
+    const int g = group_of_tile(i);
+    ttab[i] = make_int4(g, g_off[g] + 128 * (i - g_tile[g]), g_off[g + 1], 0);
+  }
+  // split points: thread 8k + x (x = 1..7) finds the first tile whose cost
+  // prefix reaches x/8 of the total (its m-tile by a search over the groups'
+  // cost prefixes, then within the group)
+  const int64_t C = g_cost[G];
+  if (threadIdx.x < 16) {
+    const int k = threadIdx.x >> 3, x = threadIdx.x & 7;
+    const int64_t q = k ? nt_dn : nt_gu;
+    const int n_tiles = n_mt * (int)q;
+    int res;
+    if (x == 0) {
+      res = 0;
+    } else {
+      const int64_t tau = (x * q * C + 7) / 8;  // in tile-cost units (each m-tile's cost counts q times)
+      if (tau >= q * C) {
+        res = n_tiles;
+      } else {
+        int lo = 0, hi = G;  // q * g_cost[lo] <= tau < q * g_cost[hi]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (q * g_cost[mid] <= tau) lo = mid; else hi = mid;
+        }
+        const int rows = g_off[lo + 1] - g_off[lo], n = (rows + 127) / 128;
+        const int clast = tile_cost(rows - 128 * (n - 1));
+        const int64_t o = tau - q * g_cost[lo];
+        int64_t m = o / (10 * q);
+        if (m > n - 1) m = n - 1;
+        const int64_t r = o - m * 10 * q;
+        const int c = m < n - 1 ? 10 : clast;
+        res = (int)((g_tile[lo] + m) * q + (r + c - 1) / c);
+      }
+    }
+    split[9 * k + x] = res;
+    if (x == 7) split[9 * k + 8] = n_tiles;
   }
 }
 
 hipError_t launch_route_scan(int32_t* chunk_hist, int n_chunks, int E, int pairs, int T,
                              int n_shared, int32_t* counts, int32_t* off, int32_t* tile_off,
-                             hipStream_t stream) {
+                             int4* ttab, int nt_gu, int nt_dn, int32_t* split, hipStream_t stream) {
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, stream, chunk_hist, n_chunks, E, pairs,
-                     T, n_shared, counts, off, tile_off);
+                     T, n_shared, counts, off, tile_off, ttab, nt_gu, nt_dn, split);
   return hipGetLastError();
 }
 
