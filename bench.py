@@ -62,33 +62,39 @@ def rec_bytes(L, I, gateup_bits=4):
 DECODE_STAGE_KERNELS = {"down": ("k_dec_down", "k_dec_combine")}
 
 
-def kernel_bytes(d, T, n_routed, decode=True):
+def kernel_bytes(d, T, n_routed, decode=True, folded=True):
     """Algorithmic HBM bytes of each kernel of one layer call: every weight
     byte it must read once (4-bit codes, or 3-bit E1M1 gate/up codes in the
     mixed record, + E4M3 block scales + fp32 matrix scales for experts, bf16
-    for D / R / U) plus its activation inputs and outputs."""
+    for D / R / U, the folded router W = R D as bf16 hi + lo) plus its
+    activation inputs and outputs. Decode path: front (D and, folded, the
+    logits from x), router (only when not folded), gate/up (routed experts
+    and the shared one, slot 0), down (writes z as 64-bit fixed point),
+    U (reads it)."""
     L, H, E, I, k = d.latent, d.hidden, d.n_experts, d.inter, d.top_k
+    G = getattr(d, "n_groups", 1)
+    GL = G * L
     fp4 = lambda n_, k_, b=4: n_ * k_ * b // 8 + n_ * k_ // 16
     gu = 2 * fp4(I, L, d.gateup_bits) + 8   # gate + up of one expert
     dn = fp4(L, I) + 4               # down of one expert
     sh = d.n_shared
     x = out = T * H * 2
-    h2 = T * L * 2 * 2               # latent as bf16 hi + lo
+    h2 = T * GL * 2 * 2              # latent as bf16 hi + lo
     if decode:
         return {
-            "dproj": L * H * 2 + x + h2,
-            "router": E * L * 2 + E * 4 + h2 + T * E * 4 + sh * (gu + T * I * 2),
-            "gateup": n_routed * (gu + T * I * 2) + T * L * 2 + T * E * 4,
-            "down": (n_routed + sh) * (dn + T * I * 2) + 2 * T * L * 4,
-            "uproj": H * L * 2 + 2 * T * L * 4 + out,
+            "dproj": GL * H * 2 + x + h2 + (2 * E * H * 2 + 2 * T * E * 4 if folded else 0),
+            "router": 0 if folded else E * L * 2 + E * 4 + h2 + T * E * 4,
+            "gateup": (n_routed + sh) * (gu + T * I * 2) + T * GL * 2 + 2 * T * E * 4,
+            "down": (n_routed + sh) * (dn + T * I * 2) + T * GL * 8,
+            "uproj": H * GL * 2 + T * GL * 8 + out,
         }
     rows = T * k + T * sh
     return {
-        "dproj": L * H * 2 + x + h2,
+        "dproj": GL * H * 2 + x + h2,
         "router": E * L * 2 + h2 + T * E * 4,
         "gateup": (n_routed + sh) * gu + rows * (L * 2 + I * 2),
         "down": (n_routed + sh) * dn + rows * (I * 2 + L * 2),
-        "uproj": H * L * 2 + T * L * 2 + out,
+        "uproj": H * GL * 2 + T * GL * 2 + out,
     }
 
 
