@@ -317,6 +317,83 @@ __device__ __forceinline__ void mainloop(ALoader<BK>& al, const BL& bl, int KT, 
   wait_vmcnt<0>();
 }
 
+// The dense GEMMs' loop: A three stages deep in LDS as above, the bf16
+// weights (B) only one step ahead in two register sets (B set kt % 2, A
+// stage kt % 3; unrolled over six steps). Two sets instead of three keep a
+// wave within 256 registers, so two workgroups share a CU (two waves per
+// SIMD) and one wave's waits overlap the other's matrix-core work; with
+// three sets the kernels needed about 284 registers and ran one wave per
+// SIMD. Step kt issues B of kt + 1 and then A of kt + 2, computes, and
+// waits for all but the newest A loads: B of kt + 1 and A of kt + 1 are
+// then complete.
+template <int BK, int SA, int SB, int NI, class BL>
+__device__ __forceinline__ void dense_step(int kt, int KT, ALoader<BK>& al, const BL& bl,
+                                           const Pipe& p, typename BL::Set (&bs)[2],
+                                           const int (&frag)[Geo<BK>::kSub],
+                                           f32x16 (&acc)[NI][2]) {
+  using G = Geo<BK>;
+  constexpr int A2 = (SA + 2) % 3, B1 = (SB + 1) % 2;
+  bl.issue(min(kt + 1, KT - 1), bs[B1]);  // set B1 was used last in step kt - 1
+  __builtin_amdgcn_sched_barrier(0);       // B's loads first, then A's
+  al.issue(min(kt + 2, KT - 1), p.a[A2]);  // stage A2 was read last in step kt - 1
+  __builtin_amdgcn_sched_barrier(0);
+  const uint16_t* ca = p.a[SA];
+#pragma unroll
+  for (int ks = 0; ks < G::kSub; ++ks) {
+    bf16x8 a[NI], b[2];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) a[i] = *(const bf16x8*)(ca + i * 32 * BK + frag[ks]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = bl.frag(bs[SB], j, ks);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(b[j], a[i], acc[i][j]);
+  }
+#pragma unroll
+  for (int m = 0; m < G::kSub * NI * 2; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, BL::kValuPerMfma, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+  }
+  wait_vmcnt<ALoader<BK>::V>();
+  dma_barrier();
+}
+
+template <int BK, int NI, class BL>
+__device__ __forceinline__ void mainloop_dense(ALoader<BK>& al, const BL& bl, int KT, const Pipe& p,
+                                               f32x16 (&acc)[NI][2]) {
+  using G = Geo<BK>;
+  const int lane = threadIdx.x & 63;
+  int frag[G::kSub];
+#pragma unroll
+  for (int ks = 0; ks < G::kSub; ++ks)
+    frag[ks] = swz<BK>(lane & 31, (lane >> 5) * G::kSub + ks) * 8;
+  typename BL::Set bs[2];
+  // prologue: A and B of step 0, A of step 1 in flight
+  bl.issue(0, bs[0]);
+  al.issue(0, p.a[0]);
+  al.issue(min(1, KT - 1), p.a[1]);
+  wait_vmcnt<ALoader<BK>::V>();
+  dma_barrier();
+  int kt = 0;
+  for (; kt + 6 <= KT; kt += 6) {
+    dense_step<BK, 0, 0, NI>(kt, KT, al, bl, p, bs, frag, acc);
+    dense_step<BK, 1, 1, NI>(kt + 1, KT, al, bl, p, bs, frag, acc);
+    dense_step<BK, 2, 0, NI>(kt + 2, KT, al, bl, p, bs, frag, acc);
+    dense_step<BK, 0, 1, NI>(kt + 3, KT, al, bl, p, bs, frag, acc);
+    dense_step<BK, 1, 0, NI>(kt + 4, KT, al, bl, p, bs, frag, acc);
+    dense_step<BK, 2, 1, NI>(kt + 5, KT, al, bl, p, bs, frag, acc);
+  }
+  if (kt < KT) dense_step<BK, 0, 0, NI>(kt, KT, al, bl, p, bs, frag, acc);
+  if (kt + 1 < KT) dense_step<BK, 1, 1, NI>(kt + 1, KT, al, bl, p, bs, frag, acc);
+  if (kt + 2 < KT) dense_step<BK, 2, 0, NI>(kt + 2, KT, al, bl, p, bs, frag, acc);
+  if (kt + 3 < KT) dense_step<BK, 0, 1, NI>(kt + 3, KT, al, bl, p, bs, frag, acc);
+  if (kt + 4 < KT) dense_step<BK, 1, 0, NI>(kt + 4, KT, al, bl, p, bs, frag, acc);
+  // the repeated tail loads into LDS land before the workgroup can end
+  wait_vmcnt<0>();
+}
+
 // The products are computed transposed (weights as the first matrix-core
 // operand): result register r of lane l belongs to matrix-core row
 // m = (r/4)*8 + (l/32)*4 + r%4, i.e. to the weight row loaded by lane m of
@@ -350,11 +427,15 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
 
 // ------------------------------------------------------------------ dense
 
-template <int BK, int EPI, bool PK>
-__global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restrict__ A, int lda,
-                                                         const uint16_t* __restrict__ B, int ldb,
-                                                         int kwrap, int M, int N, int K,
-                                                         DenseEpilogue ep) {
+// TWO: the two-set loop at two waves per SIMD (mainloop_dense), for grids of
+// at least two workgroups per CU; else the three-set loop at one wave per
+// SIMD (about 284 registers), which prefetches the weights a step further
+// and wins when there is only one workgroup per CU anyway (the router: 16K
+// tokens x 512 experts is 256 tiles; 10% faster there).
+template <int BK, int EPI, bool PK, bool TWO>
+__device__ __forceinline__ void dense_tile(const uint16_t* __restrict__ A, int lda,
+                                           const uint16_t* __restrict__ B, int ldb, int kwrap,
+                                           int M, int N, int K, const DenseEpilogue& ep) {
   MOE_GEMM_LDS(BK);
   const int nt = (N + kBN - 1) / kBN;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -376,7 +457,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
   }
   f32x16 acc[4][2];
   zero_acc<4>(acc);
-  mainloop<BK, 4>(al, bl, K / BK, pipe, acc);
+  if (TWO) mainloop_dense<BK, 4>(al, bl, K / BK, pipe, acc);
+  else mainloop<BK, 4>(al, bl, K / BK, pipe, acc);
 
   const int nbase = n0 + wave * 64;
   // 8-wide stores need the row starts 16-byte aligned
@@ -446,6 +528,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restr
         }
       }
   }
+}
+
+template <int BK, int EPI, bool PK>
+__global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restrict__ A, int lda,
+                                                         const uint16_t* __restrict__ B, int ldb,
+                                                         int kwrap, int M, int N, int K,
+                                                         DenseEpilogue ep) {
+  dense_tile<BK, EPI, PK, false>(A, lda, B, ldb, kwrap, M, N, K, ep);
+}
+
+template <int BK, int EPI, bool PK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_dense2(
+    const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B, int ldb, int kwrap,
+    int M, int N, int K, DenseEpilogue ep) {
+  dense_tile<BK, EPI, PK, true>(A, lda, B, ldb, kwrap, M, N, K, ep);
 }
 
 // ------------------------------------------------------------------ grouped
@@ -1115,15 +1212,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 static inline int pick_bk(int K, int kwrap) { return (K % 64 == 0 && kwrap % 64 == 0) ? 64 : 32; }
 
+// Two persistent workgroups per CU, a multiple of 8 in all (every XCD the
+// same number).
+static int persistent_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
+      n = 256;
+    cached[dev] = 2 * (n / kXcds) * kXcds;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t* B, int ldb,
                              int kwrap, int M, int N, int K, const DenseEpilogue& ep,
                              hipStream_t stream, bool packed) {
   dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), block(kThreads);
   const int bk = pick_bk(K, kwrap);
   if (packed && (bk != 64 || N % 32)) return hipErrorInvalidValue;
+  const bool two = (int)grid.x >= persistent_grid();  // at least two workgroups per CU
 #define MOE_LAUNCH_DENSE(BKV, EPIV, PKV)                                                      \
-  hipLaunchKernelGGL((k_gemm_dense<BKV, EPIV, PKV>), grid, block, 0, stream, A, lda, B, ldb,  \
-                     kwrap, M, N, K, ep)
+  do {                                                                                        \
+    if (two)                                                                                  \
+      hipLaunchKernelGGL((k_gemm_dense2<BKV, EPIV, PKV>), grid, block, 0, stream, A, lda, B,  \
+                         ldb, kwrap, M, N, K, ep);                                            \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_gemm_dense<BKV, EPIV, PKV>), grid, block, 0, stream, A, lda, B,   \
+                         ldb, kwrap, M, N, K, ep);                                            \
+  } while (0)
   if (packed) {
     if (epi == kEpiSplit) MOE_LAUNCH_DENSE(64, kEpiSplit, true);
     else if (epi == kEpiLogits) MOE_LAUNCH_DENSE(64, kEpiLogits, true);
@@ -1141,20 +1260,6 @@ hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t
   return hipGetLastError();
 }
 
-// Two persistent workgroups per CU, a multiple of 8 in all (every XCD the
-// same number).
-static int persistent_grid() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8)
-      n = 256;
-    cached[dev] = 2 * (n / kXcds) * kXcds;
-  }
-  return cached[dev];
-}
 
 hipError_t launch_expert_gateup(const uint16_t* hcat, int ldh, const RouteView& rv,
                                 const ExpertsView& ex, uint16_t* act, int inter, int latent,
