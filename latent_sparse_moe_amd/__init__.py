@@ -18,7 +18,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "_lib", "libmoe_latent.so")
+# MOE_LATENT_LIB names another build of the same library (the host-sanitizer copy)
+LIB_PATH = os.environ.get("MOE_LATENT_LIB") or os.path.join(_HERE, "_lib", "libmoe_latent.so")
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 PATH_AUTO, PATH_GROUPED, PATH_DECODE = 0, 1, 2
