@@ -58,8 +58,15 @@ def rec_bytes(L, I, gateup_bits=4):
     return 2 * L * I * gateup_bits // 8 + L * I // 2 + 3 * L * I // 16
 
 
-# decode stages made of more than one kernel
-DECODE_STAGE_KERNELS = {"down": ("k_dec_down", "k_dec_combine")}
+# the kernels that run each stage, by the base name of the kernel template
+# (the first one present in the stored counter run is used)
+DECODE_STAGE_KERNELS = {"dproj": ("k_dec_front",), "router": ("k_dec_router",),
+                        "gateup": ("k_dec_gateup",), "down": ("k_dec_down",),
+                        "uproj": ("k_dec_uproj",)}
+GROUPED_STAGE_KERNELS = {"gateup": ("k_expert_gateup_p", "k_expert_gateup"),
+                         "down": ("k_expert_down_p", "k_expert_down")}
+# workloads whose counter runs traffic.json holds (bench.py --only argument)
+TRAFFIC_WORKLOADS = {"decode145": "decode", "prefill145": "prefill", "prefill120": "prefill120"}
 
 
 def kernel_bytes(d, T, n_routed, decode=True, folded=True):
@@ -148,16 +155,14 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel_prefix):
-    """HBM bytes per launch of a kernel (or the sum over a tuple of kernels
-    that make up one stage) from profiles/traffic.json (written from two
-    rocprofv3 --pmc runs, FETCH_SIZE and WRITE_SIZE, each divided by the
-    factor the same counter reads on the copy kernel), or None when that
-    file is absent, lacks one of them, or was taken on different kernel
-    sources."""
-    if isinstance(kernel_prefix, tuple):
-        parts = [stored_traffic(k) for k in kernel_prefix]
-        return None if any(p is None for p in parts) else sum(parts)
+def stored_traffic(kernels, workload):
+    """HBM bytes per launch of a stage's kernel on one workload, from
+    profiles/traffic.json (two rocprofv3 --pmc runs of that workload,
+    FETCH_SIZE and WRITE_SIZE, each divided by the factor the same counter
+    reads on the copy kernel). kernels: base names of the kernel templates
+    that can run the stage; the first one the counter run saw is used. None
+    when the file is absent, lacks the workload or the kernel, or was taken
+    on different kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as fh:
@@ -166,9 +171,11 @@ def stored_traffic(kernel_prefix):
         return None
     if t.get("source_digest") != source_digest():
         return None
-    for name, k in sorted(t.get("kernels", {}).items()):
-        if name.split("<")[0] == kernel_prefix:
-            return k.get("hbm_bytes_per_launch")
+    seen = t.get("workloads", {}).get(workload, {})
+    for base in kernels:
+        for name, k in sorted(seen.items()):
+            if name.split("<")[0] == base:
+                return k.get("hbm_bytes_per_launch")
     return None
 
 
@@ -198,29 +205,33 @@ def summarize_pmc(path):
 
 
 def write_traffic(d):
-    """HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
-    dispatch), each divided by what the same counter reads per byte on the
-    1 GiB copy kernel."""
+    """HBM bytes per launch of each kernel of each workload: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) from DIR/{workload}_{fetch,write}.csv, each
+    divided by what the same counter reads per byte on the 1 GiB copy kernel
+    (DIR/copy_{fetch,write}.csv)."""
     gib_kib = (1 << 30) / 1024.0
     copy_f = pmc_averages(os.path.join(d, "copy_fetch.csv"))
     copy_w = pmc_averages(os.path.join(d, "copy_write.csv"))
     cf = max(v for (k, c), (n, v) in copy_f.items() if "copyBuffer" in k) / gib_kib
     cw = max(v for (k, c), (n, v) in copy_w.items() if "copyBuffer" in k) / gib_kib
-    kernels = {}
-    for wl in ("decode", "prefill"):
-        f = pmc_averages(os.path.join(d, f"{wl}_fetch.csv"))
-        w = pmc_averages(os.path.join(d, f"{wl}_write.csv"))
+    workloads = {}
+    for wl in TRAFFIC_WORKLOADS:
+        fp, wp = os.path.join(d, f"{wl}_fetch.csv"), os.path.join(d, f"{wl}_write.csv")
+        if not (os.path.exists(fp) and os.path.exists(wp)):
+            continue
+        f, w = pmc_averages(fp), pmc_averages(wp)
+        kernels = {}
         for (k, c), (n, v) in f.items():
             if not k.startswith("k_"):
                 continue
             wv = w.get((k, "WRITE_SIZE"), (0, 0.0))[1]
-            kernels[k] = {"workload": wl, "dispatches": n, "fetch_kib": round(v, 1),
-                          "write_kib": round(wv, 1),
+            kernels[k] = {"dispatches": n, "fetch_kib": round(v, 1), "write_kib": round(wv, 1),
                           "hbm_bytes_per_launch": round((v / cf + wv / cw) * 1024.0)}
+        workloads[wl] = kernels
     out = {"source_digest": source_digest(),
            "calibration": {"copy_bytes": 1 << 30, "fetch_counter_per_byte": cf,
                            "write_counter_per_byte": cw},
-           "kernels": kernels}
+           "workloads": workloads}
     print(json.dumps(out, indent=1))
 
 
@@ -360,8 +371,8 @@ def bench_decode(args, torch, lsm, synth, dev):
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS if achieved else None,
-            "traffic": stored_traffic(DECODE_STAGE_KERNELS.get(dom, "k_dec_" + dom) if use_decode
-                                      else "k_" + dom),
+            "traffic": (stored_traffic(DECODE_STAGE_KERNELS.get(dom, ("k_dec_" + dom,)),
+                                       "decode145") if use_decode else None),
             "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes,
             "kernel_us": dom_ms * 1e3,
         },
@@ -482,8 +493,7 @@ def bench_prefill(args, torch, lsm, synth, dev, name="prefill145"):
         "algorithmic_tflop_per_step": total_flop / 1e12,
         "roofline": {"bound": "mfma", "achieved": dom_tf, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": dom_tf / BF16_PEAK_TFLOPS if dom_tf else None,
-                     "traffic": stored_traffic({"gateup": "k_expert_gateup",
-                                                "down": "k_expert_down"}.get(dom, "")),
+                     "traffic": stored_traffic(GROUPED_STAGE_KERNELS.get(dom, ()), name),
                      "kernel": dom,
                      "kernel_ms": dom_ms},
         "step_ms_with_events": {k: round(v, 4) for k, v in percentiles(step_ms).items()},
