@@ -669,13 +669,12 @@ hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int coun
 }
 
 // Blocks of 32 rows holding the tile's rows (1..4). The last tile of an
-// expert's rows is usually partial; gate/up runs it with 1, 2 or 4 blocks
-// of matrix-core work (at the 16K-token routing this cuts the padded rows
-// from 15% to 4%). Each count has its own copy of the tile body, so nothing
-// stays live across the dispatch. Down keeps one copy (four blocks): its
-// tile body already spills a few registers per lane in the packed layout,
-// and more copies made the K loop spill more, which cost more than the
-// padding.
+// expert's rows is usually partial; gate/up and down run it with 1, 2 or 4
+// blocks of matrix-core work (at the 16K-token routing this cuts the padded
+// rows from 15% to 4%). Each count has its own copy of the tile body, so
+// nothing stays live across the dispatch. With the three copies the
+// one-tile down kernel spills 12 bytes per lane and the persistent one 104,
+// in both outside the K loop (reloads after the steps, before the epilogue).
 __device__ __forceinline__ int row_blocks(const TileWork& tw) {
   return min(4, (tw.rend - tw.rbeg + 31) / 32);
 }
