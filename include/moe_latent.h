@@ -210,7 +210,10 @@ typedef struct moe_route_debug {
  * of 256 with latent <= 1792, inter a multiple of 128 up to 640, and with
  * routing groups n_experts / G a multiple of 16). AUTO picks the decode
  * kernels whenever T and the dims allow it; DECODE with other sizes returns
- * MOE_LATENT_EUNSUPPORTED. */
+ * MOE_LATENT_EUNSUPPORTED. The decode path sums the expert outputs of a
+ * token in 64-bit fixed point (units of 2^-32), exact for |z| < 2^31 per
+ * latent element; a layer whose combined expert output reaches that
+ * magnitude needs the grouped path. */
 #define MOE_LATENT_PATH_AUTO 0
 #define MOE_LATENT_PATH_GROUPED 1
 #define MOE_LATENT_PATH_DECODE 2
