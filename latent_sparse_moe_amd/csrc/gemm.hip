@@ -669,12 +669,13 @@ hipError_t launch_pack_fp4(const uint8_t* codes, const uint8_t* scales, int coun
 }
 
 // Blocks of 32 rows holding the tile's rows (1..4). The last tile of an
-// expert's rows is usually partial; gate/up and down run it with 1, 2 or 4
-// blocks of matrix-core work (at the 16K-token routing this cuts the padded
-// rows from 15% to 4%). Each count has its own copy of the tile body, so
-// nothing stays live across the dispatch. With the three copies the
-// one-tile down kernel spills 12 bytes per lane and the persistent one 104,
-// in both outside the K loop (reloads after the steps, before the epilogue).
+// expert's rows is usually partial; the one-tile kernels run it with 1, 2 or
+// 4 blocks of matrix-core work, the persistent ones with 1, 2, 3 or 4 (at
+// the 16K-token routing this cuts the padded rows from 15% to 4%; at 4096
+// tokens with uniform routing, about 80 rows per expert, three blocks
+// instead of four take a quarter of the work off most tiles). Each count
+// has its own copy of the tile body, so nothing stays live across the
+// dispatch.
 __device__ __forceinline__ int row_blocks(const TileWork& tw) {
   return min(4, (tw.rend - tw.rbeg + 31) / 32);
 }
@@ -1176,6 +1177,7 @@ __device__ __forceinline__ void pkernel(const Op& op) {
     const int nb = row_blocks(cur);
     if (nb == 1) ptile_run<1>(op, cur, n0, shift, has_next, is, aln, bln, ps, s, frag, between);
     else if (nb == 2) ptile_run<2>(op, cur, n0, shift, has_next, is, aln, bln, ps, s, frag, between);
+    else if (nb == 3) ptile_run<3>(op, cur, n0, shift, has_next, is, aln, bln, ps, s, frag, between);
     else ptile_run<4>(op, cur, n0, shift, has_next, is, aln, bln, ps, s, frag, between);
     if (!has_next) break;
     t += nq;

@@ -168,8 +168,8 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
 //   tiles [split[9k+x], split[9k+x+1])). An m-tile's cost is tile_cost of
 //   its row count, the same for each of its n-tiles.
 __device__ __forceinline__ int tile_cost(int rows) {
-  const int nb = (rows + 31) / 32;  // blocks of 32 rows the tile runs with: 1, 2 or 4
-  return nb <= 1 ? 6 : nb <= 2 ? 7 : 10;
+  const int nb = (rows + 31) / 32;  // blocks of 32 rows the tile runs with: 1 to 4
+  return nb <= 1 ? 6 : nb == 2 ? 7 : nb == 3 ? 8 : 10;
 }
 
 // Cost of the m-tiles of a group of cnt > 0 rows: 10 per full tile, the
