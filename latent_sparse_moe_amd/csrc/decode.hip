@@ -1024,11 +1024,17 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMark
       return hipErrorInvalidValue;  // excluded by decode_supported
     } else {
       const int tasks = (1 + a.max_active) * (I / 16);
-      // one workgroup per CU, at most 8 tasks each when fewer suffice, and
-      // at most inter/16 tasks each (so a workgroup's tasks span at most
-      // two slots: the two latent regions of the routing-group staging)
-      const int grid = std::max(std::min(cu_count(), (tasks + kDecWaves - 1) / kDecWaves),
-                                (tasks + I / 16 - 1) / (I / 16));
+      // at most one workgroup per CU: 8 tasks each (one per wave) when that
+      // keeps at least half the CUs busy, else every CU with fewer tasks
+      // each (measured at the 145B shapes: T = 2, 105 workgroups of 8
+      // tasks, 36.1 us per step; 256 of 3 or 4, 33.5 us; at T = 3 and 4 the
+      // 8-task grid is as fast or faster); and at most inter/16 tasks each
+      // (so a workgroup's tasks span at most two slots: the two latent
+      // regions of the routing-group staging)
+      const int cus = cu_count();
+      const int full = (tasks + kDecWaves - 1) / kDecWaves;
+      const int grid =
+          std::max(std::min(cus, full < cus / 2 ? tasks : full), (tasks + I / 16 - 1) / (I / 16));
       const auto fn = k_dec_gateup<2 * n, bits>;
       hipError_t e = ensure_lds((const void*)fn, gateup_lds(kDecodeMaxT, L));
       if (e == hipSuccess)

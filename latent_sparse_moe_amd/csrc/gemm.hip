@@ -902,6 +902,7 @@ struct PGateUp {
   using W = PWeights<PK, BITS>;
   static constexpr int kTileN = kBN / 2;  // SwiGLU columns per tile
   static constexpr int kSplit = 0;
+  static constexpr bool kStagedEpi = false;
   const uint16_t* hcat;
   int ldh;
   RouteView rv;
@@ -931,7 +932,8 @@ struct PGateUp {
     }
   }
   template <int NI>
-  __device__ __forceinline__ void epilogue(const TileWork& tw, int n0, const f32x16 (&acc)[NI][2]) const {
+  __device__ __forceinline__ void epilogue(const TileWork& tw, int n0, const f32x16 (&acc)[NI][2],
+                                           uint16_t* /*stage*/) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int le;
     const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
@@ -960,6 +962,7 @@ struct PDown {
   using W = PWeights<PK, 4>;
   static constexpr int kTileN = kBN;
   static constexpr int kSplit = 1;
+  static constexpr bool kStagedEpi = true;  // the epilogue writes through LDS (below)
   const uint16_t* act;
   RouteView rv;
   ExpertsView ex;
@@ -980,25 +983,42 @@ struct PDown {
       bl.set(j, c, s);
     }
   }
+  // The wave's 128 x 64 outputs go out one 32-row block at a time through
+  // its own 4 KB of the LDS stage that no load is filling (stage): the
+  // accumulators give a lane 8-column pieces of one row (two lanes share a
+  // row), so direct stores would touch 32 rows per instruction; read back
+  // by rows, eight lanes cover one row's 128 bytes and a store instruction
+  // writes eight whole 128-byte lines. The 16-byte chunks of a row are
+  // XOR-swizzled by row. One wave's LDS accesses complete in order, so the
+  // region needs no barrier between blocks; the caller holds a workgroup
+  // barrier before any load may fill the stage again.
   template <int NI>
-  __device__ __forceinline__ void epilogue(const TileWork& tw, int n0, const f32x16 (&acc)[NI][2]) const {
+  __device__ __forceinline__ void epilogue(const TileWork& tw, int n0, const f32x16 (&acc)[NI][2],
+                                           uint16_t* stage) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int le;
     const Fp4Set& set = pick_set(ex, tw.group, rv.n_experts, &le);
     const float gsd = set.down.gscale[le];
     const int nbase = n0 + wave * 64;
+    uint16_t* st = stage + wave * (32 * 64);  // [32 rows][64 columns] bf16
+    const int wr = lane & 31;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int row = tw.rbeg + i * 32 + (lane & 31);
-      if (row >= tw.rend) continue;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const int nc = nbase + j * 32 + acc_col(q, lane);
-          if (nc >= latent) continue;  // latent is a multiple of 32: all eight or none
-          *(uint4*)(y + (size_t)row * latent + nc) = pack_bf16x8(acc[i][j], q, gsd);
+          const int c = 4 * j + 2 * q + (lane >> 5);  // the row's 16-byte chunk (acc_col / 8)
+          *(uint4*)(st + wr * 64 + (c ^ (wr & 7)) * 8) = pack_bf16x8(acc[i][j], q, gsd);
         }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int rr = it * 8 + (lane >> 3), c = lane & 7;
+        const uint4 v = *(const uint4*)(st + rr * 64 + (c ^ (rr & 7)) * 8);
+        const int row = tw.rbeg + i * 32 + rr, nc = nbase + c * 8;
+        // latent is a multiple of 32: a chunk is all in or all out
+        if (row < tw.rend && nc < latent) *(uint4*)(y + (size_t)row * latent + nc) = v;
+      }
     }
   }
 };
@@ -1099,7 +1119,13 @@ __device__ __forceinline__ void ptile_run(const Op& op, const TileWork& tw, int 
   else psteps<2, NI>(KT, has_next, is, aln, bln, ps, shift, frag, acc);
   s = (s + KT) % kPStages;
   between();
-  op.template epilogue<NI>(tw, n0, acc);
+  // the stage of the tile's last step: every wave finished reading it at
+  // that step's barrier, and no load fills it until the next tile's first
+  // step issues its loads (picked by selects: indexing the pointer array at
+  // run time made the compiler spill hundreds of registers)
+  const int sl = (s + 2) % kPStages;
+  op.template epilogue<NI>(tw, n0, acc, sl == 0 ? ps.a[0] : (sl == 1 ? ps.a[1] : ps.a[2]));
+  if constexpr (Op::kStagedEpi) dma_barrier();
 }
 
 template <class Op>
