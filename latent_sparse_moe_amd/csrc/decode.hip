@@ -372,7 +372,7 @@ struct XStage {
 // n_parts K parts: l_part = x_part . (W_hi + W_lo)_part (the bias with part
 // 0). NCH = hidden / 256, NCHR = NCH / n_parts. The workgroups also zero
 // the fixed-point sum the down kernel adds into.
-template <int NCH, int NCHR>
+template <int NCH, int NCHR, int TM>
 __global__ __launch_bounds__(kDecThreads) void k_dec_front(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int H = a.hidden, L = a.latent, T = a.T, E = a.n_experts;
@@ -385,7 +385,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_front(DecodeArgs a) {
   for (int i = blockIdx.x * kDecThreads + tid; i < T * GL; i += gridDim.x * kDecThreads)
     a.zfix[i] = 0ull;  // the down kernel adds into it
   const int nd = GL / 16;
-  XStage<(NCH + 1) / 2> xr;  // T x hidden, hidden = 256 NCH
+  XStage<(TM * NCH + 15) / 16> xr;  // T x hidden, T <= TM, hidden = 256 NCH
   if ((int)blockIdx.x < nd) {
     const int row0 = blockIdx.x * 16;
     const int kb = wave * (H / kDecWaves);
@@ -862,7 +862,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(6, 
 
 // ------------------------------------------------------------------ 4. U
 
-template <int NCH>
+template <int NCH, int TM>
 __global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   const int L = a.latent, H = a.hidden, T = a.T;
@@ -878,7 +878,7 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_uproj(DecodeArgs a) {
     const int kb = grp * L + wave * (L / kDecWaves);
     // z_g = bf16(zfix * 2^-32): thread i converts pairs 2 (i + 512 j) of the
     // T x latent sums (loads issued before the weight loads)
-    constexpr int NZ = (kDecodeMaxT * 256 * NCH / 2 + kDecThreads - 1) / kDecThreads;
+    constexpr int NZ = (TM * 256 * NCH / 2 + kDecThreads - 1) / kDecThreads;  // T <= TM
     ulonglong2 zv[NZ];
 #pragma unroll
     for (int j = 0; j < NZ; ++j) {
@@ -998,7 +998,9 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMark
   err = with_nch(H / 256, [&](auto N) {
     constexpr int n = decltype(N)::value;
     constexpr int nr = n % 2 == 0 ? n / 2 : n;
-    const auto fn = k_dec_front<n, nr>;
+    // x staged for at most 4 or 8 tokens: at T <= 4 half the loads of the
+    // T <= 8 copy would re-read the last slot
+    const auto fn = T <= 4 ? k_dec_front<n, nr, 4> : k_dec_front<n, nr, kDecodeMaxT>;
     hipError_t e = ensure_lds((const void*)fn, front_lds(kDecodeMaxT, H));
     const int grid = a.n_groups * L / 16 + (a.RD ? nparts * (E / 16) : 0);
     if (e == hipSuccess) e = mk.launch(kStageDproj, fn, dim3(grid), block, front_lds(T, H), a);
@@ -1064,9 +1066,10 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMark
   // 4. out = z U^T (+ x)
   return with_nch(L / 256, [&](auto N) {
     constexpr int n = decltype(N)::value;
-    hipError_t e = ensure_lds((const void*)k_dec_uproj<n>, uproj_lds(kDecodeMaxT, L));
+    const auto fn = T <= 4 ? k_dec_uproj<n, 4> : k_dec_uproj<n, kDecodeMaxT>;  // as the front
+    hipError_t e = ensure_lds((const void*)fn, uproj_lds(kDecodeMaxT, L));
     if (e == hipSuccess)
-      e = mk.launch(kStageUproj, k_dec_uproj<n>, dim3((H + 15) / 16), block, uproj_lds(T, L), a);
+      e = mk.launch(kStageUproj, fn, dim3((H + 15) / 16), block, uproj_lds(T, L), a);
     return e;
   });
 }
