@@ -11,6 +11,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -65,6 +67,26 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float s) {
   r[4] = (__bf16)(q2[0] * s); r[5] = (__bf16)(q2[1] * s);
   r[6] = (__bf16)(q3[0] * s); r[7] = (__bf16)(q3[1] * s);
   return r;
+}
+
+// As dequant8, to fp16: e2m1 (at most 2 significant bits, magnitude <= 6)
+// times E4M3 (at most 4 significant bits, 2^-9 <= magnitude <= 448) needs at
+// most 6 significant bits and lies in [2^-10, 2688], inside fp16's normal
+// range, so these products are exact too. The fp16 conversions produce the
+// codes' values as fp16 pairs and one packed fp16 multiply per pair applies
+// the scale: 8 vector ops per 8 weights against 16 for the bf16 route (gfx950
+// has no packed bf16 multiply). s16 = the block scale as fp16 (exact).
+__device__ __forceinline__ f16x8 dequant8_f16(uint32_t codes, _Float16 s16) {
+  const f16x2 ss = {s16, s16};
+  const f16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
+  const f16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
+  const f16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
+  const f16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
+  return f16x8{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Elements 8G .. 8G+7 of a 32-element E1M1 chunk (3-bit codes: sign,

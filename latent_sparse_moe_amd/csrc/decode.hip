@@ -367,8 +367,9 @@ struct XStage {
 // Workgroups [0, G*latent/16) compute h for 16 latent rows each (K split
 // over the 8 waves; with routing groups the rows of every group's D_g) and
 // write bf16(h), plus the low half h - bf16(h) when hlo is set (the
-// unfolded router reads both). With a folded router (a.RD), the
-// next n_parts * E/16 workgroups compute logits for 16 experts over one of
+// unfolded router reads both), and with one routing group bf16(h) as fp16
+// with the workgroup's flag (1 when a value is not exact in fp16). With a
+// folded router (a.RD), the next n_parts * E/16 workgroups compute logits for 16 experts over one of
 // n_parts K parts: l_part = x_part . (W_hi + W_lo)_part (the bias with part
 // 0). NCH = hidden / 256, NCHR = NCH / n_parts. The workgroups also zero
 // the fixed-point sum the down kernel adds into.
@@ -397,13 +398,28 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_front(DecodeArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     wr.mma(xs + min(t, T - 1) * H, kb, g, acc);  // token columns >= T are not stored
     const f32x4 tot = reduce_waves(acc, red);
-    if (wave == 0 && t < T) {
+    if (wave == 0) {
+      bool inexact = false;
+      if (t < T) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = row0 + g * 4 + r;
-        const uint16_t hi = f32_to_bf16_bits(tot[r]);
-        a.hhi[(size_t)t * GL + n] = hi;
-        if (a.hlo) a.hlo[(size_t)t * GL + n] = f32_to_bf16_bits(tot[r] - bf16_bits_to_f32(hi));
+        for (int r = 0; r < 4; ++r) {
+          const int n = row0 + g * 4 + r;
+          const uint16_t hi = f32_to_bf16_bits(tot[r]);
+          const float v = bf16_bits_to_f32(hi);
+          a.hhi[(size_t)t * GL + n] = hi;
+          if (a.hlo) a.hlo[(size_t)t * GL + n] = f32_to_bf16_bits(tot[r] - v);
+          if (a.h16) {
+            // bf16(h) as fp16: exact unless out of range, too small for
+            // fp16's subnormals, or NaN
+            const _Float16 f = (_Float16)v;
+            inexact |= !((float)f == v);
+            a.h16[(size_t)t * L + n] = __builtin_bit_cast(uint16_t, f);
+          }
+        }
+      }
+      if (a.h16) {
+        const bool any = __ballot(inexact) != 0ull;
+        if (lane == 0) a.hflag[blockIdx.x] = any ? 1 : 0;
       }
     }
     return;
@@ -634,7 +650,7 @@ __device__ __forceinline__ void store_gateup(const f32x4& g4, const f32x4& u4, f
 // stream instead of piling up after it (measured at the 145B decode shapes
 // with T = 4: 20.1 us with every chunk issued up front, 17.5 us with
 // W = 2, 18.6 us with 4 and 20.3 us with 8).
-template <int NCH, int BITS>
+template <int NCH, int BITS, bool F16>
 __device__ __forceinline__ void gateup_task(const DecodeArgs& a, const uint16_t* hs, int slot,
                                             int e, int n0) {
   constexpr int W = 2;  // chunk pairs in flight per wave (measured best of 2, 4, 8)
@@ -675,11 +691,22 @@ __device__ __forceinline__ void gateup_task(const DecodeArgs& a, const uint16_t*
     const uint32_t spu = ((g & 2) ? wu.s[i].y : wu.s[i].x) >> (16 * (g & 1));
     const float g0 = e4m3_to_f32(spg & 0xFFu), g1 = e4m3_to_f32((spg >> 8) & 0xFFu);
     const float u0 = e4m3_to_f32(spu & 0xFFu), u1 = e4m3_to_f32((spu >> 8) & 0xFFu);
+    if constexpr (F16) {  // hs holds the token rows as fp16 (all exact)
+      const _Float16 hg0 = (_Float16)g0, hg1 = (_Float16)g1;
+      const _Float16 hu0 = (_Float16)u0, hu1 = (_Float16)u1;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bf16x8 b = *(const bf16x8*)(row + (i * 4 + g) * 32 + q * 8);
-      ag = mfma16x16x32(dequant8(wg.codes8(i, q), q < 2 ? g0 : g1), b, ag);
-      au = mfma16x16x32(dequant8(wu.codes8(i, q), q < 2 ? u0 : u1), b, au);
+      for (int q = 0; q < 4; ++q) {
+        const f16x8 b = *(const f16x8*)(row + (i * 4 + g) * 32 + q * 8);
+        ag = mfma16x16x32_f16(dequant8_f16(wg.codes8(i, q), q < 2 ? hg0 : hg1), b, ag);
+        au = mfma16x16x32_f16(dequant8_f16(wu.codes8(i, q), q < 2 ? hu0 : hu1), b, au);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8 b = *(const bf16x8*)(row + (i * 4 + g) * 32 + q * 8);
+        ag = mfma16x16x32(dequant8(wg.codes8(i, q), q < 2 ? g0 : g1), b, ag);
+        au = mfma16x16x32(dequant8(wu.codes8(i, q), q < 2 ? u0 : u1), b, au);
+      }
     }
   }
   store_gateup(ag, au, gsg, gsu, a.act + (size_t)slot * T * I, I, T, n0, lane);
@@ -709,19 +736,31 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
   for (int i = tid; i < kMaxExperts / 32; i += kDecThreads) rl.flags[i] = 0u;
   const float* lrow = a.logits + (size_t)min(wave, T - 1) * E;
   const bool one_group = a.n_groups == 1;  // the rows are known before the routing
+  // with one group the rows come both as bf16 (region 0) and as fp16
+  // (region 1), and the front's flags say whether the fp16 copy is exact
+  const int nfl = a.h16 ? L / 16 : 0;
+  const int fl = nfl > 0 ? a.hflag[min(tid, nfl - 1)] : 0;  // (the flags exist whenever h16 does)
+  auto stage_rows = [&]() {
+    if (one_group) {
+      stage_dma<NV>(a.hhi, T * L, hs);
+      if (a.h16) stage_dma<NV>(a.h16, T * L, hs + region);
+    }
+  };
   if (E <= 512) {
     float v[8];
     wave_load_keys<8>(lrow, E, T * E, a.n_parts, v);
-    if (one_group) stage_dma<NV>(a.hhi, T * L, hs);
+    stage_rows();
     if (wave < T) wave_topk<8>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
   } else {
     float v[16];
     wave_load_keys<16>(lrow, E, T * E, a.n_parts, v);
-    if (one_group) stage_dma<NV>(a.hhi, T * L, hs);
+    stage_rows();
     if (wave < T) wave_topk<16>(v, E, a.top_k, rl.idx + wave * a.top_k, rl.w + wave * a.top_k);
   }
   __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
-  __syncthreads();
+  // the barrier every thread passes (not under the && below)
+  const int inexact = __syncthreads_or(tid < nfl && fl != 0);
+  const bool use16 = nfl > 0 && !inexact;
   build_active_list(E, T * a.top_k, rl);
   if (blockIdx.x == 0) publish_routing(a, rl);
   const int s0 = a.n_shared ? 0 : 1;  // first live slot
@@ -741,10 +780,19 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
   }
   if (!one_group) __syncthreads();
+  if (use16) {  // one group: every task reads region 1
+    for (int p = p0 + wave; p < p1; p += kDecWaves) {
+      const int slot = s0 + p / tiles;
+      gateup_task<NCH, BITS, true>(a, hs + region, slot, slot == 0 ? 0 : rl.list[slot - 1],
+                                   (p % tiles) * 16);
+    }
+    return;
+  }
   for (int p = p0 + wave; p < p1; p += kDecWaves) {
     const int slot = s0 + p / tiles;
     const uint16_t* rows = hs + (group_of(slot) == ga ? 0 : region);
-    gateup_task<NCH, BITS>(a, rows, slot, slot == 0 ? 0 : rl.list[slot - 1], (p % tiles) * 16);
+    gateup_task<NCH, BITS, false>(a, rows, slot, slot == 0 ? 0 : rl.list[slot - 1],
+                                  (p % tiles) * 16);
   }
 }
 

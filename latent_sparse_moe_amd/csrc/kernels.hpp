@@ -180,6 +180,11 @@ struct DecodeArgs {
   // scratch (workspace)
   uint16_t* hhi;       // [T][G*latent] bf16(h)
   uint16_t* hlo;       // [T][G*latent] h - bf16(h) (unfolded router only; else null)
+  // one routing group only (else null): bf16(h) as fp16 [T][latent], and
+  // one flag per front workgroup of h rows (1: one of its values is not
+  // exact in fp16); with no flag set gate/up takes its fp16 route
+  uint16_t* h16;
+  int* hflag;          // [latent / 16]
   float* logits;       // [n_parts][T][E]
   uint16_t* act;       // [1 + max_active][T][inter]   slot 0: shared expert
   // [T][G*latent] combined expert output in 64-bit fixed point (units of

@@ -57,6 +57,7 @@ struct Layout {
   size_t z;         // bf16 [T][G*latent]
   // decode path (T <= kDecodeMaxT)
   size_t d_hhi, d_hlo;   // bf16 [T][G*latent]
+  size_t d_h16, d_hflag; // fp16 [T][G*latent], int32 [G*latent/16]
   size_t d_logits;       // fp32 [2][T][E]
   size_t d_act;          // bf16 [1 + max_active][T][inter]
   size_t d_zfix;         // int64 [T][G*latent] (fixed point)
@@ -96,6 +97,8 @@ Layout layout_of(const moe_latent_dims& d, int64_t T) {
     const int64_t max_act = d.n_experts < T * d.top_k ? d.n_experts : T * d.top_k;
     L.d_hhi = take(T * GL * 2);
     L.d_hlo = take(T * GL * 2);
+    L.d_h16 = take(T * GL * 2);
+    L.d_hflag = take(GL / 16 * 4 + 4);
     L.d_logits = take(2 * T * d.n_experts * 4);
     L.d_act = take((1 + max_act) * T * d.inter * 2);
     L.d_zfix = take(T * GL * 8);
@@ -103,7 +106,8 @@ Layout layout_of(const moe_latent_dims& d, int64_t T) {
     L.d_list = take(max_act * 4);
     L.d_wtab = take((1 + max_act) * T * 4);
   } else {
-    L.d_hhi = L.d_hlo = L.d_logits = L.d_act = L.d_zfix = L.d_n_act = L.d_list = L.d_wtab = 0;
+    L.d_hhi = L.d_hlo = L.d_h16 = L.d_hflag = L.d_logits = L.d_act = L.d_zfix = L.d_n_act =
+        L.d_list = L.d_wtab = 0;
   }
   L.total = at;
   return L;
@@ -345,6 +349,8 @@ int run_decode(const moe_latent_dims& d, int T, const uint16_t* x, const uint16_
   a.T = T;
   a.hhi = (uint16_t*)(ws + L.d_hhi);
   a.hlo = a.RD ? nullptr : (uint16_t*)(ws + L.d_hlo);
+  a.h16 = a.n_groups == 1 ? (uint16_t*)(ws + L.d_h16) : nullptr;
+  a.hflag = a.n_groups == 1 ? (int*)(ws + L.d_hflag) : nullptr;
   a.logits = (float*)(ws + L.d_logits);
   a.act = (uint16_t*)(ws + L.d_act);
   a.zfix = (unsigned long long*)(ws + L.d_zfix);

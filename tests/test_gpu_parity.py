@@ -217,6 +217,30 @@ def test_decode_path_120b():
     run_case("120b decode-path T=4", host, dl, x, lsm.PATH_DECODE)
 
 
+@pytest.mark.parametrize("folded", [False, True])
+def test_decode_path_bf16_route(folded):
+    """The decode gate/up multiplies in fp16 when every value of bf16(h)
+    converts to fp16 exactly (the front kernel checks and flags), else in
+    bf16. Latent row 0 of D scaled by 2^-20 (exact: a power of two) puts
+    bf16(h)[:, 0] below fp16's subnormal grid for most tokens, so these calls
+    take the bf16 route; the oracle runs on the same scaled layer."""
+    import dataclasses
+    cfg, host0, _ = layer_for("decode145")
+    D = host0.D.copy()
+    row = (D[0].astype(np.uint32) << 16).view(np.float32) * np.float32(2.0 ** -20)
+    D[0] = (row.view(np.uint32) >> 16).astype(np.uint16)
+    host = dataclasses.replace(host0, D=D)
+    x = synth.make_x(4, cfg.dims.hidden, 77)
+    # precondition: some token's bf16(h)[0] is not exact in fp16
+    xf = torch.from_numpy(oracle.bf16_value(x)).double()
+    h0 = (xf @ torch.from_numpy(oracle.bf16_value(D[0])).double()).float().to(torch.bfloat16).float()
+    assert (h0.to(torch.float16).float() != h0).sum() >= 2, h0
+    dl = lsm.DeviceLayer.from_host(host, device())
+    if folded:
+        dl = dl.pack(grouped=False).drop_plain()
+    run_case(f"decode145 row-0 scaled (bf16 route) folded={folded}", host, dl, x, lsm.PATH_DECODE)
+
+
 @pytest.mark.parametrize("variant", ["small", "small_no_shared", "small_hot", "small_k1"])
 def test_decode_path_variants(variant):
     d, bias, zs = DEC_SMALL, "none", 1.1
