@@ -213,7 +213,11 @@ typedef struct moe_route_debug {
  * MOE_LATENT_EUNSUPPORTED. The decode path sums the expert outputs of a
  * token in 64-bit fixed point (units of 2^-32), exact for |z| < 2^31 per
  * latent element; a layer whose combined expert output reaches that
- * magnitude needs the grouped path. */
+ * magnitude needs the grouped path. With one routing group its gate/up
+ * products run in fp16 when every value of bf16(h) converts to fp16
+ * exactly (checked per call), else in bf16: the dequantised weights are
+ * exact in both, so the products are the same and only the order of the
+ * fp32 sums differs between the two. */
 #define MOE_LATENT_PATH_AUTO 0
 #define MOE_LATENT_PATH_GROUPED 1
 #define MOE_LATENT_PATH_DECODE 2
