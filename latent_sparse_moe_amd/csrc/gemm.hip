@@ -432,14 +432,17 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
 // SIMD (about 284 registers), which prefetches the weights a step further
 // and wins when there is only one workgroup per CU anyway (the router: 16K
 // tokens x 512 experts is 256 tiles; 10% faster there).
-template <int BK, int EPI, bool PK, bool TWO>
+// NI: 32-row blocks per tile (4: 128 x 256 tiles; 2: 64 x 256 tiles for
+// small grids, whose A loads still fill the 128-row LDS tile and are half
+// used: twice the workgroups for twice the A traffic).
+template <int BK, int EPI, bool PK, bool TWO, int NI>
 __device__ __forceinline__ void dense_tile(const uint16_t* __restrict__ A, int lda,
                                            const uint16_t* __restrict__ B, int ldb, int kwrap,
                                            int M, int N, int K, const DenseEpilogue& ep) {
   MOE_GEMM_LDS(BK);
   const int nt = (N + kBN - 1) / kBN;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int m0 = (tile / nt) * kBM, n0 = (tile % nt) * kBN;
+  const int m0 = (tile / nt) * (32 * NI), n0 = (tile % nt) * kBN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   ALoader<BK> al;
   al.init([&](int r) { return A + (size_t)min(m0 + r, M - 1) * lda; });
@@ -455,10 +458,10 @@ __device__ __forceinline__ void dense_tile(const uint16_t* __restrict__ A, int l
       bl.set(j, B + (size_t)min(nb + weight_row(lane & 31), N - 1) * ldb + (lane >> 5) * (BK / 2));
     }
   }
-  f32x16 acc[4][2];
-  zero_acc<4>(acc);
-  if (TWO) mainloop_dense<BK, 4>(al, bl, K / BK, pipe, acc);
-  else mainloop<BK, 4>(al, bl, K / BK, pipe, acc);
+  f32x16 acc[NI][2];
+  zero_acc<NI>(acc);
+  if (TWO) mainloop_dense<BK, NI>(al, bl, K / BK, pipe, acc);
+  else mainloop<BK, NI>(al, bl, K / BK, pipe, acc);
 
   const int nbase = n0 + wave * 64;
   // 8-wide stores need the row starts 16-byte aligned
@@ -467,7 +470,7 @@ __device__ __forceinline__ void dense_tile(const uint16_t* __restrict__ A, int l
                        : (ep.ldo & 7) == 0 && (EPI != kEpiSplit || (ep.lo_off & 7) == 0) &&
                              (EPI != kEpiOut || !ep.resid || (ep.ldr & 7) == 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int m = m0 + i * 32 + (lane & 31);
     if (m >= M) continue;
 #pragma unroll
@@ -530,19 +533,19 @@ __device__ __forceinline__ void dense_tile(const uint16_t* __restrict__ A, int l
   }
 }
 
-template <int BK, int EPI, bool PK>
+template <int BK, int EPI, bool PK, int NI = 4>
 __global__ __launch_bounds__(kThreads) void k_gemm_dense(const uint16_t* __restrict__ A, int lda,
                                                          const uint16_t* __restrict__ B, int ldb,
                                                          int kwrap, int M, int N, int K,
                                                          DenseEpilogue ep) {
-  dense_tile<BK, EPI, PK, false>(A, lda, B, ldb, kwrap, M, N, K, ep);
+  dense_tile<BK, EPI, PK, false, NI>(A, lda, B, ldb, kwrap, M, N, K, ep);
 }
 
-template <int BK, int EPI, bool PK>
+template <int BK, int EPI, bool PK, int NI = 4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_dense2(
     const uint16_t* __restrict__ A, int lda, const uint16_t* __restrict__ B, int ldb, int kwrap,
     int M, int N, int K, DenseEpilogue ep) {
-  dense_tile<BK, EPI, PK, true>(A, lda, B, ldb, kwrap, M, N, K, ep);
+  dense_tile<BK, EPI, PK, true, NI>(A, lda, B, ldb, kwrap, M, N, K, ep);
 }
 
 // ------------------------------------------------------------------ grouped
@@ -1257,18 +1260,29 @@ static int persistent_grid() {
 hipError_t launch_gemm_dense(int epi, const uint16_t* A, int lda, const uint16_t* B, int ldb,
                              int kwrap, int M, int N, int K, const DenseEpilogue& ep,
                              hipStream_t stream, bool packed) {
-  dim3 grid(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)), block(kThreads);
+  const int nt = (N + kBN - 1) / kBN;
+  // 64-row tiles when 128-row tiles would fill at most half the CUs
+  // (measured on the 4096-token 120B layer: its router, 64 tiles, 42 -> 32
+  // us; its D, 160 tiles, 53 -> 59 us, so at 160 the 128-row tiles stay)
+  const bool half = nt * ((M + kBM - 1) / kBM) <= persistent_grid() / 4;
+  dim3 grid(nt * ((M + (half ? kBM / 2 : kBM) - 1) / (half ? kBM / 2 : kBM))), block(kThreads);
   const int bk = pick_bk(K, kwrap);
   if (packed && (bk != 64 || N % 32)) return hipErrorInvalidValue;
   const bool two = (int)grid.x >= persistent_grid();  // at least two workgroups per CU
-#define MOE_LAUNCH_DENSE(BKV, EPIV, PKV)                                                      \
-  do {                                                                                        \
-    if (two)                                                                                  \
-      hipLaunchKernelGGL((k_gemm_dense2<BKV, EPIV, PKV>), grid, block, 0, stream, A, lda, B,  \
-                         ldb, kwrap, M, N, K, ep);                                            \
-    else                                                                                      \
-      hipLaunchKernelGGL((k_gemm_dense<BKV, EPIV, PKV>), grid, block, 0, stream, A, lda, B,   \
-                         ldb, kwrap, M, N, K, ep);                                            \
+#define MOE_LAUNCH_DENSE(BKV, EPIV, PKV)                                                       \
+  do {                                                                                         \
+    if (half && two)                                                                           \
+      hipLaunchKernelGGL((k_gemm_dense2<BKV, EPIV, PKV, 2>), grid, block, 0, stream, A, lda, B, \
+                         ldb, kwrap, M, N, K, ep);                                             \
+    else if (half)                                                                             \
+      hipLaunchKernelGGL((k_gemm_dense<BKV, EPIV, PKV, 2>), grid, block, 0, stream, A, lda, B,  \
+                         ldb, kwrap, M, N, K, ep);                                             \
+    else if (two)                                                                              \
+      hipLaunchKernelGGL((k_gemm_dense2<BKV, EPIV, PKV>), grid, block, 0, stream, A, lda, B,   \
+                         ldb, kwrap, M, N, K, ep);                                             \
+    else                                                                                       \
+      hipLaunchKernelGGL((k_gemm_dense<BKV, EPIV, PKV>), grid, block, 0, stream, A, lda, B,    \
+                         ldb, kwrap, M, N, K, ep);                                             \
   } while (0)
   if (packed) {
     if (epi == kEpiSplit) MOE_LAUNCH_DENSE(64, kEpiSplit, true);
