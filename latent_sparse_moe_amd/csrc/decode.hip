@@ -311,8 +311,9 @@ __host__ __device__ inline size_t gateup_region(int T, int L) { return (size_t)T
 inline size_t gateup_lds(int T, int L) { return 2 * gateup_region(T, L) * 2; }
 // a down wave's activation region (elements): T x inter rounded up to 1 KB
 __host__ __device__ inline int down_region(int T, int I) { return (T * I + 511) / 512 * 512; }
-inline size_t down_lds(int T, int I) {
-  return (size_t)kDownGroup * down_region(T, I) * 2 + kRedBytes;
+// rt: latent tiles per wave (the partial sums of each go through LDS)
+inline size_t down_lds(int T, int I, int rt) {
+  return (size_t)kDownGroup * down_region(T, I) * 2 + rt * kRedBytes;
 }
 inline size_t uproj_lds(int T, int L) { return (size_t)T * L * 2 + kRedBytes; }
 
@@ -798,13 +799,14 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
 
 // ------------------------------------------------------------------ 3. down + combine
 
-// Workgroup (16 latent rows r0 .. r0+15, slot group q): wave w takes slot
+// Workgroup (16 RT latent rows from r0, slot group q): wave w takes slot
 // s = 8q + w (slot 0 the shared expert, s >= 1 the s-th active expert;
 // slots past the active ones, and slot 0 without a shared expert, have
 // nothing to do). The wave stages its slot's activations (the matrix-core
-// token operand) into its own LDS region, streams the 16 rows of its
-// slot's down matrix chunk by chunk with the next chunk in flight, and
-// scales the product by the gate weight and the matrix scale. (Reading the
+// token operand) into its own LDS region once, streams the 16 rows of each
+// of its RT latent tiles of the slot's down matrix chunk by chunk with the
+// next chunk in flight (across the tiles too), and scales the products by
+// the gate weight and the matrix scale. (Reading the
 // token operand straight from L2 instead took four 16-byte loads per lane
 // and chunk, three quarters of them repeats at T = 4: 12.4 us for the
 // 145B layer at T = 4.) The eight
@@ -815,8 +817,8 @@ __global__ __launch_bounds__(kDecThreads) void k_dec_gateup(DecodeArgs a) {
 // Held to at most 85 registers (six waves per SIMD) so that three
 // workgroups share a CU and the grid of (latent/16) x groups workgroups
 // runs in one round at T = 4 (672 workgroups, 768 resident); at 94
-// registers it took two.
-template <int NCH>
+// registers it took two. Each of the RT tiles has its own LDS sums.
+template <int NCH, int RT>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_dec_down(
     DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // 8 activation regions, red
@@ -825,8 +827,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(6, 
   const int GL = a.n_groups * L, epg = a.n_experts / a.n_groups;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, t = lane & 15;
-  const int ntile = L / 16;
-  const int r0 = (blockIdx.x % ntile) * 16, q = blockIdx.x / ntile;
+  const int ntile = L / (16 * RT);
+  const int r0 = (blockIdx.x % ntile) * 16 * RT, q = blockIdx.x / ntile;
   const int region = down_region(T, I);
   float* red = (float*)(lds + kDownGroup * region);
   // the routing table, read together (clamped indices; used only when live)
@@ -836,7 +838,9 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(6, 
   const int e_guess = a.route_list[max(sc - 1, 0)];
   const float w_guess = a.route_wtab[sc * T + min(t, T - 1)];
   if (q >= (n_act + kDownGroup) / kDownGroup) return;  // uniform over the workgroup
-  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+  f32x4 y[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) y[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool live = (s > 0 || a.n_shared) && s <= n_act;
   if (lane == 0) wgrp[wave] = live ? (s == 0 ? 0 : e_guess / epg) : -1;
   if (live) {  // uniform over the wave
@@ -849,62 +853,74 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(6, 
     uint16_t* act = lds + wave * region;
     stage_dma_wave<2 * NCH>(a.act + (size_t)s * T * I, T * I, act);
     issue_fence();
-    const Fp4Lane l = fp4_lane(dm, a.packed, e, L, I, r0, 0);
-    Fp4Rows<NCH> wd;
+    Fp4Lane l[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) l[rt] = fp4_lane(dm, a.packed, e, L, I, r0 + 16 * rt, 0);
+    Fp4Rows<NCH * RT> wd;  // chunk i: tile i / NCH, chunk i % NCH of its row
     // software-pipelined as in the gate/up kernel: the next chunk is in
-    // flight while one is multiplied
+    // flight while one is multiplied (across the tiles too)
     auto ld = [&](int i) {
-      const uint4 v = *(const uint4*)(l.c + i * l.cstep);
+      const Fp4Lane& lt = l[i / NCH];
+      const int c = i % NCH;
+      const uint4 v = *(const uint4*)(lt.c + c * lt.cstep);
       wd.c[i][0] = v.x; wd.c[i][1] = v.y; wd.c[i][2] = v.z; wd.c[i][3] = v.w;
-      wd.s[i] = *(const uint2*)(l.s + i * l.sstep);
+      wd.s[i] = *(const uint2*)(lt.s + c * lt.sstep);
     };
     ld(0);
     issue_fence();
     wait_vmcnt<2>();  // everything but chunk 0's two loads: the staged rows have landed
     const uint16_t* arow = act + min(t, T - 1) * I;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
+    for (int i = 0; i < NCH * RT; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < NCH) ld(i + 1);
+      if (i + 1 < NCH * RT) ld(i + 1);
       __builtin_amdgcn_sched_barrier(0);
+      const int c = i % NCH;
       const uint32_t sp = ((g & 2) ? wd.s[i].y : wd.s[i].x) >> (16 * (g & 1));
       const float s0 = e4m3_to_f32(sp & 0xFFu), s1 = e4m3_to_f32((sp >> 8) & 0xFFu);
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        y = mfma16x16x32(dequant8(wd.codes8(i, k), k < 2 ? s0 : s1),
-                         *(const bf16x8*)(arow + (i * 4 + g) * 32 + k * 8), y);
+        y[i / NCH] = mfma16x16x32(dequant8(wd.codes8(i, k), k < 2 ? s0 : s1),
+                                  *(const bf16x8*)(arow + (c * 4 + g) * 32 + k * 8), y[i / NCH]);
     }
     const float sw = w_guess * gs;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] *= sw;
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[rt][r] *= sw;
   }
-  *(f32x4*)(red + (wave * 64 + lane) * 4) = y;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) *(f32x4*)(red + ((rt * kDecWaves + wave) * 64 + lane) * 4) = y[rt];
   __syncthreads();
   if (wave == 0 && t < T) {
     // the slots' products in slot order, one sum per run of slots of one
     // routing group (slots are in ascending expert order, so a group's
     // slots are adjacent), each added into that group's z
-    auto flush = [&](const f32x4& tot, int grp) {
-      unsigned long long* zp = a.zfix + (size_t)t * GL + (size_t)grp * L + r0 + g * 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const long long fx = (long long)__builtin_rintf(tot[r] * 4294967296.0f);
-        __hip_atomic_fetch_add(zp + r, (unsigned long long)fx, __ATOMIC_RELAXED, AGENT);
+    for (int rt = 0; rt < RT; ++rt) {
+      auto flush = [&](const f32x4& tot, int grp) {
+        unsigned long long* zp =
+            a.zfix + (size_t)t * GL + (size_t)grp * L + r0 + 16 * rt + g * 4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const long long fx = (long long)__builtin_rintf(tot[r] * 4294967296.0f);
+          __hip_atomic_fetch_add(zp + r, (unsigned long long)fx, __ATOMIC_RELAXED, AGENT);
+        }
+      };
+      f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+      int cur = -1;
+      for (int w = 0; w < kDecWaves; ++w) {
+        const int gw = wgrp[w];
+        if (gw < 0) continue;
+        if (gw != cur) {
+          if (cur >= 0) flush(tot, cur);
+          tot = f32x4{0.f, 0.f, 0.f, 0.f};
+          cur = gw;
+        }
+        tot += *(const f32x4*)(red + ((rt * kDecWaves + w) * 64 + lane) * 4);
       }
-    };
-    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-    int cur = -1;
-    for (int w = 0; w < kDecWaves; ++w) {
-      const int gw = wgrp[w];
-      if (gw < 0) continue;
-      if (gw != cur) {
-        if (cur >= 0) flush(tot, cur);
-        tot = f32x4{0.f, 0.f, 0.f, 0.f};
-        cur = gw;
-      }
-      tot += *(const f32x4*)(red + (w * 64 + lane) * 4);
+      if (cur >= 0) flush(tot, cur);
     }
-    if (cur >= 0) flush(tot, cur);
   }
 }
 
@@ -1015,7 +1031,7 @@ bool decode_supported(int hidden, int latent, int inter, int n_experts, int top_
   const size_t lim = 96 * 1024;
   return front_lds(kDecodeMaxT, hidden) <= lim && router_lds(kDecodeMaxT, latent) <= lim &&
          gateup_lds(kDecodeMaxT, latent) + sizeof(RouteLds) <= lim &&
-         down_lds(kDecodeMaxT, inter) <= lim && uproj_lds(kDecodeMaxT, latent) <= lim;
+         down_lds(kDecodeMaxT, inter, 2) <= lim && uproj_lds(kDecodeMaxT, latent) <= lim;
 }
 
 int decode_front_parts(int hidden) { return (hidden / 256) % 2 == 0 ? 2 : 1; }
@@ -1103,10 +1119,15 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t st, const StageMark
     if constexpr (n > 7) {
       return hipErrorInvalidValue;  // excluded by decode_supported
     } else {
-      const int grid = (L / 16) * decode_down_groups(a.max_active);
-      hipError_t e = ensure_lds((const void*)k_dec_down<n>, down_lds(kDecodeMaxT, I));
-      if (e == hipSuccess)
-        e = mk.launch(kStageDown, k_dec_down<n>, dim3(grid), block, down_lds(T, I), a);
+      // from T = 5 a slot's staged activations (T x inter) outweigh the
+      // wave's 16 weight rows, so each wave takes two latent tiles of its
+      // slot and stages them once (measured at the 145B shapes: T = 5
+      // 46.3 -> 45.3 us, T = 8 68.7 -> 65.5 us per step; T <= 4 slower)
+      const int rt = (T >= 5 && (L / 16) % 2 == 0) ? 2 : 1;
+      const int grid = (L / (16 * rt)) * decode_down_groups(a.max_active);
+      const auto fn = rt == 2 ? k_dec_down<n, 2> : k_dec_down<n, 1>;
+      hipError_t e = ensure_lds((const void*)fn, down_lds(kDecodeMaxT, I, rt));
+      if (e == hipSuccess) e = mk.launch(kStageDown, fn, dim3(grid), block, down_lds(T, I, rt), a);
       return e;
     }
   });
