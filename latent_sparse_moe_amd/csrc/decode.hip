@@ -12,29 +12,33 @@
 //                  gives l = x W^T = (x D^T) R^T. Without a folded router the
 //                  logits come from h in a second launch (dec_dproj writes h
 //                  as bf16 hi + lo, dec_router reads both halves).
-//   2. dec_gateup  one workgroup per CU; each takes the top-k of every token
-//                  from the logits and builds the active-expert list
-//                  (workgroup 0 publishes the routing table); then the
+//   2. dec_gateup  at most one workgroup per CU; each takes the top-k of
+//                  every token from the logits and builds the active-expert
+//                  list (workgroup 0 publishes the routing table); then the
 //                  (expert slot, 16 intermediate rows) tasks are split
 //                  evenly over the grid, one per wave at a time: the gate
 //                  and the up tile over the whole latent width, SiLU * up
-//                  in registers. Slot 0 is the shared expert.
-//   3. dec_down    one workgroup per (16 latent rows, group of 8 slots), one
-//                  slot per wave; the weighted products are summed in slot
-//                  order and added into z in 64-bit fixed point with
-//                  integer atomics (exact, so the arrival order does not
-//                  matter)
+//                  in registers. Slot 0 is the shared expert. With one
+//                  routing group the products run in fp16 when the front
+//                  kernel found every value of bf16(h) exact in fp16.
+//   3. dec_down    one workgroup per (16 or 32 latent rows, group of 8
+//                  slots), one slot per wave; the weighted products are
+//                  summed in slot order and added into z in 64-bit fixed
+//                  point with integer atomics (exact, so the arrival order
+//                  does not matter)
 //   4. dec_uproj   out = bf16(z) U^T (+ x)
 //
-// Matrix-core tiles are v_mfma_f32_16x16x32_bf16 with weight rows as the M
-// operand (16 rows) and tokens as the N operand (16 columns, T used; the rest
-// repeat token T - 1 and are never stored, so no operand load is
-// conditional). Lane l serves weight row l%16; its lane group g = l/16 takes
-// every fourth chunk of the wave's K range (chunk c*4 + g at step c), so one
-// load instruction reads 64 contiguous bytes of each of 16 rows (1 KB of
-// contiguous memory on the decode-packed copies). K order inside a dot
+// Matrix-core tiles are v_mfma_f32_16x16x32_bf16 (or _f16) with weight rows
+// as the M operand (16 rows) and tokens as the N operand (16 columns, T
+// used; the rest repeat token T - 1 and are never stored, so no operand load
+// is conditional). Lane l serves weight row l%16; its lane group g = l/16
+// takes every fourth chunk of the wave's K range (chunk c*4 + g at step c),
+// so one load instruction reads 64 contiguous bytes of each of 16 rows (1 KB
+// of contiguous memory on the decode-packed copies). K order inside a dot
 // product is free; the token operand is read with the same chunk mapping.
-// Every wave issues all its weight loads before its first product.
+// The expert weight streams keep the next chunks' loads in flight while one
+// is dequantised and multiplied; D, U and the router issue all their weight
+// loads before their first product.
 #include <limits.h>
 
 #include <map>
@@ -370,10 +374,11 @@ struct XStage {
 // write bf16(h), plus the low half h - bf16(h) when hlo is set (the
 // unfolded router reads both), and with one routing group bf16(h) as fp16
 // with the workgroup's flag (1 when a value is not exact in fp16). With a
-// folded router (a.RD), the next n_parts * E/16 workgroups compute logits for 16 experts over one of
-// n_parts K parts: l_part = x_part . (W_hi + W_lo)_part (the bias with part
-// 0). NCH = hidden / 256, NCHR = NCH / n_parts. The workgroups also zero
-// the fixed-point sum the down kernel adds into.
+// folded router (a.RD), the next n_parts * E/16 workgroups compute logits
+// for 16 experts over one of n_parts K parts: l_part = x_part . (W_hi +
+// W_lo)_part (the bias with part 0). NCH = hidden / 256, NCHR = NCH /
+// n_parts, TM >= T (the x staging's size). The workgroups also zero the
+// fixed-point sum the down kernel adds into.
 template <int NCH, int NCHR, int TM>
 __global__ __launch_bounds__(kDecThreads) void k_dec_front(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
